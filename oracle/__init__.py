@@ -1,0 +1,63 @@
+"""CPU oracle of the sparse-MoE layer forward -- TEST INFRASTRUCTURE ONLY.
+
+This package is the slow, plain, obviously-correct statement of what the GPU
+path computes.  Only the test suite, the smoke check of ``__graft_entry__`` and
+the ``cpu_baseline`` leg of ``bench.py`` may import it.  The library and its
+Python binding never call it, and it shares no code with them: the two meet
+only in the seeded inputs of the ``synth`` package.
+
+Precision: everything that is compared with a tolerance is computed in float64
+(numpy matmul as the only library primitive).  The weighted combine, which the
+pages make part of the numerical contract (operand conversion, accumulator
+precision and reduction order), is emulated exactly in float32 with one IEEE
+rounding per operation.
+
+Pins (the tests that tie each function to something other than itself):
+  router_logits      exact rational dot products on the tiny layer; one-hot/zero rows
+  scores             torch.softmax / torch.sigmoid (library routines)
+  select_topk        O(E^2) dominance count, exhaustive K-subsets, closed-form ties
+  topk_weights       sum = route_scale, top-1 renorm = 1, zero row = 1/K
+  permute            numpy stable argsort; bijection and segment invariants
+  expert_mlp         dense all-experts formulation with torch.nn.functional.silu;
+                     E=1, K=1 reduces to a dense SwiGLU MLP
+  round_bf16         exact rational round-half-even; torch's float32->bfloat16 cast
+  combine_fp32       exact rational arithmetic rounded to float32 per operation;
+                     720-order enumeration (360 classes) printed by the arXiv abstract
+No function is parity-unpinned.
+"""
+
+from .moe import (
+    EXEMPT_REL_MARGIN,
+    OracleResult,
+    bf16_bits_of,
+    combine_fp32,
+    combine_orders,
+    expert_mlp,
+    forward,
+    permute,
+    round_bf16,
+    router_logits,
+    scores,
+    select_topk,
+    silu,
+    topk_weights,
+    widen,
+)
+
+__all__ = [
+    "EXEMPT_REL_MARGIN",
+    "OracleResult",
+    "bf16_bits_of",
+    "combine_fp32",
+    "combine_orders",
+    "expert_mlp",
+    "forward",
+    "permute",
+    "round_bf16",
+    "router_logits",
+    "scores",
+    "select_topk",
+    "silu",
+    "topk_weights",
+    "widen",
+]

@@ -1,0 +1,398 @@
+"""Pins of the CPU oracle to things other than itself (CPU only).
+
+Each test ties one oracle function to an independent statement of the same
+fact: exact rational arithmetic, a library routine, a brute-force search, a
+closed form, or a number the pages print.
+"""
+
+import itertools
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import get_config, make_inputs
+from synth.configs import TIE_TOKENS
+from tests.oracle_bridge import oracle_forward
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------- exact rounding
+
+def _round_rational(q: Fraction, p: int) -> Fraction:
+    """Round a rational to p significant bits, ties to even (normal range only)."""
+    if q == 0:
+        return Fraction(0)
+    sign = -1 if q < 0 else 1
+    a = abs(q)
+    e = a.numerator.bit_length() - a.denominator.bit_length() - p
+    while a / Fraction(2) ** e >= 2 ** p:
+        e += 1
+    while a / Fraction(2) ** e < 2 ** (p - 1):
+        e -= 1
+    m = a / Fraction(2) ** e
+    n = m.numerator // m.denominator
+    r = m - n
+    if r > Fraction(1, 2) or (r == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    return sign * n * Fraction(2) ** e
+
+
+def _r32(q):
+    return _round_rational(q, 24)
+
+
+def _rbf16(q):
+    return _round_rational(q, 8)
+
+
+def test_round_bf16_matches_exact_rational():
+    rng = np.random.default_rng(11)
+    vals = list(rng.standard_normal(2000) * 10.0 ** rng.integers(-6, 6, 2000))
+    # exact midpoints between neighbouring bf16 values, with even and odd lower neighbour
+    for sig in (128, 129, 200, 201, 254, 255):
+        for ex in (-20, -3, 0, 5):
+            vals.append((sig + 0.5) * 2.0 ** ex)
+            vals.append(-(sig + 0.5) * 2.0 ** ex)
+    v = np.array(vals, dtype=np.float64)
+    got = oracle.round_bf16(v)
+    for a, g in zip(v, got):
+        assert Fraction(float(g)) == _rbf16(Fraction(float(a)))
+
+
+def test_round_bf16_is_one_rounding_from_float64():
+    # (129 + 1/2 + 2^-30) * 2^-7 lies just above a bf16 midpoint: a direct rounding goes
+    # up to 130, while rounding to float32 first lands exactly on the midpoint and then
+    # rounds to the even neighbour 129.
+    v = np.array([(129.5 + 2.0 ** -30) * 2.0 ** -7])
+    assert float(np.float32(v[0])) == 129.5 * 2.0 ** -7
+    assert oracle.round_bf16(v)[0] == 130.0 * 2.0 ** -7
+
+
+def test_bf16_bits_match_torch_cast():
+    rng = np.random.default_rng(12)
+    a = (rng.standard_normal(100000) * 10.0 ** rng.integers(-8, 8, 100000)).astype(np.float32)
+    bits = a.view(np.uint32)
+    # force many exact float32 -> bf16 ties
+    a2 = ((bits & np.uint32(0xFFFF0000)) | np.uint32(0x8000)).view(np.float32)
+    for arr in (a, a2):
+        ours = oracle.bf16_bits_of(arr)
+        ref = torch.from_numpy(arr).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        np.testing.assert_array_equal(ours, ref)
+
+
+# ---------------------------------------------------------------- routing
+
+def test_router_logits_match_exact_rational():
+    cfg = get_config("tiny")
+    inp = make_inputs(cfg)
+    x64, wr64 = oracle.widen(inp.x), oracle.widen(inp.w_router)
+    lg = oracle.router_logits(x64, wr64)
+    D = cfg.D
+    u = 2.0 ** -53
+    gamma = D * u / (1 - D * u)
+    for t in (0, 1, 2, 40, 63):
+        for e in range(cfg.E):
+            exact = sum(Fraction(float(a)) * Fraction(float(b)) for a, b in zip(x64[t], wr64[e]))
+            bound = gamma * float(np.sum(np.abs(x64[t] * wr64[e])))
+            assert abs(Fraction(float(lg[t, e])) - exact) <= Fraction(bound)
+    # one-hot and zero rows: logits are exactly a router column, or exactly zero
+    assert np.all(lg[5] == 0.0)
+    for t, col in ((17, 0), (33, 1), (60, 2)):
+        np.testing.assert_array_equal(lg[t], wr64[:, col])
+
+
+def test_scores_match_torch():
+    rng = np.random.default_rng(13)
+    lg = rng.standard_normal((64, 256)) * 3.0
+    sm = oracle.scores(lg, "softmax")
+    sg = oracle.scores(lg, "sigmoid")
+    np.testing.assert_allclose(sm, torch.softmax(torch.from_numpy(lg), dim=1).numpy(), rtol=1e-13, atol=0)
+    np.testing.assert_allclose(sg, torch.sigmoid(torch.from_numpy(lg)).numpy(), rtol=1e-13, atol=0)
+    with pytest.raises(ValueError):
+        oracle.scores(lg, "sqrtsoftplus")
+
+
+def test_silu_matches_torch():
+    v = np.concatenate([np.linspace(-800, 800, 4001), np.random.default_rng(14).standard_normal(1000)])
+    np.testing.assert_allclose(oracle.silu(v), torch.nn.functional.silu(torch.from_numpy(v)).numpy(),
+                               rtol=1e-14, atol=1e-300)
+
+
+@pytest.mark.parametrize("K", [1, 2, 3, 5, 8])
+def test_select_topk_matches_dominance_count(K):
+    E = 8
+    rng = np.random.default_rng(100 + K)
+    c = rng.integers(0, 4, size=(500, E)) / 4.0   # many exact ties
+    ids, _ = oracle.select_topk(c, K)
+    for t in range(c.shape[0]):
+        rank = [sum(1 for j in range(E) if c[t, j] > c[t, e] or (c[t, j] == c[t, e] and j < e))
+                for e in range(E)]
+        brute = sorted(e for e in range(E) if rank[e] < K)
+        assert list(ids[t]) == brute
+
+
+def test_select_topk_matches_exhaustive_subsets():
+    E, K = 8, 3
+    rng = np.random.default_rng(7)
+    c = rng.integers(-2, 3, size=(200, E)).astype(np.float64)
+    ids, _ = oracle.select_topk(c, K)
+
+    def beats(t, i, j):
+        return c[t, i] > c[t, j] or (c[t, i] == c[t, j] and i < j)
+
+    for t in range(c.shape[0]):
+        good = [S for S in itertools.combinations(range(E), K)
+                if all(beats(t, i, j) for i in S for j in range(E) if j not in S)]
+        assert len(good) == 1
+        assert tuple(ids[t]) == good[0]
+
+
+def test_negative_zero_ties_positive_zero():
+    c = np.array([[0.0, -0.0, -0.0, 0.0, -1.0]])
+    ids, margin = oracle.select_topk(c, 2)
+    assert list(ids[0]) == [0, 1]
+    assert margin[0] == 0.0
+
+
+def test_tiny_tie_tokens_closed_form():
+    cfg = get_config("tiny")
+    res = oracle_forward(make_inputs(cfg))
+    # token 5: zero row, eight-way tie -> the two lowest ids, weights exactly 1/2
+    assert list(res.ids[5]) == [0, 1]
+    assert list(res.weights[5]) == [0.5, 0.5]
+    # token 17: expert 1 first, experts 2 and 3 tie for rank 2 -> {1, 2}
+    assert list(res.ids[17]) == [1, 2]
+    # token 33: experts 1 and 3 tie at the top -> {1, 3}, equal weights
+    assert list(res.ids[33]) == [1, 3]
+    assert res.weights[33, 0] == res.weights[33, 1] == 0.5
+    # token 60: expert 0 first, experts 2, 4, 6 tie for rank 2 -> {0, 2}
+    assert list(res.ids[60]) == [0, 2]
+    # ties across the K-th/(K+1)-th boundary have zero margin and are never exempt;
+    # token 33's tie sits inside the top-2, so its boundary margin is positive
+    for t in (5, 17, 60):
+        assert res.rel_margin[t] == 0.0
+    assert res.rel_margin[33] > 1e-3
+    assert not res.exempt[list(TIE_TOKENS)].any()
+
+
+def test_exemption_flags_near_ties_only():
+    c = np.array([[1.0, 1.0 - 5e-7, 0.5],       # rel margin 5e-7: exempt
+                  [1.0, 1.0 - 5e-6, 0.5],       # 5e-6: not exempt
+                  [1.0, 1.0, 0.5]])             # exact tie: not exempt
+    _, m = oracle.select_topk(c, 1)
+    ex = (m > 0) & (m < oracle.EXEMPT_REL_MARGIN)
+    assert list(ex) == [True, False, False]
+    np.testing.assert_allclose(m[:2], [5e-7, 5e-6], rtol=1e-9)
+
+
+def test_weights_sum_to_route_scale():
+    rng = np.random.default_rng(15)
+    s = oracle.scores(rng.standard_normal((300, 256)), "sigmoid")
+    ids, _ = oracle.select_topk(s + rng.uniform(-0.05, 0.05, 256)[None, :], 6)
+    w = oracle.topk_weights(s, ids, True, 2.5)
+    np.testing.assert_allclose(w.sum(axis=1), 2.5, rtol=0, atol=1e-12)
+    # weights come from the unbiased scores
+    np.testing.assert_allclose(w / 2.5 * np.take_along_axis(s, ids, 1).sum(1, keepdims=True),
+                               np.take_along_axis(s, ids, 1), rtol=1e-13)
+
+
+def test_top1_renorm_is_one_and_zero_row_is_uniform():
+    rng = np.random.default_rng(16)
+    s = oracle.scores(rng.standard_normal((50, 16)), "softmax")
+    ids, _ = oracle.select_topk(s, 1)
+    assert np.all(oracle.topk_weights(s, ids, True, 1.0) == 1.0)
+    for K in (1, 2, 4, 8):
+        s0 = oracle.scores(np.zeros((1, 16)), "softmax")
+        ids0, _ = oracle.select_topk(s0, K)
+        assert list(ids0[0]) == list(range(K))
+        assert np.all(oracle.topk_weights(s0, ids0, True, 1.0) == 1.0 / K)
+
+
+def test_no_renorm_weight_is_the_softmax_probability():
+    cfg = get_config("dspark", T=64)
+    inp = make_inputs(cfg)
+    res = oracle_forward(inp)
+    p = torch.softmax(torch.from_numpy(res.logits), dim=1).numpy()
+    np.testing.assert_allclose(res.weights[:, 0], np.take_along_axis(p, res.ids, 1)[:, 0], rtol=1e-13)
+    assert np.all(res.weights < 1.0)
+    # the bias moved the choice but not the weight
+    assert not np.array_equal(np.argmax(res.scores, axis=1), res.ids[:, 0])
+
+
+# ---------------------------------------------------------------- dispatch
+
+def test_permutation_matches_stable_argsort_and_invariants():
+    rng = np.random.default_rng(17)
+    T, E, K = 777, 37, 5
+    ids = np.sort(np.stack([rng.choice(E, K, replace=False) for _ in range(T)]), axis=1).astype(np.int32)
+    masked = rng.random(T) < 0.1
+    ids[masked] = -1
+    pm = oracle.permute(ids, E)
+    t_of = np.repeat(np.arange(T), K)
+    e_of = ids.reshape(-1)
+    keep = e_of >= 0
+    order = np.argsort(e_of[keep].astype(np.int64) * T + t_of[keep], kind="stable")
+    np.testing.assert_array_equal(pm["perm_token"], t_of[keep][order])
+    np.testing.assert_array_equal(pm["counts"], np.bincount(e_of[keep], minlength=E))
+    assert pm["offsets"][0] == 0 and pm["offsets"][E] == keep.sum()
+    inv = pm["inv_pos"]
+    assert np.all(inv[masked] == -1)
+    pos = inv[~masked].reshape(-1)
+    assert sorted(pos.tolist()) == list(range(keep.sum()))      # bijection
+    for t in np.nonzero(~masked)[0][:200]:
+        for j in range(K):
+            assert pm["perm_token"][inv[t, j]] == t
+            e = ids[t, j]
+            assert pm["offsets"][e] <= inv[t, j] < pm["offsets"][e + 1]
+    for e in range(E):
+        seg = pm["perm_token"][pm["offsets"][e]:pm["offsets"][e + 1]]
+        assert np.all(np.diff(seg) > 0)
+
+
+# ---------------------------------------------------------------- expert MLP
+
+def _torch_swiglu(x, w1, w2):
+    I = w2.shape[1]
+    h = x @ w1.T
+    return (torch.nn.functional.silu(h[:, :I]) * h[:, I:]) @ w2.T
+
+
+def test_layer_matches_dense_all_experts_formulation():
+    cfg = get_config("tiny")
+    inp = make_inputs(cfg)
+    res = oracle_forward(inp)
+    x = torch.from_numpy(oracle.widen(inp.x))
+    gate = torch.zeros(cfg.T, cfg.E, dtype=torch.float64)
+    for t in range(cfg.T):
+        for j in range(cfg.K):
+            gate[t, res.ids[t, j]] = res.weights[t, j]
+    dense = torch.zeros(cfg.T, cfg.D, dtype=torch.float64)
+    for e in range(cfg.E):
+        ye = _torch_swiglu(x, torch.from_numpy(oracle.widen(inp.w_gate_up[e])),
+                           torch.from_numpy(oracle.widen(inp.w_down[e])))
+        dense += gate[:, e:e + 1] * ye
+    rms = float(torch.sqrt(torch.mean(dense ** 2)))
+    assert float(torch.max(torch.abs(dense - torch.from_numpy(res.out)))) <= 1e-12 * rms
+
+
+def test_single_expert_top1_is_a_dense_swiglu_mlp():
+    rng = np.random.default_rng(18)
+    T, D, I = 40, 64, 96
+    x = rng.standard_normal((T, D)).astype(np.float32)
+    wr = rng.standard_normal((1, D)).astype(np.float32)
+    w1 = (rng.standard_normal((1, 2 * I, D)) * 0.1).astype(np.float32)
+    w2 = (rng.standard_normal((1, D, I)) * 0.1).astype(np.float32)
+    res = oracle.forward(x, wr, w1, w2, K=1, score="softmax", renorm=True, route_scale=1.0,
+                         bf16_mode=False)
+    assert np.all(res.weights == 1.0)
+    ref = _torch_swiglu(torch.from_numpy(x.astype(np.float64)), torch.from_numpy(w1[0].astype(np.float64)),
+                        torch.from_numpy(w2[0].astype(np.float64))).numpy()
+    np.testing.assert_allclose(res.out, ref, rtol=1e-12, atol=1e-14)
+
+
+def test_shared_expert_added_on_every_kept_token():
+    cfg = get_config("tiny")
+    inp = make_inputs(cfg)
+    rng = np.random.default_rng(19)
+    w1s = (rng.standard_normal((2 * 64, cfg.D)) * 0.02).astype(np.float32)
+    w2s = (rng.standard_normal((cfg.D, 64)) * 0.02).astype(np.float32)
+    mask = np.ones(cfg.T, dtype=np.uint8)
+    mask[[3, 9]] = 0
+    base = oracle_forward(inp, mask=mask)
+    inp.w_gate_up_s, inp.w_down_s = w1s, w2s
+    with_s = oracle_forward(inp, mask=mask)
+    sh = _torch_swiglu(torch.from_numpy(oracle.widen(inp.x)), torch.from_numpy(w1s.astype(np.float64)),
+                       torch.from_numpy(w2s.astype(np.float64))).numpy()
+    sh[[3, 9]] = 0.0
+    np.testing.assert_allclose(with_s.out - base.out, sh, rtol=1e-10, atol=1e-15)
+    assert np.all(with_s.out[[3, 9]] == 0.0)
+    assert np.all(with_s.ids[[3, 9]] == -1) and with_s.offsets[-1] == (cfg.T - 2) * cfg.K
+
+
+def test_bf16_mode_rounds_activation_and_output():
+    cfg = get_config("dspark", T=16)
+    inp = make_inputs(cfg)
+    res = oracle_forward(inp)
+    assert np.array_equal(oracle.round_bf16(res.y), res.y)      # expert outputs on the bf16 grid
+
+
+# ---------------------------------------------------------------- combine
+
+def test_combine_matches_exact_rational_per_operation():
+    rng = np.random.default_rng(20)
+    T, K, D = 5, 6, 24
+    y = oracle.bf16_bits_of(rng.standard_normal((T * K, D)).astype(np.float32))
+    inv = rng.permutation(T * K).reshape(T, K).astype(np.int32)
+    w = rng.uniform(0.0, 1.0, (T, K)).astype(np.float32)
+    sh = oracle.bf16_bits_of(rng.standard_normal((T, D)).astype(np.float32))
+    got32 = oracle.combine_fp32(y, inv, w, sh, out="f32")
+    gotbf = oracle.combine_fp32(y, inv, w, sh, out="bf16")
+    yf = oracle.widen(y)
+    sf = oracle.widen(sh)
+    for t in range(T):
+        for d in range(D):
+            acc = Fraction(0)
+            for j in range(K):
+                p = _r32(Fraction(float(w[t, j])) * Fraction(float(yf[inv[t, j], d])))
+                acc = _r32(acc + p)
+            acc = _r32(acc + Fraction(float(sf[t, d])))
+            assert Fraction(float(got32[t, d])) == acc
+            bf = (np.uint32(gotbf[t, d]) << np.uint32(16)).view(np.float32)
+            assert Fraction(float(bf)) == _rbf16(acc)
+
+
+def test_combine_is_the_sum_of_weighted_terms_within_fold_bound():
+    rng = np.random.default_rng(21)
+    T, K, D = 64, 6, 256
+    y = oracle.bf16_bits_of(rng.standard_normal((T * K, D)).astype(np.float32))
+    inv = np.arange(T * K, dtype=np.int32).reshape(T, K)
+    w = rng.uniform(0, 1, (T, K)).astype(np.float32)
+    got = oracle.combine_fp32(y, inv, w, out="f32").astype(np.float64)
+    terms = w.astype(np.float64)[:, :, None] * oracle.widen(y)[inv]
+    exact = terms.sum(axis=1)
+    u = 2.0 ** -24
+    bound = (2 * K) * u * np.abs(terms).sum(axis=1)   # K products and K sums, first order
+    assert np.all(np.abs(got - exact) <= bound * 1.01)
+
+
+def test_combine_top1_unit_weight_is_identity():
+    rng = np.random.default_rng(22)
+    y = rng.standard_normal((10, 32)).astype(np.float32)
+    inv = np.arange(10, dtype=np.int32).reshape(10, 1)
+    out = oracle.combine_fp32(y, inv, np.ones((10, 1), np.float32), out="f32")
+    assert np.array_equal(out.view(np.uint32), y.view(np.uint32))
+
+
+def test_combine_720_orders_give_360_classes_as_printed():
+    with open(os.path.join(GOLDEN, "arxiv_2607_28097_reduction_orders.json")) as f:
+        g = json.load(f)
+    K = g["routed_terms"]
+    rng = np.random.default_rng(23)
+    T, D = 6, 256
+    y = oracle.bf16_bits_of((rng.standard_normal((T * K, D)) * 0.3).astype(np.float32))
+    inv = rng.permutation(T * K).reshape(T, K).astype(np.int32)
+    # weights of comparable size, as renormalised routing weights are (a term far below
+    # the others can make some orders coincide on every element, giving fewer classes)
+    w = rng.uniform(0.5, 1.5, (T, K))
+    w = (w / w.sum(axis=1, keepdims=True) * 2.5).astype(np.float32)
+    res = oracle.combine_orders(y, inv, w)
+    assert len(res) == g["orders"]
+    ident = tuple(range(K))
+    swap01 = (1, 0) + tuple(range(2, K))
+    for pi, r in res.items():
+        pj = (pi[1], pi[0]) + pi[2:]
+        assert np.array_equal(r.view(np.uint32), res[pj].view(np.uint32))
+    for t in range(T):
+        classes = {res[pi][t].tobytes() for pi in res}
+        assert len(classes) == g["b_mode_exact_structural_classes"]
+        canon = res[ident][t].tobytes()
+        same = {pi for pi in res if res[pi][t].tobytes() == canon}
+        assert same == {ident, swap01}
+    # the canonical order is the default combine
+    assert np.array_equal(res[ident], oracle.combine_fp32(y, inv, w, out="f32"))
