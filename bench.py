@@ -1,0 +1,254 @@
+"""Benchmark of the sparse-MoE layer forward on one MI355X.
+
+One step = one full layer forward (route, permute, routed experts, shared
+expert, combine) over one batch of synthetic tokens already resident in HBM.
+Prints one JSON line.  Default workload: the DeepSeek-V4-Flash-like layer
+(T=32768, D=4096, 256 experts, top-6 sigmoid with selection bias and
+route_scale 2.5, expert intermediate 2048, one shared expert of 2048), bf16
+operands with fp32 accumulation.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s @1 GPU; expert-GEMM % bf16 MFMA peak; batch-invariant"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="dsv4", choices=["dsv4", "qnext", "q30", "dspark", "tiny"])
+    ap.add_argument("--tokens", type=int, default=0, help="override T (0: the config's T)")
+    ap.add_argument("--cpu-sample", type=int, default=128, help="tokens timed on the CPU oracle (0: skip)")
+    ap.add_argument("--no-invariance", action="store_true")
+    return ap.parse_args()
+
+
+def stage_bytes(cfg, T, nvalid_pairs):
+    """Algorithmic HBM bytes of the route, permute and combine stages."""
+    b = cfg.operand_bytes
+    P = nvalid_pairs
+    route = T * cfg.D * b + cfg.E * cfg.D * b + T * cfg.K * 8
+    permute = T * cfg.K * 4 + 2 * P * 4 + (cfg.E * 2 + 1) * 4
+    combine = P * cfg.D * b + (T * cfg.D * b if cfg.Is else 0) + T * cfg.D * 2 + T * cfg.K * 8
+    return route, permute, combine
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1 "
+                                   "(the multi-GPU expert-parallel design is described, not built)"}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import routing_grouped_gemm_gemv_amd as moe
+    from synth import get_config, make_inputs
+
+    cfg = get_config(args.config, T=args.tokens or None)
+    T = cfg.T
+    t0 = time.time()
+    inp = make_inputs(cfg)
+    log(f"inputs drawn in {time.time() - t0:.1f}s ({cfg.name}, T={T})")
+
+    def dev(a):
+        if a is None:
+            return None
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to("cuda").view(torch.bfloat16)
+        return torch.from_numpy(a).to("cuda")
+
+    torch.cuda.set_device(0)
+    shape = moe.Shape(T=T, D=cfg.D, E=cfg.E, K=cfg.K, I=cfg.I, Is=cfg.Is, score=cfg.score,
+                      renorm=cfg.renorm, route_scale=cfg.route_scale, dtype=cfg.dtype)
+    x = dev(inp.x)
+    layer = moe.MoeLayer(shape, dev(inp.w_router), dev(inp.w_gate_up), dev(inp.w_down),
+                         dev(inp.w_gate_up_s), dev(inp.w_down_s), dev(inp.bias))
+    out = torch.empty(T, cfg.D, dtype=torch.bfloat16, device="cuda")
+    ws = layer.workspace(shape)
+    torch.cuda.synchronize()
+    log(f"uploaded; workspace {ws.numel() / 2**30:.2f} GiB")
+
+    # ---- timed region 1: moe_forward, whole steps ---------------------------
+    for _ in range(args.warmup):
+        layer.forward(x, out=out)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        layer.forward(x, out=out)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_per_step = wall / args.steps * 1e3
+    log(f"moe_forward: {ms_per_step:.3f} ms/step")
+
+    # ---- timed region 2: the same layer through the stage entry points, with
+    # HIP events between stages on the stream the kernels run on -------------
+    stream = torch.cuda.current_stream()
+    tr = layer.new_trace(shape)
+    B = moe.binding
+    sh_shape = shape.replace(E=1, K=1, I=cfg.Is, Is=0) if cfg.Is else None
+    names = ["route", "permute", "experts_routed"] + (["experts_shared"] if cfg.Is else []) + ["combine"]
+
+    def run_stages(evs):
+        evs[0].record(stream)
+        B.moe_route(shape, x, layer.weights["router"], layer.sel_bias, None, None, tr["topk_ids"], tr["topk_w"], ws)
+        evs[1].record(stream)
+        B.moe_permute(shape, tr["topk_ids"], tr["counts"], tr["offsets"], tr["perm_token"], tr["inv_pos"], ws)
+        evs[2].record(stream)
+        B.moe_experts(shape, x, tr["perm_token"], tr["offsets"], layer.weights["gate_up"], layer.weights["down"],
+                      tr["y"], ws)
+        evs[3].record(stream)
+        i = 3
+        shared = None
+        if cfg.Is:
+            B.moe_experts(sh_shape, x, None, None, layer.weights["gate_up_shared"], layer.weights["down_shared"],
+                          tr["shared_out"], ws)
+            i += 1
+            evs[i].record(stream)
+            shared = tr["shared_out"]
+        B.moe_combine(shape, tr["y"], tr["inv_pos"], tr["topk_w"], shared, out)
+        evs[i + 1].record(stream)
+
+    for _ in range(max(1, args.warmup)):
+        run_stages([torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)])
+    torch.cuda.synchronize()
+    all_evs = []
+    for _ in range(args.steps):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+        run_stages(evs)
+        all_evs.append(evs)
+    torch.cuda.synchronize()
+    stage_ms = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in all_evs])) for i, n in enumerate(names)}
+    staged_total = float(np.mean([e[0].elapsed_time(e[-1]) for e in all_evs]))
+    log("stages (ms): " + json.dumps({k: round(v, 4) for k, v in stage_ms.items()}))
+    same_bits = bool(torch.equal(out.view(torch.int16), layer.forward(x).view(torch.int16)))
+
+    counts = tr["counts"].cpu().numpy()
+    P = int(counts.sum())
+    gemm_flops = 6.0 * cfg.D * cfg.I * P
+    shared_flops = 6.0 * cfg.D * cfg.Is * T
+    layer_flops = 2.0 * cfg.D * cfg.E * T + gemm_flops + shared_flops
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+    achieved = gemm_flops / (stage_ms["experts_routed"] * 1e-3) / 1e12
+    rb, pb, cb = stage_bytes(cfg, T, P)
+    hbm = {
+        "route_gbs": rb / (stage_ms["route"] * 1e-3) / 1e9,
+        "permute_gbs": pb / (stage_ms["permute"] * 1e-3) / 1e9,
+        "combine_gbs": cb / (stage_ms["combine"] * 1e-3) / 1e9,
+        "route_permute_combine_frac": (rb + pb + cb)
+        / ((stage_ms["route"] + stage_ms["permute"] + stage_ms["combine"]) * 1e-3) / 1e9 / PEAK_HBM_GBS,
+    }
+
+    # ---- batch invariance spot check: a prefix of the batch, bitwise --------
+    invariant = None
+    if not args.no_invariance and T > 1:
+        Tp = max(1, min(T - 1, 1000))
+        sub = layer.forward(x[:Tp].contiguous())
+        full = layer.forward(x)
+        invariant = bool(torch.equal(sub.view(torch.int16), full[:Tp].view(torch.int16)))
+    torch.cuda.synchronize()
+
+    # ---- CPU oracle on a bounded sample of the same workload ---------------
+    cpu = None
+    if args.cpu_sample > 0:
+        cpu = cpu_baseline(cfg, inp, min(args.cpu_sample, T))
+
+    line = {
+        "metric": METRIC,
+        "value": T / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded; shapes and value distributions of the configs, random-init weights)",
+        "config": {
+            "workload": f"{cfg.name}-like MoE layer forward",
+            "T": T, "D": cfg.D, "E": cfg.E, "K": cfg.K, "I": cfg.I, "Is": cfg.Is,
+            "score": cfg.score, "renorm": cfg.renorm, "route_scale": cfg.route_scale,
+            "selection_bias": cfg.bias is not None, "operands": cfg.dtype, "accumulate": "fp32",
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "kernel": "moe_experts routed (grouped gate_up+SwiGLU GEMM, grouped down GEMM)",
+            "bound": "mfma",
+            "achieved": achieved,
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": achieved / peak,
+            "traffic": None,
+        },
+        "layer_tflops": layer_flops / (ms_per_step * 1e-3) / 1e12,
+        "stage_ms": stage_ms,
+        "staged_ms_per_step": staged_total,
+        "stages_bitwise_equal_forward": same_bits,
+        "hbm": hbm,
+        "batch_invariant_prefix_check": invariant,
+        "routed_pairs": P,
+        "expert_load_max_over_mean": float(counts.max() / max(1e-9, counts.mean())),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(cfg, inp, n):
+    """The oracle, as it stands, on the first n tokens of the same layer."""
+    import numpy as np
+
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    cores = len(os.sched_getaffinity(0))
+    log(f"cpu oracle on {n} tokens ({threads} BLAS threads, {cores} cores in affinity)")
+    t0 = time.perf_counter()
+    oracle.forward(inp.x[:n], inp.w_router, inp.w_gate_up, inp.w_down, K=cfg.K, score=cfg.score,
+                   renorm=cfg.renorm, route_scale=cfg.route_scale, bias=inp.bias,
+                   shared_gate_up=inp.w_gate_up_s, shared_down=inp.w_down_s, bf16_mode=(cfg.dtype == "bf16"))
+    dt = time.perf_counter() - t0
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {
+        "value": n / dt,
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"first {n} tokens of the same {cfg.name}-like layer (all experts' weights), "
+                  f"fp64 numpy oracle, {dt:.1f} s, {model}",
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,203 @@
+/*
+ * moe.h -- C ABI of the sparse-MoE layer forward on one MI355X (gfx950).
+ *
+ * The forward is split at the semantic boundaries that the RL-Kernel roadmap
+ * ("DSV4 Flash MoE Train-Inference Consistency Roadmap", Problem 2:
+ * Single-Operator Boundaries May Not Be Meaningful) asks to compare:
+ *   routing   -> moe_route    router logits, top-k ids, top-k weights
+ *   dispatch  -> moe_permute  per-expert counts, offsets, token permutation
+ *   expert    -> moe_experts  SwiGLU expert MLPs as one grouped GEMM pair
+ *   reduction -> moe_combine  weighted combine in a fixed order and dtype
+ * and moe_forward runs all of them (plus the shared expert) on one stream.
+ *
+ * Conventions common to every entry point
+ *   - Pointers named as device data are HIP device pointers; the caller owns
+ *     every buffer.  The library allocates nothing, keeps no pointer after it
+ *     returns, never synchronises the stream and holds no state between calls
+ *     (the selection bias is an input, never state: SpecForge pull request
+ *     #1003, review thread, the router forward is stateless).
+ *   - Tensors are row-major and contiguous.  bf16 tensors hold IEEE bfloat16
+ *     bit patterns.  "Operand dtype" is moe_shape.dtype: MOE_BF16 means bf16
+ *     activations and weights with fp32 accumulation; MOE_F32 means fp32
+ *     activations and weights.
+ *   - Arguments are validated before anything is launched.  On any error no
+ *     kernel runs, outputs are untouched and the status says why; the text of
+ *     the last error of the calling thread is in moe_last_error().  There is
+ *     no fallback to other numerics (fail closed: RL-Kernel roadmap, issue
+ *     buckets).  T == 0 returns MOE_OK and launches nothing.
+ *   - Kernel faults surface at the caller's next synchronisation; launch
+ *     errors return MOE_ERR_HIP.
+ *   - Supported shapes: D, I (and Is when non-zero) multiples of 64;
+ *     1 <= E <= 1024; 1 <= K <= min(E, 16); T*K < 2^31; device gfx950.
+ *     Anything else returns MOE_ERR_UNSUPPORTED (or MOE_ERR_INVALID for
+ *     values that cannot describe a layer at all).
+ *   - Inputs must be finite; NaN or Inf inputs give unspecified outputs.
+ *   - Results are deterministic and batch invariant: a token's ids, weights
+ *     and output bits do not depend on T, on the other tokens, on padding or
+ *     on token order.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID = 1,      /* a NULL required pointer, a negative size, an unknown enum */
+    MOE_ERR_UNSUPPORTED = 2,  /* a valid layer this library does not run (shape limits, device) */
+    MOE_ERR_WORKSPACE = 3,    /* ws is NULL or ws_bytes below moe_workspace_size() */
+    MOE_ERR_HIP = 4           /* a HIP runtime call or kernel launch failed */
+} moe_status;
+
+typedef enum { MOE_BF16 = 0, MOE_F32 = 1 } moe_dtype;
+
+/* Router score function (RL-Kernel roadmap, Problem 1: router softmax; SpecForge
+ * pull request #1003 commit notes: sigmoid routers).  The score is computed in
+ * float64 from float64-accumulated logits. */
+typedef enum { MOE_SOFTMAX = 0, MOE_SIGMOID = 1 } moe_score;
+
+/* The layer's profile (the ModelProfile of the RL-Kernel roadmap, WS1). */
+typedef struct {
+    int64_t T;          /* tokens in this call */
+    int32_t D;          /* hidden size */
+    int32_t E;          /* routed experts */
+    int32_t K;          /* experts per token */
+    int32_t I;          /* routed expert SwiGLU intermediate size */
+    int32_t Is;         /* shared expert intermediate size, 0 = no shared expert */
+    int32_t score;      /* moe_score */
+    int32_t renorm;     /* 1: weights renormalised over the K selected experts */
+    float route_scale;  /* multiplies the (renormalised) weights; finite, > 0 */
+    int32_t dtype;      /* moe_dtype: operand dtype of x, weights, expert activations and outputs */
+} moe_shape;
+
+/* Weights of one layer (device pointers, operand dtype unless noted).
+ *   router          [E, D]
+ *   gate_up         [E, 2I, D]  rows 0..I-1 gate projection, rows I..2I-1 up projection
+ *   down            [E, D, I]
+ *   gate_up_shared  [2Is, D]    (NULL when Is == 0)
+ *   down_shared     [D, Is]     (NULL when Is == 0)                                  */
+typedef struct {
+    const void* router;
+    const void* gate_up;
+    const void* down;
+    const void* gate_up_shared;
+    const void* down_shared;
+} moe_weights;
+
+/* Optional copies of every boundary tensor of moe_forward (the SemanticTrace of
+ * the RL-Kernel roadmap, WS1).  Each pointer may be NULL; a non-NULL pointer
+ * must hold the full tensor and receives exactly what the corresponding stage
+ * entry point would write.
+ *   logits      float [T, E]      router logits (float64 accumulation rounded to float32)
+ *   topk_ids    int32 [T, K]
+ *   topk_w      float [T, K]
+ *   counts      int32 [E]
+ *   offsets     int32 [E+1]
+ *   perm_token  int32 [T*K]       first offsets[E] entries written
+ *   inv_pos     int32 [T, K]
+ *   y           operand dtype [T*K, D]   routed expert outputs, permuted order
+ *   shared_out  operand dtype [T, D]     shared expert output (Is > 0)            */
+typedef struct {
+    float* logits;
+    int32_t* topk_ids;
+    float* topk_w;
+    int32_t* counts;
+    int32_t* offsets;
+    int32_t* perm_token;
+    int32_t* inv_pos;
+    void* y;
+    void* shared_out;
+} moe_trace;
+
+/* Workspace bytes moe_forward needs for this shape.  The same amount is enough
+ * for every stage entry point.  Host-only; launches nothing. */
+moe_status moe_workspace_size(const moe_shape* shape, size_t* bytes);
+
+/* Routing (RL-Kernel roadmap, Problem 1 and the routing boundary of Problem 2;
+ * SpecForge pull request #1003, commit notes on the router).
+ *   logits[t,e] = sum_d x[t,d] * router[e,d], accumulated in float64 from
+ *   float32 partial sums of 64 products each (bf16 mode) or in float64 (f32 mode);
+ *   s = softmax over e, or sigmoid, in float64;
+ *   choice = s + sel_bias[e] (sel_bias may be NULL);
+ *   the K experts with the largest choice are selected, ties to the lower id;
+ *   topk_ids[t,:] lists them in ascending id order;
+ *   topk_w[t,j] = s[id_j] (unbiased), divided by the sum over the selection when
+ *   renorm, times route_scale, rounded once to float32.
+ * x [T,D] and router [E,D] in operand dtype; sel_bias float [E] or NULL;
+ * mask uint8 [T] or NULL (0 = masked token: ids -1, weights 0);
+ * logits float [T,E] or NULL (optional export); topk_ids int32 [T,K];
+ * topk_w float [T,K]; ws of at least moe_workspace_size() bytes. */
+moe_status moe_route(const moe_shape* shape, const void* x, const void* router,
+                     const float* sel_bias, const uint8_t* mask, float* logits,
+                     int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes,
+                     hipStream_t stream);
+
+/* Dispatch (RL-Kernel roadmap, Problem 2: token-to-expert map, valid token
+ * counts, padding provenance).  A stable counting sort of the T*K (token, slot)
+ * pairs by expert id, built without atomics.
+ *   counts[e]        pairs routed to e (slots holding -1 are skipped)
+ *   offsets[e]       exclusive prefix sum of counts, offsets[E] = kept pairs
+ *   perm_token[p]    token of row p of the expert-sorted order; within one
+ *                    expert the tokens ascend
+ *   inv_pos[t,j]     row of pair (t,j) in that order, -1 for skipped slots
+ * topk_ids int32 [T,K] (ids in [0,E) or -1); outputs as above (device). */
+moe_status moe_permute(const moe_shape* shape, const int32_t* topk_ids, int32_t* counts,
+                       int32_t* offsets, int32_t* perm_token, int32_t* inv_pos,
+                       void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Expert MLPs (RL-Kernel roadmap, Problem 2: gate_and_up -> down; SpecForge
+ * pull request #1003, "Design notes": the routed experts as grouped GEMMs).
+ * For every group g in [0, shape->E) and row p in [offsets[g], offsets[g+1]):
+ *   h = x[src(p)] . gate_up[g]^T            (fp32 accumulate, K order fixed)
+ *   a = silu(h[0:I]) * h[I:2I]              (fp32; rounded to bf16 in bf16 mode)
+ *   y[p] = a . down[g]^T                    (fp32 accumulate; bf16 in bf16 mode)
+ * src(p) = perm_token[p], or p when perm_token is NULL.  offsets int32 [E+1]
+ * (device), or NULL for one group of all T rows (requires E == 1).  The row
+ * count is at most T*K.  gate_up [E,2I,D], down [E,D,I], x [*,D], y [T*K,D],
+ * all operand dtype.  The shared expert is this call with E = K = 1, I = Is,
+ * perm_token = offsets = NULL. */
+moe_status moe_experts(const moe_shape* shape, const void* x, const int32_t* perm_token,
+                       const int32_t* offsets, const void* gate_up, const void* down,
+                       void* y, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Weighted combine, the final reduction (RL-Kernel roadmap, Problem 3; arXiv
+ * 2607.28097, Abstract: operand conversion, accumulator precision and
+ * reduction order belong to the numerical contract).  For each kept token t:
+ *   acc = +0.0f
+ *   for j = 0..K-1 (ascending expert id):  acc = fl32(acc + fl32(topk_w[t,j] * f32(y[inv_pos[t,j]])))
+ *   if shared_out:                         acc = fl32(acc + f32(shared_out[t]))
+ *   out[t] = acc rounded to bf16 nearest-even (out_dtype MOE_BF16) or acc (MOE_F32)
+ * No fused multiply-add.  A token whose inv_pos slots are all -1 gets a +0 row.
+ * y [T*K,D] and shared_out [T,D] (or NULL) in operand dtype; inv_pos int32
+ * [T,K]; topk_w float [T,K]; out [T,D] in out_dtype. */
+moe_status moe_combine(const moe_shape* shape, const void* y, const int32_t* inv_pos,
+                       const float* topk_w, const void* shared_out, int32_t out_dtype,
+                       void* out, hipStream_t stream);
+
+/* The whole layer: route, permute, routed experts, shared expert (when Is > 0,
+ * ungated, on every token: SpecForge pull request #1003, "Design notes"), and
+ * combine, in that order on one stream.  out [T,D] in out_dtype; trace may be
+ * NULL.  Bitwise equal to calling the stages one after another. */
+moe_status moe_forward(const moe_shape* shape, const moe_weights* weights, const void* x,
+                       const float* sel_bias, const uint8_t* mask, int32_t out_dtype,
+                       void* out, const moe_trace* trace, void* ws, size_t ws_bytes,
+                       hipStream_t stream);
+
+/* Static text for a status code. */
+const char* moe_status_string(moe_status status);
+
+/* Text of the last error returned on the calling thread ("" if none). */
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,283 @@
+// C ABI of the MoE layer forward: argument validation, workspace layout and
+// the order of launches.  Every check happens before the first launch, so a
+// rejected call leaves the outputs untouched (fail closed, as the RL-Kernel
+// roadmap's issue buckets require of unsupported configurations).
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+
+#include "../../include/moe.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+moe_status fail(moe_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+moe_status ok() {
+    g_last_error.clear();
+    return MOE_OK;
+}
+
+size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
+
+constexpr int64_t kMaxPairs = (static_cast<int64_t>(1) << 31) - 1;
+
+moe_status check_shape(const moe_shape* s) {
+    if (s == nullptr) return fail(MOE_ERR_INVALID, "shape is NULL");
+    if (s->T < 0) return fail(MOE_ERR_INVALID, "T = %lld is negative", static_cast<long long>(s->T));
+    if (s->D <= 0 || s->E <= 0 || s->K <= 0 || s->I <= 0 || s->Is < 0)
+        return fail(MOE_ERR_INVALID, "D, E, K, I must be positive and Is non-negative (D=%d E=%d K=%d I=%d Is=%d)",
+                    s->D, s->E, s->K, s->I, s->Is);
+    if (s->score != MOE_SOFTMAX && s->score != MOE_SIGMOID)
+        return fail(MOE_ERR_INVALID, "unknown score function %d", s->score);
+    if (s->dtype != MOE_BF16 && s->dtype != MOE_F32) return fail(MOE_ERR_INVALID, "unknown operand dtype %d", s->dtype);
+    if (s->renorm != 0 && s->renorm != 1) return fail(MOE_ERR_INVALID, "renorm must be 0 or 1, got %d", s->renorm);
+    if (!isfinite(s->route_scale) || !(s->route_scale > 0.0f))
+        return fail(MOE_ERR_INVALID, "route_scale must be finite and positive");
+    if (s->K > s->E) return fail(MOE_ERR_INVALID, "K = %d exceeds E = %d", s->K, s->E);
+    if (s->E > 1024) return fail(MOE_ERR_UNSUPPORTED, "E = %d exceeds 1024", s->E);
+    if (s->K > 16) return fail(MOE_ERR_UNSUPPORTED, "K = %d exceeds 16", s->K);
+    if (s->D % 64 != 0) return fail(MOE_ERR_UNSUPPORTED, "D = %d is not a multiple of 64", s->D);
+    if (s->I % 64 != 0) return fail(MOE_ERR_UNSUPPORTED, "I = %d is not a multiple of 64", s->I);
+    if (s->Is % 64 != 0) return fail(MOE_ERR_UNSUPPORTED, "Is = %d is not a multiple of 64", s->Is);
+    if (s->T > kMaxPairs / s->K) return fail(MOE_ERR_UNSUPPORTED, "T*K exceeds 2^31 - 1");
+    return MOE_OK;
+}
+
+// gfx950 only; the answer is cached per device
+moe_status check_device() {
+    static std::mutex mu;
+    static int verdict[64];  // 0 unknown, 1 ok, 2 unsupported
+    int dev = -1;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return fail(MOE_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(err));
+    if (dev < 0 || dev >= 64) return fail(MOE_ERR_UNSUPPORTED, "device index %d out of range", dev);
+    std::lock_guard<std::mutex> lock(mu);
+    if (verdict[dev] == 0) {
+        hipDeviceProp_t prop;
+        err = hipGetDeviceProperties(&prop, dev);
+        if (err != hipSuccess) return fail(MOE_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(err));
+        verdict[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        if (verdict[dev] == 2) return fail(MOE_ERR_UNSUPPORTED, "device %d is %s, not gfx950", dev, prop.gcnArchName);
+    }
+    if (verdict[dev] == 2) return fail(MOE_ERR_UNSUPPORTED, "device %d is not gfx950", dev);
+    return MOE_OK;
+}
+
+moe_status hip_status(hipError_t err, const char* what) {
+    if (err != hipSuccess) return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(err));
+    return MOE_OK;
+}
+
+size_t elem_bytes(int dtype) { return dtype == MOE_BF16 ? 2 : 4; }
+
+size_t route_ws(const moe_shape* s) { return align256(sizeof(double) * static_cast<size_t>(s->T) * s->E); }
+size_t permute_ws(const moe_shape* s) { return align256(moe::permute_ws_bytes(s->T * s->K, s->E)); }
+size_t experts_ws(const moe_shape* s) { return align256(moe::experts_ws_bytes(s->T * s->K, s->E, s->I, s->dtype)); }
+
+// Workspace of moe_forward, in order: logits64, ids, weights, counts, offsets,
+// perm_token, inv_pos, permute scratch, expert scratch, y, shared_out.
+struct ForwardLayout {
+    size_t logits64, ids, w, counts, offsets, perm, inv, perm_ws, exp_ws, y, shared, total;
+};
+
+ForwardLayout forward_layout(const moe_shape* s) {
+    ForwardLayout L;
+    const size_t T = static_cast<size_t>(s->T);
+    const size_t P = T * s->K;
+    const size_t eb = elem_bytes(s->dtype);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off += align256(bytes);
+        return at;
+    };
+    L.logits64 = take(sizeof(double) * T * s->E);
+    L.ids = take(sizeof(int32_t) * P);
+    L.w = take(sizeof(float) * P);
+    L.counts = take(sizeof(int32_t) * s->E);
+    L.offsets = take(sizeof(int32_t) * (s->E + 1));
+    L.perm = take(sizeof(int32_t) * P);
+    L.inv = take(sizeof(int32_t) * P);
+    L.perm_ws = take(moe::permute_ws_bytes(static_cast<int64_t>(P), s->E));
+    const size_t ex_routed = moe::experts_ws_bytes(static_cast<int64_t>(P), s->E, s->I, s->dtype);
+    const size_t ex_shared = s->Is > 0 ? moe::experts_ws_bytes(s->T, 1, s->Is, s->dtype) : 0;
+    L.exp_ws = take(ex_routed > ex_shared ? ex_routed : ex_shared);
+    L.y = take(eb * P * s->D);
+    L.shared = take(s->Is > 0 ? eb * T * s->D : 0);
+    L.total = off;
+    return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status status) {
+    switch (status) {
+        case MOE_OK: return "MOE_OK";
+        case MOE_ERR_INVALID: return "MOE_ERR_INVALID";
+        case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+        case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+        case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    }
+    return "unknown moe_status";
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+moe_status moe_workspace_size(const moe_shape* shape, size_t* bytes) {
+    moe_status st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    if (bytes == nullptr) return fail(MOE_ERR_INVALID, "bytes is NULL");
+    *bytes = forward_layout(shape).total;
+    return ok();
+}
+
+moe_status moe_route(const moe_shape* shape, const void* x, const void* router, const float* sel_bias,
+                     const uint8_t* mask, float* logits, int32_t* topk_ids, float* topk_w, void* ws,
+                     size_t ws_bytes, hipStream_t stream) {
+    moe_status st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    if (!x || !router || !topk_ids || !topk_w) return fail(MOE_ERR_INVALID, "moe_route: x, router, topk_ids and topk_w are required");
+    if (shape->T == 0) return ok();
+    if (!ws || ws_bytes < route_ws(shape))
+        return fail(MOE_ERR_WORKSPACE, "moe_route needs %zu workspace bytes, got %zu", route_ws(shape), ws ? ws_bytes : 0);
+    if ((st = check_device()) != MOE_OK) return st;
+    double* l64 = static_cast<double*>(ws);
+    if ((st = hip_status(moe::launch_router_logits(x, router, shape->T, shape->D, shape->E, shape->dtype, l64, stream),
+                         "router logits launch")) != MOE_OK)
+        return st;
+    if ((st = hip_status(moe::launch_topk(l64, shape->T, shape->E, shape->K, shape->score, shape->renorm,
+                                          shape->route_scale, sel_bias, mask, logits, topk_ids, topk_w, stream),
+                         "top-k launch")) != MOE_OK)
+        return st;
+    return ok();
+}
+
+moe_status moe_permute(const moe_shape* shape, const int32_t* topk_ids, int32_t* counts, int32_t* offsets,
+                       int32_t* perm_token, int32_t* inv_pos, void* ws, size_t ws_bytes, hipStream_t stream) {
+    moe_status st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    if (!topk_ids || !counts || !offsets || !perm_token || !inv_pos)
+        return fail(MOE_ERR_INVALID, "moe_permute: topk_ids, counts, offsets, perm_token and inv_pos are required");
+    if (shape->T == 0) return ok();
+    if (!ws || ws_bytes < permute_ws(shape))
+        return fail(MOE_ERR_WORKSPACE, "moe_permute needs %zu workspace bytes, got %zu", permute_ws(shape), ws ? ws_bytes : 0);
+    if ((st = check_device()) != MOE_OK) return st;
+    if ((st = hip_status(moe::launch_permute(topk_ids, shape->T, shape->K, shape->E, static_cast<int32_t*>(ws), counts,
+                                             offsets, perm_token, inv_pos, stream),
+                         "permute launch")) != MOE_OK)
+        return st;
+    return ok();
+}
+
+moe_status moe_experts(const moe_shape* shape, const void* x, const int32_t* perm_token, const int32_t* offsets,
+                       const void* gate_up, const void* down, void* y, void* ws, size_t ws_bytes,
+                       hipStream_t stream) {
+    moe_status st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    if (!x || !gate_up || !down || !y) return fail(MOE_ERR_INVALID, "moe_experts: x, gate_up, down and y are required");
+    if (offsets == nullptr && shape->E != 1)
+        return fail(MOE_ERR_INVALID, "moe_experts: offsets may be NULL only for a single group (E == 1)");
+    if (shape->T == 0) return ok();
+    if (!ws || ws_bytes < experts_ws(shape))
+        return fail(MOE_ERR_WORKSPACE, "moe_experts needs %zu workspace bytes, got %zu", experts_ws(shape), ws ? ws_bytes : 0);
+    if ((st = check_device()) != MOE_OK) return st;
+    const int64_t rows = shape->T * shape->K;
+    if ((st = hip_status(moe::launch_experts(x, perm_token, offsets, shape->E, rows, shape->D, shape->I, shape->dtype,
+                                             gate_up, down, y, ws, stream),
+                         "experts launch")) != MOE_OK)
+        return st;
+    return ok();
+}
+
+moe_status moe_combine(const moe_shape* shape, const void* y, const int32_t* inv_pos, const float* topk_w,
+                       const void* shared_out, int32_t out_dtype, void* out, hipStream_t stream) {
+    moe_status st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    if (!y || !inv_pos || !topk_w || !out) return fail(MOE_ERR_INVALID, "moe_combine: y, inv_pos, topk_w and out are required");
+    if (out_dtype != MOE_BF16 && out_dtype != MOE_F32) return fail(MOE_ERR_INVALID, "unknown out_dtype %d", out_dtype);
+    if (shape->T == 0) return ok();
+    if ((st = check_device()) != MOE_OK) return st;
+    if ((st = hip_status(moe::launch_combine(y, inv_pos, topk_w, shared_out, shape->T, shape->D, shape->K, shape->dtype,
+                                             out_dtype, out, stream),
+                         "combine launch")) != MOE_OK)
+        return st;
+    return ok();
+}
+
+moe_status moe_forward(const moe_shape* shape, const moe_weights* weights, const void* x, const float* sel_bias,
+                       const uint8_t* mask, int32_t out_dtype, void* out, const moe_trace* trace, void* ws,
+                       size_t ws_bytes, hipStream_t stream) {
+    moe_status st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    if (!weights || !x || !out) return fail(MOE_ERR_INVALID, "moe_forward: weights, x and out are required");
+    if (!weights->router || !weights->gate_up || !weights->down)
+        return fail(MOE_ERR_INVALID, "moe_forward: router, gate_up and down weights are required");
+    if (shape->Is > 0 && (!weights->gate_up_shared || !weights->down_shared))
+        return fail(MOE_ERR_INVALID, "moe_forward: Is > 0 needs gate_up_shared and down_shared");
+    if (out_dtype != MOE_BF16 && out_dtype != MOE_F32) return fail(MOE_ERR_INVALID, "unknown out_dtype %d", out_dtype);
+    if (shape->T == 0) return ok();
+    const ForwardLayout L = forward_layout(shape);
+    if (!ws || ws_bytes < L.total)
+        return fail(MOE_ERR_WORKSPACE, "moe_forward needs %zu workspace bytes, got %zu", L.total, ws ? ws_bytes : 0);
+    if ((st = check_device()) != MOE_OK) return st;
+
+    uint8_t* base = static_cast<uint8_t*>(ws);
+    moe_trace tr{};
+    if (trace) tr = *trace;
+    double* l64 = reinterpret_cast<double*>(base + L.logits64);
+    int32_t* ids = tr.topk_ids ? tr.topk_ids : reinterpret_cast<int32_t*>(base + L.ids);
+    float* tw = tr.topk_w ? tr.topk_w : reinterpret_cast<float*>(base + L.w);
+    int32_t* counts = tr.counts ? tr.counts : reinterpret_cast<int32_t*>(base + L.counts);
+    int32_t* offsets = tr.offsets ? tr.offsets : reinterpret_cast<int32_t*>(base + L.offsets);
+    int32_t* perm = tr.perm_token ? tr.perm_token : reinterpret_cast<int32_t*>(base + L.perm);
+    int32_t* inv = tr.inv_pos ? tr.inv_pos : reinterpret_cast<int32_t*>(base + L.inv);
+    void* y = tr.y ? tr.y : static_cast<void*>(base + L.y);
+    void* sh = shape->Is > 0 ? (tr.shared_out ? tr.shared_out : static_cast<void*>(base + L.shared)) : nullptr;
+    void* exw = base + L.exp_ws;
+    const int64_t T = shape->T;
+
+    if ((st = hip_status(moe::launch_router_logits(x, weights->router, T, shape->D, shape->E, shape->dtype, l64, stream),
+                         "router logits launch")) != MOE_OK)
+        return st;
+    if ((st = hip_status(moe::launch_topk(l64, T, shape->E, shape->K, shape->score, shape->renorm, shape->route_scale,
+                                          sel_bias, mask, tr.logits, ids, tw, stream),
+                         "top-k launch")) != MOE_OK)
+        return st;
+    if ((st = hip_status(moe::launch_permute(ids, T, shape->K, shape->E, reinterpret_cast<int32_t*>(base + L.perm_ws),
+                                             counts, offsets, perm, inv, stream),
+                         "permute launch")) != MOE_OK)
+        return st;
+    if ((st = hip_status(moe::launch_experts(x, perm, offsets, shape->E, T * shape->K, shape->D, shape->I, shape->dtype,
+                                             weights->gate_up, weights->down, y, exw, stream),
+                         "routed experts launch")) != MOE_OK)
+        return st;
+    if (sh != nullptr) {
+        if ((st = hip_status(moe::launch_experts(x, nullptr, nullptr, 1, T, shape->D, shape->Is, shape->dtype,
+                                                 weights->gate_up_shared, weights->down_shared, sh, exw, stream),
+                             "shared expert launch")) != MOE_OK)
+            return st;
+    }
+    if ((st = hip_status(moe::launch_combine(y, inv, tw, sh, T, shape->D, shape->K, shape->dtype, out_dtype, out, stream),
+                         "combine launch")) != MOE_OK)
+        return st;
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,42 @@
+// Host-side launchers of the MoE kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---- routing -----------------------------------------------------------------
+// logits64 [T, E] float64 = x [T, D] . router [E, D]^T
+hipError_t launch_router_logits(const void* x, const void* router, int64_t T, int D, int E,
+                                int dtype, double* logits64, hipStream_t stream);
+// scores, selection bias, top-k, weights; optional float32 logits export
+hipError_t launch_topk(const double* logits64, int64_t T, int E, int K, int score, int renorm,
+                       float route_scale, const float* bias, const uint8_t* mask,
+                       float* logits_out, int32_t* ids, float* w, hipStream_t stream);
+
+// ---- dispatch ----------------------------------------------------------------
+struct PermutePlan {
+    int pairs_per_block;  // multiple of 256
+    int blocks;
+    int id_bits;          // bits that distinguish expert ids
+};
+PermutePlan permute_plan(int64_t P, int E);
+size_t permute_ws_bytes(int64_t P, int E);  // block histogram + block bases
+hipError_t launch_permute(const int32_t* ids, int64_t T, int K, int E, int32_t* ws_i32,
+                          int32_t* counts, int32_t* offsets, int32_t* perm_token, int32_t* inv_pos,
+                          hipStream_t stream);
+
+// ---- experts -----------------------------------------------------------------
+size_t experts_ws_bytes(int64_t rows_max, int G, int I, int dtype);
+hipError_t launch_experts(const void* x, const int32_t* perm_token, const int32_t* offsets,
+                          int G, int64_t rows_max, int D, int I, int dtype, const void* gate_up,
+                          const void* down, void* y, void* ws, hipStream_t stream);
+
+// ---- combine -----------------------------------------------------------------
+hipError_t launch_combine(const void* y, const int32_t* inv_pos, const float* w, const void* shared,
+                          int64_t T, int D, int K, int dtype, int out_dtype, void* out,
+                          hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,196 @@
+// Dispatch: per-expert counts, offsets and a stable token permutation.
+//
+// The dispatch boundary of the RL-Kernel roadmap ("DSV4 Flash MoE
+// Train-Inference Consistency Roadmap", Problem 2: the token-to-expert map,
+// valid token counts and padding provenance) as a stable counting sort of the
+// T*K (token, slot) pairs by expert id.  No atomics, global or LDS: every
+// count is produced by exactly one lane, so the result is the same on every
+// run.
+//
+//   pass 1 (count):   each block takes a contiguous range of pairs; each wave
+//                     walks 64-pair segments of its sub-range and, with a
+//                     ballot per id bit, finds for every lane the lanes holding
+//                     the same expert (a "match mask").  The lowest such lane
+//                     adds the popcount to the wave's LDS histogram row.
+//   pass 2 (scan):    one workgroup scans the block histograms in (expert,
+//                     block) order: the base row of every (expert, block), the
+//                     expert offsets and counts.
+//   pass 3 (scatter): each block recomputes its wave histograms, turns them
+//                     into per-wave bases, and walks its segments again; a
+//                     pair's row is its wave base plus the pairs of the same
+//                     expert in earlier segments plus its rank in the segment.
+//
+// Pairs of one expert therefore keep their flat (token, slot) order, and since
+// a token lists distinct experts, tokens ascend within every expert.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+constexpr int kPermWaves = 4;
+constexpr int kMaxExperts = 1024;
+
+PermutePlan permute_plan(int64_t P, int E) {
+    PermutePlan pl;
+    int64_t ppb = 2048;
+    // keep the scan's (expert, block) table small
+    while ((P + ppb - 1) / ppb > 1024) ppb *= 2;
+    pl.pairs_per_block = static_cast<int>(ppb);
+    pl.blocks = static_cast<int>(P > 0 ? (P + ppb - 1) / ppb : 1);
+    int bits = 0;
+    while ((1 << bits) < E) ++bits;
+    pl.id_bits = bits;
+    return pl;
+}
+
+size_t permute_ws_bytes(int64_t P, int E) {
+    const PermutePlan pl = permute_plan(P, E);
+    return 2 * sizeof(int32_t) * static_cast<size_t>(E) * pl.blocks;
+}
+
+// lanes of this wave whose id equals mine (valid lanes only)
+__device__ __forceinline__ uint64_t match_mask(int e, bool valid, int id_bits) {
+    uint64_t m = __ballot(valid);
+    for (int b = 0; b < id_bits; ++b) {
+        const bool bit = (e >> b) & 1;
+        const uint64_t bm = __ballot(bit);
+        m &= bit ? bm : ~bm;
+    }
+    return m;
+}
+
+// Fill hist[w][*] with the per-expert pair counts of wave w's sub-range.
+__device__ __forceinline__ void wave_histogram(const int32_t* __restrict__ ids, int64_t P, int64_t w_begin,
+                                               int64_t w_end, int id_bits, int* hist_row) {
+    const int lane = lane_id();
+    const uint64_t lt = (1ull << lane) - 1ull;
+    for (int64_t seg = w_begin; seg < w_end; seg += 64) {
+        const int64_t p = seg + lane;
+        int e = -1;
+        if (p < w_end && p < P) e = ids[p];
+        const bool valid = e >= 0;
+        const uint64_t m = match_mask(valid ? e : 0, valid, id_bits);
+        if (valid && (m & lt) == 0ull) hist_row[e] += __popcll(m);
+    }
+}
+
+__global__ __launch_bounds__(256) void permute_count_kernel(
+    const int32_t* __restrict__ ids, int64_t P, int E, int ppb, int nblocks, int id_bits,
+    int32_t* __restrict__ block_hist) {
+    __shared__ int hist[kPermWaves][kMaxExperts];
+    const int tid = threadIdx.x;
+    const int wv = tid >> 6;
+    for (int i = tid; i < kPermWaves * E; i += 256) hist[i / E][i % E] = 0;
+    __syncthreads();
+    const int64_t base = static_cast<int64_t>(blockIdx.x) * ppb;
+    const int per_wave = ppb / kPermWaves;
+    wave_histogram(ids, P, base + wv * per_wave, base + (wv + 1) * per_wave, id_bits, hist[wv]);
+    __syncthreads();
+    for (int e = tid; e < E; e += 256)
+        block_hist[static_cast<int64_t>(e) * nblocks + blockIdx.x] = hist[0][e] + hist[1][e] + hist[2][e] + hist[3][e];
+}
+
+// Exclusive scan of block_hist in (expert, block) order by one workgroup.
+__global__ __launch_bounds__(1024) void permute_scan_kernel(
+    const int32_t* __restrict__ block_hist, int E, int nblocks, int32_t* __restrict__ block_base,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
+    __shared__ int part[1024];
+    __shared__ int offs[kMaxExperts + 1];
+    const int tid = threadIdx.x;
+    const int64_t N = static_cast<int64_t>(E) * nblocks;
+    const int64_t chunk = (N + 1023) / 1024;
+    const int64_t lo = tid * chunk;
+    const int64_t hi = lo + chunk < N ? lo + chunk : N;
+    int sum = 0;
+    for (int64_t j = lo; j < hi; ++j) sum += block_hist[j];
+    part[tid] = sum;
+    __syncthreads();
+    // Hillis-Steele inclusive scan of the 1024 partial sums
+    for (int d = 1; d < 1024; d <<= 1) {
+        const int v = tid >= d ? part[tid - d] : 0;
+        __syncthreads();
+        part[tid] += v;
+        __syncthreads();
+    }
+    int run = part[tid] - sum;  // exclusive prefix of this thread's chunk
+    for (int64_t j = lo; j < hi; ++j) {
+        block_base[j] = run;
+        if (j % nblocks == 0) offs[j / nblocks] = run;
+        run += block_hist[j];
+    }
+    if (tid == 1023) offs[E] = part[1023];
+    __syncthreads();
+    for (int e = tid; e <= E; e += 1024) {
+        offsets[e] = offs[e];
+        if (e < E) counts[e] = offs[e + 1] - offs[e];
+    }
+}
+
+__global__ __launch_bounds__(256) void permute_scatter_kernel(
+    const int32_t* __restrict__ ids, int64_t P, int K, int E, int ppb, int nblocks, int id_bits,
+    const int32_t* __restrict__ block_base, int32_t* __restrict__ perm_token, int32_t* __restrict__ inv_pos) {
+    __shared__ int hist[kPermWaves][kMaxExperts];
+    const int tid = threadIdx.x;
+    const int wv = tid >> 6;
+    const int lane = lane_id();
+    for (int i = tid; i < kPermWaves * E; i += 256) hist[i / E][i % E] = 0;
+    __syncthreads();
+    const int64_t base = static_cast<int64_t>(blockIdx.x) * ppb;
+    const int per_wave = ppb / kPermWaves;
+    const int64_t w_begin = base + wv * per_wave;
+    const int64_t w_end = w_begin + per_wave;
+    wave_histogram(ids, P, w_begin, w_end, id_bits, hist[wv]);
+    __syncthreads();
+    // per-wave base rows: block base of the expert plus earlier waves' pairs
+    for (int e = tid; e < E; e += 256) {
+        int run = block_base[static_cast<int64_t>(e) * nblocks + blockIdx.x];
+#pragma unroll
+        for (int w = 0; w < kPermWaves; ++w) {
+            const int h = hist[w][e];
+            hist[w][e] = run;
+            run += h;
+        }
+    }
+    __syncthreads();
+    const uint64_t lt = (1ull << lane) - 1ull;
+    int* row = hist[wv];
+    for (int64_t seg = w_begin; seg < w_end; seg += 64) {
+        const int64_t p = seg + lane;
+        const bool in = p < w_end && p < P;
+        int e = -1;
+        if (in) e = ids[p];
+        const bool valid = e >= 0;
+        const uint64_t m = match_mask(valid ? e : 0, valid, id_bits);
+        if (valid) {
+            const int pos = row[e] + __popcll(m & lt);
+            perm_token[pos] = static_cast<int32_t>(p / K);
+            inv_pos[p] = pos;
+        } else if (in) {
+            inv_pos[p] = -1;
+        }
+        __builtin_amdgcn_wave_barrier();
+        if (valid && (m & lt) == 0ull) row[e] += __popcll(m);
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
+hipError_t launch_permute(const int32_t* ids, int64_t T, int K, int E, int32_t* ws_i32,
+                          int32_t* counts, int32_t* offsets, int32_t* perm_token, int32_t* inv_pos,
+                          hipStream_t stream) {
+    const int64_t P = T * K;
+    const PermutePlan pl = permute_plan(P, E);
+    int32_t* block_hist = ws_i32;
+    int32_t* block_base = ws_i32 + static_cast<int64_t>(E) * pl.blocks;
+    permute_count_kernel<<<pl.blocks, 256, 0, stream>>>(ids, P, E, pl.pairs_per_block, pl.blocks, pl.id_bits,
+                                                       block_hist);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    permute_scan_kernel<<<1, 1024, 0, stream>>>(block_hist, E, pl.blocks, block_base, counts, offsets);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    permute_scatter_kernel<<<pl.blocks, 256, 0, stream>>>(ids, P, K, E, pl.pairs_per_block, pl.blocks,
+                                                         pl.id_bits, block_base, perm_token, inv_pos);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,95 @@
+"""Batch invariance on the GPU: a token's ids, weights and output bits do not
+depend on how many tokens share the batch, on padding, or on token order.
+
+The RL-Kernel roadmap ("DSV4 Flash MoE Train-Inference Consistency Roadmap",
+Problem 1 and the WS1 issue buckets) asks that routing metadata stay stable
+across batch and padding sweeps and that any mismatch be reported; this is that
+sweep on a Qwen3-30B-A3B-like layer (8192-token pool, 128 experts, top-8).
+Self-consistency only: no oracle is needed.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from synth import get_config, make_inputs, padding_rows, shuffle_perm
+from tests.gpu_util import make_layer, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pool():
+    cfg = get_config("q30")
+    inp = make_inputs(cfg)
+    layer = make_layer(inp)
+    x = to_dev(inp.x)
+    out, tr = layer.forward(x, trace=True)
+    torch.cuda.synchronize()
+    ref = {
+        "out": to_host(out),
+        "ids": to_host(tr["topk_ids"]),
+        "w": to_host(tr["topk_w"]).view(np.uint32),
+    }
+    print(f"[invariance] pool T={cfg.T} ready", flush=True)
+    return cfg, inp, layer, x, ref
+
+
+def _run(layer, x, mask=None):
+    out, tr = layer.forward(x, mask, trace=True)
+    return to_host(out), to_host(tr["topk_ids"]), to_host(tr["topk_w"]).view(np.uint32)
+
+
+def _same(T, got, ref, rows=None):
+    o, i, w = got
+    sel = slice(0, T) if rows is None else rows
+    bad = np.nonzero(~(np.all(o[:T] == ref["out"][sel], axis=1) & np.all(i[:T] == ref["ids"][sel], axis=1)
+                       & np.all(w[:T] == ref["w"][sel], axis=1)))[0]
+    return bad
+
+
+def test_every_batch_size_1_to_256(pool):
+    cfg, inp, layer, x, ref = pool
+    bad = {}
+    for T in range(1, 257):
+        b = _same(T, _run(layer, x[:T].contiguous()), ref)
+        if b.size:
+            bad[T] = b[:10].tolist()
+    assert not bad, f"tokens whose bits changed with the batch size: {bad}"
+
+
+@pytest.mark.parametrize("T", [257, 511, 1000, 2048, 4095, 4096, 8191])
+def test_large_batch_sizes(pool, T):
+    cfg, inp, layer, x, ref = pool
+    b = _same(T, _run(layer, x[:T].contiguous()), ref)
+    assert b.size == 0, b[:10]
+
+
+@pytest.mark.parametrize("T", [1, 100, 1000, 4095])
+@pytest.mark.parametrize("masked", [True, False])
+def test_padding_to_multiple_of_128(pool, T, masked):
+    cfg, inp, layer, x, ref = pool
+    Tp = (T + 127) // 128 * 128 + 128
+    pad = to_dev(padding_rows(cfg, Tp - T, stream=T))
+    xp = torch.cat([x[:T], pad]).contiguous()
+    mask = None
+    if masked:
+        m = torch.zeros(Tp, dtype=torch.uint8, device="cuda")
+        m[:T] = 1
+        mask = m
+    o, i, w = _run(layer, xp, mask)
+    b = _same(T, (o, i, w), ref)
+    assert b.size == 0, b[:10]
+    if masked:
+        assert np.all(o[T:] == 0) and np.all(i[T:] == -1)
+
+
+@pytest.mark.parametrize("k", [0, 1, 2])
+def test_token_shuffles(pool, k):
+    cfg, inp, layer, x, ref = pool
+    perm = shuffle_perm(cfg, cfg.T, k)
+    xs = x[torch.from_numpy(perm).to("cuda")].contiguous()
+    o, i, w = _run(layer, xs)
+    assert np.array_equal(o, ref["out"][perm])
+    assert np.array_equal(i, ref["ids"][perm])
+    assert np.array_equal(w, ref["w"][perm])
