@@ -25,9 +25,14 @@ Conventions (the plainest reading where the pages leave a step open):
   * an expert is a SwiGLU MLP: gate and up projections (rows 0..I-1 and
     I..2I-1 of the [2I, D] gate_up matrix), silu(gate) * up, then the [D, I]
     down projection [RLK, Problem 2: gate_and_up -> down];
-  * in the bf16 operand mode the activation fed to the down projection and the
-    expert output are rounded to bf16 (nearest-even, one rounding from the
-    exact value); in the fp32 mode nothing is rounded;
+  * in the bf16 operand mode the activation fed to the down projection is a
+    bf16 operand (rounded nearest-even, one rounding from the exact value) and
+    the expert output crosses the expert boundary as bf16; in the fp32 mode
+    nothing is rounded;
+  * the reference layer output is the float64 sum of the weighted exact expert
+    outputs (before their bf16 conversion) and the exact shared output: the
+    conversion itself belongs to the combine, whose arithmetic is emulated
+    bit for bit separately;
   * the shared expert is the same MLP applied to every kept token, ungated,
     added after the routed terms [SPF, "Design notes"];
   * the combine accumulates in float32, from +0, over the K routed terms in
@@ -206,11 +211,14 @@ def permute(ids: np.ndarray, E: int) -> Dict[str, np.ndarray]:
 # expert boundary [RLK, Problem 2: expert inputs/outputs, accumulation dtype]
 # ----------------------------------------------------------------------------
 
-def expert_mlp(x64: np.ndarray, w1: np.ndarray, w2: np.ndarray, bf16_mode: bool) -> np.ndarray:
+def expert_mlp(x64: np.ndarray, w1: np.ndarray, w2: np.ndarray, bf16_mode: bool,
+               exact_output: bool = False) -> np.ndarray:
     """One SwiGLU expert on the rows of x64, float64.
 
     h = x . W1^T ([n, 2I]); a = silu(h[:, :I]) * h[:, I:]; y = a . W2^T ([n, D]).
-    In bf16 mode a and y are rounded to bf16 (nearest-even).
+    In bf16 mode a is rounded to bf16 (nearest-even) before the down projection
+    and y is returned on the bf16 grid, unless ``exact_output`` asks for the
+    value before that last conversion.
     """
     w1_64 = widen(w1)
     w2_64 = widen(w2)
@@ -221,7 +229,7 @@ def expert_mlp(x64: np.ndarray, w1: np.ndarray, w2: np.ndarray, bf16_mode: bool)
     if bf16_mode:
         a = round_bf16(a)
     y = a @ w2_64.T
-    if bf16_mode:
+    if bf16_mode and not exact_output:
         y = round_bf16(y)
     return y
 
@@ -293,9 +301,11 @@ class OracleResult:
     offsets: np.ndarray       # [E+1] int32
     perm_token: np.ndarray    # [P] int32
     inv_pos: np.ndarray       # [T, K] int32
-    y: np.ndarray             # [P, D] float64 (on the bf16 grid in bf16 mode)
-    shared: Optional[np.ndarray]  # [T, D] float64 or None
-    out: np.ndarray           # [T, D] float64: sum_j w_j y_j + shared, unrounded
+    y: np.ndarray             # [P, D] float64 expert outputs at the boundary (bf16 grid in bf16 mode)
+    shared: Optional[np.ndarray]  # [T, D] float64 shared output at the boundary, or None
+    out: np.ndarray           # [T, D] float64 reference: sum_j w_j y_exact_j + shared_exact
+    y_exact: Optional[np.ndarray] = None       # [P, D] expert outputs before the bf16 conversion
+    shared_exact: Optional[np.ndarray] = None  # [T, D]
     extra: Dict[str, object] = field(default_factory=dict)
 
 
@@ -334,28 +344,30 @@ def forward(x: np.ndarray, w_router: np.ndarray,
     offsets = pm["offsets"]
     perm_token = pm["perm_token"]
     D = x64.shape[1]
-    y = np.zeros((int(offsets[E]), D), dtype=np.float64)
+    y_ex = np.zeros((int(offsets[E]), D), dtype=np.float64)
     get1 = gate_up if callable(gate_up) else (lambda e: gate_up[e])
     get2 = down if callable(down) else (lambda e: down[e])
     for e in range(E):
         lo, hi = int(offsets[e]), int(offsets[e + 1])
         if hi > lo:
-            y[lo:hi] = expert_mlp(x64[perm_token[lo:hi]], get1(e), get2(e), bf16_mode)
+            y_ex[lo:hi] = expert_mlp(x64[perm_token[lo:hi]], get1(e), get2(e), bf16_mode, exact_output=True)
+    y = round_bf16(y_ex) if bf16_mode else y_ex
 
-    sh = None
+    sh = sh_ex = None
     if shared_gate_up is not None:
-        sh = np.zeros((T, D), dtype=np.float64)
+        sh_ex = np.zeros((T, D), dtype=np.float64)
         if valid.any():
-            sh[valid] = expert_mlp(x64[valid], shared_gate_up, shared_down, bf16_mode)
+            sh_ex[valid] = expert_mlp(x64[valid], shared_gate_up, shared_down, bf16_mode, exact_output=True)
+        sh = round_bf16(sh_ex) if bf16_mode else sh_ex
 
     out = np.zeros((T, D), dtype=np.float64)
     inv_pos = pm["inv_pos"]
     for j in range(K):
         rows = inv_pos[:, j]
         ok = rows >= 0
-        out[ok] += w[ok, j:j + 1] * y[rows[ok]]
-    if sh is not None:
-        out += sh
+        out[ok] += w[ok, j:j + 1] * y_ex[rows[ok]]
+    if sh_ex is not None:
+        out += sh_ex
     out[~valid] = 0.0
     return OracleResult(logits, s, c, ids, w, margin, exempt, pm["counts"], offsets,
-                        perm_token, inv_pos, y, sh, out)
+                        perm_token, inv_pos, y, sh, out, y_ex, sh_ex)

@@ -320,6 +320,28 @@ def test_bf16_mode_rounds_activation_and_output():
     inp = make_inputs(cfg)
     res = oracle_forward(inp)
     assert np.array_equal(oracle.round_bf16(res.y), res.y)      # expert outputs on the bf16 grid
+    assert np.array_equal(oracle.round_bf16(res.y_exact), res.y)
+    assert not np.array_equal(res.y_exact, res.y)
+    # the reference output is built from the exact expert outputs
+    ref = np.zeros_like(res.out)
+    for j in range(cfg.K):
+        ref += res.weights[:, j:j + 1] * res.y_exact[res.inv_pos[:, j]]
+    np.testing.assert_array_equal(res.out, ref)
+    # the activation is a bf16 operand: one expert recomputed with torch, a rounded by torch's cast
+    e = int(res.ids[0, 0])
+    rows = res.perm_token[res.offsets[e]:res.offsets[e + 1]]
+    x = torch.from_numpy(oracle.widen(inp.x[rows]))
+    w1 = torch.from_numpy(oracle.widen(inp.w_gate_up[e]))
+    w2 = torch.from_numpy(oracle.widen(inp.w_down[e]))
+    I = cfg.I
+    h = (x @ w1.T).numpy()
+    a64 = oracle.silu(h[:, :I]) * h[:, I:]
+    # torch's cast goes through float32, so it may differ from the single rounding on the
+    # rare values that round twice; everywhere else the two agree
+    a_bf = torch.from_numpy(a64).float().to(torch.bfloat16).double().numpy()
+    assert np.mean(a_bf == oracle.round_bf16(a64)) > 0.999
+    y_ref = (torch.from_numpy(oracle.round_bf16(a64)) @ w2.T).numpy()
+    np.testing.assert_allclose(res.y_exact[res.offsets[e]:res.offsets[e + 1]], y_ref, rtol=1e-12, atol=1e-18)
 
 
 # ---------------------------------------------------------------- combine
