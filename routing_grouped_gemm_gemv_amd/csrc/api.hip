@@ -199,8 +199,9 @@ moe_status moe_experts(const moe_shape* shape, const void* x, const int32_t* per
         return fail(MOE_ERR_WORKSPACE, "moe_experts needs %zu workspace bytes, got %zu", experts_ws(shape), ws ? ws_bytes : 0);
     if ((st = check_device()) != MOE_OK) return st;
     const int64_t rows = shape->T * shape->K;
-    if ((st = hip_status(moe::launch_experts(x, perm_token, offsets, shape->E, rows, shape->D, shape->I, shape->dtype,
-                                             gate_up, down, y, ws, stream),
+    const int64_t x_rows = perm_token != nullptr ? shape->T : rows;
+    if ((st = hip_status(moe::launch_experts(x, x_rows, perm_token, offsets, shape->E, rows, shape->D, shape->I,
+                                             shape->dtype, gate_up, down, y, ws, stream),
                          "experts launch")) != MOE_OK)
         return st;
     return ok();
@@ -264,12 +265,12 @@ moe_status moe_forward(const moe_shape* shape, const moe_weights* weights, const
                                              counts, offsets, perm, inv, stream),
                          "permute launch")) != MOE_OK)
         return st;
-    if ((st = hip_status(moe::launch_experts(x, perm, offsets, shape->E, T * shape->K, shape->D, shape->I, shape->dtype,
-                                             weights->gate_up, weights->down, y, exw, stream),
+    if ((st = hip_status(moe::launch_experts(x, T, perm, offsets, shape->E, T * shape->K, shape->D, shape->I,
+                                             shape->dtype, weights->gate_up, weights->down, y, exw, stream),
                          "routed experts launch")) != MOE_OK)
         return st;
     if (sh != nullptr) {
-        if ((st = hip_status(moe::launch_experts(x, nullptr, nullptr, 1, T, shape->D, shape->Is, shape->dtype,
+        if ((st = hip_status(moe::launch_experts(x, T, nullptr, nullptr, 1, T, shape->D, shape->Is, shape->dtype,
                                                  weights->gate_up_shared, weights->down_shared, sh, exw, stream),
                              "shared expert launch")) != MOE_OK)
             return st;

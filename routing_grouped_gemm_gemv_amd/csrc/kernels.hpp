@@ -30,7 +30,8 @@ hipError_t launch_permute(const int32_t* ids, int64_t T, int K, int E, int32_t* 
 
 // ---- experts -----------------------------------------------------------------
 size_t experts_ws_bytes(int64_t rows_max, int G, int I, int dtype);
-hipError_t launch_experts(const void* x, const int32_t* perm_token, const int32_t* offsets,
+// x_rows: rows of x (the gathered rows index it); rows_max: rows of the output
+hipError_t launch_experts(const void* x, int64_t x_rows, const int32_t* perm_token, const int32_t* offsets,
                           int G, int64_t rows_max, int D, int I, int dtype, const void* gate_up,
                           const void* down, void* y, void* ws, hipStream_t stream);
 
