@@ -38,6 +38,9 @@
 #include "common.hpp"
 #include "kernels.hpp"
 
+// M0 is reserved to the compiler; the DMA asm below sets it on purpose
+#pragma clang diagnostic ignored "-Winline-asm"
+
 namespace moe {
 
 constexpr int kRowBytes = 128;  // bytes of one tile row per k slice
@@ -125,25 +128,58 @@ __device__ __forceinline__ int swz(int row, int chunk) { return row * kRowBytes 
 __device__ __forceinline__ float silu_mul(float g, float u) { return (g / (1.0f + expf(-g))) * u; }
 
 // ===========================================================================
-// bf16 operands: 256 x 256 tiles, direct-to-LDS slices
+// bf16 operands: 256 x 256 tiles, direct-to-LDS slices, 5-stage pipeline
 // ===========================================================================
 constexpr int kBM2 = 256;
 constexpr int kBN2 = 256;
-constexpr int kStage2 = (kBM2 + kBN2) * kRowBytes;  // 64 KiB: one A and one B slice
+constexpr int kSlice2 = 32;                         // k per slice
+constexpr int kRow2 = kSlice2 * 2;                  // 64 bytes per tile row per slice
+constexpr int kStage2 = (kBM2 + kBN2) * kRow2;      // 32 KiB: one A and one B slice
+constexpr int kStages2 = 5;                         // 160 KiB of LDS
+constexpr int kDmaPerSlice2 = 8;                    // DMA instructions per wave per slice
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) const void gbl_void_t;
 
-// 16 bytes per lane from global memory into LDS at wave_base + 16 * lane
-__device__ __forceinline__ void dma16(const void* g, uint8_t* wave_base) {
-    __builtin_amdgcn_global_load_lds((gbl_void_t*)g, (lds_void_t*)wave_base, 16, 0, 0);
+// 16 bytes per lane from global memory (base + 32-bit per-lane offset) into
+// LDS at wave_base + 16 * lane: global_load_lds_dwordx4 with M0 holding the
+// wave's LDS base.  It is issued from inline asm on purpose: the compiler's
+// wait-count tracking of LDS DMA cannot tell the stages of this pipeline
+// apart and would drain every DMA in flight before each fragment read.  The
+// instruction has no destination register; completion is awaited with the
+// explicit vmcnt waits of the pipeline, and no other code in these kernels
+// uses M0.
+__device__ __forceinline__ void dma16(const uint8_t* gbase, uint32_t voff, uint8_t* wave_base) {
+    const uint32_t lds = __builtin_amdgcn_readfirstlane(
+        static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)wave_base)));
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(lds), "v"(voff), "s"(gbase)
+                 : "memory", "m0");
 }
 
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x3F70); }  // vmcnt(0)
+// s_waitcnt with vmcnt(n) and the other counters left alone
+constexpr int vmcnt_imm(int n) { return 0x3F70 | (n & 15) | (((n >> 4) & 3) << 14); }
+template <int N>
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(vmcnt_imm(N)); }
+
+// Chunk swizzle of a 64-byte row (four 16-byte chunks): chunk ^ ((row / 2) % 4).
+// The eight lanes of a ds_read_b128 group read rows r..r+7 at one logical
+// chunk; the swizzle spreads them over all 32 banks.
+__device__ __forceinline__ int swz64(int row, int chunk) { return row * kRow2 + ((chunk ^ ((row >> 1) & 3)) << 4); }
 
 template <bool GATE_UP>
 __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmParams p) {
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kStage2];
+    // one array per stage: with compile-time stage indices the compiler can
+    // tell that a DMA in flight to one stage never aliases reads of another
+    __shared__ __attribute__((aligned(1024))) uint8_t lds0[kStage2];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds1[kStage2];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds2[kStage2];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds3[kStage2];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds4[kStage2];
+    auto stage = [&](int st) -> uint8_t* {
+        return st == 0 ? lds0 : st == 1 ? lds1 : st == 2 ? lds2 : st == 3 ? lds3 : lds4;
+    };
 
     TileCoord tc;
     if (!locate_tile<kBM2>(p, tc)) return;
@@ -154,21 +190,20 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmParams p) {
     const int wm = wv >> 1;
     const int wn = wv & 1;
 
-    // ---- per-lane sources of the 8 + 8 DMA instructions of this wave ------
-    // Instruction i fills rows wv*64 + 8i .. +7 of the A and B slices; lane l
-    // lands on row (l / 8) of that group at physical chunk l % 8, so it fetches
-    // logical chunk (l % 8) ^ (row % 8).
-    // Byte offsets fit 32 bits: x, the activations and one group's weights are
-    // each below 4 GiB (checked by the launcher), so the DMA addresses are a
-    // uniform base plus one 32-bit offset per instruction.
+    // ---- per-lane sources of the 4 + 4 DMA instructions of this wave ------
+    // Instruction i fills rows wv*64 + 16i .. +15 of the A (or B) slice; lane l
+    // lands on row l / 4 of that group at physical chunk l % 4, so it fetches
+    // the logical chunk (l % 4) ^ ((row / 2) % 4).  Byte offsets fit 32 bits:
+    // x, the activations and one group's weights are each below 4 GiB
+    // (checked by the launcher).
     const uint8_t* __restrict__ abase = static_cast<const uint8_t*>(p.a);
     const uint8_t* __restrict__ wbase =
         static_cast<const uint8_t*>(p.w) + static_cast<int64_t>(tc.g) * p.w_group_stride * 2;
-    const int chunk = (lane & 7) ^ ((lane >> 3) & 7);
-    uint32_t aoff[8], boff[8];
+    const int chunk = (lane & 3) ^ ((lane >> 3) & 3);
+    uint32_t aoff[4], boff[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int r = wv * 64 + 8 * i + (lane >> 3);
+    for (int i = 0; i < 4; ++i) {
+        const int r = wv * 64 + 16 * i + (lane >> 2);
         const int rr = r < tc.rows ? r : tc.rows - 1;  // rows past the group repeat its last row; never stored
         int64_t src = tc.m0 + rr;
         if (GATE_UP && p.perm != nullptr) src = p.perm[src];
@@ -184,16 +219,17 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmParams p) {
         }
         boff[i] = static_cast<uint32_t>(static_cast<int64_t>(wrow) * p.Kd * 2 + chunk * 16);
     }
-    uint8_t* const a_dst = smem + wv * 64 * kRowBytes;
-    uint8_t* const b_dst = smem + kBM2 * kRowBytes + wv * 64 * kRowBytes;
+    const int a_dst = wv * 64 * kRow2;
+    const int b_dst = kBM2 * kRow2 + wv * 64 * kRow2;
 
-    // LDS byte offsets of this lane's MFMA fragments: block b adds b * 16 rows;
-    // the swizzle term depends only on the lane (row % 8 == lane % 8)
-    const int a_frag = (wm * 128 + (lane & 15)) * kRowBytes;
-    const int b_frag = ((GATE_UP ? wn * 64 : wn * 128) + (lane & 15)) * kRowBytes;
+    // LDS byte offsets of this lane's MFMA fragments: block b adds b * 16 rows,
+    // and the swizzle term depends only on the lane (row % 16 == lane % 16)
+    const int xo = ((lane >> 4) ^ ((lane >> 1) & 3)) << 4;
+    const int a_frag = (wm * 128 + (lane & 15)) * kRow2 + xo;
+    const int b_frag = kBM2 * kRow2 + ((GATE_UP ? wn * 64 : wn * 128) + (lane & 15)) * kRow2 + xo;
     auto b_row_off = [&](int b) {
-        if (GATE_UP) return (b < 4 ? b * 16 : 128 + (b - 4) * 16) * kRowBytes;
-        return b * 16 * kRowBytes;
+        if (GATE_UP) return (b < 4 ? b * 16 : 128 + (b - 4) * 16) * kRow2;
+        return b * 16 * kRow2;
     };
 
     f32x4 acc[8][8];
@@ -202,43 +238,78 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmParams p) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int nk = p.Kd / 64;
+    // DMA instruction q (0..3: A rows, 4..7: B rows) of slice kt into stage
+    // kt % 5.  Slices past the end re-fetch the last slice: every step then
+    // issues the same eight instructions (uniform waits, no tail code), and
+    // the stage they land in is never read for results again.
+    const int nk = p.Kd / kSlice2;
+    auto dma = [&](int kt, int st, int q) {
+        uint8_t* sb = stage(st);
+        const uint32_t kb = static_cast<uint32_t>(kt < nk ? kt : nk - 1) * kRow2;
+        if (q < 4) dma16(abase, aoff[q] + kb, sb + a_dst + q * 16 * kRow2);
+        else dma16(wbase, boff[q - 4] + kb, sb + b_dst + (q - 4) * 16 * kRow2);
+    };
+    // Fragment k of the slice in stage st, in the order the MFMAs consume
+    // them: A block 0, B blocks 0..7, then A blocks 1..7.
+    auto frag = [&](int st, int k) -> u32x4 {
+        const uint8_t* base = stage(st);
+        if (k == 0) return *reinterpret_cast<const u32x4*>(base + a_frag);
+        if (k <= 8) return *reinterpret_cast<const u32x4*>(base + b_frag + b_row_off(k - 1));
+        return *reinterpret_cast<const u32x4*>(base + a_frag + (k - 8) * 16 * kRow2);
+    };
+
+    // Pipeline.  Slice kt lives in stage kt % 5.  At the top of step kt the
+    // fragments of slice kt are in registers (f) and the DMAs of slices
+    // kt+1 .. kt+4 are in flight.  The step waits for slice kt+1 only (the 24
+    // younger DMA instructions may stay outstanding), then a barrier makes it
+    // visible and proves every wave has read slice kt, whose stage then
+    // receives slice kt+5.  The 64 MFMAs of slice kt run with the 16 fragment
+    // reads of slice kt+1 spread through them (one per 4 MFMAs) and the 8 DMA
+    // instructions in their first half.
+    auto step = [&](int kt, int st, const u32x4 (&f)[16], u32x4 (&g)[16]) {
+        wait_vmem<(kStages2 - 2) * kDmaPerSlice2>();
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+        const int gst = st + 1 == kStages2 ? 0 : st + 1;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        dma16(abase + aoff[i], a_dst + i * 8 * kRowBytes);
-        dma16(wbase + boff[i], b_dst + i * 8 * kRowBytes);
-    }
-    wait_vmem();
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) {
-            const int st = (cur ^ 1) * kStage2;
-            const int kb = (kt + 1) * 128;  // bytes
+        for (int mb = 0; mb < 8; ++mb) {
+            const u32x4 a = mb == 0 ? f[0] : f[8 + mb];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                dma16(abase + (aoff[i] + kb), a_dst + st + i * 8 * kRowBytes);
-                dma16(wbase + (boff[i] + kb), b_dst + st + i * 8 * kRowBytes);
+            for (int h = 0; h < 2; ++h) {
+#pragma unroll
+                for (int nb = 4 * h; nb < 4 * h + 4; ++nb) acc[mb][nb] = mfma_bf16(a, f[1 + nb], acc[mb][nb]);
+                const int q = 2 * mb + h;
+                g[q] = frag(gst, q);
+                if (q < kDmaPerSlice2) dma(kt + kStages2, st, q);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
-        const uint8_t* sa = smem + cur * kStage2;
-        const uint8_t* sb = sa + kBM2 * kRowBytes;
+    };
+
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const int xo = ((4 * s + (lane >> 4)) ^ (lane & 7)) << 4;
-            u32x4 af[8], bf[8];
+    for (int j = 0; j < kStages2; ++j)
 #pragma unroll
-            for (int b = 0; b < 8; ++b) af[b] = *reinterpret_cast<const u32x4*>(sa + a_frag + xo + b * 16 * kRowBytes);
+        for (int q = 0; q < kDmaPerSlice2; ++q) dma(j, j, q);
+    wait_vmem<(kStages2 - 1) * kDmaPerSlice2>();
+    __syncthreads();
+    u32x4 f0[16], f1[16];
 #pragma unroll
-            for (int b = 0; b < 8; ++b) bf[b] = *reinterpret_cast<const u32x4*>(sb + b_frag + xo + b_row_off(b));
+    for (int k = 0; k < 16; ++k) f0[k] = frag(0, k);
+    // Ten steps per trip, so that stage indices (kt % 5) and the register
+    // sets (kt % 2) are compile-time constants; then the tail (nk is even).
+    int kt = 0;
+    for (; kt + 10 <= nk; kt += 10) {
 #pragma unroll
-            for (int mb = 0; mb < 8; ++mb)
-#pragma unroll
-                for (int nb = 0; nb < 8; ++nb) acc[mb][nb] = mfma_bf16(af[mb], bf[nb], acc[mb][nb]);
+        for (int j = 0; j < 10; j += 2) {
+            step(kt + j, j % kStages2, f0, f1);
+            step(kt + j + 1, (j + 1) % kStages2, f1, f0);
         }
-        wait_vmem();
-        __syncthreads();
     }
+    for (; kt < nk; kt += 2) {
+        step(kt, kt % kStages2, f0, f1);
+        step(kt + 1, (kt + 1) % kStages2, f1, f0);
+    }
+    wait_vmem<0>();
 
     // ---- epilogue ---------------------------------------------------------
     uint16_t* __restrict__ out = static_cast<uint16_t*>(p.out);
