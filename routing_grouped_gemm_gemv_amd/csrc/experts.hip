@@ -127,6 +127,12 @@ __device__ __forceinline__ int swz(int row, int chunk) { return row * kRowBytes 
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return (g / (1.0f + expf(-g))) * u; }
 
+// silu(g) * u with the hardware exponential and reciprocal (about 2 ulp in
+// float32); used where the activation is then rounded to bf16
+__device__ __forceinline__ float silu_mul_fast(float g, float u) {
+    return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
+
 // ===========================================================================
 // bf16 operands: 256 x 256 tiles, direct-to-LDS slices, 5-stage pipeline
 // ===========================================================================
@@ -278,9 +284,14 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmParams p) {
             for (int h = 0; h < 2; ++h) {
 #pragma unroll
                 for (int nb = 4 * h; nb < 4 * h + 4; ++nb) acc[mb][nb] = mfma_bf16(a, f[1 + nb], acc[mb][nb]);
+                // first half of the step: two fragment reads and one DMA per 4
+                // MFMAs, so the reads have landed before the next barrier
                 const int q = 2 * mb + h;
-                g[q] = frag(gst, q);
-                if (q < kDmaPerSlice2) dma(kt + kStages2, st, q);
+                if (q < 8) {
+                    g[2 * q] = frag(gst, 2 * q);
+                    g[2 * q + 1] = frag(gst, 2 * q + 1);
+                    dma(kt + kStages2, st, q);
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -323,7 +334,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmParams p) {
                 for (int i = 0; i < 4; ++i) {
                     const int row = wm * 128 + mb * 16 + 4 * (lane >> 4) + i;
                     if (row < tc.rows && col < p.I)
-                        out[(tc.m0 + row) * p.ldo + col] = f32_to_bf16(silu_mul(acc[mb][nb][i], acc[mb][nb + 4][i]));
+                        out[(tc.m0 + row) * p.ldo + col] = f32_to_bf16(silu_mul_fast(acc[mb][nb][i], acc[mb][nb + 4][i]));
                 }
             }
     } else {
