@@ -134,18 +134,11 @@ __device__ __forceinline__ float silu_mul_fast(float g, float u) {
 }
 
 // ===========================================================================
-// bf16 operands: 256 x 256 tiles, direct-to-LDS slices, 5-stage pipeline
+// bf16 operands: direct-to-LDS slices, deep pipeline
 // ===========================================================================
-constexpr int kBM2 = 256;
-constexpr int kBN2 = 256;
-constexpr int kSlice2 = 32;                         // k per slice
-constexpr int kRow2 = kSlice2 * 2;                  // 64 bytes per tile row per slice
-constexpr int kStage2 = (kBM2 + kBN2) * kRow2;      // 32 KiB: one A and one B slice
-constexpr int kStages2 = 5;                         // 160 KiB of LDS
-constexpr int kDmaPerSlice2 = 8;                    // DMA instructions per wave per slice
-
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) const void gbl_void_t;
+constexpr int kSlice2 = 32;   // k per slice
+constexpr int kRow2 = 64;     // bytes per tile row per slice
+constexpr int kLds2 = 160 * 1024;
 
 // 16 bytes per lane from global memory (base + 32-bit per-lane offset) into
 // LDS at wave_base + 16 * lane: global_load_lds_dwordx4 with M0 holding the
@@ -155,86 +148,209 @@ typedef __attribute__((address_space(1))) const void gbl_void_t;
 // instruction has no destination register; completion is awaited with the
 // explicit vmcnt waits of the pipeline, and no other code in these kernels
 // uses M0.
-__device__ __forceinline__ void dma16(const uint8_t* gbase, uint32_t voff, uint8_t* wave_base) {
-    const uint32_t lds = __builtin_amdgcn_readfirstlane(
-        static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)wave_base)));
+__device__ __forceinline__ void dma16(const uint8_t* gbase, uint32_t voff, uint32_t lds_wave_base) {
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
                  :
-                 : "s"(lds), "v"(voff), "s"(gbase)
+                 : "s"(lds_wave_base), "v"(voff), "s"(gbase)
                  : "memory", "m0");
 }
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
 
 // s_waitcnt with vmcnt(n) and the other counters left alone
 constexpr int vmcnt_imm(int n) { return 0x3F70 | (n & 15) | (((n >> 4) & 3) << 14); }
 template <int N>
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(vmcnt_imm(N)); }
 
-// Chunk swizzle of a 64-byte row (four 16-byte chunks): chunk ^ ((row / 2) % 4).
-// The eight lanes of a ds_read_b128 group read rows r..r+7 at one logical
-// chunk; the swizzle spreads them over all 32 banks.
-__device__ __forceinline__ int swz64(int row, int chunk) { return row * kRow2 + ((chunk ^ ((row >> 1) & 3)) << 4); }
+// Tiles of one group of c rows.  Full tiles are 256 rows x one n-tile.  When
+// the number of n-tiles is even, the last c % 256 rows, if at most 128, form
+// tail tiles of 128 rows x two n-tiles (the same work per wave as a full
+// tile), which halves the rows a group pads on average.
+struct GroupTiles {
+    int full;   // 256-row m-tiles
+    int tail;   // 1 if a 128-row tail exists
+};
+__host__ __device__ __forceinline__ GroupTiles group_tiles(int c, int n_tiles) {
+    GroupTiles t;
+    const int r = c & 255;
+    if ((n_tiles & 1) == 0 && r > 0 && r <= 128) {
+        t.full = c >> 8;
+        t.tail = 1;
+    } else {
+        t.full = (c + 255) >> 8;
+        t.tail = 0;
+    }
+    return t;
+}
+__host__ __device__ __forceinline__ int tiles_of(int c, int n_tiles) {
+    const GroupTiles t = group_tiles(c, n_tiles);
+    return t.tail ? (n_tiles >> 1) * (2 * t.full + 1) : n_tiles * t.full;
+}
 
-template <bool GATE_UP>
-__global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmParams p) {
-    // one array per stage: with compile-time stage indices the compiler can
-    // tell that a DMA in flight to one stage never aliases reads of another
-    __shared__ __attribute__((aligned(1024))) uint8_t lds0[kStage2];
-    __shared__ __attribute__((aligned(1024))) uint8_t lds1[kStage2];
-    __shared__ __attribute__((aligned(1024))) uint8_t lds2[kStage2];
-    __shared__ __attribute__((aligned(1024))) uint8_t lds3[kStage2];
-    __shared__ __attribute__((aligned(1024))) uint8_t lds4[kStage2];
-    auto stage = [&](int st) -> uint8_t* {
-        return st == 0 ? lds0 : st == 1 ? lds1 : st == 2 ? lds2 : st == 3 ? lds3 : lds4;
-    };
+// Tile prefix sums of both GEMMs (gate_up and down have different n-tiles).
+__global__ __launch_bounds__(1024) void build_tiles_bf16_kernel(const int32_t* __restrict__ offsets, int G,
+                                                                int nt1, int nt2, int32_t* __restrict__ ts1,
+                                                                int32_t* __restrict__ ts2) {
+    __shared__ int part1[1024];
+    __shared__ int part2[1024];
+    const int tid = threadIdx.x;
+    int a = 0, b = 0;
+    if (tid < G) {
+        const int c = offsets[tid + 1] - offsets[tid];
+        a = tiles_of(c, nt1);
+        b = tiles_of(c, nt2);
+    }
+    part1[tid] = a;
+    part2[tid] = b;
+    __syncthreads();
+    for (int d = 1; d < 1024; d <<= 1) {
+        const int v1 = tid >= d ? part1[tid - d] : 0;
+        const int v2 = tid >= d ? part2[tid - d] : 0;
+        __syncthreads();
+        part1[tid] += v1;
+        part2[tid] += v2;
+        __syncthreads();
+    }
+    if (tid < G) {
+        ts1[tid] = part1[tid] - a;
+        ts2[tid] = part2[tid] - b;
+    }
+    if (tid == G - 1) {
+        ts1[G] = part1[tid];
+        ts2[G] = part2[tid];
+    }
+}
 
-    TileCoord tc;
-    if (!locate_tile<kBM2>(p, tc)) return;
+struct Tile2 {
+    int g;
+    int64_t m0;
+    int rows;
+    int n;      // first n-tile
+    bool tail;  // 128 rows x two n-tiles
+};
+
+// Tile order inside a group: for each pair of n-tiles, the full tiles of the
+// first n-tile (m fastest), those of the second, then the pair's tail tile,
+// so the tail reads weight slices its group's full tiles have just used.
+__device__ __forceinline__ bool locate_tile2(const GemmParams& p, Tile2& t) {
+    int64_t total;
+    if (p.offsets == nullptr) total = tiles_of(static_cast<int>(p.ident_rows), p.n_tiles);
+    else total = p.tile_start[p.G];
+    const int64_t padded = (total + 7) & ~static_cast<int64_t>(7);
+    if (static_cast<int64_t>(blockIdx.x) >= padded) return false;
+    const int64_t L = xcd_remap(blockIdx.x, padded);
+    if (L >= total) return false;
+    int g = 0;
+    int64_t base = 0, local = L;
+    int c;
+    if (p.offsets == nullptr) {
+        c = static_cast<int>(p.ident_rows);
+    } else {
+        int lo = 0, hi = p.G - 1;  // last g with tile_start[g] <= L (empty groups share a start)
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (p.tile_start[mid] <= L) lo = mid; else hi = mid - 1;
+        }
+        g = lo;
+        base = p.offsets[g];
+        local = L - p.tile_start[g];
+        c = p.offsets[g + 1] - p.offsets[g];
+    }
+    const GroupTiles gt = group_tiles(c, p.n_tiles);
+    t.g = g;
+    int n, m;
+    bool tail = false;
+    if (gt.tail) {
+        const int per_pair = 2 * gt.full + 1;
+        const int j = static_cast<int>(local / per_pair);
+        const int rem = static_cast<int>(local % per_pair);
+        if (rem < 2 * gt.full) {
+            n = 2 * j + rem / gt.full;
+            m = rem % gt.full;
+        } else {
+            n = 2 * j;
+            m = gt.full;
+            tail = true;
+        }
+    } else {
+        n = static_cast<int>(local / gt.full);
+        m = static_cast<int>(local % gt.full);
+    }
+    t.n = n;
+    t.tail = tail;
+    t.m0 = base + static_cast<int64_t>(m) * 256;
+    const int left = c - m * 256;
+    t.rows = left < 256 ? left : 256;
+    return true;
+}
+
+// One tile of BM rows x BN weight rows (gate_up: BN/2 gate rows and the
+// matching BN/2 up rows) through a STAGES-deep pipeline of 32-wide k slices.
+// Four waves; each computes a 128 x 128 block (64 MFMA accumulators of
+// 16 x 16): with BM = 256 the waves are 2 x 2, with BM = 128 they are 1 x 4.
+template <bool GATE_UP, int BM, int BN, int STAGES>
+__device__ __forceinline__ void tile_pipeline(const GemmParams& p, const Tile2& tc, lds_u8* smem) {
+    constexpr int kWN = BM == 256 ? 2 : 4;               // waves along n
+    constexpr int kStage = (BM + BN) * kRow2;            // bytes per stage
+    constexpr int kDmaA = BM / 64;                       // 16-row DMA instructions per wave per slice
+    constexpr int kDmaB = BN / 64;
+    constexpr int kDma = kDmaA + kDmaB;
+    static_assert(kStage * STAGES <= kLds2, "LDS");
+    static_assert(kDma <= 16, "DMA issue slots");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wv = tid >> 6;
-    const int wm = wv >> 1;
-    const int wn = wv & 1;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
+    const int wm = wv / kWN;
+    const int wn = wv % kWN;
+    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem));
 
-    // ---- per-lane sources of the 4 + 4 DMA instructions of this wave ------
-    // Instruction i fills rows wv*64 + 16i .. +15 of the A (or B) slice; lane l
-    // lands on row l / 4 of that group at physical chunk l % 4, so it fetches
-    // the logical chunk (l % 4) ^ ((row / 2) % 4).  Byte offsets fit 32 bits:
-    // x, the activations and one group's weights are each below 4 GiB
+    // ---- per-lane DMA sources ---------------------------------------------
+    // A instruction i fills rows wv*(BM/4) + 16i .. +15; B instruction i fills
+    // weight rows wv*(BN/4) + 16i .. +15.  Lane l lands on row l / 4 of its
+    // group at physical chunk l % 4 of the 64-byte row, so it fetches the
+    // logical chunk (l % 4) ^ ((row / 2) % 4), the swizzle that spreads the
+    // eight lanes of a fragment read over all 32 banks.  Byte offsets fit 32
+    // bits: x, the activations and one group's weights are each below 4 GiB
     // (checked by the launcher).
     const uint8_t* __restrict__ abase = static_cast<const uint8_t*>(p.a);
     const uint8_t* __restrict__ wbase =
         static_cast<const uint8_t*>(p.w) + static_cast<int64_t>(tc.g) * p.w_group_stride * 2;
     const int chunk = (lane & 3) ^ ((lane >> 3) & 3);
-    uint32_t aoff[4], boff[4];
+    uint32_t aoff[kDmaA], boff[kDmaB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = wv * 64 + 16 * i + (lane >> 2);
+    for (int i = 0; i < kDmaA; ++i) {
+        const int r = wv * (BM / 4) + 16 * i + (lane >> 2);
         const int rr = r < tc.rows ? r : tc.rows - 1;  // rows past the group repeat its last row; never stored
         int64_t src = tc.m0 + rr;
         if (GATE_UP && p.perm != nullptr) src = p.perm[src];
         aoff[i] = static_cast<uint32_t>(src * p.Kd * 2 + chunk * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < kDmaB; ++i) {
+        const int r = wv * (BN / 4) + 16 * i + (lane >> 2);
         int wrow;
         if (GATE_UP) {
-            int c = tc.n * 128 + (r & 127);  // gate row; the matching up row is I + c
-            if (c >= p.I) c = p.I - 1;       // I % 128 == 64: last tile half full
-            wrow = r < 128 ? c : p.I + c;
+            int c = tc.n * 128 + (r % (BN / 2));  // gate row; the matching up row is I + c
+            if (c >= p.I) c = p.I - 1;           // I % 128 == 64: last tile half full
+            wrow = r < BN / 2 ? c : p.I + c;
         } else {
-            wrow = tc.n * kBN2 + r;
+            wrow = tc.n * 256 + r;
             if (wrow >= p.ldo) wrow = p.ldo - 1;
         }
         boff[i] = static_cast<uint32_t>(static_cast<int64_t>(wrow) * p.Kd * 2 + chunk * 16);
     }
-    const int a_dst = wv * 64 * kRow2;
-    const int b_dst = kBM2 * kRow2 + wv * 64 * kRow2;
+    const int a_dst = wv * (BM / 4) * kRow2;
+    const int b_dst = BM * kRow2 + wv * (BN / 4) * kRow2;
 
     // LDS byte offsets of this lane's MFMA fragments: block b adds b * 16 rows,
     // and the swizzle term depends only on the lane (row % 16 == lane % 16)
     const int xo = ((lane >> 4) ^ ((lane >> 1) & 3)) << 4;
     const int a_frag = (wm * 128 + (lane & 15)) * kRow2 + xo;
-    const int b_frag = kBM2 * kRow2 + ((GATE_UP ? wn * 64 : wn * 128) + (lane & 15)) * kRow2 + xo;
+    const int b_frag = BM * kRow2 + ((GATE_UP ? wn * 64 : wn * 128) + (lane & 15)) * kRow2 + xo;
     auto b_row_off = [&](int b) {
-        if (GATE_UP) return (b < 4 ? b * 16 : 128 + (b - 4) * 16) * kRow2;
+        if (GATE_UP) return (b < 4 ? b * 16 : BN / 2 + (b - 4) * 16) * kRow2;
         return b * 16 * kRow2;
     };
 
@@ -244,39 +360,38 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmParams p) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // DMA instruction q (0..3: A rows, 4..7: B rows) of slice kt into stage
-    // kt % 5.  Slices past the end re-fetch the last slice: every step then
-    // issues the same eight instructions (uniform waits, no tail code), and
-    // the stage they land in is never read for results again.
+    // DMA instruction q (A first, then B) of slice kt into its stage.  Slices
+    // past the end re-fetch the last slice: every step then issues the same
+    // instructions (uniform waits, no tail code), and the stage they land in
+    // is never read for results again.
     const int nk = p.Kd / kSlice2;
-    auto dma = [&](int kt, int st, int q) {
-        uint8_t* sb = stage(st);
+    auto dma = [&](int kt, uint32_t stage_off, int q) {
         const uint32_t kb = static_cast<uint32_t>(kt < nk ? kt : nk - 1) * kRow2;
-        if (q < 4) dma16(abase, aoff[q] + kb, sb + a_dst + q * 16 * kRow2);
-        else dma16(wbase, boff[q - 4] + kb, sb + b_dst + (q - 4) * 16 * kRow2);
+        if (q < kDmaA) dma16(abase, aoff[q] + kb, lds0 + stage_off + a_dst + q * 16 * kRow2);
+        else dma16(wbase, boff[q - kDmaA] + kb, lds0 + stage_off + b_dst + (q - kDmaA) * 16 * kRow2);
     };
-    // Fragment k of the slice in stage st, in the order the MFMAs consume
+    // Fragment k of the slice in a stage, in the order the MFMAs consume
     // them: A block 0, B blocks 0..7, then A blocks 1..7.
-    auto frag = [&](int st, int k) -> u32x4 {
-        const uint8_t* base = stage(st);
-        if (k == 0) return *reinterpret_cast<const u32x4*>(base + a_frag);
-        if (k <= 8) return *reinterpret_cast<const u32x4*>(base + b_frag + b_row_off(k - 1));
-        return *reinterpret_cast<const u32x4*>(base + a_frag + (k - 8) * 16 * kRow2);
+    auto frag = [&](uint32_t stage_off, int k) -> u32x4 {
+        const lds_u8* st = smem + stage_off;
+        if (k == 0) return *reinterpret_cast<lds_u32x4*>(st + a_frag);
+        if (k <= 8) return *reinterpret_cast<lds_u32x4*>(st + b_frag + b_row_off(k - 1));
+        return *reinterpret_cast<lds_u32x4*>(st + a_frag + (k - 8) * 16 * kRow2);
     };
 
-    // Pipeline.  Slice kt lives in stage kt % 5.  At the top of step kt the
-    // fragments of slice kt are in registers (f) and the DMAs of slices
-    // kt+1 .. kt+4 are in flight.  The step waits for slice kt+1 only (the 24
-    // younger DMA instructions may stay outstanding), then a barrier makes it
-    // visible and proves every wave has read slice kt, whose stage then
-    // receives slice kt+5.  The 64 MFMAs of slice kt run with the 16 fragment
-    // reads of slice kt+1 spread through them (one per 4 MFMAs) and the 8 DMA
-    // instructions in their first half.
-    auto step = [&](int kt, int st, const u32x4 (&f)[16], u32x4 (&g)[16]) {
-        wait_vmem<(kStages2 - 2) * kDmaPerSlice2>();
+    // Pipeline.  Slice kt lives in stage kt % STAGES.  At the top of step kt
+    // the fragments of slice kt are in registers (f) and the DMAs of the next
+    // STAGES-1 slices are in flight.  The step waits for slice kt+1 only,
+    // then a barrier makes it visible and proves every wave has read slice
+    // kt, whose stage then receives slice kt+STAGES.  The 64 MFMAs of slice kt
+    // run with the 16 fragment reads of slice kt+1 and this step's DMAs issued
+    // during their first half, so the reads land before the next barrier.
+    auto step = [&](int kt, const u32x4 (&f)[16], u32x4 (&g)[16]) {
+        wait_vmem<(STAGES - 2) * kDma>();
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
-        const int gst = st + 1 == kStages2 ? 0 : st + 1;
+        const uint32_t cur = static_cast<uint32_t>(kt % STAGES) * kStage;
+        const uint32_t nxt = static_cast<uint32_t>((kt + 1) % STAGES) * kStage;
 #pragma unroll
         for (int mb = 0; mb < 8; ++mb) {
             const u32x4 a = mb == 0 ? f[0] : f[8 + mb];
@@ -284,41 +399,30 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmParams p) {
             for (int h = 0; h < 2; ++h) {
 #pragma unroll
                 for (int nb = 4 * h; nb < 4 * h + 4; ++nb) acc[mb][nb] = mfma_bf16(a, f[1 + nb], acc[mb][nb]);
-                // first half of the step: two fragment reads and one DMA per 4
-                // MFMAs, so the reads have landed before the next barrier
                 const int q = 2 * mb + h;
                 if (q < 8) {
-                    g[2 * q] = frag(gst, 2 * q);
-                    g[2 * q + 1] = frag(gst, 2 * q + 1);
-                    dma(kt + kStages2, st, q);
+                    g[2 * q] = frag(nxt, 2 * q);
+                    g[2 * q + 1] = frag(nxt, 2 * q + 1);
                 }
+                if (q < kDma) dma(kt + STAGES, cur, q);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
     };
 
 #pragma unroll
-    for (int j = 0; j < kStages2; ++j)
+    for (int j = 0; j < STAGES; ++j)
 #pragma unroll
-        for (int q = 0; q < kDmaPerSlice2; ++q) dma(j, j, q);
-    wait_vmem<(kStages2 - 1) * kDmaPerSlice2>();
+        for (int q = 0; q < kDma; ++q) dma(j, j * kStage, q);
+    wait_vmem<(STAGES - 1) * kDma>();
     __syncthreads();
     u32x4 f0[16], f1[16];
 #pragma unroll
     for (int k = 0; k < 16; ++k) f0[k] = frag(0, k);
-    // Ten steps per trip, so that stage indices (kt % 5) and the register
-    // sets (kt % 2) are compile-time constants; then the tail (nk is even).
-    int kt = 0;
-    for (; kt + 10 <= nk; kt += 10) {
-#pragma unroll
-        for (int j = 0; j < 10; j += 2) {
-            step(kt + j, j % kStages2, f0, f1);
-            step(kt + j + 1, (j + 1) % kStages2, f1, f0);
-        }
-    }
-    for (; kt < nk; kt += 2) {
-        step(kt, kt % kStages2, f0, f1);
-        step(kt + 1, (kt + 1) % kStages2, f1, f0);
+    // nk is even: D and I are multiples of 64
+    for (int kt = 0; kt < nk; kt += 2) {
+        step(kt, f0, f1);
+        step(kt + 1, f1, f0);
     }
     wait_vmem<0>();
 
@@ -342,7 +446,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmParams p) {
         for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
             for (int nb = 0; nb < 8; ++nb) {
-                const int col = tc.n * kBN2 + wn * 128 + nb * 16 + (lane & 15);
+                const int col = tc.n * 256 + wn * 128 + nb * 16 + (lane & 15);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int row = wm * 128 + mb * 16 + 4 * (lane >> 4) + i;
@@ -350,6 +454,16 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmParams p) {
                 }
             }
     }
+}
+
+template <bool GATE_UP>
+__global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmParams p) {
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[kLds2];
+    Tile2 tc;
+    if (!locate_tile2(p, tc)) return;
+    lds_u8* lds = (lds_u8*)(smem);  // the array lives in LDS: an address-space cast
+    if (tc.tail) tile_pipeline<GATE_UP, 128, 512, 4>(p, tc, lds);
+    else tile_pipeline<GATE_UP, 256, 256, 5>(p, tc, lds);
 }
 
 // ===========================================================================
@@ -501,69 +615,76 @@ static size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255);
 
 size_t experts_ws_bytes(int64_t rows_max, int G, int I, int dtype) {
     const size_t eb = dtype == 0 ? 2 : 4;
-    return align256(sizeof(int32_t) * (G + 1)) + align256(static_cast<size_t>(rows_max) * I * eb);
+    return align256(2 * sizeof(int32_t) * (G + 1)) + align256(static_cast<size_t>(rows_max) * I * eb);
 }
 
 hipError_t launch_experts(const void* x, int64_t x_rows, const int32_t* perm_token, const int32_t* offsets, int G,
                           int64_t rows_max, int D, int I, int dtype, const void* gate_up, const void* down,
                           void* y, void* ws, hipStream_t stream) {
     const bool bf16 = dtype == 0;
-    const int BM = bf16 ? kBM2 : kBM1;
-    const int gate_cols = bf16 ? 128 : 64;   // gate (and up) rows per gate_up tile
-    const int down_cols = bf16 ? kBN2 : kBN1;
-    int32_t* tile_start = static_cast<int32_t*>(ws);
-    void* act = static_cast<uint8_t*>(ws) + align256(sizeof(int32_t) * (G + 1));
-    if (offsets != nullptr) {
-        build_tiles_kernel<<<1, 1024, 0, stream>>>(offsets, G, BM, tile_start);
-        hipError_t err = hipGetLastError();
-        if (err != hipSuccess) return err;
-    }
-    // upper bound of m-tiles: every group adds at most one partial tile
-    const int64_t mt_max = (rows_max + BM - 1) / BM + (offsets != nullptr ? G : 0);
+    int32_t* ts1 = static_cast<int32_t*>(ws);
+    int32_t* ts2 = ts1 + (G + 1);
+    void* act = static_cast<uint8_t*>(ws) + align256(2 * sizeof(int32_t) * (G + 1));
 
     GemmParams p1{};
     p1.a = x;
     p1.perm = perm_token;
     p1.offsets = offsets;
-    p1.tile_start = offsets != nullptr ? tile_start : nullptr;
     p1.ident_rows = rows_max;
     p1.G = G;
     p1.Kd = D;
     p1.w = gate_up;
     p1.w_group_stride = static_cast<int64_t>(2) * I * D;
     p1.I = I;
-    p1.n_tiles = (I + gate_cols - 1) / gate_cols;
     p1.out = act;
     p1.ldo = I;
-    const int64_t nwg1 = ((mt_max * p1.n_tiles) + 7) & ~static_cast<int64_t>(7);
-
     GemmParams p2 = p1;
     p2.a = act;
     p2.perm = nullptr;
     p2.Kd = I;
     p2.w = down;
     p2.w_group_stride = static_cast<int64_t>(D) * I;
-    p2.n_tiles = (D + down_cols - 1) / down_cols;
     p2.out = y;
     p2.ldo = D;
-    const int64_t nwg2 = ((mt_max * p2.n_tiles) + 7) & ~static_cast<int64_t>(7);
 
+    hipError_t err;
     if (bf16) {
         // the bf16 kernel addresses x, the activations and one group's weights
         // with 32-bit byte offsets
         const int64_t lim = static_cast<int64_t>(1) << 32;
         if (static_cast<int64_t>(2) * I * D * 2 >= lim || rows_max * I * 2 >= lim || x_rows * D * 2 >= lim)
             return hipErrorInvalidValue;
+        p1.n_tiles = (I + 127) / 128;
+        p2.n_tiles = (D + 255) / 256;
+        if (offsets != nullptr) {
+            build_tiles_bf16_kernel<<<1, 1024, 0, stream>>>(offsets, G, p1.n_tiles, p2.n_tiles, ts1, ts2);
+            if ((err = hipGetLastError()) != hipSuccess) return err;
+            p1.tile_start = ts1;
+            p2.tile_start = ts2;
+        }
+        // upper bound of tiles: every group adds at most one partial m-tile
+        const int64_t mt_max = (rows_max + 255) / 256 + (offsets != nullptr ? G : 0);
+        const int64_t nwg1 = ((mt_max * p1.n_tiles) + 7) & ~static_cast<int64_t>(7);
+        const int64_t nwg2 = ((mt_max * p2.n_tiles) + 7) & ~static_cast<int64_t>(7);
         grouped_gemm_bf16_kernel<true><<<static_cast<unsigned>(nwg1), 256, 0, stream>>>(p1);
-        hipError_t err = hipGetLastError();
-        if (err != hipSuccess) return err;
+        if ((err = hipGetLastError()) != hipSuccess) return err;
         grouped_gemm_bf16_kernel<false><<<static_cast<unsigned>(nwg2), 256, 0, stream>>>(p2);
-    } else {
-        grouped_gemm_f32_kernel<true><<<static_cast<unsigned>(nwg1), 256, 0, stream>>>(p1);
-        hipError_t err = hipGetLastError();
-        if (err != hipSuccess) return err;
-        grouped_gemm_f32_kernel<false><<<static_cast<unsigned>(nwg2), 256, 0, stream>>>(p2);
+        return hipGetLastError();
     }
+    p1.n_tiles = (I + 63) / 64;
+    p2.n_tiles = (D + kBN1 - 1) / kBN1;
+    if (offsets != nullptr) {
+        build_tiles_kernel<<<1, 1024, 0, stream>>>(offsets, G, kBM1, ts1);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+        p1.tile_start = ts1;
+        p2.tile_start = ts1;
+    }
+    const int64_t mt_max = (rows_max + kBM1 - 1) / kBM1 + (offsets != nullptr ? G : 0);
+    const int64_t nwg1 = ((mt_max * p1.n_tiles) + 7) & ~static_cast<int64_t>(7);
+    const int64_t nwg2 = ((mt_max * p2.n_tiles) + 7) & ~static_cast<int64_t>(7);
+    grouped_gemm_f32_kernel<true><<<static_cast<unsigned>(nwg1), 256, 0, stream>>>(p1);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    grouped_gemm_f32_kernel<false><<<static_cast<unsigned>(nwg2), 256, 0, stream>>>(p2);
     return hipGetLastError();
 }
 
