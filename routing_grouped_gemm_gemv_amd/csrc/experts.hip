@@ -399,12 +399,16 @@ __device__ __forceinline__ void tile_pipeline(const GemmParams& p, const Tile2& 
             for (int h = 0; h < 2; ++h) {
 #pragma unroll
                 for (int nb = 4 * h; nb < 4 * h + 4; ++nb) acc[mb][nb] = mfma_bf16(a, f[1 + nb], acc[mb][nb]);
+                // fragment reads in the first half (so they land before the
+                // next barrier); DMAs spread over the whole step so the
+                // address unit never queues more than the MFMA stream hides
                 const int q = 2 * mb + h;
                 if (q < 8) {
                     g[2 * q] = frag(nxt, 2 * q);
                     g[2 * q + 1] = frag(nxt, 2 * q + 1);
                 }
-                if (q < kDma) dma(kt + STAGES, cur, q);
+                constexpr int kEvery = 16 / kDma;  // 2 for eight DMAs, 1 for ten
+                if (q % kEvery == kEvery - 1 && q / kEvery < kDma) dma(kt + STAGES, cur, q / kEvery);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
