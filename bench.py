@@ -37,9 +37,52 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="dsv4", choices=["dsv4", "qnext", "q30", "dspark", "tiny"])
     ap.add_argument("--tokens", type=int, default=0, help="override T (0: the config's T)")
-    ap.add_argument("--cpu-sample", type=int, default=128, help="tokens timed on the CPU oracle (0: skip)")
+    ap.add_argument("--cpu-sample", type=int, default=384, help="tokens timed on the CPU oracle (0: skip)")
     ap.add_argument("--no-invariance", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only copy a 1 GiB buffer 5 times (reference kernel for the HBM byte counters)")
     return ap.parse_args()
+
+
+COPY_BYTES = 1 << 30
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "dsv4_experts_traffic.json")
+KERNEL_SOURCES = ("experts.hip", "common.hpp", "kernels.hpp")
+
+
+def kernel_source_hash() -> str:
+    """sha256 of the sources of the grouped-GEMM kernels."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "routing_grouped_gemm_gemv_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per launch of the routed expert GEMMs from the committed counter
+    record, or None when the kernels changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_RECORD) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != kernel_source_hash() or rec.get("workload") != workload:
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def copy_calibration():
+    """A plain device copy of known size: FETCH_SIZE and WRITE_SIZE should each
+    read COPY_BYTES per dispatch; the ratio scales the counters of other kernels."""
+    import torch
+    a = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": COPY_BYTES, "dispatches": 5}), flush=True)
 
 
 def stage_bytes(cfg, T, nvalid_pairs):
@@ -54,6 +97,9 @@ def stage_bytes(cfg, T, nvalid_pairs):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1 "
                                    "(the multi-GPU expert-parallel design is described, not built)"}))
@@ -201,7 +247,7 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": achieved / peak,
-            "traffic": None,
+            "traffic": recorded_traffic(f"{cfg.name}-T{T}") if cfg.name == "dsv4" else None,
         },
         "layer_tflops": layer_flops / (ms_per_step * 1e-3) / 1e12,
         "stage_ms": stage_ms,
