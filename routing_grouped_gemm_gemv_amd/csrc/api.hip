@@ -87,7 +87,7 @@ size_t elem_bytes(int dtype) { return dtype == MOE_BF16 ? 2 : 4; }
 
 size_t route_ws(const moe_shape* s) { return align256(sizeof(double) * static_cast<size_t>(s->T) * s->E); }
 size_t permute_ws(const moe_shape* s) { return align256(moe::permute_ws_bytes(s->T * s->K, s->E)); }
-size_t experts_ws(const moe_shape* s) { return align256(moe::experts_ws_bytes(s->T * s->K, s->E, s->I, s->dtype)); }
+size_t experts_ws(const moe_shape* s) { return align256(moe::experts_ws_bytes(s->T * s->K, s->E, s->D, s->I, s->dtype)); }
 
 // Workspace of moe_forward, in order: logits64, ids, weights, counts, offsets,
 // perm_token, inv_pos, permute scratch, expert scratch, y, shared_out.
@@ -114,8 +114,8 @@ ForwardLayout forward_layout(const moe_shape* s) {
     L.perm = take(sizeof(int32_t) * P);
     L.inv = take(sizeof(int32_t) * P);
     L.perm_ws = take(moe::permute_ws_bytes(static_cast<int64_t>(P), s->E));
-    const size_t ex_routed = moe::experts_ws_bytes(static_cast<int64_t>(P), s->E, s->I, s->dtype);
-    const size_t ex_shared = s->Is > 0 ? moe::experts_ws_bytes(s->T, 1, s->Is, s->dtype) : 0;
+    const size_t ex_routed = moe::experts_ws_bytes(static_cast<int64_t>(P), s->E, s->D, s->I, s->dtype);
+    const size_t ex_shared = s->Is > 0 ? moe::experts_ws_bytes(s->T, 1, s->D, s->Is, s->dtype) : 0;
     L.exp_ws = take(ex_routed > ex_shared ? ex_routed : ex_shared);
     L.y = take(eb * P * s->D);
     L.shared = take(s->Is > 0 ? eb * T * s->D : 0);
@@ -159,12 +159,10 @@ moe_status moe_route(const moe_shape* shape, const void* x, const void* router, 
         return fail(MOE_ERR_WORKSPACE, "moe_route needs %zu workspace bytes, got %zu", route_ws(shape), ws ? ws_bytes : 0);
     if ((st = check_device()) != MOE_OK) return st;
     double* l64 = static_cast<double*>(ws);
-    if ((st = hip_status(moe::launch_router_logits(x, router, shape->T, shape->D, shape->E, shape->dtype, l64, stream),
-                         "router logits launch")) != MOE_OK)
-        return st;
-    if ((st = hip_status(moe::launch_topk(l64, shape->T, shape->E, shape->K, shape->score, shape->renorm,
-                                          shape->route_scale, sel_bias, mask, logits, topk_ids, topk_w, stream),
-                         "top-k launch")) != MOE_OK)
+    if ((st = hip_status(moe::launch_route(x, router, shape->T, shape->D, shape->E, shape->K, shape->dtype,
+                                           shape->score, shape->renorm, shape->route_scale, sel_bias, mask, l64,
+                                           logits, topk_ids, topk_w, stream),
+                         "routing launch")) != MOE_OK)
         return st;
     return ok();
 }
@@ -254,12 +252,10 @@ moe_status moe_forward(const moe_shape* shape, const moe_weights* weights, const
     void* exw = base + L.exp_ws;
     const int64_t T = shape->T;
 
-    if ((st = hip_status(moe::launch_router_logits(x, weights->router, T, shape->D, shape->E, shape->dtype, l64, stream),
-                         "router logits launch")) != MOE_OK)
-        return st;
-    if ((st = hip_status(moe::launch_topk(l64, T, shape->E, shape->K, shape->score, shape->renorm, shape->route_scale,
-                                          sel_bias, mask, tr.logits, ids, tw, stream),
-                         "top-k launch")) != MOE_OK)
+    if ((st = hip_status(moe::launch_route(x, weights->router, T, shape->D, shape->E, shape->K, shape->dtype,
+                                           shape->score, shape->renorm, shape->route_scale, sel_bias, mask, l64,
+                                           tr.logits, ids, tw, stream),
+                         "routing launch")) != MOE_OK)
         return st;
     if ((st = hip_status(moe::launch_permute(ids, T, shape->K, shape->E, reinterpret_cast<int32_t*>(base + L.perm_ws),
                                              counts, offsets, perm, inv, stream),

@@ -49,7 +49,8 @@ struct GemmParams {
     const void* a;             // gate_up: x [*, Kd] (rows via perm); down: act [rows, Kd]
     const int32_t* perm;       // gate_up: perm_token or nullptr (identity)
     const int32_t* offsets;    // [G+1] or nullptr (one group of ident_rows rows)
-    const int32_t* tile_start; // [G+1] m-tile prefix sums (with offsets)
+    const int32_t* tile_start; // fp32 kernel: [G+1] m-tile prefix sums (with offsets)
+    const u32x4* tiles;        // bf16 kernel: one descriptor per workgroup (with offsets)
     int64_t ident_rows;
     int G;
     int Kd;                    // reduction length
@@ -133,6 +134,11 @@ __device__ __forceinline__ float silu_mul_fast(float g, float u) {
     return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
 }
 
+// two floats -> two bf16 (round to nearest even), low half first
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+    return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
 // ===========================================================================
 // bf16 operands: direct-to-LDS slices, deep pipeline
 // ===========================================================================
@@ -188,40 +194,6 @@ __host__ __device__ __forceinline__ int tiles_of(int c, int n_tiles) {
     return t.tail ? (n_tiles >> 1) * (2 * t.full + 1) : n_tiles * t.full;
 }
 
-// Tile prefix sums of both GEMMs (gate_up and down have different n-tiles).
-__global__ __launch_bounds__(1024) void build_tiles_bf16_kernel(const int32_t* __restrict__ offsets, int G,
-                                                                int nt1, int nt2, int32_t* __restrict__ ts1,
-                                                                int32_t* __restrict__ ts2) {
-    __shared__ int part1[1024];
-    __shared__ int part2[1024];
-    const int tid = threadIdx.x;
-    int a = 0, b = 0;
-    if (tid < G) {
-        const int c = offsets[tid + 1] - offsets[tid];
-        a = tiles_of(c, nt1);
-        b = tiles_of(c, nt2);
-    }
-    part1[tid] = a;
-    part2[tid] = b;
-    __syncthreads();
-    for (int d = 1; d < 1024; d <<= 1) {
-        const int v1 = tid >= d ? part1[tid - d] : 0;
-        const int v2 = tid >= d ? part2[tid - d] : 0;
-        __syncthreads();
-        part1[tid] += v1;
-        part2[tid] += v2;
-        __syncthreads();
-    }
-    if (tid < G) {
-        ts1[tid] = part1[tid] - a;
-        ts2[tid] = part2[tid] - b;
-    }
-    if (tid == G - 1) {
-        ts1[G] = part1[tid];
-        ts2[G] = part2[tid];
-    }
-}
-
 struct Tile2 {
     int g;
     int64_t m0;
@@ -230,37 +202,13 @@ struct Tile2 {
     bool tail;  // 128 rows x two n-tiles
 };
 
-// Tile order inside a group: for each pair of n-tiles, the full tiles of the
-// first n-tile (m fastest), those of the second, then the pair's tail tile,
-// so the tail reads weight slices its group's full tiles have just used.
-__device__ __forceinline__ bool locate_tile2(const GemmParams& p, Tile2& t) {
-    int64_t total;
-    if (p.offsets == nullptr) total = tiles_of(static_cast<int>(p.ident_rows), p.n_tiles);
-    else total = p.tile_start[p.G];
-    const int64_t padded = (total + 7) & ~static_cast<int64_t>(7);
-    if (static_cast<int64_t>(blockIdx.x) >= padded) return false;
-    const int64_t L = xcd_remap(blockIdx.x, padded);
-    if (L >= total) return false;
-    int g = 0;
-    int64_t base = 0, local = L;
-    int c;
-    if (p.offsets == nullptr) {
-        c = static_cast<int>(p.ident_rows);
-    } else {
-        int lo = 0, hi = p.G - 1;  // last g with tile_start[g] <= L (empty groups share a start)
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (p.tile_start[mid] <= L) lo = mid; else hi = mid - 1;
-        }
-        g = lo;
-        base = p.offsets[g];
-        local = L - p.tile_start[g];
-        c = p.offsets[g + 1] - p.offsets[g];
-    }
-    const GroupTiles gt = group_tiles(c, p.n_tiles);
-    t.g = g;
-    int n, m;
-    bool tail = false;
+// Tile `local` of a group of c rows.  Order inside a group: for each pair of
+// n-tiles, the full tiles of the first n-tile (m fastest), those of the
+// second, then the pair's tail tile, so the tail reads weight slices its
+// group's full tiles have just used.
+__host__ __device__ __forceinline__ void decode_tile(int c, int n_tiles, int64_t local, int& n, int& m, bool& tail) {
+    const GroupTiles gt = group_tiles(c, n_tiles);
+    tail = false;
     if (gt.tail) {
         const int per_pair = 2 * gt.full + 1;
         const int j = static_cast<int>(local / per_pair);
@@ -277,9 +225,108 @@ __device__ __forceinline__ bool locate_tile2(const GemmParams& p, Tile2& t) {
         n = static_cast<int>(local / gt.full);
         m = static_cast<int>(local % gt.full);
     }
+}
+
+__device__ __forceinline__ u32x4 tile_desc(int g, int64_t m0, int rows, int n, bool tail) {
+    return u32x4{static_cast<uint32_t>(g), static_cast<uint32_t>(m0), static_cast<uint32_t>(rows),
+                 static_cast<uint32_t>(n) | (tail ? 0x10000u : 0u)};
+}
+
+// Descriptors of every workgroup of both GEMMs (gate_up and down have
+// different n-tiles): workgroup b runs logical tile xcd_remap(b) of the
+// grouped order, or nothing (g = -1).  Each block rebuilds the tile prefix
+// sums of the groups in LDS and fills a strided share of both tables, so a
+// GEMM workgroup finds its tile with one load.
+__global__ __launch_bounds__(1024) void build_tile_table_kernel(const int32_t* __restrict__ offsets, int G, int nt1,
+                                                                int nt2, u32x4* __restrict__ desc1, int nwg1,
+                                                                u32x4* __restrict__ desc2, int nwg2) {
+    __shared__ int part1[1024];
+    __shared__ int part2[1024];
+    __shared__ int off[1025];
+    const int tid = threadIdx.x;
+    int a = 0, b = 0;
+    if (tid < G) {
+        const int o0 = offsets[tid], o1 = offsets[tid + 1];
+        off[tid] = o0;
+        if (tid == G - 1) off[G] = o1;
+        const int c = o1 - o0;
+        a = tiles_of(c, nt1);
+        b = tiles_of(c, nt2);
+    }
+    part1[tid] = a;
+    part2[tid] = b;
+    __syncthreads();
+    for (int d = 1; d < 1024; d <<= 1) {
+        const int v1 = tid >= d ? part1[tid - d] : 0;
+        const int v2 = tid >= d ? part2[tid - d] : 0;
+        __syncthreads();
+        part1[tid] += v1;
+        part2[tid] += v2;
+        __syncthreads();
+    }
+    // exclusive starts: part[g] - tiles(g); total = part[G - 1]
+    const int total1 = part1[G - 1], total2 = part2[G - 1];
+    for (int t = 0; t < 2; ++t) {
+        const int* part = t == 0 ? part1 : part2;
+        const int nt = t == 0 ? nt1 : nt2;
+        const int total = t == 0 ? total1 : total2;
+        const int nwg = t == 0 ? nwg1 : nwg2;
+        u32x4* desc = t == 0 ? desc1 : desc2;
+        const int64_t padded = (static_cast<int64_t>(total) + 7) & ~static_cast<int64_t>(7);
+        for (int w = blockIdx.x * 1024 + tid; w < nwg; w += gridDim.x * 1024) {
+            u32x4 d = u32x4{0xFFFFFFFFu, 0u, 0u, 0u};
+            if (w < padded) {
+                const int64_t L = xcd_remap(w, padded);
+                if (L < total) {
+                    // last g whose exclusive start is <= L (empty groups share a start)
+                    int lo = 0, hi = G - 1;
+                    while (lo < hi) {
+                        const int mid = (lo + hi + 1) >> 1;
+                        const int st = mid == 0 ? 0 : part[mid - 1];
+                        if (st <= L) lo = mid; else hi = mid - 1;
+                    }
+                    const int g = lo;
+                    const int st = g == 0 ? 0 : part[g - 1];
+                    const int c = off[g + 1] - off[g];
+                    int n, m;
+                    bool tail;
+                    decode_tile(c, nt, L - st, n, m, tail);
+                    const int left = c - m * 256;
+                    d = tile_desc(g, static_cast<int64_t>(off[g]) + static_cast<int64_t>(m) * 256, left < 256 ? left : 256, n,
+                                  tail);
+                }
+            }
+            desc[w] = d;
+        }
+    }
+}
+
+// Which tile this workgroup owns; false if none (grid padding).
+__device__ __forceinline__ bool locate_tile2(const GemmParams& p, Tile2& t) {
+    if (p.offsets != nullptr) {
+        const u32x4 d = p.tiles[blockIdx.x];
+        if (static_cast<int>(d.x) < 0) return false;
+        t.g = static_cast<int>(d.x);
+        t.m0 = static_cast<int64_t>(d.y);
+        t.rows = static_cast<int>(d.z);
+        t.n = static_cast<int>(d.w & 0xFFFFu);
+        t.tail = (d.w >> 16) != 0;
+        return true;
+    }
+    // one group of ident_rows rows: no tables
+    const int c = static_cast<int>(p.ident_rows);
+    const int64_t total = tiles_of(c, p.n_tiles);
+    const int64_t padded = (total + 7) & ~static_cast<int64_t>(7);
+    if (static_cast<int64_t>(blockIdx.x) >= padded) return false;
+    const int64_t L = xcd_remap(blockIdx.x, padded);
+    if (L >= total) return false;
+    int n, m;
+    bool tail;
+    decode_tile(c, p.n_tiles, L, n, m, tail);
+    t.g = 0;
     t.n = n;
     t.tail = tail;
-    t.m0 = base + static_cast<int64_t>(m) * 256;
+    t.m0 = static_cast<int64_t>(m) * 256;
     const int left = c - m * 256;
     t.rows = left < 256 ? left : 256;
     return true;
@@ -398,7 +445,7 @@ __device__ __forceinline__ void tile_pipeline(const GemmParams& p, const Tile2& 
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
 #pragma unroll
-                for (int nb = 4 * h; nb < 4 * h + 4; ++nb) acc[mb][nb] = mfma_bf16(a, f[1 + nb], acc[mb][nb]);
+                for (int nb = 4 * h; nb < 4 * h + 4; ++nb) acc[mb][nb] = mfma_bf16(f[1 + nb], a, acc[mb][nb]);
                 // fragment reads in the first half (so they land before the
                 // next barrier); DMAs spread over the whole step so the
                 // address unit never queues more than the MFMA stream hides
@@ -431,32 +478,42 @@ __device__ __forceinline__ void tile_pipeline(const GemmParams& p, const Tile2& 
     wait_vmem<0>();
 
     // ---- epilogue ---------------------------------------------------------
-    uint16_t* __restrict__ out = static_cast<uint16_t*>(p.out);
+    // The MFMAs take the weight fragment as their first operand, so lane l
+    // holds output row (l % 16) of each 16 x 16 block and its four
+    // consecutive columns 4 * (l / 16) .. +3: one 8-byte store per block.
+    uint8_t* __restrict__ out = static_cast<uint8_t*>(p.out);
+    const int row0 = wm * 128 + (lane & 15);
+    const int c4 = 4 * (lane >> 4);
     if (GATE_UP) {
 #pragma unroll
-        for (int mb = 0; mb < 8; ++mb)
+        for (int mb = 0; mb < 8; ++mb) {
+            const int row = row0 + mb * 16;
 #pragma unroll
             for (int nb = 0; nb < 4; ++nb) {
-                const int col = tc.n * 128 + wn * 64 + nb * 16 + (lane & 15);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row = wm * 128 + mb * 16 + 4 * (lane >> 4) + i;
-                    if (row < tc.rows && col < p.I)
-                        out[(tc.m0 + row) * p.ldo + col] = f32_to_bf16(silu_mul_fast(acc[mb][nb][i], acc[mb][nb + 4][i]));
+                const int col = tc.n * 128 + wn * 64 + nb * 16 + c4;
+                if (row < tc.rows && col < p.I) {
+                    uint32_t w0 = pack_bf16(silu_mul_fast(acc[mb][nb][0], acc[mb][nb + 4][0]),
+                                            silu_mul_fast(acc[mb][nb][1], acc[mb][nb + 4][1]));
+                    uint32_t w1 = pack_bf16(silu_mul_fast(acc[mb][nb][2], acc[mb][nb + 4][2]),
+                                            silu_mul_fast(acc[mb][nb][3], acc[mb][nb + 4][3]));
+                    *reinterpret_cast<uint2*>(out + ((tc.m0 + row) * p.ldo + col) * 2) = uint2{w0, w1};
                 }
             }
+        }
     } else {
 #pragma unroll
-        for (int mb = 0; mb < 8; ++mb)
+        for (int mb = 0; mb < 8; ++mb) {
+            const int row = row0 + mb * 16;
 #pragma unroll
             for (int nb = 0; nb < 8; ++nb) {
-                const int col = tc.n * 256 + wn * 128 + nb * 16 + (lane & 15);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row = wm * 128 + mb * 16 + 4 * (lane >> 4) + i;
-                    if (row < tc.rows && col < p.ldo) out[(tc.m0 + row) * p.ldo + col] = f32_to_bf16(acc[mb][nb][i]);
+                const int col = tc.n * 256 + wn * 128 + nb * 16 + c4;
+                if (row < tc.rows && col < p.ldo) {
+                    const uint32_t w0 = pack_bf16(acc[mb][nb][0], acc[mb][nb][1]);
+                    const uint32_t w1 = pack_bf16(acc[mb][nb][2], acc[mb][nb][3]);
+                    *reinterpret_cast<uint2*>(out + ((tc.m0 + row) * p.ldo + col) * 2) = uint2{w0, w1};
                 }
             }
+        }
     }
 }
 
@@ -617,18 +674,32 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(GemmParams p) {
 
 static size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
 
-size_t experts_ws_bytes(int64_t rows_max, int G, int I, int dtype) {
+// Workgroups of the bf16 GEMMs: an upper bound of their tiles (every group
+// adds at most one partial m-tile; a tail tile stands in for one), rounded up
+// to a multiple of 8 for the XCD mapping.
+static void bf16_grid(int64_t rows_max, int G, bool grouped, int D, int I, int64_t& nwg1, int64_t& nwg2) {
+    const int64_t mt_max = (rows_max + 255) / 256 + (grouped ? G : 0);
+    nwg1 = ((mt_max * ((I + 127) / 128)) + 7) & ~static_cast<int64_t>(7);
+    nwg2 = ((mt_max * ((D + 255) / 256)) + 7) & ~static_cast<int64_t>(7);
+}
+
+size_t experts_ws_bytes(int64_t rows_max, int G, int D, int I, int dtype) {
     const size_t eb = dtype == 0 ? 2 : 4;
-    return align256(2 * sizeof(int32_t) * (G + 1)) + align256(static_cast<size_t>(rows_max) * I * eb);
+    size_t tables = align256(2 * sizeof(int32_t) * (G + 1));
+    if (dtype == 0) {
+        int64_t nwg1, nwg2;
+        bf16_grid(rows_max, G, true, D, I, nwg1, nwg2);
+        tables = align256(static_cast<size_t>(nwg1 + nwg2) * sizeof(u32x4));
+    }
+    return tables + align256(static_cast<size_t>(rows_max) * I * eb);
 }
 
 hipError_t launch_experts(const void* x, int64_t x_rows, const int32_t* perm_token, const int32_t* offsets, int G,
                           int64_t rows_max, int D, int I, int dtype, const void* gate_up, const void* down,
                           void* y, void* ws, hipStream_t stream) {
     const bool bf16 = dtype == 0;
-    int32_t* ts1 = static_cast<int32_t*>(ws);
-    int32_t* ts2 = ts1 + (G + 1);
-    void* act = static_cast<uint8_t*>(ws) + align256(2 * sizeof(int32_t) * (G + 1));
+    const size_t ws_total = experts_ws_bytes(rows_max, G, D, I, dtype);
+    void* act = static_cast<uint8_t*>(ws) + (ws_total - align256(static_cast<size_t>(rows_max) * I * (bf16 ? 2 : 4)));
 
     GemmParams p1{};
     p1.a = x;
@@ -660,21 +731,25 @@ hipError_t launch_experts(const void* x, int64_t x_rows, const int32_t* perm_tok
             return hipErrorInvalidValue;
         p1.n_tiles = (I + 127) / 128;
         p2.n_tiles = (D + 255) / 256;
+        int64_t nwg1, nwg2;
+        bf16_grid(rows_max, G, offsets != nullptr, D, I, nwg1, nwg2);
         if (offsets != nullptr) {
-            build_tiles_bf16_kernel<<<1, 1024, 0, stream>>>(offsets, G, p1.n_tiles, p2.n_tiles, ts1, ts2);
+            u32x4* d1 = static_cast<u32x4*>(ws);
+            u32x4* d2 = d1 + nwg1;
+            const int64_t most = nwg1 > nwg2 ? nwg1 : nwg2;
+            const unsigned blocks = static_cast<unsigned>((most + 2047) / 2048);
+            build_tile_table_kernel<<<blocks, 1024, 0, stream>>>(offsets, G, p1.n_tiles, p2.n_tiles, d1,
+                                                                static_cast<int>(nwg1), d2, static_cast<int>(nwg2));
             if ((err = hipGetLastError()) != hipSuccess) return err;
-            p1.tile_start = ts1;
-            p2.tile_start = ts2;
+            p1.tiles = d1;
+            p2.tiles = d2;
         }
-        // upper bound of tiles: every group adds at most one partial m-tile
-        const int64_t mt_max = (rows_max + 255) / 256 + (offsets != nullptr ? G : 0);
-        const int64_t nwg1 = ((mt_max * p1.n_tiles) + 7) & ~static_cast<int64_t>(7);
-        const int64_t nwg2 = ((mt_max * p2.n_tiles) + 7) & ~static_cast<int64_t>(7);
         grouped_gemm_bf16_kernel<true><<<static_cast<unsigned>(nwg1), 256, 0, stream>>>(p1);
         if ((err = hipGetLastError()) != hipSuccess) return err;
         grouped_gemm_bf16_kernel<false><<<static_cast<unsigned>(nwg2), 256, 0, stream>>>(p2);
         return hipGetLastError();
     }
+    int32_t* ts1 = static_cast<int32_t*>(ws);
     p1.n_tiles = (I + 63) / 64;
     p2.n_tiles = (D + kBN1 - 1) / kBN1;
     if (offsets != nullptr) {

@@ -15,6 +15,13 @@ hipError_t launch_router_logits(const void* x, const void* router, int64_t T, in
 hipError_t launch_topk(const double* logits64, int64_t T, int E, int K, int score, int renorm,
                        float route_scale, const float* bias, const uint8_t* mask,
                        float* logits_out, int32_t* ids, float* w, hipStream_t stream);
+// whether launch_route runs the single fused kernel (bf16 operands, E <= 512)
+bool route_fused(int E, int dtype);
+// logits + top-k: one fused kernel where route_fused(), else the two kernels
+// above through logits64 [T, E]; both give the same bits
+hipError_t launch_route(const void* x, const void* router, int64_t T, int D, int E, int K, int dtype,
+                        int score, int renorm, float route_scale, const float* bias, const uint8_t* mask,
+                        double* logits64, float* logits_out, int32_t* ids, float* w, hipStream_t stream);
 
 // ---- dispatch ----------------------------------------------------------------
 struct PermutePlan {
@@ -29,7 +36,7 @@ hipError_t launch_permute(const int32_t* ids, int64_t T, int K, int E, int32_t* 
                           hipStream_t stream);
 
 // ---- experts -----------------------------------------------------------------
-size_t experts_ws_bytes(int64_t rows_max, int G, int I, int dtype);
+size_t experts_ws_bytes(int64_t rows_max, int G, int D, int I, int dtype);
 // x_rows: rows of x (the gathered rows index it); rows_max: rows of the output
 hipError_t launch_experts(const void* x, int64_t x_rows, const int32_t* perm_token, const int32_t* offsets,
                           int G, int64_t rows_max, int D, int I, int dtype, const void* gate_up,

@@ -194,26 +194,14 @@ __device__ __forceinline__ uint64_t choice_key(double c, int e) {
     return (ord & ~0x3FFull) | static_cast<uint64_t>(1023 - e);
 }
 
+// Scores, choice and weights of one token whose float64 logits the wave holds,
+// E/64 (rounded up) per lane: lane l holds experts l, l + 64, ...  Writes the
+// K ids in ascending order and their weights (ids -1, weights 0 if masked).
 template <int EPL>
-__global__ __launch_bounds__(256) void topk_kernel(
-    const double* __restrict__ logits, int64_t T, int E, int K, int score, int renorm,
-    double route_scale, const float* __restrict__ bias, const uint8_t* __restrict__ mask,
-    float* __restrict__ logits_out, int32_t* __restrict__ ids_out, float* __restrict__ w_out) {
+__device__ __forceinline__ void topk_token(const double (&lg)[EPL], int64_t t, int E, int K, int score,
+                                           int renorm, double route_scale, const float* __restrict__ bias,
+                                           bool kept, int32_t* __restrict__ ids_out, float* __restrict__ w_out) {
     const int lane = lane_id();
-    const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-    if (t >= T) return;  // uniform per wave
-
-    double lg[EPL];
-    bool ok[EPL];
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-        const int e = lane + 64 * i;
-        ok[i] = e < E;
-        lg[i] = ok[i] ? logits[t * E + e] : 0.0;
-        if (logits_out && ok[i]) logits_out[t * E + e] = static_cast<float>(lg[i]);
-    }
-
-    const bool kept = (mask == nullptr) || (mask[t] != 0);
     if (!kept) {
         if (lane < K) {
             ids_out[t * K + lane] = -1;
@@ -221,6 +209,9 @@ __global__ __launch_bounds__(256) void topk_kernel(
         }
         return;
     }
+    bool ok[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) ok[i] = lane + 64 * i < E;
 
     double s[EPL];
     if (score == 0) {  // softmax over the experts
@@ -300,6 +291,166 @@ __global__ __launch_bounds__(256) void topk_kernel(
     }
 }
 
+template <int EPL>
+__global__ __launch_bounds__(256) void topk_kernel(
+    const double* __restrict__ logits, int64_t T, int E, int K, int score, int renorm,
+    double route_scale, const float* __restrict__ bias, const uint8_t* __restrict__ mask,
+    float* __restrict__ logits_out, int32_t* __restrict__ ids_out, float* __restrict__ w_out) {
+    const int lane = lane_id();
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;  // uniform per wave
+
+    double lg[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        const int e = lane + 64 * i;
+        lg[i] = e < E ? logits[t * E + e] : 0.0;
+        if (logits_out && e < E) logits_out[t * E + e] = static_cast<float>(lg[i]);
+    }
+    const bool kept = (mask == nullptr) || (mask[t] != 0);
+    topk_token<EPL>(lg, t, E, K, score, renorm, route_scale, bias, kept, ids_out, w_out);
+}
+
+// ---------------------------------------------------------------------------
+// fused routing, bf16 operands: logits of TB tokens x all experts in one
+// workgroup, kept in LDS as float64, then top-k per token from LDS.
+// The hidden rows are read from memory once and the logits never leave the
+// chip.  Each logit is computed exactly as router_logits_bf16_kernel does
+// (two MFMA k=32 steps into a zeroed fp32 accumulator per 64-wide k chunk,
+// chunks added in float64 in k order), so both paths give the same bits.
+// ---------------------------------------------------------------------------
+// TBB: 16-token blocks per workgroup; NBW: 16-expert blocks per wave (4 waves).
+template <int TBB, int NBW>
+struct RouteTile {
+    static constexpr int TB = 16 * TBB;        // tokens per workgroup
+    static constexpr int EMAX = 64 * NBW;      // experts per workgroup
+    static constexpr int EPL = EMAX / 64;      // experts per lane in the top-k
+    static constexpr int ROWS = TB + EMAX;     // rows staged per 64-wide k chunk
+    static constexpr int STAGE = ROWS * 128;   // bytes per chunk
+    static constexpr int LOGB = TB * EMAX * 8; // float64 logits
+    static constexpr int SMEM = (2 * STAGE > LOGB) ? 2 * STAGE : LOGB;
+    static constexpr int LOADS = ROWS * 8 / 256;  // 16-byte loads per thread per chunk
+    static_assert(ROWS % 32 == 0, "staging must divide over 256 threads");
+};
+
+template <int TBB, int NBW>
+__global__ __launch_bounds__(256) void route_fused_bf16_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int64_t T, int D, int E, int K,
+    int score, int renorm, double route_scale, const float* __restrict__ bias,
+    const uint8_t* __restrict__ mask, float* __restrict__ logits_out, int32_t* __restrict__ ids_out,
+    float* __restrict__ w_out) {
+    using RT = RouteTile<TBB, NBW>;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[RT::SMEM];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * RT::TB;
+
+    // staging: row r < TB is hidden row t0 + r, row TB + j is router row j
+    const uint8_t* src[RT::LOADS];
+    int dst[RT::LOADS];
+#pragma unroll
+    for (int j = 0; j < RT::LOADS; ++j) {
+        const int q = tid + 256 * j;
+        const int row = q >> 3, ch = q & 7;
+        dst[j] = row * 128 + ((ch ^ (row & 7)) << 4);
+        const uint8_t* p = nullptr;
+        if (row < RT::TB) {
+            if (t0 + row < T) p = reinterpret_cast<const uint8_t*>(x + (t0 + row) * D) + ch * 16;
+        } else if (row - RT::TB < E) {
+            p = reinterpret_cast<const uint8_t*>(w + static_cast<int64_t>(row - RT::TB) * D) + ch * 16;
+        }
+        src[j] = p;
+    }
+    u32x4 stg[RT::LOADS];
+    auto fetch = [&](int k0) {
+#pragma unroll
+        for (int j = 0; j < RT::LOADS; ++j)
+            stg[j] = src[j] ? *reinterpret_cast<const u32x4*>(src[j] + 2 * k0) : u32x4{0u, 0u, 0u, 0u};
+    };
+    auto store = [&](int buf) {
+#pragma unroll
+        for (int j = 0; j < RT::LOADS; ++j)
+            *reinterpret_cast<u32x4*>(smem + buf * RT::STAGE + dst[j]) = stg[j];
+    };
+
+    double acc64[TBB][NBW][4];
+#pragma unroll
+    for (int a = 0; a < TBB; ++a)
+#pragma unroll
+        for (int b = 0; b < NBW; ++b)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc64[a][b][i] = 0.0;
+
+    const int nchunks = D / 64;
+    fetch(0);
+    store(0);
+    __syncthreads();
+    for (int c = 0; c < nchunks; ++c) {
+        const int buf = c & 1;
+        if (c + 1 < nchunks) fetch((c + 1) * 64);
+        const uint8_t* sb = smem + buf * RT::STAGE;
+        f32x4 acc[TBB][NBW];
+#pragma unroll
+        for (int a = 0; a < TBB; ++a)
+#pragma unroll
+            for (int b = 0; b < NBW; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const int ch = 4 * s + (lane >> 4);
+            u32x4 af[TBB];
+#pragma unroll
+            for (int a = 0; a < TBB; ++a) {
+                const int r = a * 16 + (lane & 15);
+                af[a] = *reinterpret_cast<const u32x4*>(sb + r * 128 + ((ch ^ (r & 7)) << 4));
+            }
+#pragma unroll
+            for (int b = 0; b < NBW; ++b) {
+                const int r = RT::TB + wv * (16 * NBW) + b * 16 + (lane & 15);
+                const u32x4 bf = *reinterpret_cast<const u32x4*>(sb + r * 128 + ((ch ^ (r & 7)) << 4));
+#pragma unroll
+                for (int a = 0; a < TBB; ++a) acc[a][b] = mfma_bf16(af[a], bf, acc[a][b]);
+            }
+        }
+#pragma unroll
+        for (int a = 0; a < TBB; ++a)
+#pragma unroll
+            for (int b = 0; b < NBW; ++b)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc64[a][b][i] += static_cast<double>(acc[a][b][i]);
+        if (c + 1 < nchunks) store(buf ^ 1);
+        __syncthreads();
+    }
+
+    // logits to LDS: [TB][EMAX] float64 (the staging buffers are dead)
+    double* lgs = reinterpret_cast<double*>(smem);
+#pragma unroll
+    for (int a = 0; a < TBB; ++a)
+#pragma unroll
+        for (int b = 0; b < NBW; ++b)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int tl = a * 16 + 4 * (lane >> 4) + i;
+                const int e = wv * (16 * NBW) + b * 16 + (lane & 15);
+                lgs[tl * RT::EMAX + e] = acc64[a][b][i];
+            }
+    __syncthreads();
+
+    for (int tl = wv; tl < RT::TB; tl += 4) {
+        const int64_t t = t0 + tl;
+        if (t >= T) break;  // uniform per wave
+        double lg[RT::EPL];
+#pragma unroll
+        for (int i = 0; i < RT::EPL; ++i) {
+            const int e = lane + 64 * i;
+            lg[i] = lgs[tl * RT::EMAX + e];
+            if (logits_out && e < E) logits_out[t * E + e] = static_cast<float>(lg[i]);
+        }
+        const bool kept = (mask == nullptr) || (mask[t] != 0);
+        topk_token<RT::EPL>(lg, t, E, K, score, renorm, route_scale, bias, kept, ids_out, w_out);
+    }
+}
+
 hipError_t launch_router_logits(const void* x, const void* router, int64_t T, int D, int E,
                                 int dtype, double* logits64, hipStream_t stream) {
     if (dtype == 0) {
@@ -328,6 +479,31 @@ hipError_t launch_topk(const double* logits64, int64_t T, int E, int K, int scor
     else if (E <= 512) MOE_TOPK(8);
     else MOE_TOPK(16);
 #undef MOE_TOPK
+    return hipGetLastError();
+}
+
+bool route_fused(int E, int dtype) { return dtype == 0 && E <= 512; }
+
+hipError_t launch_route(const void* x, const void* router, int64_t T, int D, int E, int K, int dtype,
+                        int score, int renorm, float route_scale, const float* bias, const uint8_t* mask,
+                        double* logits64, float* logits_out, int32_t* ids, float* w, hipStream_t stream) {
+    if (!route_fused(E, dtype)) {
+        hipError_t err = launch_router_logits(x, router, T, D, E, dtype, logits64, stream);
+        if (err != hipSuccess) return err;
+        return launch_topk(logits64, T, E, K, score, renorm, route_scale, bias, mask, logits_out, ids, w, stream);
+    }
+    const double rs = static_cast<double>(route_scale);
+    const uint16_t* xb = static_cast<const uint16_t*>(x);
+    const uint16_t* wb = static_cast<const uint16_t*>(router);
+#define MOE_ROUTE(TBB, NBW)                                                                              \
+    route_fused_bf16_kernel<TBB, NBW><<<static_cast<unsigned>((T + 16 * TBB - 1) / (16 * TBB)), 256, 0, \
+                                         stream>>>(xb, wb, T, D, E, K, score, renorm, rs, bias, mask,      \
+                                                   logits_out, ids, w)
+    if (E <= 64) MOE_ROUTE(4, 1);
+    else if (E <= 128) MOE_ROUTE(4, 2);
+    else if (E <= 256) MOE_ROUTE(4, 4);
+    else MOE_ROUTE(2, 8);
+#undef MOE_ROUTE
     return hipGetLastError();
 }
 

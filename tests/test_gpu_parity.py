@@ -174,3 +174,13 @@ def test_repeat_runs_are_bitwise_identical():
     for _ in range(3):
         b = layer.forward(x)
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("E,K,D,I,T", [(1024, 8, 256, 128, 100), (200, 5, 256, 192, 300), (40, 3, 128, 64, 130)])
+def test_odd_expert_counts(E, K, D, I, T):
+    """Expert counts off the workloads' grid: more than 512 experts (routed
+    through float64 logits in memory), and counts that leave partial 16- and
+    64-expert blocks in the single-kernel router."""
+    from dataclasses import replace
+    cfg = replace(get_config("q30", T=T), name=f"q30-E{E}", E=E, K=K, D=D, I=I)
+    check_layer(make_inputs(cfg), label=f"E{E}-K{K}-D{D}-I{I}-T{T}")
