@@ -12,12 +12,13 @@
 //                     ballot per id bit, finds for every lane the lanes holding
 //                     the same expert (a "match mask").  The lowest such lane
 //                     adds the popcount to the wave's LDS histogram row.
-//   pass 2 (scan):    one workgroup scans the block histograms in (expert,
-//                     block) order: the base row of every (expert, block), the
-//                     expert offsets and counts.
-//   pass 3 (scatter): each block recomputes its wave histograms, turns them
-//                     into per-wave bases, and walks its segments again; a
-//                     pair's row is its wave base plus the pairs of the same
+//   pass 2 (scan):    one workgroup per expert scans that expert's block
+//                     counts: the expert's count and, per block, the pairs of
+//                     the expert in earlier blocks.
+//   pass 3 (scatter): each block scans the expert counts (the offsets; block
+//                     0 stores them), recomputes its wave histograms, turns
+//                     them into per-wave bases, and walks its segments again;
+//                     a pair's row is its wave base plus the pairs of the same
 //                     expert in earlier segments plus its rank in the segment.
 //
 // Pairs of one expert therefore keep their flat (token, slot) order, and since
@@ -90,51 +91,84 @@ __global__ __launch_bounds__(256) void permute_count_kernel(
         block_hist[static_cast<int64_t>(e) * nblocks + blockIdx.x] = hist[0][e] + hist[1][e] + hist[2][e] + hist[3][e];
 }
 
-// Exclusive scan of block_hist in (expert, block) order by one workgroup.
-__global__ __launch_bounds__(1024) void permute_scan_kernel(
-    const int32_t* __restrict__ block_hist, int E, int nblocks, int32_t* __restrict__ block_base,
-    int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
-    __shared__ int part[1024];
-    __shared__ int offs[kMaxExperts + 1];
+// Exclusive scan of one expert's block counts (workgroup e scans row e of
+// block_hist, at most 1024 blocks); counts[e] is the row total.
+__global__ __launch_bounds__(256) void permute_scan_kernel(
+    const int32_t* __restrict__ block_hist, int nblocks, int32_t* __restrict__ block_base,
+    int32_t* __restrict__ counts) {
+    __shared__ int part[256];
     const int tid = threadIdx.x;
-    const int64_t N = static_cast<int64_t>(E) * nblocks;
-    const int64_t chunk = (N + 1023) / 1024;
-    const int64_t lo = tid * chunk;
-    const int64_t hi = lo + chunk < N ? lo + chunk : N;
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * nblocks;
+    int v[4];
     int sum = 0;
-    for (int64_t j = lo; j < hi; ++j) sum += block_hist[j];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int b = 4 * tid + j;
+        v[j] = b < nblocks ? block_hist[row + b] : 0;
+        sum += v[j];
+    }
     part[tid] = sum;
     __syncthreads();
-    // Hillis-Steele inclusive scan of the 1024 partial sums
-    for (int d = 1; d < 1024; d <<= 1) {
-        const int v = tid >= d ? part[tid - d] : 0;
+    for (int d = 1; d < 256; d <<= 1) {
+        const int u = tid >= d ? part[tid - d] : 0;
         __syncthreads();
-        part[tid] += v;
+        part[tid] += u;
         __syncthreads();
     }
-    int run = part[tid] - sum;  // exclusive prefix of this thread's chunk
-    for (int64_t j = lo; j < hi; ++j) {
-        block_base[j] = run;
-        if (j % nblocks == 0) offs[j / nblocks] = run;
-        run += block_hist[j];
+    int run = part[tid] - sum;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int b = 4 * tid + j;
+        if (b < nblocks) block_base[row + b] = run;
+        run += v[j];
     }
-    if (tid == 1023) offs[E] = part[1023];
+    if (tid == 255) counts[blockIdx.x] = part[255];
+}
+
+// Exclusive scan of the E expert counts into offs[0..E] (256 threads).
+__device__ __forceinline__ void scan_counts(const int32_t* __restrict__ counts, int E, int* offs, int* part) {
+    const int tid = threadIdx.x;
+    int v[4];
+    int sum = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int e = 4 * tid + j;
+        v[j] = e < E ? counts[e] : 0;
+        sum += v[j];
+    }
+    part[tid] = sum;
     __syncthreads();
-    for (int e = tid; e <= E; e += 1024) {
-        offsets[e] = offs[e];
-        if (e < E) counts[e] = offs[e + 1] - offs[e];
+    for (int d = 1; d < 256; d <<= 1) {
+        const int u = tid >= d ? part[tid - d] : 0;
+        __syncthreads();
+        part[tid] += u;
+        __syncthreads();
     }
+    int run = part[tid] - sum;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int e = 4 * tid + j;
+        if (e < E) offs[e] = run;
+        run += v[j];
+    }
+    if (tid == 255) offs[E] = part[255];
+    __syncthreads();
 }
 
 __global__ __launch_bounds__(256) void permute_scatter_kernel(
     const int32_t* __restrict__ ids, int64_t P, int K, int E, int ppb, int nblocks, int id_bits,
-    const int32_t* __restrict__ block_base, int32_t* __restrict__ perm_token, int32_t* __restrict__ inv_pos) {
+    const int32_t* __restrict__ block_base, const int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ perm_token, int32_t* __restrict__ inv_pos) {
     __shared__ int hist[kPermWaves][kMaxExperts];
+    __shared__ int offs[kMaxExperts + 1];
+    __shared__ int part[256];
     const int tid = threadIdx.x;
     const int wv = tid >> 6;
     const int lane = lane_id();
     for (int i = tid; i < kPermWaves * E; i += 256) hist[i / E][i % E] = 0;
-    __syncthreads();
+    scan_counts(counts, E, offs, part);
+    if (blockIdx.x == 0)
+        for (int e = tid; e <= E; e += 256) offsets[e] = offs[e];
     const int64_t base = static_cast<int64_t>(blockIdx.x) * ppb;
     const int per_wave = ppb / kPermWaves;
     const int64_t w_begin = base + wv * per_wave;
@@ -143,7 +177,7 @@ __global__ __launch_bounds__(256) void permute_scatter_kernel(
     __syncthreads();
     // per-wave base rows: block base of the expert plus earlier waves' pairs
     for (int e = tid; e < E; e += 256) {
-        int run = block_base[static_cast<int64_t>(e) * nblocks + blockIdx.x];
+        int run = offs[e] + block_base[static_cast<int64_t>(e) * nblocks + blockIdx.x];
 #pragma unroll
         for (int w = 0; w < kPermWaves; ++w) {
             const int h = hist[w][e];
@@ -185,11 +219,12 @@ hipError_t launch_permute(const int32_t* ids, int64_t T, int K, int E, int32_t* 
                                                        block_hist);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    permute_scan_kernel<<<1, 1024, 0, stream>>>(block_hist, E, pl.blocks, block_base, counts, offsets);
+    permute_scan_kernel<<<E, 256, 0, stream>>>(block_hist, pl.blocks, block_base, counts);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     permute_scatter_kernel<<<pl.blocks, 256, 0, stream>>>(ids, P, K, E, pl.pairs_per_block, pl.blocks,
-                                                         pl.id_bits, block_base, perm_token, inv_pos);
+                                                         pl.id_bits, block_base, counts, offsets, perm_token,
+                                                         inv_pos);
     return hipGetLastError();
 }
 
