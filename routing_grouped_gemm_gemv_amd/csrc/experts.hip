@@ -18,16 +18,19 @@
 // many rows its expert received, where in a tile its row sits, or on T.
 //
 // bf16 kernel: 256 x 256 output tile per 256-thread workgroup (4 waves as
-// 2 x 2, 128 x 128 per wave: 64 accumulator blocks of 16 x 16).  The k
-// dimension advances in 64-element slices (128 bytes per row) double-buffered
-// in 128 KiB of LDS.  Slices are fetched with global_load_lds_dwordx4, which
-// writes each lane's 16 bytes straight into LDS at (wave base + 16 * lane):
-// the XOR swizzle of the 16-byte chunks of a row (chunk ^ row % 8, which makes
-// the MFMA fragment reads conflict-free) is therefore applied to the global
-// addresses each lane fetches.  The next slice is in flight while the current
-// one is multiplied.  For gate_up the 256 weight rows of a tile are 128 gate
-// rows and the matching 128 up rows, so the SwiGLU epilogue pairs registers
-// of the same wave.
+// 2 x 2, 128 x 128 per wave: 64 accumulator blocks of 16 x 16); the last
+// <= 128 rows of a group form 128 x 512 tail tiles (4 waves as 1 x 4).  The
+// k dimension advances in 64-element stages (128 bytes per row), two stages
+// in LDS.  Stages are fetched with global_load_lds_dwordx4, which writes each
+// lane's 16 bytes straight into LDS at (wave base + 16 * lane), 8 rows x 128
+// bytes per instruction, so every 128-byte line of an operand row is fetched
+// whole; the XOR swizzle of the 16-byte chunks of a row (chunk ^ row % 8,
+// which keeps the MFMA fragment reads conflict-free) is applied to the global
+// addresses each lane fetches.  The MFMAs step through each stage in two
+// 32-wide halves with the fragments of the next half read ahead.  For
+// gate_up the weight rows of a tile are gate rows and the matching up rows,
+// so the SwiGLU epilogue pairs registers of the same wave.  The epilogue
+// stages the bf16 tile in LDS and stores whole rows in 16-byte pieces.
 //
 // fp32 kernel (the fp32-operand mode): 128 x 128 tiles staged through
 // registers, 16x16x4 f32 MFMA.
@@ -140,10 +143,8 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 }
 
 // ===========================================================================
-// bf16 operands: direct-to-LDS slices, deep pipeline
+// bf16 operands: direct-to-LDS stages of 64-wide k
 // ===========================================================================
-constexpr int kSlice2 = 32;   // k per slice
-constexpr int kRow2 = 64;     // bytes per tile row per slice
 constexpr int kLds2 = 160 * 1024;
 
 // 16 bytes per lane from global memory (base + 32-bit per-lane offset) into
@@ -333,54 +334,49 @@ __device__ __forceinline__ bool locate_tile2(const GemmParams& p, Tile2& t) {
 }
 
 // One tile of BM rows x BN weight rows (gate_up: BN/2 gate rows and the
-// matching BN/2 up rows) through a STAGES-deep pipeline of 32-wide k slices.
-// Four waves; each computes a 128 x 128 block (64 MFMA accumulators of
-// 16 x 16): with BM = 256 the waves are 2 x 2, with BM = 128 they are 1 x 4.
-template <bool GATE_UP, int BM, int BN, int STAGES>
+// matching BN/2 up rows).  Stage st holds k = 64 st .. 64 st + 63 of all the
+// tile's rows; each DMA instruction moves 8 rows x 128 bytes.  A stage feeds
+// two 32-wide MFMA sub-steps, and one wait + barrier per stage serves both.
+template <bool GATE_UP, int BM, int BN>
 __device__ __forceinline__ void tile_pipeline(const GemmParams& p, const Tile2& tc, lds_u8* smem) {
-    constexpr int kWN = BM == 256 ? 2 : 4;               // waves along n
-    constexpr int kStage = (BM + BN) * kRow2;            // bytes per stage
-    constexpr int kDmaA = BM / 64;                       // 16-row DMA instructions per wave per slice
-    constexpr int kDmaB = BN / 64;
+    constexpr int kWN = BM == 256 ? 2 : 4;
+    constexpr int kRow = 128;
+    constexpr int kStage = (BM + BN) * kRow;
+    constexpr int kDmaA = BM / 32;   // 8-row DMA instructions per wave per stage
+    constexpr int kDmaB = BN / 32;
     constexpr int kDma = kDmaA + kDmaB;
-    static_assert(kStage * STAGES <= kLds2, "LDS");
-    static_assert(kDma <= 16, "DMA issue slots");
+    static_assert(2 * kStage <= kLds2, "LDS");
+    static_assert(kDma <= 32, "DMA issue slots");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wv / kWN;
     const int wn = wv % kWN;
     const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem));
 
-    // ---- per-lane DMA sources ---------------------------------------------
-    // A instruction i fills rows wv*(BM/4) + 16i .. +15; B instruction i fills
-    // weight rows wv*(BN/4) + 16i .. +15.  Lane l lands on row l / 4 of its
-    // group at physical chunk l % 4 of the 64-byte row, so it fetches the
-    // logical chunk (l % 4) ^ ((row / 2) % 4), the swizzle that spreads the
-    // eight lanes of a fragment read over all 32 banks.  Byte offsets fit 32
-    // bits: x, the activations and one group's weights are each below 4 GiB
-    // (checked by the launcher).
     const uint8_t* __restrict__ abase = static_cast<const uint8_t*>(p.a);
     const uint8_t* __restrict__ wbase =
         static_cast<const uint8_t*>(p.w) + static_cast<int64_t>(tc.g) * p.w_group_stride * 2;
-    const int chunk = (lane & 3) ^ ((lane >> 3) & 3);
+    // lane l lands on row l / 8 of its 8-row group at physical chunk l % 8 and
+    // fetches logical chunk (l % 8) ^ (row % 8)
+    const int chunk = (lane & 7) ^ (lane >> 3);
     uint32_t aoff[kDmaA], boff[kDmaB];
 #pragma unroll
     for (int i = 0; i < kDmaA; ++i) {
-        const int r = wv * (BM / 4) + 16 * i + (lane >> 2);
-        const int rr = r < tc.rows ? r : tc.rows - 1;  // rows past the group repeat its last row; never stored
+        const int r = wv * (BM / 4) + 8 * i + (lane >> 3);
+        const int rr = r < tc.rows ? r : tc.rows - 1;
         int64_t src = tc.m0 + rr;
         if (GATE_UP && p.perm != nullptr) src = p.perm[src];
         aoff[i] = static_cast<uint32_t>(src * p.Kd * 2 + chunk * 16);
     }
 #pragma unroll
     for (int i = 0; i < kDmaB; ++i) {
-        const int r = wv * (BN / 4) + 16 * i + (lane >> 2);
+        const int r = wv * (BN / 4) + 8 * i + (lane >> 3);
         int wrow;
         if (GATE_UP) {
-            int c = tc.n * 128 + (r % (BN / 2));  // gate row; the matching up row is I + c
-            if (c >= p.I) c = p.I - 1;           // I % 128 == 64: last tile half full
+            int c = tc.n * 128 + (r % (BN / 2));
+            if (c >= p.I) c = p.I - 1;
             wrow = r < BN / 2 ? c : p.I + c;
         } else {
             wrow = tc.n * 256 + r;
@@ -388,17 +384,18 @@ __device__ __forceinline__ void tile_pipeline(const GemmParams& p, const Tile2& 
         }
         boff[i] = static_cast<uint32_t>(static_cast<int64_t>(wrow) * p.Kd * 2 + chunk * 16);
     }
-    const int a_dst = wv * (BM / 4) * kRow2;
-    const int b_dst = BM * kRow2 + wv * (BN / 4) * kRow2;
+    const int a_dst = wv * (BM / 4) * kRow;
+    const int b_dst = BM * kRow + wv * (BN / 4) * kRow;
 
-    // LDS byte offsets of this lane's MFMA fragments: block b adds b * 16 rows,
-    // and the swizzle term depends only on the lane (row % 16 == lane % 16)
-    const int xo = ((lane >> 4) ^ ((lane >> 1) & 3)) << 4;
-    const int a_frag = (wm * 128 + (lane & 15)) * kRow2 + xo;
-    const int b_frag = BM * kRow2 + ((GATE_UP ? wn * 64 : wn * 128) + (lane & 15)) * kRow2 + xo;
+    // fragment of sub-step j (k 32j .. 32j+31 of the stage): logical chunk
+    // 4j + lane/16 of row lane%16 (+ 16 per block), physical chunk ^ (lane % 8)
+    const int xo0 = (((lane >> 4)) ^ (lane & 7)) << 4;
+    const int xo1 = ((4 + (lane >> 4)) ^ (lane & 7)) << 4;
+    const int a_frag = (wm * 128 + (lane & 15)) * kRow;
+    const int b_frag = BM * kRow + ((GATE_UP ? wn * 64 : wn * 128) + (lane & 15)) * kRow;
     auto b_row_off = [&](int b) {
-        if (GATE_UP) return (b < 4 ? b * 16 : BN / 2 + (b - 4) * 16) * kRow2;
-        return b * 16 * kRow2;
+        if (GATE_UP) return (b < 4 ? b * 16 : BN / 2 + (b - 4) * 16) * kRow;
+        return b * 16 * kRow;
     };
 
     f32x4 acc[8][8];
@@ -407,38 +404,22 @@ __device__ __forceinline__ void tile_pipeline(const GemmParams& p, const Tile2& 
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // DMA instruction q (A first, then B) of slice kt into its stage.  Slices
-    // past the end re-fetch the last slice: every step then issues the same
-    // instructions (uniform waits, no tail code), and the stage they land in
-    // is never read for results again.
-    const int nk = p.Kd / kSlice2;
-    auto dma = [&](int kt, uint32_t stage_off, int q) {
-        const uint32_t kb = static_cast<uint32_t>(kt < nk ? kt : nk - 1) * kRow2;
-        if (q < kDmaA) dma16(abase, aoff[q] + kb, lds0 + stage_off + a_dst + q * 16 * kRow2);
-        else dma16(wbase, boff[q - kDmaA] + kb, lds0 + stage_off + b_dst + (q - kDmaA) * 16 * kRow2);
+    const int ns = p.Kd / 64;  // stages of the k loop
+    auto dma = [&](int st, uint32_t stage_off, int q) {
+        const uint32_t kb = static_cast<uint32_t>(st < ns ? st : ns - 1) * kRow;
+        if (q < kDmaA) dma16(abase, aoff[q] + kb, lds0 + stage_off + a_dst + q * 8 * kRow);
+        else dma16(wbase, boff[q - kDmaA] + kb, lds0 + stage_off + b_dst + (q - kDmaA) * 8 * kRow);
     };
-    // Fragment k of the slice in a stage, in the order the MFMAs consume
-    // them: A block 0, B blocks 0..7, then A blocks 1..7.
-    auto frag = [&](uint32_t stage_off, int k) -> u32x4 {
+    auto frag = [&](uint32_t stage_off, int xo, int k) -> u32x4 {
         const lds_u8* st = smem + stage_off;
-        if (k == 0) return *reinterpret_cast<lds_u32x4*>(st + a_frag);
-        if (k <= 8) return *reinterpret_cast<lds_u32x4*>(st + b_frag + b_row_off(k - 1));
-        return *reinterpret_cast<lds_u32x4*>(st + a_frag + (k - 8) * 16 * kRow2);
+        if (k == 0) return *reinterpret_cast<lds_u32x4*>(st + a_frag + xo);
+        if (k <= 8) return *reinterpret_cast<lds_u32x4*>(st + b_frag + b_row_off(k - 1) + xo);
+        return *reinterpret_cast<lds_u32x4*>(st + a_frag + (k - 8) * 16 * kRow + xo);
     };
-
-    // Pipeline.  Slice kt lives in stage kt % STAGES.  At the top of step kt
-    // the fragments of slice kt are in registers (f) and the DMAs of the next
-    // STAGES-1 slices are in flight.  The step waits for slice kt+1 only,
-    // then a barrier makes it visible and proves every wave has read slice
-    // kt, whose stage then receives slice kt+STAGES.  The 64 MFMAs of slice kt
-    // run with the 16 fragment reads of slice kt+1 and this step's DMAs issued
-    // during their first half, so the reads land before the next barrier.
-    auto step = [&](int kt, const u32x4 (&f)[16], u32x4 (&g)[16]) {
-        wait_vmem<(STAGES - 2) * kDma>();
-        __syncthreads();
-        __builtin_amdgcn_sched_barrier(0);
-        const uint32_t cur = static_cast<uint32_t>(kt % STAGES) * kStage;
-        const uint32_t nxt = static_cast<uint32_t>((kt + 1) % STAGES) * kStage;
+    // one 32-wide sub-step: 64 MFMAs on f, the 16 fragment reads of the next
+    // sub-step (stage rs, half xo) in the first half, and DO_DMA: this
+    // stage's DMAs spread over the sub-step
+    auto sub = [&](const u32x4 (&f)[16], u32x4 (&g)[16], uint32_t rs, int xo, bool do_dma, int dst, uint32_t ds) {
 #pragma unroll
         for (int mb = 0; mb < 8; ++mb) {
             const u32x4 a = mb == 0 ? f[0] : f[8 + mb];
@@ -446,74 +427,88 @@ __device__ __forceinline__ void tile_pipeline(const GemmParams& p, const Tile2& 
             for (int h = 0; h < 2; ++h) {
 #pragma unroll
                 for (int nb = 4 * h; nb < 4 * h + 4; ++nb) acc[mb][nb] = mfma_bf16(f[1 + nb], a, acc[mb][nb]);
-                // fragment reads in the first half (so they land before the
-                // next barrier); DMAs spread over the whole step so the
-                // address unit never queues more than the MFMA stream hides
                 const int q = 2 * mb + h;
                 if (q < 8) {
-                    g[2 * q] = frag(nxt, 2 * q);
-                    g[2 * q + 1] = frag(nxt, 2 * q + 1);
+                    g[2 * q] = frag(rs, xo, 2 * q);
+                    g[2 * q + 1] = frag(rs, xo, 2 * q + 1);
                 }
-                constexpr int kEvery = 16 / kDma;  // 2 for eight DMAs, 1 for ten
-                if (q % kEvery == kEvery - 1 && q / kEvery < kDma) dma(kt + STAGES, cur, q / kEvery);
+                if (do_dma) {
+                    constexpr int kPer = (kDma + 15) / 16;  // DMAs per 4 MFMAs
+#pragma unroll
+                    for (int u = 0; u < kPer; ++u)
+                        if (q * kPer + u < kDma) dma(dst, ds, q * kPer + u);
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
     };
 
+    dma(0, 0, 0);
 #pragma unroll
-    for (int j = 0; j < STAGES; ++j)
+    for (int q = 1; q < kDma; ++q) dma(0, 0, q);
 #pragma unroll
-        for (int q = 0; q < kDma; ++q) dma(j, j * kStage, q);
-    wait_vmem<(STAGES - 1) * kDma>();
+    for (int q = 0; q < kDma; ++q) dma(1, kStage, q);
+    wait_vmem<kDma>();
     __syncthreads();
     u32x4 f0[16], f1[16];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) f0[k] = frag(0, k);
-    // nk is even: D and I are multiples of 64
-    for (int kt = 0; kt < nk; kt += 2) {
-        step(kt, f0, f1);
-        step(kt + 1, f1, f0);
+    for (int k = 0; k < 16; ++k) f0[k] = frag(0, xo0, k);
+    for (int st = 0; st < ns; ++st) {
+        const uint32_t cur = static_cast<uint32_t>(st & 1) * kStage;
+        const uint32_t nxt = static_cast<uint32_t>((st + 1) & 1) * kStage;
+        // first half of the stage: fragments of its second half
+        sub(f0, f1, cur, xo1, false, 0, 0);
+        // stage st+1 has landed and every wave is done with stage st
+        wait_vmem<0>();
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+        // second half: fragments of the next stage's first half; stage st+2 into stage st's buffer
+        sub(f1, f0, nxt, xo0, true, st + 2, cur);
     }
     wait_vmem<0>();
+    __syncthreads();
 
-    // ---- epilogue ---------------------------------------------------------
-    // The MFMAs take the weight fragment as their first operand, so lane l
-    // holds output row (l % 16) of each 16 x 16 block and its four
-    // consecutive columns 4 * (l / 16) .. +3: one 8-byte store per block.
-    uint8_t* __restrict__ out = static_cast<uint8_t*>(p.out);
+    constexpr int NC = GATE_UP ? BN / 2 : BN;
+    constexpr int kOutRow = NC * 2 + 16;
+    static_assert(BM * kOutRow <= kLds2, "LDS");
     const int row0 = wm * 128 + (lane & 15);
     const int c4 = 4 * (lane >> 4);
     if (GATE_UP) {
 #pragma unroll
-        for (int mb = 0; mb < 8; ++mb) {
-            const int row = row0 + mb * 16;
+        for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
             for (int nb = 0; nb < 4; ++nb) {
-                const int col = tc.n * 128 + wn * 64 + nb * 16 + c4;
-                if (row < tc.rows && col < p.I) {
-                    uint32_t w0 = pack_bf16(silu_mul_fast(acc[mb][nb][0], acc[mb][nb + 4][0]),
-                                            silu_mul_fast(acc[mb][nb][1], acc[mb][nb + 4][1]));
-                    uint32_t w1 = pack_bf16(silu_mul_fast(acc[mb][nb][2], acc[mb][nb + 4][2]),
-                                            silu_mul_fast(acc[mb][nb][3], acc[mb][nb + 4][3]));
-                    *reinterpret_cast<uint2*>(out + ((tc.m0 + row) * p.ldo + col) * 2) = uint2{w0, w1};
-                }
+                const uint32_t w0 = pack_bf16(silu_mul_fast(acc[mb][nb][0], acc[mb][nb + 4][0]),
+                                              silu_mul_fast(acc[mb][nb][1], acc[mb][nb + 4][1]));
+                const uint32_t w1 = pack_bf16(silu_mul_fast(acc[mb][nb][2], acc[mb][nb + 4][2]),
+                                              silu_mul_fast(acc[mb][nb][3], acc[mb][nb + 4][3]));
+                const int off = (row0 + mb * 16) * kOutRow + (wn * 64 + nb * 16 + c4) * 2;
+                *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(smem + off) = u32x2{w0, w1};
             }
-        }
     } else {
 #pragma unroll
-        for (int mb = 0; mb < 8; ++mb) {
-            const int row = row0 + mb * 16;
+        for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
             for (int nb = 0; nb < 8; ++nb) {
-                const int col = tc.n * 256 + wn * 128 + nb * 16 + c4;
-                if (row < tc.rows && col < p.ldo) {
-                    const uint32_t w0 = pack_bf16(acc[mb][nb][0], acc[mb][nb][1]);
-                    const uint32_t w1 = pack_bf16(acc[mb][nb][2], acc[mb][nb][3]);
-                    *reinterpret_cast<uint2*>(out + ((tc.m0 + row) * p.ldo + col) * 2) = uint2{w0, w1};
-                }
+                const uint32_t w0 = pack_bf16(acc[mb][nb][0], acc[mb][nb][1]);
+                const uint32_t w1 = pack_bf16(acc[mb][nb][2], acc[mb][nb][3]);
+                const int off = (row0 + mb * 16) * kOutRow + (wn * 128 + nb * 16 + c4) * 2;
+                *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(smem + off) = u32x2{w0, w1};
             }
-        }
+    }
+    __syncthreads();
+    constexpr int kChunks = NC / 8;
+    constexpr int kRowsPerPass = 256 / kChunks;
+    const int col_base = GATE_UP ? tc.n * 128 : tc.n * 256;
+    const int col_lim = GATE_UP ? p.I : p.ldo;
+    const int ch = tid % kChunks;
+    const int col = col_base + ch * 8;
+    uint8_t* __restrict__ out = static_cast<uint8_t*>(p.out);
+#pragma unroll 4
+    for (int r = tid / kChunks; r < BM; r += kRowsPerPass) {
+        const u32x4 v = *reinterpret_cast<lds_u32x4*>(smem + r * kOutRow + ch * 16);
+        if (r < tc.rows && col < col_lim)
+            *reinterpret_cast<u32x4*>(out + ((tc.m0 + r) * p.ldo + col) * 2) = v;
     }
 }
 
@@ -522,9 +517,9 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmParams p) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[kLds2];
     Tile2 tc;
     if (!locate_tile2(p, tc)) return;
-    lds_u8* lds = (lds_u8*)(smem);  // the array lives in LDS: an address-space cast
-    if (tc.tail) tile_pipeline<GATE_UP, 128, 512, 4>(p, tc, lds);
-    else tile_pipeline<GATE_UP, 256, 256, 5>(p, tc, lds);
+    lds_u8* lds = (lds_u8*)(smem);
+    if (tc.tail) tile_pipeline<GATE_UP, 128, 512>(p, tc, lds);
+    else tile_pipeline<GATE_UP, 256, 256>(p, tc, lds);
 }
 
 // ===========================================================================
