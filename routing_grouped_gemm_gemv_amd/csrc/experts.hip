@@ -53,7 +53,8 @@ struct GemmParams {
     const int32_t* perm;       // gate_up: perm_token or nullptr (identity)
     const int32_t* offsets;    // [G+1] or nullptr (one group of ident_rows rows)
     const int32_t* tile_start; // fp32 kernel: [G+1] m-tile prefix sums (with offsets)
-    const u32x4* tiles;        // bf16 kernel: one descriptor per workgroup (with offsets)
+    const u32x4* tiles;        // bf16 kernel: tile descriptors in grouped order
+    int32_t* ctl;              // bf16 kernel: tile count and work-queue counters of this GEMM
     int64_t ident_rows;
     int G;
     int Kd;                    // reduction length
@@ -233,21 +234,28 @@ __device__ __forceinline__ u32x4 tile_desc(int g, int64_t m0, int rows, int n, b
                  static_cast<uint32_t>(n) | (tail ? 0x10000u : 0u)};
 }
 
-// Descriptors of every workgroup of both GEMMs (gate_up and down have
-// different n-tiles): workgroup b runs logical tile xcd_remap(b) of the
-// grouped order, or nothing (g = -1).  Each block rebuilds the tile prefix
-// sums of the groups in LDS and fills a strided share of both tables, so a
-// GEMM workgroup finds its tile with one load.
-__global__ __launch_bounds__(1024) void build_tile_table_kernel(const int32_t* __restrict__ offsets, int G, int nt1,
-                                                                int nt2, u32x4* __restrict__ desc1, int nwg1,
-                                                                u32x4* __restrict__ desc2, int nwg2) {
+// Control block of one GEMM launch: the tile count, then one work-queue
+// counter per XCD, each on its own 128-byte line.
+constexpr int kCtlInts = 8 * 32 + 32;
+__host__ __device__ __forceinline__ int ctl_queue(int x) { return 32 + 32 * x; }
+
+// Tile descriptors of both GEMMs (gate_up and down have different n-tiles) in
+// grouped order, the tile counts, and zeroed queue counters.  offsets ==
+// nullptr means one group of ident_rows rows.  Each block rebuilds the tile
+// prefix sums of the groups in LDS and fills a strided share of both tables.
+__global__ __launch_bounds__(1024) void build_tile_table_kernel(const int32_t* __restrict__ offsets, int G,
+                                                                int ident_rows, int nt1, int nt2,
+                                                                u32x4* __restrict__ desc1, int cap1,
+                                                                u32x4* __restrict__ desc2, int cap2,
+                                                                int32_t* __restrict__ ctl1, int32_t* __restrict__ ctl2) {
     __shared__ int part1[1024];
     __shared__ int part2[1024];
     __shared__ int off[1025];
     const int tid = threadIdx.x;
     int a = 0, b = 0;
     if (tid < G) {
-        const int o0 = offsets[tid], o1 = offsets[tid + 1];
+        const int o0 = offsets ? offsets[tid] : 0;
+        const int o1 = offsets ? offsets[tid + 1] : ident_rows;
         off[tid] = o0;
         if (tid == G - 1) off[G] = o1;
         const int c = o1 - o0;
@@ -267,78 +275,84 @@ __global__ __launch_bounds__(1024) void build_tile_table_kernel(const int32_t* _
     }
     // exclusive starts: part[g] - tiles(g); total = part[G - 1]
     const int total1 = part1[G - 1], total2 = part2[G - 1];
+    if (blockIdx.x == 0 && tid < kCtlInts) {
+        ctl1[tid] = tid == 0 ? total1 : 0;
+        ctl2[tid] = tid == 0 ? total2 : 0;
+    }
     for (int t = 0; t < 2; ++t) {
         const int* part = t == 0 ? part1 : part2;
         const int nt = t == 0 ? nt1 : nt2;
         const int total = t == 0 ? total1 : total2;
-        const int nwg = t == 0 ? nwg1 : nwg2;
+        const int cap = t == 0 ? cap1 : cap2;
         u32x4* desc = t == 0 ? desc1 : desc2;
-        const int64_t padded = (static_cast<int64_t>(total) + 7) & ~static_cast<int64_t>(7);
-        for (int w = blockIdx.x * 1024 + tid; w < nwg; w += gridDim.x * 1024) {
-            u32x4 d = u32x4{0xFFFFFFFFu, 0u, 0u, 0u};
-            if (w < padded) {
-                const int64_t L = xcd_remap(w, padded);
-                if (L < total) {
-                    // last g whose exclusive start is <= L (empty groups share a start)
-                    int lo = 0, hi = G - 1;
-                    while (lo < hi) {
-                        const int mid = (lo + hi + 1) >> 1;
-                        const int st = mid == 0 ? 0 : part[mid - 1];
-                        if (st <= L) lo = mid; else hi = mid - 1;
-                    }
-                    const int g = lo;
-                    const int st = g == 0 ? 0 : part[g - 1];
-                    const int c = off[g + 1] - off[g];
-                    int n, m;
-                    bool tail;
-                    decode_tile(c, nt, L - st, n, m, tail);
-                    const int left = c - m * 256;
-                    d = tile_desc(g, static_cast<int64_t>(off[g]) + static_cast<int64_t>(m) * 256, left < 256 ? left : 256, n,
-                                  tail);
-                }
+        for (int L = blockIdx.x * 1024 + tid; L < total && L < cap; L += gridDim.x * 1024) {
+            // last g whose exclusive start is <= L (empty groups share a start)
+            int lo = 0, hi = G - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                const int st = mid == 0 ? 0 : part[mid - 1];
+                if (st <= L) lo = mid; else hi = mid - 1;
             }
-            desc[w] = d;
+            const int g = lo;
+            const int st = g == 0 ? 0 : part[g - 1];
+            const int c = off[g + 1] - off[g];
+            int n, m;
+            bool tail;
+            decode_tile(c, nt, L - st, n, m, tail);
+            const int left = c - m * 256;
+            desc[L] = tile_desc(g, static_cast<int64_t>(off[g]) + static_cast<int64_t>(m) * 256,
+                                left < 256 ? left : 256, n, tail);
         }
     }
 }
 
-// Which tile this workgroup owns; false if none (grid padding).
-__device__ __forceinline__ bool locate_tile2(const GemmParams& p, Tile2& t) {
-    if (p.offsets != nullptr) {
-        const u32x4 d = p.tiles[blockIdx.x];
-        if (static_cast<int>(d.x) < 0) return false;
-        t.g = static_cast<int>(d.x);
-        t.m0 = static_cast<int64_t>(d.y);
-        t.rows = static_cast<int>(d.z);
-        t.n = static_cast<int>(d.w & 0xFFFFu);
-        t.tail = (d.w >> 16) != 0;
-        return true;
+__device__ __forceinline__ Tile2 load_tile(const GemmParams& p, int L) {
+    const u32x4 d = p.tiles[L];
+    Tile2 t;
+    t.g = static_cast<int>(d.x);
+    t.m0 = static_cast<int64_t>(d.y);
+    t.rows = static_cast<int>(d.z);
+    t.n = static_cast<int>(d.w & 0xFFFFu);
+    t.tail = (d.w >> 16) != 0;
+    return t;
+}
+
+// Work queues.  The tiles in grouped order are cut into 8 contiguous ranges,
+// one per XCD (workgroup b runs on XCD b % 8), so tiles that share operands
+// run in one L2.  A workgroup takes the next tile of its own range with an
+// atomic increment and, once that range is used up, of the others in turn.
+// Which workgroup computes a tile never changes its result.
+struct Queues {
+    int total;
+    int per;  // tiles per range
+};
+__device__ __forceinline__ int queue_tile(const Queues& qs, int q, int i) {
+    const int L = q * qs.per + i;
+    return (i < qs.per && L < qs.total) ? L : -1;
+}
+// Next tile for the calling wave starting at range q (updated), or -1.  Lane
+// 0 performs the atomics; the result is uniform over the wave.
+__device__ __forceinline__ int take_tile(int32_t* ctl, const Queues& qs, int& q) {
+    for (int k = 0; k < 8; ++k) {
+        int i = 0;
+        if (lane_id() == 0) i = __hip_atomic_fetch_add(ctl + ctl_queue(q), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        i = __builtin_amdgcn_readfirstlane(i);
+        const int L = queue_tile(qs, q, i);
+        if (L >= 0) return L;
+        q = (q + 1) & 7;
     }
-    // one group of ident_rows rows: no tables
-    const int c = static_cast<int>(p.ident_rows);
-    const int64_t total = tiles_of(c, p.n_tiles);
-    const int64_t padded = (total + 7) & ~static_cast<int64_t>(7);
-    if (static_cast<int64_t>(blockIdx.x) >= padded) return false;
-    const int64_t L = xcd_remap(blockIdx.x, padded);
-    if (L >= total) return false;
-    int n, m;
-    bool tail;
-    decode_tile(c, p.n_tiles, L, n, m, tail);
-    t.g = 0;
-    t.n = n;
-    t.tail = tail;
-    t.m0 = static_cast<int64_t>(m) * 256;
-    const int left = c - m * 256;
-    t.rows = left < 256 ? left : 256;
-    return true;
+    return -1;
 }
 
 // One tile of BM rows x BN weight rows (gate_up: BN/2 gate rows and the
 // matching BN/2 up rows).  Stage st holds k = 64 st .. 64 st + 63 of all the
 // tile's rows; each DMA instruction moves 8 rows x 128 bytes.  A stage feeds
 // two 32-wide MFMA sub-steps, and one wait + barrier per stage serves both.
+// claim: a work-queue counter that lane 0 of wave 0 increments once the
+// first stage has landed (so the atomic never holds up the prologue); the
+// value it returns is the result (0 elsewhere).
 template <bool GATE_UP, int BM, int BN>
-__device__ __forceinline__ void tile_pipeline(const GemmParams& p, const Tile2& tc, lds_u8* smem) {
+__device__ __forceinline__ int tile_pipeline(const GemmParams& p, const Tile2& tc, lds_u8* smem, int32_t* claim) {
     constexpr int kWN = BM == 256 ? 2 : 4;
     constexpr int kRow = 128;
     constexpr int kStage = (BM + BN) * kRow;
@@ -348,7 +362,11 @@ __device__ __forceinline__ void tile_pipeline(const GemmParams& p, const Tile2& 
     static_assert(2 * kStage <= kLds2, "LDS");
     static_assert(kDma <= 32, "DMA issue slots");
 
-    const int tid = threadIdx.x;
+    // The thread index passes through an empty asm so that the per-lane
+    // addresses below are computed per tile, not hoisted out of the
+    // persistent loop and kept (spilled) across the pipeline.
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
     const int lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wv / kWN;
@@ -359,31 +377,43 @@ __device__ __forceinline__ void tile_pipeline(const GemmParams& p, const Tile2& 
     const uint8_t* __restrict__ wbase =
         static_cast<const uint8_t*>(p.w) + static_cast<int64_t>(tc.g) * p.w_group_stride * 2;
     // lane l lands on row l / 8 of its 8-row group at physical chunk l % 8 and
-    // fetches logical chunk (l % 8) ^ (row % 8)
+    // fetches logical chunk (l % 8) ^ (row % 8).  Byte offsets fit 32 bits: x,
+    // the activations and one group's weights are each below 4 GiB (checked
+    // by the launcher).  Offsets are recomputed per DMA from a few registers;
+    // only the gathered rows of gate_up are held (their token ids are loads).
     const int chunk = (lane & 7) ^ (lane >> 3);
-    uint32_t aoff[kDmaA], boff[kDmaB];
+    const uint32_t row_bytes = static_cast<uint32_t>(p.Kd) * 2;
+    const int ra = wv * (BM / 4) + (lane >> 3);  // tile row of A instruction 0
+    const int rb = wv * (BN / 4) + (lane >> 3);  // weight row of B instruction 0
+    const bool gather = GATE_UP && p.perm != nullptr;
+    uint32_t aoff_g[GATE_UP ? kDmaA : 1];
+    if (GATE_UP) {
 #pragma unroll
-    for (int i = 0; i < kDmaA; ++i) {
-        const int r = wv * (BM / 4) + 8 * i + (lane >> 3);
-        const int rr = r < tc.rows ? r : tc.rows - 1;
-        int64_t src = tc.m0 + rr;
-        if (GATE_UP && p.perm != nullptr) src = p.perm[src];
-        aoff[i] = static_cast<uint32_t>(src * p.Kd * 2 + chunk * 16);
+        for (int i = 0; i < kDmaA; ++i) {
+            const int r = ra + 8 * i;
+            const int rr = r < tc.rows ? r : tc.rows - 1;  // rows past the group repeat its last row; never stored
+            aoff_g[i] = gather ? static_cast<uint32_t>(p.perm[tc.m0 + rr]) * row_bytes + chunk * 16 : 0u;
+        }
     }
-#pragma unroll
-    for (int i = 0; i < kDmaB; ++i) {
-        const int r = wv * (BN / 4) + 8 * i + (lane >> 3);
+    auto a_off = [&](int i) -> uint32_t {
+        if (GATE_UP && gather) return aoff_g[i];
+        const int r = ra + 8 * i;
+        const int rr = r < tc.rows ? r : tc.rows - 1;
+        return static_cast<uint32_t>(tc.m0 + rr) * row_bytes + chunk * 16;
+    };
+    auto b_off = [&](int i) -> uint32_t {
+        const int r = rb + 8 * i;
         int wrow;
         if (GATE_UP) {
-            int c = tc.n * 128 + (r % (BN / 2));
-            if (c >= p.I) c = p.I - 1;
+            int c = tc.n * 128 + (r % (BN / 2));  // gate row; the matching up row is I + c
+            if (c >= p.I) c = p.I - 1;           // I % 128 == 64: last tile half full
             wrow = r < BN / 2 ? c : p.I + c;
         } else {
             wrow = tc.n * 256 + r;
             if (wrow >= p.ldo) wrow = p.ldo - 1;
         }
-        boff[i] = static_cast<uint32_t>(static_cast<int64_t>(wrow) * p.Kd * 2 + chunk * 16);
-    }
+        return static_cast<uint32_t>(wrow) * row_bytes + chunk * 16;
+    };
     const int a_dst = wv * (BM / 4) * kRow;
     const int b_dst = BM * kRow + wv * (BN / 4) * kRow;
 
@@ -407,8 +437,8 @@ __device__ __forceinline__ void tile_pipeline(const GemmParams& p, const Tile2& 
     const int ns = p.Kd / 64;  // stages of the k loop
     auto dma = [&](int st, uint32_t stage_off, int q) {
         const uint32_t kb = static_cast<uint32_t>(st < ns ? st : ns - 1) * kRow;
-        if (q < kDmaA) dma16(abase, aoff[q] + kb, lds0 + stage_off + a_dst + q * 8 * kRow);
-        else dma16(wbase, boff[q - kDmaA] + kb, lds0 + stage_off + b_dst + (q - kDmaA) * 8 * kRow);
+        if (q < kDmaA) dma16(abase, a_off(q) + kb, lds0 + stage_off + a_dst + q * 8 * kRow);
+        else dma16(wbase, b_off(q - kDmaA) + kb, lds0 + stage_off + b_dst + (q - kDmaA) * 8 * kRow);
     };
     auto frag = [&](uint32_t stage_off, int xo, int k) -> u32x4 {
         const lds_u8* st = smem + stage_off;
@@ -449,6 +479,8 @@ __device__ __forceinline__ void tile_pipeline(const GemmParams& p, const Tile2& 
 #pragma unroll
     for (int q = 0; q < kDma; ++q) dma(1, kStage, q);
     wait_vmem<kDma>();
+    int claimed = 0;
+    if (wv == 0 && lane == 0) claimed = __hip_atomic_fetch_add(claim, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     u32x4 f0[16], f1[16];
 #pragma unroll
@@ -510,16 +542,51 @@ __device__ __forceinline__ void tile_pipeline(const GemmParams& p, const Tile2& 
         if (r < tc.rows && col < col_lim)
             *reinterpret_cast<u32x4*>(out + ((tc.m0 + r) * p.ldo + col) * 2) = v;
     }
+    return claimed;
 }
 
+// Value of wave 0 to every wave of the workgroup (through LDS word 0, which
+// no stage or output row is using at this point).
+__device__ __forceinline__ int broadcast_from_wave0(lds_u8* smem, int v) {
+    __syncthreads();
+    if (threadIdx.x == 0) *reinterpret_cast<__attribute__((address_space(3))) int*>(smem) = v;
+    __syncthreads();
+    const int r = *reinterpret_cast<__attribute__((address_space(3))) int*>(smem);
+    __syncthreads();
+    return r;
+}
+
+// Persistent: one workgroup per CU takes tiles from the work queues until
+// none are left; the next tile of its range is claimed while the current one
+// runs.
 template <bool GATE_UP>
 __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmParams p) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[kLds2];
-    Tile2 tc;
-    if (!locate_tile2(p, tc)) return;
-    lds_u8* lds = (lds_u8*)(smem);
-    if (tc.tail) tile_pipeline<GATE_UP, 128, 512>(p, tc, lds);
-    else tile_pipeline<GATE_UP, 256, 256>(p, tc, lds);
+    lds_u8* lds = (lds_u8*)(smem);  // the array lives in LDS: an address-space cast
+    const bool w0 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) == 0;
+    Queues qs;
+    qs.total = p.ctl[0];
+    qs.per = (qs.total + 7) >> 3;
+    int q = blockIdx.x & 7;
+    int L = -1;
+    if (w0) L = take_tile(p.ctl, qs, q);
+    L = broadcast_from_wave0(lds, L);
+    while (L >= 0) {
+        const Tile2 tc = load_tile(p, L);
+        int32_t* ctr = p.ctl + ctl_queue(q);
+        int claim;
+        if (tc.tail) claim = tile_pipeline<GATE_UP, 128, 512>(p, tc, lds, ctr);
+        else claim = tile_pipeline<GATE_UP, 256, 256>(p, tc, lds, ctr);
+        int next = -1;
+        if (w0) {
+            next = queue_tile(qs, q, __builtin_amdgcn_readfirstlane(claim));
+            if (next < 0) {
+                q = (q + 1) & 7;
+                next = take_tile(p.ctl, qs, q);
+            }
+        }
+        L = broadcast_from_wave0(lds, next);
+    }
 }
 
 // ===========================================================================
@@ -678,13 +745,28 @@ static void bf16_grid(int64_t rows_max, int G, bool grouped, int D, int I, int64
     nwg2 = ((mt_max * ((D + 255) / 256)) + 7) & ~static_cast<int64_t>(7);
 }
 
+constexpr size_t kCtlBytes = 2 * kCtlInts * sizeof(int32_t);
+
+// CUs of the current device (queried once per device)
+static int compute_units() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
 size_t experts_ws_bytes(int64_t rows_max, int G, int D, int I, int dtype) {
     const size_t eb = dtype == 0 ? 2 : 4;
     size_t tables = align256(2 * sizeof(int32_t) * (G + 1));
     if (dtype == 0) {
         int64_t nwg1, nwg2;
         bf16_grid(rows_max, G, true, D, I, nwg1, nwg2);
-        tables = align256(static_cast<size_t>(nwg1 + nwg2) * sizeof(u32x4));
+        tables = align256(kCtlBytes + static_cast<size_t>(nwg1 + nwg2) * sizeof(u32x4));
     }
     return tables + align256(static_cast<size_t>(rows_max) * I * eb);
 }
@@ -728,20 +810,27 @@ hipError_t launch_experts(const void* x, int64_t x_rows, const int32_t* perm_tok
         p2.n_tiles = (D + 255) / 256;
         int64_t nwg1, nwg2;
         bf16_grid(rows_max, G, offsets != nullptr, D, I, nwg1, nwg2);
-        if (offsets != nullptr) {
-            u32x4* d1 = static_cast<u32x4*>(ws);
-            u32x4* d2 = d1 + nwg1;
-            const int64_t most = nwg1 > nwg2 ? nwg1 : nwg2;
-            const unsigned blocks = static_cast<unsigned>((most + 2047) / 2048);
-            build_tile_table_kernel<<<blocks, 1024, 0, stream>>>(offsets, G, p1.n_tiles, p2.n_tiles, d1,
-                                                                static_cast<int>(nwg1), d2, static_cast<int>(nwg2));
-            if ((err = hipGetLastError()) != hipSuccess) return err;
-            p1.tiles = d1;
-            p2.tiles = d2;
-        }
-        grouped_gemm_bf16_kernel<true><<<static_cast<unsigned>(nwg1), 256, 0, stream>>>(p1);
+        int32_t* ctl1 = static_cast<int32_t*>(ws);
+        int32_t* ctl2 = ctl1 + kCtlInts;
+        u32x4* d1 = reinterpret_cast<u32x4*>(static_cast<uint8_t*>(ws) + kCtlBytes);
+        u32x4* d2 = d1 + nwg1;
+        const int64_t most = nwg1 > nwg2 ? nwg1 : nwg2;
+        const unsigned blocks = static_cast<unsigned>((most + 2047) / 2048);
+        build_tile_table_kernel<<<blocks, 1024, 0, stream>>>(offsets, offsets ? G : 1, static_cast<int>(rows_max),
+                                                            p1.n_tiles, p2.n_tiles, d1, static_cast<int>(nwg1), d2,
+                                                            static_cast<int>(nwg2), ctl1, ctl2);
         if ((err = hipGetLastError()) != hipSuccess) return err;
-        grouped_gemm_bf16_kernel<false><<<static_cast<unsigned>(nwg2), 256, 0, stream>>>(p2);
+        p1.tiles = d1;
+        p2.tiles = d2;
+        p1.ctl = ctl1;
+        p2.ctl = ctl2;
+        // one workgroup per CU (each holds all of a CU's LDS), a multiple of 8
+        const int slots = (compute_units() + 7) & ~7;
+        const unsigned g1 = static_cast<unsigned>(nwg1 < slots ? nwg1 : slots);
+        const unsigned g2 = static_cast<unsigned>(nwg2 < slots ? nwg2 : slots);
+        grouped_gemm_bf16_kernel<true><<<g1, 256, 0, stream>>>(p1);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+        grouped_gemm_bf16_kernel<false><<<g2, 256, 0, stream>>>(p2);
         return hipGetLastError();
     }
     int32_t* ts1 = static_cast<int32_t*>(ws);
