@@ -48,4 +48,36 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t nwg) {
     return (bid & 7) * per + (bid >> 3);
 }
 
+// M0 is reserved to the compiler; the DMA asm below sets it on purpose
+#pragma clang diagnostic ignored "-Winline-asm"
+
+// 16 bytes per lane from global memory (base + 32-bit per-lane offset) into
+// LDS at wave_base + 16 * lane: global_load_lds_dwordx4 with M0 holding the
+// wave's LDS base.  It is issued from inline asm on purpose: the compiler's
+// wait-count tracking of LDS DMA cannot tell the stages of this pipeline
+// apart and would drain every DMA in flight before each fragment read.  The
+// instruction has no destination register; completion is awaited with the
+// explicit vmcnt waits of the pipelines that use it, and no other code in
+// those kernels uses M0.
+// The base address and the LDS base are wave-uniform; readfirstlane states
+// that to the compiler where it cannot prove it.
+__device__ __forceinline__ void dma16(const uint8_t* gbase, uint32_t voff, uint32_t lds_wave_base) {
+    const uint64_t g = reinterpret_cast<uint64_t>(gbase);
+    const uint64_t gu = (static_cast<uint64_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(g >> 32))) << 32) |
+                        static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(g)));
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_wave_base);
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(m0), "v"(voff), "s"(reinterpret_cast<const uint8_t*>(gu))
+                 : "memory", "m0");
+}
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
+
+// s_waitcnt with vmcnt(n) and the other counters left alone
+constexpr int vmcnt_imm(int n) { return 0x3F70 | (n & 15) | (((n >> 4) & 3) << 14); }
+template <int N>
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(vmcnt_imm(N)); }
+
 }  // namespace moe

@@ -41,8 +41,6 @@
 #include "common.hpp"
 #include "kernels.hpp"
 
-// M0 is reserved to the compiler; the DMA asm below sets it on purpose
-#pragma clang diagnostic ignored "-Winline-asm"
 
 namespace moe {
 
@@ -148,28 +146,7 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 // ===========================================================================
 constexpr int kLds2 = 160 * 1024;
 
-// 16 bytes per lane from global memory (base + 32-bit per-lane offset) into
-// LDS at wave_base + 16 * lane: global_load_lds_dwordx4 with M0 holding the
-// wave's LDS base.  It is issued from inline asm on purpose: the compiler's
-// wait-count tracking of LDS DMA cannot tell the stages of this pipeline
-// apart and would drain every DMA in flight before each fragment read.  The
-// instruction has no destination register; completion is awaited with the
-// explicit vmcnt waits of the pipeline, and no other code in these kernels
-// uses M0.
-__device__ __forceinline__ void dma16(const uint8_t* gbase, uint32_t voff, uint32_t lds_wave_base) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
-                 :
-                 : "s"(lds_wave_base), "v"(voff), "s"(gbase)
-                 : "memory", "m0");
-}
 
-typedef __attribute__((address_space(3))) uint8_t lds_u8;
-typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
-
-// s_waitcnt with vmcnt(n) and the other counters left alone
-constexpr int vmcnt_imm(int n) { return 0x3F70 | (n & 15) | (((n >> 4) & 3) << 14); }
-template <int N>
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(vmcnt_imm(N)); }
 
 // Tiles of one group of c rows.  Full tiles are 256 rows x one n-tile.  When
 // the number of n-tiles is even, the last c % 256 rows, if at most 128, form

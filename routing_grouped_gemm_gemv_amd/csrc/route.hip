@@ -10,10 +10,11 @@
 //
 // Precision: a top-k decision is discrete, so the logits are accumulated far
 // more accurately than the score margins that decide it.  In bf16 mode the
-// GEMM runs on MFMA with fp32 accumulation over chunks of 64 products, and the
-// chunk sums are added in float64; in fp32 mode each logit is a float64 FMA
-// chain (the fp32 x fp32 products are exact in float64).  Scores, choices and
-// weights are then float64; the weights are rounded once to float32.
+// GEMM runs on MFMA with fp32 accumulation over chunks of 128 products (the
+// last chunk may hold 64), and the chunk sums are added in float64; in fp32
+// mode each logit is a float64 FMA chain (the fp32 x fp32 products are exact
+// in float64).  Scores, choices and weights are then float64; the weights are
+// rounded once to float32.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -24,7 +25,7 @@ namespace moe {
 // ---------------------------------------------------------------------------
 constexpr int kRtTok = 64;
 constexpr int kRtExp = 64;
-constexpr int kRtK = 64;  // k per chunk: fp32 partial sums of 64 products, then float64
+constexpr int kRtK = 64;  // k per LDS stage; fp32 partial sums span two stages (128 products)
 
 __global__ __launch_bounds__(256) void router_logits_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int64_t T, int D, int E,
@@ -42,6 +43,7 @@ __global__ __launch_bounds__(256) void router_logits_bf16_kernel(
     for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc64[nb][i] = 0.0;
+    f32x4 acc[4];
 
     for (int k0 = 0; k0 < D; k0 += kRtK) {
 #pragma unroll
@@ -59,9 +61,10 @@ __global__ __launch_bounds__(256) void router_logits_bf16_kernel(
             *reinterpret_cast<u32x4*>(sw + off) = vw;
         }
         __syncthreads();
-        f32x4 acc[4];
+        if ((k0 & 127) == 0) {
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int nb = 0; nb < 4; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             const int ch = 4 * s + (lane >> 4);
@@ -74,10 +77,12 @@ __global__ __launch_bounds__(256) void router_logits_bf16_kernel(
                 acc[nb] = mfma_bf16(a, b, acc[nb]);
             }
         }
+        if ((k0 & 127) == 64 || k0 + kRtK == D) {
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
+            for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc64[nb][i] += static_cast<double>(acc[nb][i]);
+                for (int i = 0; i < 4; ++i) acc64[nb][i] += static_cast<double>(acc[nb][i]);
+        }
         __syncthreads();
     }
 #pragma unroll
@@ -291,6 +296,137 @@ __device__ __forceinline__ void topk_token(const double (&lg)[EPL], int64_t t, i
     }
 }
 
+// ---- sixteen lanes per token ------------------------------------------------
+// The same selection for four tokens per wave: row r (lanes 16r .. 16r+15)
+// takes one token, lane j of the row holds experts j, j + 16, ...  The row
+// reductions use the first four DPP steps of the wave reductions above, which
+// leave every lane of the row with the row's result.
+__device__ __forceinline__ uint64_t row_max_u64(uint64_t k) {
+    k = umax64(k, dpp_u64<0xB1>(k));
+    k = umax64(k, dpp_u64<0x4E>(k));
+    k = umax64(k, dpp_u64<0x141>(k));
+    return umax64(k, dpp_u64<0x140>(k));
+}
+__device__ __forceinline__ double row_max_f64(double v) {
+    v = fmax(v, dpp_f64<0xB1>(v));
+    v = fmax(v, dpp_f64<0x4E>(v));
+    v = fmax(v, dpp_f64<0x141>(v));
+    return fmax(v, dpp_f64<0x140>(v));
+}
+__device__ __forceinline__ double row_sum_f64(double v) {
+    v = v + dpp_f64<0xB1>(v);
+    v = v + dpp_f64<0x4E>(v);
+    v = v + dpp_f64<0x141>(v);
+    return v + dpp_f64<0x140>(v);
+}
+// value of lane src (an absolute lane index) to the calling lane
+__device__ __forceinline__ int lane_get(int v, int src) { return __builtin_amdgcn_ds_bpermute(src << 2, v); }
+__device__ __forceinline__ double lane_get_f64(double v, int src) {
+    const uint64_t b = static_cast<uint64_t>(__double_as_longlong(v));
+    const uint32_t lo = static_cast<uint32_t>(lane_get(static_cast<int>(static_cast<uint32_t>(b)), src));
+    const uint32_t hi = static_cast<uint32_t>(lane_get(static_cast<int>(static_cast<uint32_t>(b >> 32)), src));
+    return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+}
+
+// Token t of this lane's row, whose float64 logits the row holds (EPL16 per
+// lane: experts j, j + 16, ... for lane j of the row).  Every lane of the wave
+// must call it (rows whose token does not exist pass live = false and write
+// nothing).  Same arithmetic as topk_token except the order of the softmax
+// sums across lanes.
+template <int EPL16>
+__device__ __forceinline__ void topk_row16(const double (&lg)[EPL16], int64_t t, bool live, int E, int K, int score,
+                                           int renorm, double route_scale, const float* __restrict__ bias,
+                                           bool kept, int32_t* __restrict__ ids_out, float* __restrict__ w_out) {
+    const int lane = lane_id();
+    const int j = lane & 15;
+    const int rbase = lane & 48;
+    bool ok[EPL16];
+#pragma unroll
+    for (int i = 0; i < EPL16; ++i) ok[i] = j + 16 * i < E;
+
+    double s[EPL16];
+    if (score == 0) {
+        double m = -1.7976931348623157e308;
+#pragma unroll
+        for (int i = 0; i < EPL16; ++i)
+            if (ok[i]) m = fmax(m, lg[i]);
+        m = row_max_f64(m);
+        double part = 0.0;
+#pragma unroll
+        for (int i = 0; i < EPL16; ++i) {
+            s[i] = ok[i] ? exp(lg[i] - m) : 0.0;
+            part += s[i];
+        }
+        const double z = row_sum_f64(part);
+#pragma unroll
+        for (int i = 0; i < EPL16; ++i) s[i] = s[i] / z;
+    } else {
+#pragma unroll
+        for (int i = 0; i < EPL16; ++i) s[i] = ok[i] ? 1.0 / (1.0 + exp(-lg[i])) : 0.0;
+    }
+
+    uint64_t key[EPL16];
+#pragma unroll
+    for (int i = 0; i < EPL16; ++i) {
+        const int e = j + 16 * i;
+        double c = s[i];
+        if (bias != nullptr && ok[i]) c += static_cast<double>(bias[e]);
+        key[i] = ok[i] ? choice_key(c, e) : 0ull;
+    }
+
+    // K rounds of row argmax; lane r of the row keeps the r-th pick
+    int my_e = -1;
+    double my_s = 0.0;
+    for (int r = 0; r < K; ++r) {
+        uint64_t best = key[0];
+#pragma unroll
+        for (int i = 1; i < EPL16; ++i) best = umax64(best, key[i]);
+        const uint64_t win = row_max_u64(best);
+        const int ew = 1023 - static_cast<int>(win & 0x3FFull);
+        const int owner = ew & 15;
+        const int slot = ew >> 4;
+        double sw = -1.0;  // scores are >= 0: the row max picks the owner's value
+#pragma unroll
+        for (int i = 0; i < EPL16; ++i) {
+            if (j == owner && i == slot) {
+                sw = s[i];
+                key[i] = 0ull;
+            }
+        }
+        sw = row_max_f64(sw);
+        if (j == r) {
+            my_e = ew;
+            my_s = sw;
+        }
+    }
+
+    // ascending id order: rank of each pick among the row's K picks
+    int rank = 0;
+    for (int i = 0; i < K; ++i) {
+        const int ei = lane_get(my_e, rbase + i);
+        rank += (j < K && ei < my_e) ? 1 : 0;
+    }
+    double den = 1.0;
+    if (renorm) {
+        den = 0.0;
+        for (int r = 0; r < K; ++r) {
+            const uint64_t holders = __ballot(j < K && rank == r);
+            const int holder = __builtin_ctzll((holders >> rbase) & 0xFFFFull) + rbase;
+            den += lane_get_f64(my_s, holder);
+        }
+    }
+    if (live && j < K) {
+        if (kept) {
+            const double wv = renorm ? (my_s / den) * route_scale : my_s * route_scale;
+            ids_out[t * K + rank] = my_e;
+            w_out[t * K + rank] = static_cast<float>(wv);
+        } else {
+            ids_out[t * K + j] = -1;
+            w_out[t * K + j] = 0.f;
+        }
+    }
+}
+
 template <int EPL>
 __global__ __launch_bounds__(256) void topk_kernel(
     const double* __restrict__ logits, int64_t T, int E, int K, int score, int renorm,
@@ -316,21 +452,33 @@ __global__ __launch_bounds__(256) void topk_kernel(
 // workgroup, kept in LDS as float64, then top-k per token from LDS.
 // The hidden rows are read from memory once and the logits never leave the
 // chip.  Each logit is computed exactly as router_logits_bf16_kernel does
-// (two MFMA k=32 steps into a zeroed fp32 accumulator per 64-wide k chunk,
-// chunks added in float64 in k order), so both paths give the same bits.
+// (MFMA k=32 steps into an fp32 accumulator zeroed every 128 k, the 128-wide
+// partial sums added in float64 in k order), so both paths give the same bits.
+// The chunks stream through two LDS stages filled by global_load_lds_dwordx4
+// (8 rows x 128 bytes per instruction, the 16-byte chunks of a row XOR-
+// swizzled by row % 8), so loads run a whole chunk ahead of the MFMAs.
 // ---------------------------------------------------------------------------
 // TBB: 16-token blocks per workgroup; NBW: 16-expert blocks per wave (4 waves).
+// Hidden rows stream from memory through a ring of XS stages (loads run XS-1
+// chunks ahead); router rows, read by every workgroup and so mostly served
+// from L2, through a ring of WS stages.
 template <int TBB, int NBW>
 struct RouteTile {
     static constexpr int TB = 16 * TBB;        // tokens per workgroup
     static constexpr int EMAX = 64 * NBW;      // experts per workgroup
     static constexpr int EPL = EMAX / 64;      // experts per lane in the top-k
-    static constexpr int ROWS = TB + EMAX;     // rows staged per 64-wide k chunk
-    static constexpr int STAGE = ROWS * 128;   // bytes per chunk
+    static constexpr int XSTAGE = TB * 128;    // bytes of hidden rows per 64-wide k chunk
+    static constexpr int WSTAGE = EMAX * 128;  // bytes of router rows per chunk
+    static constexpr int XS = 8;
+    static constexpr int WS = (3 * WSTAGE + XS * XSTAGE <= 160 * 1024) ? 3 : 2;
+    static constexpr int WOFF = XS * XSTAGE;   // LDS offset of the router ring
+    static constexpr int RING = WOFF + WS * WSTAGE;
     static constexpr int LOGB = TB * EMAX * 8; // float64 logits
-    static constexpr int SMEM = (2 * STAGE > LOGB) ? 2 * STAGE : LOGB;
-    static constexpr int LOADS = ROWS * 8 / 256;  // 16-byte loads per thread per chunk
-    static_assert(ROWS % 32 == 0, "staging must divide over 256 threads");
+    static constexpr int SMEM = RING > LOGB ? RING : LOGB;
+    static constexpr int XPER = TB / 32;       // 8-row DMA instructions per wave per chunk
+    static constexpr int WPER = EMAX / 32;
+    static_assert(TB % 32 == 0 && EMAX % 32 == 0, "8-row DMA groups over 4 waves");
+    static_assert(SMEM <= 160 * 1024, "LDS");
 };
 
 template <int TBB, int NBW>
@@ -340,38 +488,49 @@ __global__ __launch_bounds__(256) void route_fused_bf16_kernel(
     const uint8_t* __restrict__ mask, float* __restrict__ logits_out, int32_t* __restrict__ ids_out,
     float* __restrict__ w_out) {
     using RT = RouteTile<TBB, NBW>;
-    __shared__ __attribute__((aligned(16))) uint8_t smem[RT::SMEM];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[RT::SMEM];
+    lds_u8* smem = (lds_u8*)(smem_raw);  // the array lives in LDS: an address-space cast
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t t0 = static_cast<int64_t>(blockIdx.x) * RT::TB;
+    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem));
 
-    // staging: row r < TB is hidden row t0 + r, row TB + j is router row j
-    const uint8_t* src[RT::LOADS];
-    int dst[RT::LOADS];
+    // DMA sources.  Each instruction moves 8 rows x 128 bytes; lane l lands
+    // on row l / 8 at physical chunk l % 8 and fetches logical chunk
+    // (l % 8) ^ (row % 8).  Hidden rows past T repeat row T-1 and router rows
+    // past E repeat row E-1; their logits are never used.  Hidden-row offsets
+    // are relative to the workgroup's first row, so they stay below TB*D*2.
+    // Chunks past the end re-fetch the last chunk into a stage nothing reads
+    // again, so every chunk issues the same instructions (uniform waits).
+    const uint8_t* xb = reinterpret_cast<const uint8_t*>(x + t0 * D);
+    const uint8_t* wb = reinterpret_cast<const uint8_t*>(w);
+    const uint32_t row_bytes = static_cast<uint32_t>(D) * 2;
+    const int chunk = (lane & 7) ^ (lane >> 3);
+    const int ns = D / 64;
+    auto issue_x = [&](int st) {
+        const int c = st < ns ? st : ns - 1;
+        const uint32_t kb = static_cast<uint32_t>(c) * 128 + chunk * 16;
+        const uint32_t dst = lds0 + (st % RT::XS) * RT::XSTAGE;
 #pragma unroll
-    for (int j = 0; j < RT::LOADS; ++j) {
-        const int q = tid + 256 * j;
-        const int row = q >> 3, ch = q & 7;
-        dst[j] = row * 128 + ((ch ^ (row & 7)) << 4);
-        const uint8_t* p = nullptr;
-        if (row < RT::TB) {
-            if (t0 + row < T) p = reinterpret_cast<const uint8_t*>(x + (t0 + row) * D) + ch * 16;
-        } else if (row - RT::TB < E) {
-            p = reinterpret_cast<const uint8_t*>(w + static_cast<int64_t>(row - RT::TB) * D) + ch * 16;
+        for (int i = 0; i < RT::XPER; ++i) {
+            const int q = wv * RT::XPER + i;
+            int64_t rr = 8 * q + (lane >> 3);
+            if (t0 + rr >= T) rr = T - 1 - t0;
+            dma16(xb, static_cast<uint32_t>(rr) * row_bytes + kb, dst + q * 1024);
         }
-        src[j] = p;
-    }
-    u32x4 stg[RT::LOADS];
-    auto fetch = [&](int k0) {
-#pragma unroll
-        for (int j = 0; j < RT::LOADS; ++j)
-            stg[j] = src[j] ? *reinterpret_cast<const u32x4*>(src[j] + 2 * k0) : u32x4{0u, 0u, 0u, 0u};
     };
-    auto store = [&](int buf) {
+    auto issue_w = [&](int st) {
+        const int c = st < ns ? st : ns - 1;
+        const uint32_t kb = static_cast<uint32_t>(c) * 128 + chunk * 16;
+        const uint32_t dst = lds0 + RT::WOFF + (st % RT::WS) * RT::WSTAGE;
 #pragma unroll
-        for (int j = 0; j < RT::LOADS; ++j)
-            *reinterpret_cast<u32x4*>(smem + buf * RT::STAGE + dst[j]) = stg[j];
+        for (int i = 0; i < RT::WPER; ++i) {
+            const int q = wv * RT::WPER + i;
+            int er = 8 * q + (lane >> 3);
+            if (er >= E) er = E - 1;
+            dma16(wb, static_cast<uint32_t>(er) * row_bytes + kb, dst + q * 1024);
+        }
     };
 
     double acc64[TBB][NBW][4];
@@ -381,49 +540,66 @@ __global__ __launch_bounds__(256) void route_fused_bf16_kernel(
         for (int b = 0; b < NBW; ++b)
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc64[a][b][i] = 0.0;
+    f32x4 acc[TBB][NBW];
 
-    const int nchunks = D / 64;
-    fetch(0);
-    store(0);
-    __syncthreads();
-    for (int c = 0; c < nchunks; ++c) {
-        const int buf = c & 1;
-        if (c + 1 < nchunks) fetch((c + 1) * 64);
-        const uint8_t* sb = smem + buf * RT::STAGE;
-        f32x4 acc[TBB][NBW];
+    // fragment of half j of a chunk: logical chunk 4j + lane/16 of row
+    // lane%16 (+16 per block), stored at chunk ^ (lane % 8)
+    const int xo0 = ((lane >> 4) ^ (lane & 7)) << 4;
+    const int xo1 = ((4 + (lane >> 4)) ^ (lane & 7)) << 4;
+    const int arow = (lane & 15) * 128;
+    const int brow = (wv * (16 * NBW) + (lane & 15)) * 128;
+
+    // Chunk st needs hidden stage st and router stage st.  At the top of
+    // chunk t the DMAs of router chunk t+WS-1 and hidden chunk t+XS-1 are
+    // issued (in that order) into the buffers chunk t-1 used; the router
+    // chunk a step needs was issued WS-1 steps earlier, and only its own
+    // step's hidden DMAs and the WS-2 later steps' DMAs are younger.
+    constexpr int kWaitN = RT::XPER + (RT::WS - 2) * (RT::WPER + RT::XPER);
+    for (int j = 0; j < RT::XS - 1; ++j) issue_x(j);
+    for (int j = 0; j < RT::WS - 1; ++j) issue_w(j);
+    wait_vmem<0>();
+    // one k64 stage: wait, barrier, next DMAs, two MFMA k=32 steps into acc
+    auto stage = [&](int st) {
+        if (st > 0) wait_vmem<kWaitN>();
+        __syncthreads();  // chunk st visible; every wave is done with chunk st-1
+        issue_w(st + RT::WS - 1);
+        issue_x(st + RT::XS - 1);
+        const lds_u8* xs = smem + (st % RT::XS) * RT::XSTAGE;
+        const lds_u8* ws = smem + RT::WOFF + (st % RT::WS) * RT::WSTAGE;
 #pragma unroll
-        for (int a = 0; a < TBB; ++a)
-#pragma unroll
-            for (int b = 0; b < NBW; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const int ch = 4 * s + (lane >> 4);
+        for (int j = 0; j < 2; ++j) {
+            const int xoj = j == 0 ? xo0 : xo1;
             u32x4 af[TBB];
 #pragma unroll
-            for (int a = 0; a < TBB; ++a) {
-                const int r = a * 16 + (lane & 15);
-                af[a] = *reinterpret_cast<const u32x4*>(sb + r * 128 + ((ch ^ (r & 7)) << 4));
-            }
+            for (int a = 0; a < TBB; ++a) af[a] = *reinterpret_cast<lds_u32x4*>(xs + arow + a * 16 * 128 + xoj);
 #pragma unroll
             for (int b = 0; b < NBW; ++b) {
-                const int r = RT::TB + wv * (16 * NBW) + b * 16 + (lane & 15);
-                const u32x4 bf = *reinterpret_cast<const u32x4*>(sb + r * 128 + ((ch ^ (r & 7)) << 4));
+                const u32x4 bf = *reinterpret_cast<lds_u32x4*>(ws + brow + b * 16 * 128 + xoj);
 #pragma unroll
                 for (int a = 0; a < TBB; ++a) acc[a][b] = mfma_bf16(af[a], bf, acc[a][b]);
             }
         }
+    };
+    // 128-wide partial sums: two stages per fp32 accumulation, then float64
+    for (int st = 0; st < ns; st += 2) {
+#pragma unroll
+        for (int a = 0; a < TBB; ++a)
+#pragma unroll
+            for (int b = 0; b < NBW; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+        stage(st);
+        if (st + 1 < ns) stage(st + 1);
 #pragma unroll
         for (int a = 0; a < TBB; ++a)
 #pragma unroll
             for (int b = 0; b < NBW; ++b)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) acc64[a][b][i] += static_cast<double>(acc[a][b][i]);
-        if (c + 1 < nchunks) store(buf ^ 1);
-        __syncthreads();
     }
+    wait_vmem<0>();
+    __syncthreads();  // the stages are dead: the logits take their place
 
-    // logits to LDS: [TB][EMAX] float64 (the staging buffers are dead)
-    double* lgs = reinterpret_cast<double*>(smem);
+    // logits to LDS: [TB][EMAX] float64
+    __attribute__((address_space(3))) double* lgs = (__attribute__((address_space(3))) double*)(smem);
 #pragma unroll
     for (int a = 0; a < TBB; ++a)
 #pragma unroll
@@ -436,18 +612,37 @@ __global__ __launch_bounds__(256) void route_fused_bf16_kernel(
             }
     __syncthreads();
 
-    for (int tl = wv; tl < RT::TB; tl += 4) {
-        const int64_t t = t0 + tl;
-        if (t >= T) break;  // uniform per wave
-        double lg[RT::EPL];
+    if constexpr (RT::EMAX <= 256) {
+        // four tokens per wave, sixteen lanes each
+        constexpr int EPL16 = RT::EMAX / 16;
+        for (int tb = 4 * wv; tb < RT::TB; tb += 16) {
+            const int tl = tb + (lane >> 4);
+            const int64_t t = t0 + tl;
+            const bool live = t < T;
+            double lg[EPL16];
 #pragma unroll
-        for (int i = 0; i < RT::EPL; ++i) {
-            const int e = lane + 64 * i;
-            lg[i] = lgs[tl * RT::EMAX + e];
-            if (logits_out && e < E) logits_out[t * E + e] = static_cast<float>(lg[i]);
+            for (int i = 0; i < EPL16; ++i) {
+                const int e = (lane & 15) + 16 * i;
+                lg[i] = lgs[tl * RT::EMAX + e];
+                if (logits_out && live && e < E) logits_out[t * E + e] = static_cast<float>(lg[i]);
+            }
+            const bool kept = live && ((mask == nullptr) || (mask[t] != 0));
+            topk_row16<EPL16>(lg, t, live, E, K, score, renorm, route_scale, bias, kept, ids_out, w_out);
         }
-        const bool kept = (mask == nullptr) || (mask[t] != 0);
-        topk_token<RT::EPL>(lg, t, E, K, score, renorm, route_scale, bias, kept, ids_out, w_out);
+    } else {
+        for (int tl = wv; tl < RT::TB; tl += 4) {
+            const int64_t t = t0 + tl;
+            if (t >= T) break;  // uniform per wave
+            double lg[RT::EPL];
+#pragma unroll
+            for (int i = 0; i < RT::EPL; ++i) {
+                const int e = lane + 64 * i;
+                lg[i] = lgs[tl * RT::EMAX + e];
+                if (logits_out && e < E) logits_out[t * E + e] = static_cast<float>(lg[i]);
+            }
+            const bool kept = (mask == nullptr) || (mask[t] != 0);
+            topk_token<RT::EPL>(lg, t, E, K, score, renorm, route_scale, bias, kept, ids_out, w_out);
+        }
     }
 }
 
