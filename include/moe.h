@@ -63,6 +63,17 @@ typedef enum { MOE_BF16 = 0, MOE_F32 = 1 } moe_dtype;
  * float64 from float64-accumulated logits. */
 typedef enum { MOE_SOFTMAX = 0, MOE_SIGMOID = 1 } moe_score;
 
+/* Combine arithmetic (moe_combine, moe_forward).
+ *   MOE_COMBINE_F32_FOLD: float32 left fold in ascending expert id (the
+ *     default; 6 routed terms give 6!/2 = 360 distinct orders, the count of
+ *     arXiv 2607.28097, Abstract).
+ *   MOE_COMBINE_F64: the products w * y are exact in float64 and summed there
+ *     in ascending expert id, the shared term added, then rounded once to the
+ *     output dtype.  Whenever that float64 sum is exact (the products'
+ *     exponents span less than about 20 bits) the result does not depend on
+ *     the order of the terms: an order-invariant reduction. */
+typedef enum { MOE_COMBINE_F32_FOLD = 0, MOE_COMBINE_F64 = 1 } moe_combine_mode;
+
 /* The layer's profile (the ModelProfile of the RL-Kernel roadmap, WS1). */
 typedef struct {
     int64_t T;          /* tokens in this call */
@@ -75,6 +86,7 @@ typedef struct {
     int32_t renorm;     /* 1: weights renormalised over the K selected experts */
     float route_scale;  /* multiplies the (renormalised) weights; finite, > 0 */
     int32_t dtype;      /* moe_dtype: operand dtype of x, weights, expert activations and outputs */
+    int32_t combine;    /* moe_combine_mode */
 } moe_shape;
 
 /* Weights of one layer (device pointers, operand dtype unless noted).
@@ -174,7 +186,10 @@ moe_status moe_experts(const moe_shape* shape, const void* x, const int32_t* per
  *   for j = 0..K-1 (ascending expert id):  acc = fl32(acc + fl32(topk_w[t,j] * f32(y[inv_pos[t,j]])))
  *   if shared_out:                         acc = fl32(acc + f32(shared_out[t]))
  *   out[t] = acc rounded to bf16 nearest-even (out_dtype MOE_BF16) or acc (MOE_F32)
- * No fused multiply-add.  A token whose inv_pos slots are all -1 gets a +0 row.
+ * No fused multiply-add.  With shape->combine == MOE_COMBINE_F64 the same
+ * terms are formed and summed in float64 and the sum is rounded once (to bf16
+ * or float32, nearest-even).  A token whose inv_pos slots are all -1 gets a +0
+ * row.
  * y [T*K,D] and shared_out [T,D] (or NULL) in operand dtype; inv_pos int32
  * [T,K]; topk_w float [T,K]; out [T,D] in out_dtype. */
 moe_status moe_combine(const moe_shape* shape, const void* y, const int32_t* inv_pos,
@@ -189,6 +204,26 @@ moe_status moe_forward(const moe_shape* shape, const moe_weights* weights, const
                        const float* sel_bias, const uint8_t* mask, int32_t out_dtype,
                        void* out, const moe_trace* trace, void* ws, size_t ws_bytes,
                        hipStream_t stream);
+
+/* Routing replay (RL-Kernel roadmap, "R3 Should Not Be A Prerequisite": the
+ * experts a token used in another run are replayed, the router still scores
+ * them).  The router logits and scores are computed as in moe_route, but the
+ * K experts of token t are replay_ids[t*K .. t*K+K-1] (int32 [T,K], device)
+ * instead of the K largest choices; the weights are this router's scores of
+ * those experts, renormalised and scaled as in moe_route, and topk_ids
+ * returns the replayed ids in ascending order with their weights.  A token
+ * that is masked, or whose replayed ids are not K distinct ids in [0, E)
+ * (for instance -1 rows of a masked token), is treated as masked.  No
+ * selection bias takes part.  Outputs and workspace as in moe_route. */
+moe_status moe_route_replay(const moe_shape* shape, const void* x, const void* router, const int32_t* replay_ids,
+                            const uint8_t* mask, float* logits, int32_t* topk_ids, float* topk_w, void* ws,
+                            size_t ws_bytes, hipStream_t stream);
+
+/* moe_forward with moe_route_replay in place of moe_route (replay_ids as
+ * there).  Everything after routing, and the trace, as in moe_forward. */
+moe_status moe_forward_replay(const moe_shape* shape, const moe_weights* weights, const void* x,
+                              const int32_t* replay_ids, const uint8_t* mask, int32_t out_dtype, void* out,
+                              const moe_trace* trace, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Static text for a status code. */
 const char* moe_status_string(moe_status status);

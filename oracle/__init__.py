@@ -23,6 +23,8 @@ Pins (the tests that tie each function to something other than itself):
   round_bf16         exact rational round-half-even; torch's float32->bfloat16 cast
   combine_fp32       exact rational arithmetic rounded to float32 per operation;
                      720-order enumeration (360 classes) printed by the arXiv abstract
+  combine_f64        exact rational sum rounded once (bf16 and float32); all 720
+                     orders of six terms give one result
 No function is parity-unpinned.
 """
 
@@ -30,6 +32,7 @@ from .moe import (
     EXEMPT_REL_MARGIN,
     OracleResult,
     bf16_bits_of,
+    combine_f64,
     combine_fp32,
     combine_orders,
     expert_mlp,
@@ -48,6 +51,7 @@ __all__ = [
     "EXEMPT_REL_MARGIN",
     "OracleResult",
     "bf16_bits_of",
+    "combine_f64",
     "combine_fp32",
     "combine_orders",
     "expert_mlp",

@@ -38,7 +38,12 @@ Conventions (the plainest reading where the pages leave a step open):
   * the combine accumulates in float32, from +0, over the K routed terms in
     ascending expert id, each term the float32 product of the float32 weight
     and the widened expert output, then adds the shared output, then rounds to
-    bf16 [RLK, Problem 3; ARX, Abstract].
+    bf16 [RLK, Problem 3; ARX, Abstract];
+  * the order-invariant combine mode forms the same products exactly in
+    float64, sums them and the shared output in float64 in the same order and
+    rounds once (a reduction whose result does not depend on the order of the
+    terms whenever that sum is exact, the property [ARX, Abstract] measures
+    order dependence against).
 """
 
 from __future__ import annotations
@@ -272,16 +277,53 @@ def combine_fp32(y: np.ndarray, inv_pos: np.ndarray, w32: np.ndarray,
     return bf16_bits_of(acc)
 
 
+def combine_f64(y: np.ndarray, inv_pos: np.ndarray, w32: np.ndarray,
+                shared: Optional[np.ndarray] = None, order: Optional[Sequence[int]] = None,
+                out: str = "bf16") -> np.ndarray:
+    """The order-invariant combine: the terms in float64, rounded once.
+
+    Each product w[t, j] * y[inv_pos[t, j]] of a float32 weight and a bf16 (or
+    float32) expert output is exact in float64; acc = +0; for j in ``order``
+    (default ascending expert id): acc = fl64(acc + product); then acc =
+    fl64(acc + shared[t]); the result is acc rounded once, nearest-even, to
+    bf16 (``out`` = "bf16", bit patterns) or float32 (``out`` = "f32").  When
+    the float64 sum is exact the order of the terms does not matter: the
+    order-invariant reduction the reduction-order results of [ARX, Abstract]
+    motivate.  Masked tokens (inv_pos -1) give a +0 row.
+    """
+    T, K = inv_pos.shape
+    y64 = widen(y)
+    D = y64.shape[1] if y64.ndim == 2 else widen(shared).shape[1]
+    w64 = np.asarray(w32, dtype=np.float32).astype(np.float64)
+    order = range(K) if order is None else order
+    kept = (inv_pos >= 0).any(axis=1) if K > 0 else np.zeros(T, dtype=bool)
+    acc = np.zeros((T, D), dtype=np.float64)
+    for j in order:
+        rows = inv_pos[:, j]
+        yj = np.zeros((T, D), dtype=np.float64)
+        yj[rows >= 0] = y64[rows[rows >= 0]]
+        acc = acc + w64[:, j:j + 1] * yj   # the product is exact; one rounding per add
+    if shared is not None:
+        acc = acc + widen(shared)
+    acc[~kept] = 0.0
+    if out == "f32":
+        return acc.astype(np.float32)      # one rounding, nearest-even
+    return bf16_bits_of(acc)               # one rounding from float64
+
+
 def combine_orders(y: np.ndarray, inv_pos: np.ndarray, w32: np.ndarray,
                    shared: Optional[np.ndarray] = None,
-                   orders: Optional[Iterable[Sequence[int]]] = None) -> Dict[Tuple[int, ...], np.ndarray]:
-    """The float32 combine (float32 output) for each order of the K routed terms.
+                   orders: Optional[Iterable[Sequence[int]]] = None,
+                   mode: str = "f32") -> Dict[Tuple[int, ...], np.ndarray]:
+    """The combine (float32 output) for each order of the K routed terms.
 
     Default: all K! permutations (720 for the six routed terms of [ARX]).
+    ``mode`` "f32" is the float32 fold, "f64" the order-invariant sum.
     """
     K = inv_pos.shape[1]
     orders = itertools.permutations(range(K)) if orders is None else orders
-    return {tuple(o): combine_fp32(y, inv_pos, w32, shared, order=o, out="f32") for o in orders}
+    fn = combine_f64 if mode == "f64" else combine_fp32
+    return {tuple(o): fn(y, inv_pos, w32, shared, order=o, out="f32") for o in orders}
 
 
 # ----------------------------------------------------------------------------

@@ -23,6 +23,7 @@ LIB_PATH = os.path.join(_PKG, "libmoe.so")
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_BF16, MOE_F32 = 0, 1
 MOE_SOFTMAX, MOE_SIGMOID = 0, 1
+MOE_COMBINE_F32_FOLD, MOE_COMBINE_F64 = 0, 1
 
 EXPORTED = (
     "moe_workspace_size",
@@ -31,6 +32,8 @@ EXPORTED = (
     "moe_experts",
     "moe_combine",
     "moe_forward",
+    "moe_route_replay",
+    "moe_forward_replay",
     "moe_status_string",
     "moe_last_error",
 )
@@ -54,6 +57,7 @@ class _Shape(ctypes.Structure):
         ("renorm", ctypes.c_int32),
         ("route_scale", ctypes.c_float),
         ("dtype", ctypes.c_int32),
+        ("combine", ctypes.c_int32),
     ]
 
 
@@ -79,12 +83,14 @@ class Shape:
     renorm: bool = True
     route_scale: float = 1.0
     dtype: str = "bf16"         # operand dtype: "bf16" | "f32"
+    combine: str = "f32"        # combine arithmetic: "f32" (float32 fold) | "f64" (order-invariant sum)
 
     def c(self) -> _Shape:
         return _Shape(self.T, self.D, self.E, self.K, self.I, self.Is,
                       {"softmax": MOE_SOFTMAX, "sigmoid": MOE_SIGMOID}.get(self.score, -1),
                       int(self.renorm), float(self.route_scale),
-                      {"bf16": MOE_BF16, "f32": MOE_F32}.get(self.dtype, -1))
+                      {"bf16": MOE_BF16, "f32": MOE_F32}.get(self.dtype, -1),
+                      {"f32": MOE_COMBINE_F32_FOLD, "f64": MOE_COMBINE_F64}.get(self.combine, -1))
 
     @property
     def torch_dtype(self) -> torch.dtype:
@@ -117,7 +123,11 @@ def lib() -> ctypes.CDLL:
     L.moe_combine.argtypes = [S, P, P, P, P, ctypes.c_int32, P, P]
     L.moe_forward.argtypes = [S, ctypes.POINTER(_Weights), P, P, P, ctypes.c_int32, P,
                               ctypes.POINTER(_Trace), P, ctypes.c_size_t, P]
-    for fn in ("moe_workspace_size", "moe_route", "moe_permute", "moe_experts", "moe_combine", "moe_forward"):
+    L.moe_route_replay.argtypes = [S, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    L.moe_forward_replay.argtypes = [S, ctypes.POINTER(_Weights), P, P, P, ctypes.c_int32, P,
+                                     ctypes.POINTER(_Trace), P, ctypes.c_size_t, P]
+    for fn in ("moe_workspace_size", "moe_route", "moe_permute", "moe_experts", "moe_combine", "moe_forward",
+               "moe_route_replay", "moe_forward_replay"):
         getattr(L, fn).restype = ctypes.c_int
     L.moe_status_string.argtypes = [ctypes.c_int]
     L.moe_status_string.restype = ctypes.c_char_p
@@ -176,6 +186,19 @@ def moe_route(shape: Shape, x, router, sel_bias, mask, logits, topk_ids, topk_w,
         _ptr(ws, "ws", torch.uint8), ws.numel() if ws is not None else 0, _stream()), "moe_route")
 
 
+def moe_route_replay(shape: Shape, x, router, replay_ids, mask, logits, topk_ids, topk_w, ws) -> None:
+    s = shape.c()
+    od = shape.torch_dtype
+    _check(lib().moe_route_replay(
+        ctypes.byref(s),
+        _ptr(x, "x", od, shape.T * shape.D), _ptr(router, "router", od, shape.E * shape.D),
+        _ptr(replay_ids, "replay_ids", torch.int32, shape.T * shape.K), _ptr(mask, "mask", torch.uint8, shape.T),
+        _ptr(logits, "logits", torch.float32, shape.T * shape.E),
+        _ptr(topk_ids, "topk_ids", torch.int32, shape.T * shape.K),
+        _ptr(topk_w, "topk_w", torch.float32, shape.T * shape.K),
+        _ptr(ws, "ws", torch.uint8), ws.numel() if ws is not None else 0, _stream()), "moe_route_replay")
+
+
 def moe_permute(shape: Shape, topk_ids, counts, offsets, perm_token, inv_pos, ws) -> None:
     s = shape.c()
     P = shape.T * shape.K
@@ -209,9 +232,11 @@ def moe_combine(shape: Shape, y, inv_pos, topk_w, shared_out, out) -> None:
         out_dtype, _ptr(out, "out", None, shape.T * shape.D), _stream()), "moe_combine")
 
 
-def moe_forward(shape: Shape, weights: dict, x, sel_bias, mask, out, ws, trace: Optional[dict] = None) -> None:
+def moe_forward(shape: Shape, weights: dict, x, sel_bias, mask, out, ws, trace: Optional[dict] = None,
+                replay_ids=None) -> None:
     """weights: router, gate_up, down[, gate_up_shared, down_shared]; trace: optional
-    dict of preallocated boundary tensors keyed like moe_trace's fields."""
+    dict of preallocated boundary tensors keyed like moe_trace's fields.  With
+    ``replay_ids`` ([T, K] int32) this calls moe_forward_replay instead."""
     s = shape.c()
     od = shape.torch_dtype
     w = _Weights(
@@ -236,6 +261,14 @@ def moe_forward(shape: Shape, weights: dict, x, sel_bias, mask, out, ws, trace: 
             _ptr(trace.get("shared_out"), "shared_out", od, shape.T * shape.D),
         )
     out_dtype = {torch.bfloat16: MOE_BF16, torch.float32: MOE_F32}[out.dtype]
+    if replay_ids is not None:
+        _check(lib().moe_forward_replay(
+            ctypes.byref(s), ctypes.byref(w), _ptr(x, "x", od, shape.T * shape.D),
+            _ptr(replay_ids, "replay_ids", torch.int32, shape.T * shape.K), _ptr(mask, "mask", torch.uint8, shape.T),
+            out_dtype, _ptr(out, "out", None, shape.T * shape.D),
+            ctypes.byref(tr) if tr is not None else None,
+            _ptr(ws, "ws", torch.uint8), ws.numel() if ws is not None else 0, _stream()), "moe_forward_replay")
+        return
     _check(lib().moe_forward(
         ctypes.byref(s), ctypes.byref(w), _ptr(x, "x", od, shape.T * shape.D),
         _ptr(sel_bias, "sel_bias", torch.float32, shape.E), _ptr(mask, "mask", torch.uint8, shape.T),

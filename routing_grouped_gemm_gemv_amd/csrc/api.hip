@@ -46,6 +46,8 @@ moe_status check_shape(const moe_shape* s) {
         return fail(MOE_ERR_INVALID, "unknown score function %d", s->score);
     if (s->dtype != MOE_BF16 && s->dtype != MOE_F32) return fail(MOE_ERR_INVALID, "unknown operand dtype %d", s->dtype);
     if (s->renorm != 0 && s->renorm != 1) return fail(MOE_ERR_INVALID, "renorm must be 0 or 1, got %d", s->renorm);
+    if (s->combine != MOE_COMBINE_F32_FOLD && s->combine != MOE_COMBINE_F64)
+        return fail(MOE_ERR_INVALID, "unknown combine mode %d", s->combine);
     if (!isfinite(s->route_scale) || !(s->route_scale > 0.0f))
         return fail(MOE_ERR_INVALID, "route_scale must be finite and positive");
     if (s->K > s->E) return fail(MOE_ERR_INVALID, "K = %d exceeds E = %d", s->K, s->E);
@@ -167,6 +169,27 @@ moe_status moe_route(const moe_shape* shape, const void* x, const void* router, 
     return ok();
 }
 
+moe_status moe_route_replay(const moe_shape* shape, const void* x, const void* router, const int32_t* replay_ids,
+                            const uint8_t* mask, float* logits, int32_t* topk_ids, float* topk_w, void* ws,
+                            size_t ws_bytes, hipStream_t stream) {
+    moe_status st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    if (!x || !router || !replay_ids || !topk_ids || !topk_w)
+        return fail(MOE_ERR_INVALID, "moe_route_replay: x, router, replay_ids, topk_ids and topk_w are required");
+    if (shape->T == 0) return ok();
+    if (!ws || ws_bytes < route_ws(shape))
+        return fail(MOE_ERR_WORKSPACE, "moe_route_replay needs %zu workspace bytes, got %zu", route_ws(shape),
+                    ws ? ws_bytes : 0);
+    if ((st = check_device()) != MOE_OK) return st;
+    double* l64 = static_cast<double*>(ws);
+    if ((st = hip_status(moe::launch_route_replay(x, router, shape->T, shape->D, shape->E, shape->K, shape->dtype,
+                                                  shape->score, shape->renorm, shape->route_scale, replay_ids, mask,
+                                                  l64, logits, topk_ids, topk_w, stream),
+                         "routing replay launch")) != MOE_OK)
+        return st;
+    return ok();
+}
+
 moe_status moe_permute(const moe_shape* shape, const int32_t* topk_ids, int32_t* counts, int32_t* offsets,
                        int32_t* perm_token, int32_t* inv_pos, void* ws, size_t ws_bytes, hipStream_t stream) {
     moe_status st = check_shape(shape);
@@ -214,15 +237,16 @@ moe_status moe_combine(const moe_shape* shape, const void* y, const int32_t* inv
     if (shape->T == 0) return ok();
     if ((st = check_device()) != MOE_OK) return st;
     if ((st = hip_status(moe::launch_combine(y, inv_pos, topk_w, shared_out, shape->T, shape->D, shape->K, shape->dtype,
-                                             out_dtype, out, stream),
+                                             out_dtype, shape->combine, out, stream),
                          "combine launch")) != MOE_OK)
         return st;
     return ok();
 }
 
-moe_status moe_forward(const moe_shape* shape, const moe_weights* weights, const void* x, const float* sel_bias,
-                       const uint8_t* mask, int32_t out_dtype, void* out, const moe_trace* trace, void* ws,
-                       size_t ws_bytes, hipStream_t stream) {
+static moe_status forward_impl(const moe_shape* shape, const moe_weights* weights, const void* x,
+                               const float* sel_bias, const int32_t* replay_ids, const uint8_t* mask,
+                               int32_t out_dtype, void* out, const moe_trace* trace, void* ws, size_t ws_bytes,
+                               hipStream_t stream) {
     moe_status st = check_shape(shape);
     if (st != MOE_OK) return st;
     if (!weights || !x || !out) return fail(MOE_ERR_INVALID, "moe_forward: weights, x and out are required");
@@ -252,11 +276,18 @@ moe_status moe_forward(const moe_shape* shape, const moe_weights* weights, const
     void* exw = base + L.exp_ws;
     const int64_t T = shape->T;
 
-    if ((st = hip_status(moe::launch_route(x, weights->router, T, shape->D, shape->E, shape->K, shape->dtype,
-                                           shape->score, shape->renorm, shape->route_scale, sel_bias, mask, l64,
-                                           tr.logits, ids, tw, stream),
-                         "routing launch")) != MOE_OK)
+    if (replay_ids != nullptr) {
+        if ((st = hip_status(moe::launch_route_replay(x, weights->router, T, shape->D, shape->E, shape->K,
+                                                      shape->dtype, shape->score, shape->renorm, shape->route_scale,
+                                                      replay_ids, mask, l64, tr.logits, ids, tw, stream),
+                             "routing replay launch")) != MOE_OK)
+            return st;
+    } else if ((st = hip_status(moe::launch_route(x, weights->router, T, shape->D, shape->E, shape->K, shape->dtype,
+                                                  shape->score, shape->renorm, shape->route_scale, sel_bias, mask, l64,
+                                                  tr.logits, ids, tw, stream),
+                                "routing launch")) != MOE_OK) {
         return st;
+    }
     if ((st = hip_status(moe::launch_permute(ids, T, shape->K, shape->E, reinterpret_cast<int32_t*>(base + L.perm_ws),
                                              counts, offsets, perm, inv, stream),
                          "permute launch")) != MOE_OK)
@@ -271,10 +302,25 @@ moe_status moe_forward(const moe_shape* shape, const moe_weights* weights, const
                              "shared expert launch")) != MOE_OK)
             return st;
     }
-    if ((st = hip_status(moe::launch_combine(y, inv, tw, sh, T, shape->D, shape->K, shape->dtype, out_dtype, out, stream),
+    if ((st = hip_status(moe::launch_combine(y, inv, tw, sh, T, shape->D, shape->K, shape->dtype, out_dtype, shape->combine,
+                                             out, stream),
                          "combine launch")) != MOE_OK)
         return st;
     return ok();
+}
+
+moe_status moe_forward(const moe_shape* shape, const moe_weights* weights, const void* x, const float* sel_bias,
+                       const uint8_t* mask, int32_t out_dtype, void* out, const moe_trace* trace, void* ws,
+                       size_t ws_bytes, hipStream_t stream) {
+    return forward_impl(shape, weights, x, sel_bias, nullptr, mask, out_dtype, out, trace, ws, ws_bytes, stream);
+}
+
+moe_status moe_forward_replay(const moe_shape* shape, const moe_weights* weights, const void* x,
+                              const int32_t* replay_ids, const uint8_t* mask, int32_t out_dtype, void* out,
+                              const moe_trace* trace, void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (replay_ids == nullptr && shape != nullptr && shape->T > 0)
+        return fail(MOE_ERR_INVALID, "moe_forward_replay: replay_ids is required");
+    return forward_impl(shape, weights, x, nullptr, replay_ids, mask, out_dtype, out, trace, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -13,8 +13,12 @@
 //     out = bf16_rne(acc)  or  acc
 // with every multiply and add rounded on its own (contraction to FMA is off
 // for this file), so the result is a function of the K expert outputs and
-// weights only.  The pass is HBM-bound: each thread streams 16-byte chunks of
-// the K expert-output rows of its token.
+// weights only.  The order-invariant mode forms the same products in float64,
+// where they are exact (float32 x bf16 or float32 x float32 needs at most 48
+// significant bits), sums them and the shared term in float64 in the same
+// order and rounds once; while that sum is exact, every order of the terms
+// gives the same bits.  The pass is HBM-bound: each thread streams 16-byte
+// chunks of the K expert-output rows of its token.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -49,7 +53,57 @@ struct Vec8<float> {
     }
 };
 
-template <typename Tin, bool OUT_BF16>
+// float64 -> bf16 with one rounding (nearest-even): the float64 value is first
+// narrowed to float32 rounding to odd (truncate, then set the last bit if
+// anything was dropped), which keeps enough bits that the final float32 ->
+// bf16 rounding to nearest-even is the correct rounding of the float64 value.
+__device__ __forceinline__ uint16_t f64_to_bf16(double d) {
+    float f = static_cast<float>(d);
+    if (static_cast<double>(f) != d) {
+        uint32_t b = __float_as_uint(f);
+        if (fabs(static_cast<double>(f)) > fabs(d)) b -= 1;  // rounded away from zero: step back
+        f = __uint_as_float(b | 1u);
+    }
+    return f32_to_bf16(f);
+}
+
+template <bool OUT_BF16>
+__device__ __forceinline__ void store8(void* out, int64_t idx, const float (&acc)[8]) {
+    if (OUT_BF16) {
+        uint32_t pk[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            pk[i] = static_cast<uint32_t>(f32_to_bf16(acc[2 * i])) |
+                    (static_cast<uint32_t>(f32_to_bf16(acc[2 * i + 1])) << 16);
+        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + idx) = u32x4{pk[0], pk[1], pk[2], pk[3]};
+    } else {
+        float* o = static_cast<float*>(out) + idx;
+        *reinterpret_cast<float4*>(o) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        *reinterpret_cast<float4*>(o + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    }
+}
+
+template <bool OUT_BF16>
+__device__ __forceinline__ void store8(void* out, int64_t idx, const double (&acc)[8]) {
+    if (OUT_BF16) {
+        uint32_t pk[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            pk[i] = static_cast<uint32_t>(f64_to_bf16(acc[2 * i])) |
+                    (static_cast<uint32_t>(f64_to_bf16(acc[2 * i + 1])) << 16);
+        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + idx) = u32x4{pk[0], pk[1], pk[2], pk[3]};
+    } else {
+        float f[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] = static_cast<float>(acc[i]);
+        float* o = static_cast<float*>(out) + idx;
+        *reinterpret_cast<float4*>(o) = make_float4(f[0], f[1], f[2], f[3]);
+        *reinterpret_cast<float4*>(o + 4) = make_float4(f[4], f[5], f[6], f[7]);
+    }
+}
+
+// Acc: float (the float32 fold) or double (the order-invariant sum)
+template <typename Tin, bool OUT_BF16, typename Acc>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     const Tin* __restrict__ y, const int32_t* __restrict__ inv_pos, const float* __restrict__ w,
     const Tin* __restrict__ shared, int64_t T, int D, int K, void* __restrict__ out) {
@@ -68,9 +122,9 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
         }
     }
     for (int d0 = threadIdx.x * 8; d0 < D; d0 += kCombineThreads * 8) {
-        float acc[8];
+        Acc acc[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+        for (int i = 0; i < 8; ++i) acc[i] = Acc(0);
         if (kept) {
 #pragma unroll
             for (int j = 0; j < kMaxK; ++j) {
@@ -79,7 +133,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
                 Vec8<Tin>::load(y + pos[j] * D + d0, v);
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    const float prod = wt[j] * v[i];
+                    const Acc prod = static_cast<Acc>(wt[j]) * static_cast<Acc>(v[i]);
                     acc[i] = acc[i] + prod;
                 }
             }
@@ -87,38 +141,37 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
                 float v[8];
                 Vec8<Tin>::load(shared + t * D + d0, v);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) acc[i] = acc[i] + v[i];
+                for (int i = 0; i < 8; ++i) acc[i] = acc[i] + static_cast<Acc>(v[i]);
             }
         }
-        if (OUT_BF16) {
-            uint32_t pk[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                pk[i] = static_cast<uint32_t>(f32_to_bf16(acc[2 * i])) |
-                        (static_cast<uint32_t>(f32_to_bf16(acc[2 * i + 1])) << 16);
-            *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + t * D + d0) = u32x4{pk[0], pk[1], pk[2], pk[3]};
-        } else {
-            float* o = static_cast<float*>(out) + t * D + d0;
-            *reinterpret_cast<float4*>(o) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-            *reinterpret_cast<float4*>(o + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
-        }
+        store8<OUT_BF16>(out, t * D + d0, acc);
     }
 }
 
 hipError_t launch_combine(const void* y, const int32_t* inv_pos, const float* w, const void* shared,
-                          int64_t T, int D, int K, int dtype, int out_dtype, void* out, hipStream_t stream) {
+                          int64_t T, int D, int K, int dtype, int out_dtype, int mode, void* out, hipStream_t stream) {
     const unsigned grid = static_cast<unsigned>(T);
+#define MOE_COMBINE(TIN, BF16OUT, ACC)                                                                   \
+    combine_kernel<TIN, BF16OUT, ACC><<<grid, kCombineThreads, 0, stream>>>(                          \
+        static_cast<const TIN*>(y), inv_pos, w, static_cast<const TIN*>(shared), T, D, K, out)
     if (dtype == 0) {
-        const uint16_t* yy = static_cast<const uint16_t*>(y);
-        const uint16_t* ss = static_cast<const uint16_t*>(shared);
-        if (out_dtype == 0) combine_kernel<uint16_t, true><<<grid, kCombineThreads, 0, stream>>>(yy, inv_pos, w, ss, T, D, K, out);
-        else combine_kernel<uint16_t, false><<<grid, kCombineThreads, 0, stream>>>(yy, inv_pos, w, ss, T, D, K, out);
+        if (mode == 0) {
+            if (out_dtype == 0) MOE_COMBINE(uint16_t, true, float);
+            else MOE_COMBINE(uint16_t, false, float);
+        } else {
+            if (out_dtype == 0) MOE_COMBINE(uint16_t, true, double);
+            else MOE_COMBINE(uint16_t, false, double);
+        }
     } else {
-        const float* yy = static_cast<const float*>(y);
-        const float* ss = static_cast<const float*>(shared);
-        if (out_dtype == 0) combine_kernel<float, true><<<grid, kCombineThreads, 0, stream>>>(yy, inv_pos, w, ss, T, D, K, out);
-        else combine_kernel<float, false><<<grid, kCombineThreads, 0, stream>>>(yy, inv_pos, w, ss, T, D, K, out);
+        if (mode == 0) {
+            if (out_dtype == 0) MOE_COMBINE(float, true, float);
+            else MOE_COMBINE(float, false, float);
+        } else {
+            if (out_dtype == 0) MOE_COMBINE(float, true, double);
+            else MOE_COMBINE(float, false, double);
+        }
     }
+#undef MOE_COMBINE
     return hipGetLastError();
 }
 

@@ -14,7 +14,8 @@ hipError_t launch_router_logits(const void* x, const void* router, int64_t T, in
 // scores, selection bias, top-k, weights; optional float32 logits export
 hipError_t launch_topk(const double* logits64, int64_t T, int E, int K, int score, int renorm,
                        float route_scale, const float* bias, const uint8_t* mask,
-                       float* logits_out, int32_t* ids, float* w, hipStream_t stream);
+                       float* logits_out, int32_t* ids, float* w, hipStream_t stream,
+                       const int32_t* given);
 // whether launch_route runs the single fused kernel (bf16 operands, E <= 512)
 bool route_fused(int E, int dtype);
 // logits + top-k: one fused kernel where route_fused(), else the two kernels
@@ -22,6 +23,12 @@ bool route_fused(int E, int dtype);
 hipError_t launch_route(const void* x, const void* router, int64_t T, int D, int E, int K, int dtype,
                         int score, int renorm, float route_scale, const float* bias, const uint8_t* mask,
                         double* logits64, float* logits_out, int32_t* ids, float* w, hipStream_t stream);
+// routing replay: logits through logits64, then the given ids with weights
+// from their scores (tokens with invalid given ids are treated as masked)
+hipError_t launch_route_replay(const void* x, const void* router, int64_t T, int D, int E, int K, int dtype,
+                               int score, int renorm, float route_scale, const int32_t* given,
+                               const uint8_t* mask, double* logits64, float* logits_out, int32_t* ids, float* w,
+                               hipStream_t stream);
 
 // ---- dispatch ----------------------------------------------------------------
 struct PermutePlan {
@@ -43,8 +50,9 @@ hipError_t launch_experts(const void* x, int64_t x_rows, const int32_t* perm_tok
                           const void* down, void* y, void* ws, hipStream_t stream);
 
 // ---- combine -----------------------------------------------------------------
+// mode 0: float32 fold; mode 1: float64 sum rounded once
 hipError_t launch_combine(const void* y, const int32_t* inv_pos, const float* w, const void* shared,
-                          int64_t T, int D, int K, int dtype, int out_dtype, void* out,
+                          int64_t T, int D, int K, int dtype, int out_dtype, int mode, void* out,
                           hipStream_t stream);
 
 }  // namespace moe

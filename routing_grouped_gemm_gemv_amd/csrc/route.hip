@@ -202,11 +202,25 @@ __device__ __forceinline__ uint64_t choice_key(double c, int e) {
 // Scores, choice and weights of one token whose float64 logits the wave holds,
 // E/64 (rounded up) per lane: lane l holds experts l, l + 64, ...  Writes the
 // K ids in ascending order and their weights (ids -1, weights 0 if masked).
+// given != nullptr replays routing: the K experts are given[t*K .. t*K+K-1]
+// instead of the K largest choices (a token whose given ids are not K
+// distinct ids in [0, E) is treated as masked); the weights still come from
+// this token's scores.
 template <int EPL>
 __device__ __forceinline__ void topk_token(const double (&lg)[EPL], int64_t t, int E, int K, int score,
                                            int renorm, double route_scale, const float* __restrict__ bias,
-                                           bool kept, int32_t* __restrict__ ids_out, float* __restrict__ w_out) {
+                                           bool kept, int32_t* __restrict__ ids_out, float* __restrict__ w_out,
+                                           const int32_t* __restrict__ given) {
     const int lane = lane_id();
+    if (given != nullptr && kept) {
+        const int g = lane < K ? given[t * K + lane] : 0;
+        bool bad = lane < K && (g < 0 || g >= E);
+        for (int i = 0; i < K; ++i) {
+            const int gi = __builtin_amdgcn_readlane(g, i);
+            bad = bad | (lane < K && i != lane && gi == g);
+        }
+        kept = __ballot(bad) == 0ull;
+    }
     if (!kept) {
         if (lane < K) {
             ids_out[t * K + lane] = -1;
@@ -252,11 +266,16 @@ __device__ __forceinline__ void topk_token(const double (&lg)[EPL], int64_t t, i
     int my_e = -1;
     double my_s = 0.0;
     for (int r = 0; r < K; ++r) {
-        uint64_t best = key[0];
+        int ew;
+        if (given != nullptr) {
+            ew = given[t * K + r];
+        } else {
+            uint64_t best = key[0];
 #pragma unroll
-        for (int i = 1; i < EPL; ++i) best = umax64(best, key[i]);
-        const uint64_t win = wave_max_u64(best);
-        const int ew = 1023 - static_cast<int>(win & 0x3FFull);
+            for (int i = 1; i < EPL; ++i) best = umax64(best, key[i]);
+            const uint64_t win = wave_max_u64(best);
+            ew = 1023 - static_cast<int>(win & 0x3FFull);
+        }
         const int owner = ew & 63;
         const int slot = ew >> 6;
         double sw = 0.0;
@@ -431,7 +450,8 @@ template <int EPL>
 __global__ __launch_bounds__(256) void topk_kernel(
     const double* __restrict__ logits, int64_t T, int E, int K, int score, int renorm,
     double route_scale, const float* __restrict__ bias, const uint8_t* __restrict__ mask,
-    float* __restrict__ logits_out, int32_t* __restrict__ ids_out, float* __restrict__ w_out) {
+    float* __restrict__ logits_out, int32_t* __restrict__ ids_out, float* __restrict__ w_out,
+    const int32_t* __restrict__ given) {
     const int lane = lane_id();
     const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
     if (t >= T) return;  // uniform per wave
@@ -444,7 +464,7 @@ __global__ __launch_bounds__(256) void topk_kernel(
         if (logits_out && e < E) logits_out[t * E + e] = static_cast<float>(lg[i]);
     }
     const bool kept = (mask == nullptr) || (mask[t] != 0);
-    topk_token<EPL>(lg, t, E, K, score, renorm, route_scale, bias, kept, ids_out, w_out);
+    topk_token<EPL>(lg, t, E, K, score, renorm, route_scale, bias, kept, ids_out, w_out, given);
 }
 
 // ---------------------------------------------------------------------------
@@ -641,7 +661,7 @@ __global__ __launch_bounds__(256) void route_fused_bf16_kernel(
                 if (logits_out && e < E) logits_out[t * E + e] = static_cast<float>(lg[i]);
             }
             const bool kept = (mask == nullptr) || (mask[t] != 0);
-            topk_token<RT::EPL>(lg, t, E, K, score, renorm, route_scale, bias, kept, ids_out, w_out);
+            topk_token<RT::EPL>(lg, t, E, K, score, renorm, route_scale, bias, kept, ids_out, w_out, nullptr);
         }
     }
 }
@@ -662,12 +682,12 @@ hipError_t launch_router_logits(const void* x, const void* router, int64_t T, in
 
 hipError_t launch_topk(const double* logits64, int64_t T, int E, int K, int score, int renorm,
                        float route_scale, const float* bias, const uint8_t* mask,
-                       float* logits_out, int32_t* ids, float* w, hipStream_t stream) {
+                       float* logits_out, int32_t* ids, float* w, hipStream_t stream, const int32_t* given) {
     const unsigned grid = static_cast<unsigned>((T + 3) / 4);
     const double rs = static_cast<double>(route_scale);
 #define MOE_TOPK(EPL)                                                                                   \
     topk_kernel<EPL><<<grid, 256, 0, stream>>>(logits64, T, E, K, score, renorm, rs, bias, mask, \
-                                                logits_out, ids, w)
+                                                logits_out, ids, w, given)
     if (E <= 64) MOE_TOPK(1);
     else if (E <= 128) MOE_TOPK(2);
     else if (E <= 256) MOE_TOPK(4);
@@ -685,7 +705,8 @@ hipError_t launch_route(const void* x, const void* router, int64_t T, int D, int
     if (!route_fused(E, dtype)) {
         hipError_t err = launch_router_logits(x, router, T, D, E, dtype, logits64, stream);
         if (err != hipSuccess) return err;
-        return launch_topk(logits64, T, E, K, score, renorm, route_scale, bias, mask, logits_out, ids, w, stream);
+        return launch_topk(logits64, T, E, K, score, renorm, route_scale, bias, mask, logits_out, ids, w, stream,
+                           nullptr);
     }
     const double rs = static_cast<double>(route_scale);
     const uint16_t* xb = static_cast<const uint16_t*>(x);
@@ -700,6 +721,16 @@ hipError_t launch_route(const void* x, const void* router, int64_t T, int D, int
     else MOE_ROUTE(2, 8);
 #undef MOE_ROUTE
     return hipGetLastError();
+}
+
+hipError_t launch_route_replay(const void* x, const void* router, int64_t T, int D, int E, int K, int dtype,
+                               int score, int renorm, float route_scale, const int32_t* given,
+                               const uint8_t* mask, double* logits64, float* logits_out, int32_t* ids, float* w,
+                               hipStream_t stream) {
+    hipError_t err = launch_router_logits(x, router, T, D, E, dtype, logits64, stream);
+    if (err != hipSuccess) return err;
+    return launch_topk(logits64, T, E, K, score, renorm, route_scale, nullptr, mask, logits_out, ids, w, stream,
+                       given);
 }
 
 }  // namespace moe

@@ -55,13 +55,16 @@ class MoeLayer:
         return tr
 
     def forward(self, x: torch.Tensor, mask: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
-                trace: bool = False, out: Optional[torch.Tensor] = None):
+                trace: bool = False, out: Optional[torch.Tensor] = None, replay_ids: Optional[torch.Tensor] = None):
+        """The layer (moe_forward), or with ``replay_ids`` [T, K] int32 the
+        routing replay (moe_forward_replay)."""
         shape = self.with_tokens(x.shape[0])
         od = out_dtype or torch.bfloat16
         if out is None:
             out = torch.empty(shape.T, shape.D, dtype=od, device="cuda")
         tr = self.new_trace(shape) if trace else None
-        B.moe_forward(shape, self.weights, x, self.sel_bias, mask, out, self.workspace(shape), tr)
+        B.moe_forward(shape, self.weights, x, self.sel_bias, mask, out, self.workspace(shape), tr,
+                      replay_ids=replay_ids)
         return (out, tr) if trace else out
 
     def forward_stages(self, x: torch.Tensor, mask: Optional[torch.Tensor] = None,

@@ -33,10 +33,10 @@ def test_library_exports_every_declared_symbol():
 
 
 def _shape(**kw):
-    base = dict(T=64, D=128, E=8, K=2, I=256, Is=0, score=0, renorm=1, route_scale=1.0, dtype=0)
+    base = dict(T=64, D=128, E=8, K=2, I=256, Is=0, score=0, renorm=1, route_scale=1.0, dtype=0, combine=0)
     base.update(kw)
     return B._Shape(base["T"], base["D"], base["E"], base["K"], base["I"], base["Is"], base["score"],
-                    base["renorm"], base["route_scale"], base["dtype"])
+                    base["renorm"], base["route_scale"], base["dtype"], base["combine"])
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -47,6 +47,8 @@ def _shape(**kw):
     (dict(score=2), B.MOE_ERR_INVALID),
     (dict(dtype=3), B.MOE_ERR_INVALID),
     (dict(renorm=2), B.MOE_ERR_INVALID),
+    (dict(combine=2), B.MOE_ERR_INVALID),
+    (dict(combine=1), B.MOE_OK),
     (dict(route_scale=0.0), B.MOE_ERR_INVALID),
     (dict(route_scale=float("nan")), B.MOE_ERR_INVALID),
     (dict(route_scale=float("inf")), B.MOE_ERR_INVALID),

@@ -83,3 +83,31 @@ def test_combine_is_the_canonical_order_of_720(dsv4, mode):
                                                "tokens_with_360": int((ncls == 360).sum()),
                                                "min_classes": int(ncls.min())}), flush=True)
     assert ncls.max() <= 360
+
+
+@pytest.mark.parametrize("mode", ["bf16", "f32"])
+def test_order_invariant_combine_is_every_order(dsv4, mode):
+    """The float64 combine mode on the same expert outputs: bit-equal to the
+    oracle's float64 sum rounded once, and every one of the 720 orders of the
+    six routed terms gives that same result."""
+    from routing_grouped_gemm_gemv_amd import binding as B
+    layer = make_layer(dsv4)
+    x = to_dev(dsv4.x)
+    if mode == "f32":
+        layer = _layer_f32(layer)
+        x = x.float()
+    _, tr = layer.forward(x, trace=True)
+    shape = layer.with_tokens(NTOK).replace(combine="f64")
+    out32 = torch.empty(NTOK, layer.shape.D, dtype=torch.float32, device="cuda")
+    outbf = torch.empty(NTOK, layer.shape.D, dtype=torch.bfloat16, device="cuda")
+    B.moe_combine(shape, tr["y"], tr["inv_pos"], tr["topk_w"], tr["shared_out"], out32)
+    B.moe_combine(shape, tr["y"], tr["inv_pos"], tr["topk_w"], tr["shared_out"], outbf)
+    torch.cuda.synchronize()
+    y, inv, w, sh = (to_host(tr[k]) for k in ("y", "inv_pos", "topk_w", "shared_out"))
+    g32 = to_host(out32)
+    gbf = to_host(outbf)
+    assert np.array_equal(gbf, oracle.combine_f64(y, inv, w, sh, out="bf16"))
+    for pi in itertools.permutations(range(inv.shape[1])):
+        r = oracle.combine_f64(y, inv, w, sh, order=pi, out="f32")
+        assert np.array_equal(r.view(np.uint32), g32.view(np.uint32)), pi
+    print(f"[orders] f64 combine, {mode} operands: all 720 orders equal the GPU result", flush=True)

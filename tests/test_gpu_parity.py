@@ -184,3 +184,25 @@ def test_odd_expert_counts(E, K, D, I, T):
     from dataclasses import replace
     cfg = replace(get_config("q30", T=T), name=f"q30-E{E}", E=E, K=K, D=D, I=I)
     check_layer(make_inputs(cfg), label=f"E{E}-K{K}-D{D}-I{I}-T{T}")
+
+
+@pytest.mark.parametrize("name,T", [("tiny", 64), ("qnext", 200)])
+def test_order_invariant_combine_mode_layer(name, T):
+    """moe_forward with the float64 combine: the output is the oracle's float64
+    sum of the GPU's own terms rounded once, and within the layer tolerance."""
+    cfg = get_config(name, T=T)
+    inp = make_inputs(cfg)
+    layer = make_layer(inp)
+    layer.shape = layer.shape.replace(combine="f64")
+    x = to_dev(inp.x)
+    out, tr = layer.forward(x, out_dtype=torch.float32, trace=True)
+    torch.cuda.synchronize()
+    g = {k: to_host(v) for k, v in tr.items()}
+    o32 = to_host(out)
+    emu = oracle.combine_f64(g["y"], g["inv_pos"], g["topk_w"], g.get("shared_out"), out="f32")
+    assert np.array_equal(o32.view(np.uint32), emu.view(np.uint32))
+    ref = oracle_forward(inp)
+    same = np.all(g["topk_ids"] == ref.ids, axis=1)
+    pr = parity_report(o32[same], ref.out[same])
+    _say(f"[parity] f64-combine {name}-T{T} {json.dumps(pr)}")
+    assert pr["max_rel_rms"] <= TOL[cfg.dtype], pr

@@ -418,3 +418,53 @@ def test_combine_720_orders_give_360_classes_as_printed():
         assert same == {ident, swap01}
     # the canonical order is the default combine
     assert np.array_equal(res[ident], oracle.combine_fp32(y, inv, w, out="f32"))
+
+
+# ------------------------------------------------- order-invariant combine
+
+def test_combine_f64_is_the_exact_sum_rounded_once():
+    rng = np.random.default_rng(24)
+    T, K, D = 5, 6, 24
+    y = oracle.bf16_bits_of(rng.standard_normal((T * K, D)).astype(np.float32))
+    inv = rng.permutation(T * K).reshape(T, K).astype(np.int32)
+    w = rng.uniform(0.0, 1.0, (T, K)).astype(np.float32)
+    sh = oracle.bf16_bits_of(rng.standard_normal((T, D)).astype(np.float32))
+    got32 = oracle.combine_f64(y, inv, w, sh, out="f32")
+    gotbf = oracle.combine_f64(y, inv, w, sh, out="bf16")
+    yf = oracle.widen(y)
+    sf = oracle.widen(sh)
+    for t in range(T):
+        for d in range(D):
+            exact = sum(Fraction(float(w[t, j])) * Fraction(float(yf[inv[t, j], d])) for j in range(K))
+            exact += Fraction(float(sf[t, d]))
+            assert Fraction(float(got32[t, d])) == _r32(exact)
+            bf = (np.uint32(gotbf[t, d]) << np.uint32(16)).view(np.float32)
+            assert Fraction(float(bf)) == _rbf16(exact)
+
+
+def test_combine_f64_all_720_orders_agree():
+    rng = np.random.default_rng(25)
+    K, T, D = 6, 6, 256
+    y = oracle.bf16_bits_of((rng.standard_normal((T * K, D)) * 0.3).astype(np.float32))
+    inv = rng.permutation(T * K).reshape(T, K).astype(np.int32)
+    w = rng.uniform(0.5, 1.5, (T, K))
+    w = (w / w.sum(axis=1, keepdims=True) * 2.5).astype(np.float32)
+    res = oracle.combine_orders(y, inv, w, mode="f64")
+    assert len(res) == 720
+    first = next(iter(res.values())).view(np.uint32)
+    for r in res.values():
+        assert np.array_equal(r.view(np.uint32), first)
+    # while the float32 fold of the same terms splits into 360 classes per token
+    res32 = oracle.combine_orders(y, inv, w, mode="f32")
+    assert all(len({res32[pi][t].tobytes() for pi in res32}) == 360 for t in range(T))
+
+
+def test_combine_f64_masked_and_unit_weight():
+    rng = np.random.default_rng(26)
+    y = rng.standard_normal((10, 32)).astype(np.float32)
+    inv = np.arange(10, dtype=np.int32).reshape(10, 1)
+    out = oracle.combine_f64(y, inv, np.ones((10, 1), np.float32), out="f32")
+    assert np.array_equal(out.view(np.uint32), y.view(np.uint32))
+    inv[3, 0] = -1
+    out = oracle.combine_f64(y, inv, np.ones((10, 1), np.float32), out="f32")
+    assert np.all(out[3] == 0)
