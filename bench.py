@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--no-invariance", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 1 GiB buffer 5 times (reference kernel for the HBM byte counters)")
+    ap.add_argument("--dense-reference", action="store_true",
+                    help="only time the vendor dense bf16 GEMM (torch.mm) on the routed GEMMs' total shapes")
     return ap.parse_args()
 
 
@@ -85,6 +87,34 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": COPY_BYTES, "dispatches": 5}), flush=True)
 
 
+def dense_reference(cfg, rows: int, reps: int = 5):
+    """Context, not the product: the library dense bf16 GEMM (hipBLASLt through
+    torch.mm) on one matrix of all routed rows, for the gate_up shape
+    [rows, D] x [D, 2I] and the down shape [rows, I] x [I, D], normal random
+    operands.  The grouped kernels do the same FLOPs split over the experts."""
+    import torch
+    g = torch.Generator(device="cuda").manual_seed(0)
+    res = {}
+    for name, (m, n, k) in (("gate_up", (rows, 2 * cfg.I, cfg.D)), ("down", (rows, cfg.D, cfg.I))):
+        a = torch.randn(m, k, device="cuda", dtype=torch.bfloat16, generator=g)
+        b = (torch.randn(n, k, device="cuda", dtype=torch.bfloat16, generator=g) * 0.02).t()
+        for _ in range(3):
+            c = torch.mm(a, b)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            c = torch.mm(a, b)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        res[name] = {"shape_mnk": [m, n, k], "ms": ms, "tflops": 2.0 * m * n * k / ms / 1e9}
+        del a, b, c
+    total_ms = sum(r["ms"] for r in res.values())
+    flops = sum(2.0 * r["shape_mnk"][0] * r["shape_mnk"][1] * r["shape_mnk"][2] for r in res.values())
+    print(json.dumps({"dense_reference": res, "total_ms": total_ms, "tflops": flops / total_ms / 1e9}), flush=True)
+
+
 def stage_bytes(cfg, T, nvalid_pairs):
     """Algorithmic HBM bytes of the route, permute and combine stages."""
     b = cfg.operand_bytes
@@ -99,6 +129,11 @@ def main():
     args = parse()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.dense_reference:
+        from synth import get_config
+        cfg = get_config(args.config, T=args.tokens or None)
+        dense_reference(cfg, cfg.T * cfg.K)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1 "
