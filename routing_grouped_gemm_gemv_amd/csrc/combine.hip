@@ -18,7 +18,9 @@
 // significant bits), sums them and the shared term in float64 in the same
 // order and rounds once; while that sum is exact, every order of the terms
 // gives the same bits.  The pass is HBM-bound: each thread streams 16-byte
-// chunks of the K expert-output rows of its token.
+// chunks of the K expert-output rows of its token.  Every operand is read
+// once and the output written once, so all of them bypass the caches
+// (non-temporal loads and stores).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -34,7 +36,7 @@ struct Vec8;
 template <>
 struct Vec8<uint16_t> {
     static __device__ __forceinline__ void load(const uint16_t* p, float* v) {
-        const u32x4 u = *reinterpret_cast<const u32x4*>(p);
+        const u32x4 u = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
         const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -46,8 +48,8 @@ struct Vec8<uint16_t> {
 template <>
 struct Vec8<float> {
     static __device__ __forceinline__ void load(const float* p, float* v) {
-        const float4 a = *reinterpret_cast<const float4*>(p);
-        const float4 b = *reinterpret_cast<const float4*>(p + 4);
+        const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+        const f32x4 b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + 4));
         v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
         v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
     }
@@ -75,11 +77,12 @@ __device__ __forceinline__ void store8(void* out, int64_t idx, const float (&acc
         for (int i = 0; i < 4; ++i)
             pk[i] = static_cast<uint32_t>(f32_to_bf16(acc[2 * i])) |
                     (static_cast<uint32_t>(f32_to_bf16(acc[2 * i + 1])) << 16);
-        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + idx) = u32x4{pk[0], pk[1], pk[2], pk[3]};
+        __builtin_nontemporal_store(u32x4{pk[0], pk[1], pk[2], pk[3]},
+                                    reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + idx));
     } else {
         float* o = static_cast<float*>(out) + idx;
-        *reinterpret_cast<float4*>(o) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-        *reinterpret_cast<float4*>(o + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+        __builtin_nontemporal_store(f32x4{acc[0], acc[1], acc[2], acc[3]}, reinterpret_cast<f32x4*>(o));
+        __builtin_nontemporal_store(f32x4{acc[4], acc[5], acc[6], acc[7]}, reinterpret_cast<f32x4*>(o + 4));
     }
 }
 
@@ -91,14 +94,15 @@ __device__ __forceinline__ void store8(void* out, int64_t idx, const double (&ac
         for (int i = 0; i < 4; ++i)
             pk[i] = static_cast<uint32_t>(f64_to_bf16(acc[2 * i])) |
                     (static_cast<uint32_t>(f64_to_bf16(acc[2 * i + 1])) << 16);
-        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + idx) = u32x4{pk[0], pk[1], pk[2], pk[3]};
+        __builtin_nontemporal_store(u32x4{pk[0], pk[1], pk[2], pk[3]},
+                                    reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + idx));
     } else {
         float f[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) f[i] = static_cast<float>(acc[i]);
         float* o = static_cast<float*>(out) + idx;
-        *reinterpret_cast<float4*>(o) = make_float4(f[0], f[1], f[2], f[3]);
-        *reinterpret_cast<float4*>(o + 4) = make_float4(f[4], f[5], f[6], f[7]);
+        __builtin_nontemporal_store(f32x4{f[0], f[1], f[2], f[3]}, reinterpret_cast<f32x4*>(o));
+        __builtin_nontemporal_store(f32x4{f[4], f[5], f[6], f[7]}, reinterpret_cast<f32x4*>(o + 4));
     }
 }
 

@@ -347,103 +347,299 @@ __device__ __forceinline__ double lane_get_f64(double v, int src) {
     return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
 }
 
-// Token t of this lane's row, whose float64 logits the row holds (EPL16 per
-// lane: experts j, j + 16, ... for lane j of the row).  Every lane of the wave
-// must call it (rows whose token does not exist pass live = false and write
-// nothing).  Same arithmetic as topk_token except the order of the softmax
-// sums across lanes.
-template <int EPL16>
-__device__ __forceinline__ void topk_row16(const double (&lg)[EPL16], int64_t t, bool live, int E, int K, int score,
-                                           int renorm, double route_scale, const float* __restrict__ bias,
-                                           bool kept, int32_t* __restrict__ ids_out, float* __restrict__ w_out) {
+template <int CTRL>
+__device__ __forceinline__ int dpp_i32(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, true);
+}
+__device__ __forceinline__ float row_max_f32(float v) {
+    v = fmaxf(v, __int_as_float(dpp_i32<0xB1>(__float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp_i32<0x4E>(__float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp_i32<0x141>(__float_as_int(v))));
+    return fmaxf(v, __int_as_float(dpp_i32<0x140>(__float_as_int(v))));
+}
+// inclusive prefix sum over the 16 lanes of a row (row_shr 1, 2, 4, 8)
+__device__ __forceinline__ int row_scan_i32(int v) {
+    v += dpp_i32<0x111>(v);
+    v += dpp_i32<0x112>(v);
+    v += dpp_i32<0x114>(v);
+    return v + dpp_i32<0x118>(v);
+}
+__device__ __forceinline__ int row_max_i32(int v) {
+    v = max(v, dpp_i32<0xB1>(v));
+    v = max(v, dpp_i32<0x4E>(v));
+    v = max(v, dpp_i32<0x141>(v));
+    return max(v, dpp_i32<0x140>(v));
+}
+
+// The picks of P rows (lane r of a row holds its r-th pick: my_e, my_s) in
+// ascending id order with their weights, to ids_out / w_out.
+template <int P>
+__device__ __forceinline__ void write_picks16(const int (&my_e)[P], const double (&my_s)[P], const int64_t (&t)[P],
+                                              const bool (&live)[P], const bool (&kept)[P], int K, int renorm,
+                                              double route_scale, int32_t* __restrict__ ids_out,
+                                              float* __restrict__ w_out) {
     const int lane = lane_id();
     const int j = lane & 15;
     const int rbase = lane & 48;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        // ascending id order: rank of each pick among the row's K picks
+        int rank = 0;
+        for (int i = 0; i < K; ++i) {
+            const int ei = lane_get(my_e[p], rbase + i);
+            rank += (j < K && ei < my_e[p]) ? 1 : 0;
+        }
+        double den = 1.0;
+        if (renorm) {
+            den = 0.0;
+            for (int r = 0; r < K; ++r) {
+                const uint64_t holders = __ballot(j < K && rank == r);
+                const int holder = __builtin_ctzll((holders >> rbase) & 0xFFFFull) + rbase;
+                den += lane_get_f64(my_s[p], holder);
+            }
+        }
+        if (live[p] && j < K) {
+            if (kept[p]) {
+                const double wv = renorm ? (my_s[p] / den) * route_scale : my_s[p] * route_scale;
+                ids_out[t[p] * K + rank] = my_e[p];
+                w_out[t[p] * K + rank] = static_cast<float>(wv);
+            } else {
+                ids_out[t[p] * K + j] = -1;
+                w_out[t[p] * K + j] = 0.f;
+            }
+        }
+    }
+}
+
+// Sigmoid scores, screened: the same picks and scores as select_rows16, with
+// float64 scores computed only for the few experts that can be picked.
+// Every choice c = sigmoid(l) + bias is first evaluated in float32 (c32,
+// within 1e-6 + 1e-7 |c| of the float64 value, far inside the margin below).
+// mu, the K-th largest of the 16 lanes' largest c32, is at most the K-th
+// largest c32 (K lanes hold a value >= mu), so every expert the float64
+// choice can pick has c32 >= mu - margin.  Those candidates are compacted
+// one per lane through the wave's LDS scratch (16 bytes per slot, P x 64
+// slots), get their float64 choice exactly as select_rows16 computes it, and
+// K rounds of row argmax pick among them.  Returns false, with no picks,
+// when a row of the wave has more than 16 candidates.
+template <int EPL16, int P>
+__device__ __forceinline__ bool select_rows16_screened(const double (&lg)[P][EPL16], int E, int K,
+                                                       const float* __restrict__ bias, lds_u8* scr, int (&my_e)[P],
+                                                       double (&my_s)[P]) {
+    const int lane = lane_id();
+    const int j = lane & 15;
+    const int row = lane >> 4;
+    bool ok[EPL16];
+    float bv[EPL16];
+#pragma unroll
+    for (int i = 0; i < EPL16; ++i) {
+        ok[i] = j + 16 * i < E;
+        bv[i] = (bias != nullptr && ok[i]) ? bias[j + 16 * i] : 0.0f;
+    }
+    uint32_t cm[P];  // candidate bits over i
+    int off[P], n_row[P];
+    bool over = false;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        float c32[EPL16];
+#pragma unroll
+        for (int i = 0; i < EPL16; ++i) {
+            const float e = __expf(-static_cast<float>(lg[p][i]));
+            c32[i] = ok[i] ? __builtin_amdgcn_rcpf(1.0f + e) + bv[i] : -INFINITY;
+        }
+        float m[EPL16];
+#pragma unroll
+        for (int i = 0; i < EPL16; ++i) m[i] = c32[i];
+#pragma unroll
+        for (int w = EPL16 / 2; w >= 1; w /= 2)
+#pragma unroll
+            for (int i = 0; i < w; ++i) m[i] = fmaxf(m[i], m[i + w]);
+        float v = m[0], mu = -INFINITY;
+        for (int r = 0; r < K; ++r) {
+            mu = row_max_f32(v);
+            v = v == mu ? -INFINITY : v;  // equal lane maxima go together: mu only gets smaller
+        }
+        const float thr = mu - (1e-5f + 1e-6f * fabsf(mu));
+        cm[p] = 0u;
+#pragma unroll
+        for (int i = 0; i < EPL16; ++i)
+            if (ok[i] && c32[i] >= thr) cm[p] |= 1u << i;
+        const int nl = __builtin_popcount(cm[p]);
+        const int incl = row_scan_i32(nl);
+        off[p] = incl - nl;
+        n_row[p] = row_max_i32(incl);
+        over = over || n_row[p] > 16;
+    }
+    if (__ballot(over) != 0) return false;
+
+    // compaction: candidate k of row r of pass p at slot (p, r, k)
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        int k = off[p];
+#pragma unroll
+        for (int i = 0; i < EPL16; ++i) {
+            if ((cm[p] >> i) & 1u) {
+                lds_u8* sl = scr + ((p * 4 + row) * 16 + k) * 16;
+                *reinterpret_cast<__attribute__((address_space(3))) double*>(sl) = lg[p][i];
+                *reinterpret_cast<__attribute__((address_space(3))) int*>(sl + 8) = j + 16 * i;
+                *reinterpret_cast<__attribute__((address_space(3))) float*>(sl + 12) = bv[i];
+                ++k;
+            }
+        }
+    }
+    uint64_t key[P];
+    double sc[P];
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        key[p] = 0ull;
+        sc[p] = 0.0;
+        if (j < n_row[p]) {
+            const lds_u8* sl = scr + ((p * 4 + row) * 16 + j) * 16;
+            const double l = *reinterpret_cast<const __attribute__((address_space(3))) double*>(sl);
+            const int e = *reinterpret_cast<const __attribute__((address_space(3))) int*>(sl + 8);
+            const float b = *reinterpret_cast<const __attribute__((address_space(3))) float*>(sl + 12);
+            sc[p] = 1.0 / (1.0 + exp(-l));
+            double c = sc[p];
+            if (bias != nullptr) c += static_cast<double>(b);
+            key[p] = choice_key(c, e);
+        }
+    }
+
+    // K rounds of row argmax over the candidates; lane r keeps the r-th pick
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        my_e[p] = -1;
+        my_s[p] = 0.0;
+    }
+    for (int r = 0; r < K; ++r) {
+        uint64_t win[P];
+#pragma unroll
+        for (int p = 0; p < P; ++p) win[p] = row_max_u64(key[p]);
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            const bool mine = key[p] == win[p];
+            const double sw = row_max_f64(mine ? sc[p] : -1.0);
+            if (mine) key[p] = 0ull;
+            if (j == r) {
+                my_e[p] = 1023 - static_cast<int>(win[p] & 0x3FFull);
+                my_s[p] = sw;
+            }
+        }
+    }
+    return true;
+}
+
+// P tokens per row of 16 lanes: token t[p] of this lane's row, whose float64
+// logits the row holds (EPL16 per lane: experts j, j + 16, ... for lane j of
+// the row).  The P tokens are independent and handled side by side, so their
+// dependent chains (row reductions, K argmax rounds) overlap.  Every lane of
+// the wave must call it (rows whose token does not exist pass live = false
+// and write nothing).  Same arithmetic as topk_token except the order of the
+// softmax sums across lanes.
+template <int EPL16, int P>
+__device__ __forceinline__ void select_rows16(const double (&lg)[P][EPL16], int E, int K, int score,
+                                              const float* __restrict__ bias, int (&my_e)[P], double (&my_s)[P]) {
+    const int lane = lane_id();
+    const int j = lane & 15;
     bool ok[EPL16];
 #pragma unroll
     for (int i = 0; i < EPL16; ++i) ok[i] = j + 16 * i < E;
 
-    double s[EPL16];
+    double s[P][EPL16];
     if (score == 0) {
-        double m = -1.7976931348623157e308;
+        double m[P];
 #pragma unroll
-        for (int i = 0; i < EPL16; ++i)
-            if (ok[i]) m = fmax(m, lg[i]);
-        m = row_max_f64(m);
-        double part = 0.0;
+        for (int p = 0; p < P; ++p) {
+            m[p] = -1.7976931348623157e308;
 #pragma unroll
-        for (int i = 0; i < EPL16; ++i) {
-            s[i] = ok[i] ? exp(lg[i] - m) : 0.0;
-            part += s[i];
+            for (int i = 0; i < EPL16; ++i)
+                if (ok[i]) m[p] = fmax(m[p], lg[p][i]);
         }
-        const double z = row_sum_f64(part);
 #pragma unroll
-        for (int i = 0; i < EPL16; ++i) s[i] = s[i] / z;
+        for (int p = 0; p < P; ++p) m[p] = row_max_f64(m[p]);
+        double part[P];
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            part[p] = 0.0;
+#pragma unroll
+            for (int i = 0; i < EPL16; ++i) {
+                s[p][i] = ok[i] ? exp(lg[p][i] - m[p]) : 0.0;
+                part[p] += s[p][i];
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            const double z = row_sum_f64(part[p]);
+#pragma unroll
+            for (int i = 0; i < EPL16; ++i) s[p][i] = s[p][i] / z;
+        }
     } else {
 #pragma unroll
-        for (int i = 0; i < EPL16; ++i) s[i] = ok[i] ? 1.0 / (1.0 + exp(-lg[i])) : 0.0;
+        for (int p = 0; p < P; ++p)
+#pragma unroll
+            for (int i = 0; i < EPL16; ++i) s[p][i] = ok[i] ? 1.0 / (1.0 + exp(-lg[p][i])) : 0.0;
     }
 
-    uint64_t key[EPL16];
+    uint64_t key[P][EPL16];
 #pragma unroll
     for (int i = 0; i < EPL16; ++i) {
         const int e = j + 16 * i;
-        double c = s[i];
-        if (bias != nullptr && ok[i]) c += static_cast<double>(bias[e]);
-        key[i] = ok[i] ? choice_key(c, e) : 0ull;
+        const double b = (bias != nullptr && ok[i]) ? static_cast<double>(bias[e]) : 0.0;
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            double c = s[p][i];
+            if (bias != nullptr && ok[i]) c += b;
+            key[p][i] = ok[i] ? choice_key(c, e) : 0ull;
+        }
     }
 
     // K rounds of row argmax; lane r of the row keeps the r-th pick
-    int my_e = -1;
-    double my_s = 0.0;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        my_e[p] = -1;
+        my_s[p] = 0.0;
+    }
     for (int r = 0; r < K; ++r) {
-        uint64_t best = key[0];
+        uint64_t win[P];
 #pragma unroll
-        for (int i = 1; i < EPL16; ++i) best = umax64(best, key[i]);
-        const uint64_t win = row_max_u64(best);
-        const int ew = 1023 - static_cast<int>(win & 0x3FFull);
-        const int owner = ew & 15;
-        const int slot = ew >> 4;
-        double sw = -1.0;  // scores are >= 0: the row max picks the owner's value
+        for (int p = 0; p < P; ++p) {
+            uint64_t m[EPL16];  // the lane's largest key, as a tree
 #pragma unroll
-        for (int i = 0; i < EPL16; ++i) {
-            if (j == owner && i == slot) {
-                sw = s[i];
-                key[i] = 0ull;
+            for (int i = 0; i < EPL16; ++i) m[i] = key[p][i];
+#pragma unroll
+            for (int w = EPL16 / 2; w >= 1; w /= 2)
+#pragma unroll
+                for (int i = 0; i < w; ++i) m[i] = umax64(m[i], m[i + w]);
+            win[p] = m[0];
+        }
+#pragma unroll
+        for (int p = 0; p < P; ++p) win[p] = row_max_u64(win[p]);
+        double sw[P];
+        int ew[P];
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            ew[p] = 1023 - static_cast<int>(win[p] & 0x3FFull);
+            const int owner = ew[p] & 15;
+            const int slot = ew[p] >> 4;
+            sw[p] = -1.0;  // scores are >= 0: the row max picks the owner's value
+#pragma unroll
+            for (int i = 0; i < EPL16; ++i) {
+                if (j == owner && i == slot) {
+                    sw[p] = s[p][i];
+                    key[p][i] = 0ull;
+                }
             }
         }
-        sw = row_max_f64(sw);
-        if (j == r) {
-            my_e = ew;
-            my_s = sw;
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            sw[p] = row_max_f64(sw[p]);
+            if (j == r) {
+                my_e[p] = ew[p];
+                my_s[p] = sw[p];
+            }
         }
     }
 
-    // ascending id order: rank of each pick among the row's K picks
-    int rank = 0;
-    for (int i = 0; i < K; ++i) {
-        const int ei = lane_get(my_e, rbase + i);
-        rank += (j < K && ei < my_e) ? 1 : 0;
-    }
-    double den = 1.0;
-    if (renorm) {
-        den = 0.0;
-        for (int r = 0; r < K; ++r) {
-            const uint64_t holders = __ballot(j < K && rank == r);
-            const int holder = __builtin_ctzll((holders >> rbase) & 0xFFFFull) + rbase;
-            den += lane_get_f64(my_s, holder);
-        }
-    }
-    if (live && j < K) {
-        if (kept) {
-            const double wv = renorm ? (my_s / den) * route_scale : my_s * route_scale;
-            ids_out[t * K + rank] = my_e;
-            w_out[t * K + rank] = static_cast<float>(wv);
-        } else {
-            ids_out[t * K + j] = -1;
-            w_out[t * K + j] = 0.f;
-        }
-    }
 }
 
 template <int EPL>
@@ -494,7 +690,8 @@ struct RouteTile {
     static constexpr int WOFF = XS * XSTAGE;   // LDS offset of the router ring
     static constexpr int RING = WOFF + WS * WSTAGE;
     static constexpr int LOGB = TB * EMAX * 8; // float64 logits
-    static constexpr int SMEM = RING > LOGB ? RING : LOGB;
+    static constexpr int SCRB = 4 * 2 * 64 * 16;  // top-k candidate slots: 4 waves x 2 passes x 64
+    static constexpr int SMEM = RING > LOGB + SCRB ? RING : LOGB + SCRB;
     static constexpr int XPER = TB / 32;       // 8-row DMA instructions per wave per chunk
     static constexpr int WPER = EMAX / 32;
     static_assert(TB % 32 == 0 && EMAX % 32 == 0, "8-row DMA groups over 4 waves");
@@ -528,31 +725,25 @@ __global__ __launch_bounds__(256) void route_fused_bf16_kernel(
     const uint32_t row_bytes = static_cast<uint32_t>(D) * 2;
     const int chunk = (lane & 7) ^ (lane >> 3);
     const int ns = D / 64;
-    auto issue_x = [&](int st) {
+    // DMA i of this wave for hidden chunk st / router chunk st
+    auto issue_x1 = [&](int st, int i) {
         const int c = st < ns ? st : ns - 1;
         const uint32_t kb = static_cast<uint32_t>(c) * 128 + chunk * 16;
         const uint32_t dst = lds0 + (st % RT::XS) * RT::XSTAGE;
-#pragma unroll
-        for (int i = 0; i < RT::XPER; ++i) {
-            const int q = wv * RT::XPER + i;
-            int64_t rr = 8 * q + (lane >> 3);
-            if (t0 + rr >= T) rr = T - 1 - t0;
-            dma16(xb, static_cast<uint32_t>(rr) * row_bytes + kb, dst + q * 1024);
-        }
+        const int q = wv * RT::XPER + i;
+        int64_t rr = 8 * q + (lane >> 3);
+        if (t0 + rr >= T) rr = T - 1 - t0;
+        dma16(xb, static_cast<uint32_t>(rr) * row_bytes + kb, dst + q * 1024);
     };
-    auto issue_w = [&](int st) {
+    auto issue_w1 = [&](int st, int i) {
         const int c = st < ns ? st : ns - 1;
         const uint32_t kb = static_cast<uint32_t>(c) * 128 + chunk * 16;
         const uint32_t dst = lds0 + RT::WOFF + (st % RT::WS) * RT::WSTAGE;
-#pragma unroll
-        for (int i = 0; i < RT::WPER; ++i) {
-            const int q = wv * RT::WPER + i;
-            int er = 8 * q + (lane >> 3);
-            if (er >= E) er = E - 1;
-            dma16(wb, static_cast<uint32_t>(er) * row_bytes + kb, dst + q * 1024);
-        }
+        const int q = wv * RT::WPER + i;
+        int er = 8 * q + (lane >> 3);
+        if (er >= E) er = E - 1;
+        dma16(wb, static_cast<uint32_t>(er) * row_bytes + kb, dst + q * 1024);
     };
-
     double acc64[TBB][NBW][4];
 #pragma unroll
     for (int a = 0; a < TBB; ++a)
@@ -569,21 +760,25 @@ __global__ __launch_bounds__(256) void route_fused_bf16_kernel(
     const int arow = (lane & 15) * 128;
     const int brow = (wv * (16 * NBW) + (lane & 15)) * 128;
 
-    // Chunk st needs hidden stage st and router stage st.  At the top of
-    // chunk t the DMAs of router chunk t+WS-1 and hidden chunk t+XS-1 are
-    // issued (in that order) into the buffers chunk t-1 used; the router
+    // Chunk st needs hidden stage st and router stage st.  During chunk t,
+    // after its barrier and spread over its MFMAs (a burst of DMAs would
+    // stall the wave's issue), the DMAs of router chunk t+WS-1 and hidden
+    // chunk t+XS-1 are issued (in that order) into the buffers chunk t-1
+    // used; the router
     // chunk a step needs was issued WS-1 steps earlier, and only its own
     // step's hidden DMAs and the WS-2 later steps' DMAs are younger.
     constexpr int kWaitN = RT::XPER + (RT::WS - 2) * (RT::WPER + RT::XPER);
-    for (int j = 0; j < RT::XS - 1; ++j) issue_x(j);
-    for (int j = 0; j < RT::WS - 1; ++j) issue_w(j);
+    for (int j = 0; j < RT::XS - 1; ++j)
+#pragma unroll
+        for (int i = 0; i < RT::XPER; ++i) issue_x1(j, i);
+    for (int j = 0; j < RT::WS - 1; ++j)
+#pragma unroll
+        for (int i = 0; i < RT::WPER; ++i) issue_w1(j, i);
     wait_vmem<0>();
     // one k64 stage: wait, barrier, next DMAs, two MFMA k=32 steps into acc
     auto stage = [&](int st) {
         if (st > 0) wait_vmem<kWaitN>();
         __syncthreads();  // chunk st visible; every wave is done with chunk st-1
-        issue_w(st + RT::WS - 1);
-        issue_x(st + RT::XS - 1);
         const lds_u8* xs = smem + (st % RT::XS) * RT::XSTAGE;
         const lds_u8* ws = smem + RT::WOFF + (st % RT::WS) * RT::WSTAGE;
 #pragma unroll
@@ -597,6 +792,15 @@ __global__ __launch_bounds__(256) void route_fused_bf16_kernel(
                 const u32x4 bf = *reinterpret_cast<lds_u32x4*>(ws + brow + b * 16 * 128 + xoj);
 #pragma unroll
                 for (int a = 0; a < TBB; ++a) acc[a][b] = mfma_bf16(af[a], bf, acc[a][b]);
+                // this stage's DMAs spread over its MFMA groups, router rows first
+                constexpr int kQ = RT::WPER + RT::XPER;
+                constexpr int kSlots = 2 * NBW;
+                const int slot = j * NBW + b;
+#pragma unroll
+                for (int q = slot * kQ / kSlots; q < (slot + 1) * kQ / kSlots; ++q) {
+                    if (q < RT::WPER) issue_w1(st + RT::WS - 1, q);
+                    else issue_x1(st + RT::XS - 1, q - RT::WPER);
+                }
             }
         }
     };
@@ -633,21 +837,33 @@ __global__ __launch_bounds__(256) void route_fused_bf16_kernel(
     __syncthreads();
 
     if constexpr (RT::EMAX <= 256) {
-        // four tokens per wave, sixteen lanes each
+        // eight tokens per wave at a time: two per row of sixteen lanes
         constexpr int EPL16 = RT::EMAX / 16;
-        for (int tb = 4 * wv; tb < RT::TB; tb += 16) {
-            const int tl = tb + (lane >> 4);
-            const int64_t t = t0 + tl;
-            const bool live = t < T;
-            double lg[EPL16];
+        constexpr int P = 2;
+        static_assert(RT::TB % (16 * P) == 0, "tokens per wave pass");
+        for (int tb = 4 * P * wv; tb < RT::TB; tb += 16 * P) {
+            double lg[P][EPL16];
+            int64_t t[P];
+            bool live[P], kept[P];
 #pragma unroll
-            for (int i = 0; i < EPL16; ++i) {
-                const int e = (lane & 15) + 16 * i;
-                lg[i] = lgs[tl * RT::EMAX + e];
-                if (logits_out && live && e < E) logits_out[t * E + e] = static_cast<float>(lg[i]);
+            for (int p = 0; p < P; ++p) {
+                const int tl = tb + 4 * p + (lane >> 4);
+                t[p] = t0 + tl;
+                live[p] = t[p] < T;
+#pragma unroll
+                for (int i = 0; i < EPL16; ++i) {
+                    const int e = (lane & 15) + 16 * i;
+                    lg[p][i] = lgs[tl * RT::EMAX + e];
+                    if (logits_out && live[p] && e < E) logits_out[t[p] * E + e] = static_cast<float>(lg[p][i]);
+                }
+                kept[p] = live[p] && ((mask == nullptr) || (mask[t[p]] != 0));
             }
-            const bool kept = live && ((mask == nullptr) || (mask[t] != 0));
-            topk_row16<EPL16>(lg, t, live, E, K, score, renorm, route_scale, bias, kept, ids_out, w_out);
+            lds_u8* scr = smem + RT::LOGB + wv * (P * 64 * 16);
+            int my_e[P];
+            double my_s[P];
+            if (score != 1 || !select_rows16_screened<EPL16, P>(lg, E, K, bias, scr, my_e, my_s))
+                select_rows16<EPL16, P>(lg, E, K, score, bias, my_e, my_s);
+            write_picks16<P>(my_e, my_s, t, live, kept, K, renorm, route_scale, ids_out, w_out);
         }
     } else {
         for (int tl = wv; tl < RT::TB; tl += 4) {
