@@ -725,7 +725,7 @@ static void bf16_grid(int64_t rows_max, int G, bool grouped, int D, int I, int64
 constexpr size_t kCtlBytes = 2 * kCtlInts * sizeof(int32_t);
 
 // CUs of the current device (queried once per device)
-static int compute_units() {
+int compute_units() {
     static int cached[64] = {0};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;

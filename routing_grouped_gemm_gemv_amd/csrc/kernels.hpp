@@ -16,6 +16,8 @@ hipError_t launch_topk(const double* logits64, int64_t T, int E, int K, int scor
                        float route_scale, const float* bias, const uint8_t* mask,
                        float* logits_out, int32_t* ids, float* w, hipStream_t stream,
                        const int32_t* given);
+// compute units of the current device
+int compute_units();
 // whether launch_route runs the single fused kernel (bf16 operands, E <= 512)
 bool route_fused(int E, int dtype);
 // logits + top-k: one fused kernel where route_fused(), else the two kernels

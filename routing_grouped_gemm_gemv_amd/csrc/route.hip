@@ -685,11 +685,12 @@ struct RouteTile {
     static constexpr int EPL = EMAX / 64;      // experts per lane in the top-k
     static constexpr int XSTAGE = TB * 128;    // bytes of hidden rows per 64-wide k chunk
     static constexpr int WSTAGE = EMAX * 128;  // bytes of router rows per chunk
-    static constexpr int XS = 8;
+    static constexpr int XS = TB >= 128 ? 4 : 8;
     static constexpr int WS = (3 * WSTAGE + XS * XSTAGE <= 160 * 1024) ? 3 : 2;
     static constexpr int WOFF = XS * XSTAGE;   // LDS offset of the router ring
     static constexpr int RING = WOFF + WS * WSTAGE;
-    static constexpr int LOGB = TB * EMAX * 8; // float64 logits
+    static constexpr int TBP = TB < 64 ? TB : 64;  // tokens whose logits are in LDS at a time
+    static constexpr int LOGB = TBP * EMAX * 8; // float64 logits of one pass
     static constexpr int SCRB = 4 * 2 * 64 * 16;  // top-k candidate slots: 4 waves x 2 passes x 64
     static constexpr int SMEM = RING > LOGB + SCRB ? RING : LOGB + SCRB;
     static constexpr int XPER = TB / 32;       // 8-row DMA instructions per wave per chunk
@@ -697,6 +698,63 @@ struct RouteTile {
     static_assert(TB % 32 == 0 && EMAX % 32 == 0, "8-row DMA groups over 4 waves");
     static_assert(SMEM <= 160 * 1024, "LDS");
 };
+
+// Top-k of the TBP tokens starting at token tp whose float64 logits are in
+// lgs ([TBP][EMAX]); scr: the candidate slots of the screened selection.
+template <typename RT>
+__device__ __forceinline__ void route_topk_pass(const __attribute__((address_space(3))) double* lgs, lds_u8* scr_base,
+                                                int64_t tp, int64_t T, int E, int K, int score, int renorm,
+                                                double route_scale, const float* __restrict__ bias,
+                                                const uint8_t* __restrict__ mask, float* __restrict__ logits_out,
+                                                int32_t* __restrict__ ids_out, float* __restrict__ w_out) {
+    const int lane = lane_id();
+    const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+    const int64_t t0 = tp;
+    if constexpr (RT::EMAX <= 256) {
+        // eight tokens per wave at a time: two per row of sixteen lanes
+        constexpr int EPL16 = RT::EMAX / 16;
+        constexpr int P = 2;
+        static_assert(RT::TBP % (16 * P) == 0, "tokens per wave pass");
+        for (int tb = 4 * P * wv; tb < RT::TBP; tb += 16 * P) {
+            double lg[P][EPL16];
+            int64_t t[P];
+            bool live[P], kept[P];
+#pragma unroll
+            for (int p = 0; p < P; ++p) {
+                const int tl = tb + 4 * p + (lane >> 4);
+                t[p] = t0 + tl;
+                live[p] = t[p] < T;
+#pragma unroll
+                for (int i = 0; i < EPL16; ++i) {
+                    const int e = (lane & 15) + 16 * i;
+                    lg[p][i] = lgs[tl * RT::EMAX + e];
+                    if (logits_out && live[p] && e < E) logits_out[t[p] * E + e] = static_cast<float>(lg[p][i]);
+                }
+                kept[p] = live[p] && ((mask == nullptr) || (mask[t[p]] != 0));
+            }
+            lds_u8* scr = scr_base + wv * (P * 64 * 16);
+            int my_e[P];
+            double my_s[P];
+            if (score != 1 || !select_rows16_screened<EPL16, P>(lg, E, K, bias, scr, my_e, my_s))
+                select_rows16<EPL16, P>(lg, E, K, score, bias, my_e, my_s);
+            write_picks16<P>(my_e, my_s, t, live, kept, K, renorm, route_scale, ids_out, w_out);
+        }
+    } else {
+        for (int tl = wv; tl < RT::TBP; tl += 4) {
+            const int64_t t = t0 + tl;
+            if (t >= T) break;  // uniform per wave
+            double lg[RT::EPL];
+#pragma unroll
+            for (int i = 0; i < RT::EPL; ++i) {
+                const int e = lane + 64 * i;
+                lg[i] = lgs[tl * RT::EMAX + e];
+                if (logits_out && e < E) logits_out[t * E + e] = static_cast<float>(lg[i]);
+            }
+            const bool kept = (mask == nullptr) || (mask[t] != 0);
+            topk_token<RT::EPL>(lg, t, E, K, score, renorm, route_scale, bias, kept, ids_out, w_out, nullptr);
+        }
+    }
+}
 
 template <int TBB, int NBW>
 __global__ __launch_bounds__(256) void route_fused_bf16_kernel(
@@ -822,63 +880,28 @@ __global__ __launch_bounds__(256) void route_fused_bf16_kernel(
     wait_vmem<0>();
     __syncthreads();  // the stages are dead: the logits take their place
 
-    // logits to LDS: [TB][EMAX] float64
+    // Logits to LDS, TBP tokens per pass ([TBP][EMAX] float64), and the
+    // top-k of those tokens from there.
     __attribute__((address_space(3))) double* lgs = (__attribute__((address_space(3))) double*)(smem);
 #pragma unroll
-    for (int a = 0; a < TBB; ++a)
+    for (int h = 0; h < RT::TB / RT::TBP; ++h) {
+        if (h > 0) __syncthreads();  // the previous pass is done with its logits
 #pragma unroll
-        for (int b = 0; b < NBW; ++b)
+        for (int a = 0; a < TBB; ++a) {
+            if (a * 16 / RT::TBP != h) continue;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int tl = a * 16 + 4 * (lane >> 4) + i;
-                const int e = wv * (16 * NBW) + b * 16 + (lane & 15);
-                lgs[tl * RT::EMAX + e] = acc64[a][b][i];
-            }
-    __syncthreads();
-
-    if constexpr (RT::EMAX <= 256) {
-        // eight tokens per wave at a time: two per row of sixteen lanes
-        constexpr int EPL16 = RT::EMAX / 16;
-        constexpr int P = 2;
-        static_assert(RT::TB % (16 * P) == 0, "tokens per wave pass");
-        for (int tb = 4 * P * wv; tb < RT::TB; tb += 16 * P) {
-            double lg[P][EPL16];
-            int64_t t[P];
-            bool live[P], kept[P];
+            for (int b = 0; b < NBW; ++b)
 #pragma unroll
-            for (int p = 0; p < P; ++p) {
-                const int tl = tb + 4 * p + (lane >> 4);
-                t[p] = t0 + tl;
-                live[p] = t[p] < T;
-#pragma unroll
-                for (int i = 0; i < EPL16; ++i) {
-                    const int e = (lane & 15) + 16 * i;
-                    lg[p][i] = lgs[tl * RT::EMAX + e];
-                    if (logits_out && live[p] && e < E) logits_out[t[p] * E + e] = static_cast<float>(lg[p][i]);
+                for (int i = 0; i < 4; ++i) {
+                    const int tl = a * 16 + 4 * (lane >> 4) + i - h * RT::TBP;
+                    const int e = wv * (16 * NBW) + b * 16 + (lane & 15);
+                    lgs[tl * RT::EMAX + e] = acc64[a][b][i];
                 }
-                kept[p] = live[p] && ((mask == nullptr) || (mask[t[p]] != 0));
-            }
-            lds_u8* scr = smem + RT::LOGB + wv * (P * 64 * 16);
-            int my_e[P];
-            double my_s[P];
-            if (score != 1 || !select_rows16_screened<EPL16, P>(lg, E, K, bias, scr, my_e, my_s))
-                select_rows16<EPL16, P>(lg, E, K, score, bias, my_e, my_s);
-            write_picks16<P>(my_e, my_s, t, live, kept, K, renorm, route_scale, ids_out, w_out);
         }
-    } else {
-        for (int tl = wv; tl < RT::TB; tl += 4) {
-            const int64_t t = t0 + tl;
-            if (t >= T) break;  // uniform per wave
-            double lg[RT::EPL];
-#pragma unroll
-            for (int i = 0; i < RT::EPL; ++i) {
-                const int e = lane + 64 * i;
-                lg[i] = lgs[tl * RT::EMAX + e];
-                if (logits_out && e < E) logits_out[t * E + e] = static_cast<float>(lg[i]);
-            }
-            const bool kept = (mask == nullptr) || (mask[t] != 0);
-            topk_token<RT::EPL>(lg, t, E, K, score, renorm, route_scale, bias, kept, ids_out, w_out, nullptr);
-        }
+        __syncthreads();
+        const int64_t tp = t0 + h * RT::TBP;  // first token of the pass
+        route_topk_pass<RT>(lgs, smem + RT::LOGB, tp, T, E, K, score, renorm, route_scale, bias, mask, logits_out,
+                            ids_out, w_out);
     }
 }
 
@@ -931,8 +954,12 @@ hipError_t launch_route(const void* x, const void* router, int64_t T, int D, int
     route_fused_bf16_kernel<TBB, NBW><<<static_cast<unsigned>((T + 16 * TBB - 1) / (16 * TBB)), 256, 0, \
                                          stream>>>(xb, wb, T, D, E, K, score, renorm, rs, bias, mask,      \
                                                    logits_out, ids, w)
+    // 128-token tiles halve the router-matrix traffic per token once there
+    // are enough of them to give every CU one; the logits and picks do not
+    // depend on the tile
     if (E <= 64) MOE_ROUTE(4, 1);
     else if (E <= 128) MOE_ROUTE(4, 2);
+    else if (E <= 256 && T >= 128 * static_cast<int64_t>(compute_units())) MOE_ROUTE(8, 4);
     else if (E <= 256) MOE_ROUTE(4, 4);
     else MOE_ROUTE(2, 8);
 #undef MOE_ROUTE
