@@ -14,8 +14,12 @@ rounding per operation.
 
 Pins (the tests that tie each function to something other than itself):
   router_logits      exact rational dot products on the tiny layer; one-hot/zero rows
-  scores             torch.softmax / torch.sigmoid (library routines)
+  scores             torch.softmax / torch.sigmoid / softplus then sqrt (library
+                     routines); sqrtsoftplus(0) = sqrt(log 2)
   select_topk        O(E^2) dominance count, exhaustive K-subsets, closed-form ties
+  select_grouped     hand-derived examples (tests/golden); n_group = 1 and
+                     topk_group = n_group reduce to select_topk; brute-force
+                     group ranking with plain Python lists
   topk_weights       sum = route_scale, top-1 renorm = 1, zero row = 1/K
   permute            numpy stable argsort; bijection and segment invariants
   expert_mlp         dense all-experts formulation with torch.nn.functional.silu;
@@ -41,6 +45,7 @@ from .moe import (
     round_bf16,
     router_logits,
     scores,
+    select_grouped,
     select_topk,
     silu,
     topk_weights,
@@ -60,6 +65,7 @@ __all__ = [
     "round_bf16",
     "router_logits",
     "scores",
+    "select_grouped",
     "select_topk",
     "silu",
     "topk_weights",

@@ -19,6 +19,13 @@ Conventions (the plainest reading where the pages leave a step open):
     the weights are taken from the unbiased scores [SPF, router commit notes];
   * the K experts with the largest choice are selected, ties going to the lower
     expert id; the K ids of a token are returned in ascending id order;
+  * the pages name two more score functions and a select override without
+    formulas [SPF, commit notes on the load-balance loss and on select]:
+    sqrtsoftplus is read as sqrt(softplus(l)) = sqrt(log(1 + e^l)), and the
+    DeepSeek-V3 group-limited select as: the E experts form n_group groups of
+    E/n_group consecutive ids, a group's score is the sum of its two largest
+    choices, the topk_group best groups (ties to the lower group id) are
+    kept, and the K experts are chosen from the kept groups only;
   * weights are renormalised over the selected experts when ``renorm`` is set,
     then multiplied by ``route_scale`` [SPF, "Revised version", "Out of scope"];
   * masked tokens take no route, no expert work and produce a zero row;
@@ -120,7 +127,8 @@ def silu(v: np.ndarray) -> np.ndarray:
 
 
 def scores(logits: np.ndarray, score: str) -> np.ndarray:
-    """Router scores in float64: softmax over experts, or the logistic sigmoid."""
+    """Router scores in float64: softmax over experts, the logistic sigmoid, or
+    sqrtsoftplus, sqrt(log(1 + e^l)) of each logit [SPF, commit notes]."""
     if score == "softmax":
         z = logits - logits.max(axis=1, keepdims=True)
         ez = np.exp(z)
@@ -128,6 +136,9 @@ def scores(logits: np.ndarray, score: str) -> np.ndarray:
     if score == "sigmoid":
         with np.errstate(over="ignore"):
             return 1.0 / (1.0 + np.exp(-logits))
+    if score == "sqrtsoftplus":
+        # log(1 + e^l) = max(l, 0) + log(1 + e^-|l|): the same value, no overflow
+        return np.sqrt(np.maximum(logits, 0.0) + np.log1p(np.exp(-np.abs(logits))))
     raise ValueError(f"unknown score function {score!r}")
 
 
@@ -147,12 +158,53 @@ def select_topk(choice: np.ndarray, K: int, valid: Optional[np.ndarray] = None
     if K < E:
         ck = np.take_along_axis(choice, order[:, K - 1:K], axis=1)[:, 0]
         ck1 = np.take_along_axis(choice, order[:, K:K + 1], axis=1)[:, 0]
-        den = np.maximum(np.abs(ck), np.abs(ck1))
-        with np.errstate(invalid="ignore", divide="ignore"):
-            margin = np.where(den > 0, (ck - ck1) / den, 0.0)
+        margin = _rel_margin(ck, ck1)
     if valid is not None:
         ids[~valid] = -1
         margin[~valid] = np.inf
+    return ids, margin
+
+
+def _rel_margin(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """(a - b) / max(|a|, |b|) for a >= b; +inf where b is -inf (nothing else
+    competes), 0 where both are 0."""
+    den = np.maximum(np.abs(a), np.abs(b))
+    with np.errstate(invalid="ignore", divide="ignore"):
+        m = np.where(den > 0, (a - b) / np.where(den > 0, den, 1.0), 0.0)
+    return np.where(np.isneginf(b), np.inf, m)
+
+
+def select_grouped(choice: np.ndarray, K: int, n_group: int, topk_group: int,
+                   valid: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Group-limited top-K, the DeepSeek-V3 select the pages name [SPF, commit
+    notes on select], read as: group g holds experts g*E/n_group ..
+    (g+1)*E/n_group - 1; its score is the sum of its two largest choices; the
+    topk_group groups with the largest scores are kept (ties to the lower
+    group id); the K experts are then chosen among the kept groups' experts
+    as select_topk chooses them.
+
+    Returns (ids, rel_margin) like select_topk; rel_margin is the smaller of
+    the expert margin among the kept experts and the group margin between the
+    topk_group-th and the next group score, since a near tie in either
+    decision may flip a pick.
+    """
+    T, E = choice.shape
+    gs = E // n_group
+    cg = choice.reshape(T, n_group, gs)
+    top2 = -np.sort(-cg, axis=2)[:, :, :2]
+    gscore = top2[:, :, 0] + top2[:, :, 1]
+    gorder = np.argsort(-gscore, axis=1, kind="stable")
+    kept = np.zeros((T, n_group), dtype=bool)
+    np.put_along_axis(kept, gorder[:, :topk_group], True, axis=1)
+    allowed = np.repeat(kept, gs, axis=1)
+    ids, margin = select_topk(np.where(allowed, choice, -np.inf), K, valid)
+    if topk_group < n_group:
+        gk = np.take_along_axis(gscore, gorder[:, topk_group - 1:topk_group], axis=1)[:, 0]
+        gk1 = np.take_along_axis(gscore, gorder[:, topk_group:topk_group + 1], axis=1)[:, 0]
+        gm = _rel_margin(gk, gk1)
+        if valid is not None:
+            gm = np.where(valid, gm, np.inf)
+        margin = np.minimum(margin, gm)
     return ids, margin
 
 
@@ -357,14 +409,16 @@ def forward(x: np.ndarray, w_router: np.ndarray,
             *, K: int, score: str, renorm: bool, route_scale: float,
             bias: Optional[np.ndarray] = None, mask: Optional[np.ndarray] = None,
             shared_gate_up: Optional[np.ndarray] = None, shared_down: Optional[np.ndarray] = None,
-            bf16_mode: bool, ids_override: Optional[np.ndarray] = None) -> OracleResult:
+            bf16_mode: bool, ids_override: Optional[np.ndarray] = None,
+            n_group: int = 1, topk_group: int = 1) -> OracleResult:
     """The layer forward on the CPU, every boundary tensor returned.
 
     ``gate_up``/``down`` are the stacked expert weights ([E, 2I, D], [E, D, I])
     or callables returning expert e's matrices.  ``ids_override`` replays given
     top-k ids (ascending, -1 masked) instead of selecting them, as the routing
     replay of [RLK, "R3 Should Not Be A Prerequisite"] does; the weights then
-    come from the oracle's own scores of those ids.
+    come from the oracle's own scores of those ids.  ``n_group`` > 1 selects
+    with select_grouped.
     """
     x64 = widen(x)
     wr64 = widen(w_router)
@@ -375,7 +429,10 @@ def forward(x: np.ndarray, w_router: np.ndarray,
     logits = router_logits(x64, wr64)
     s = scores(logits, score)
     c = s + widen(bias)[None, :] if bias is not None else s
-    ids, margin = select_topk(c, K, valid)
+    if n_group > 1:
+        ids, margin = select_grouped(c, K, n_group, topk_group, valid)
+    else:
+        ids, margin = select_topk(c, K, valid)
     if ids_override is not None:
         ids = np.asarray(ids_override, dtype=np.int32).copy()
         ids[~valid] = -1

@@ -46,7 +46,7 @@ class LayerConfig:
     Is: int                     # shared expert intermediate (0: no shared expert)
     dtype: str                  # operand mode: "bf16" (bf16 operands, fp32 accumulate) or "f32"
     value_dtype: str            # how draws are stored: "bf16" (rounded) or "f32"
-    score: str                  # "softmax" or "sigmoid"
+    score: str                  # "softmax", "sigmoid" or "sqrtsoftplus"
     renorm: bool                # renormalise the selected weights to sum to 1
     route_scale: float          # multiplies the (renormalised) weights
     bias: Optional[Tuple[float, float]]  # selection bias U(lo, hi), or None
@@ -60,6 +60,8 @@ class LayerConfig:
     seed_b: int = 2             # selection bias
     seed_s: int = 3             # shuffles and padding rows
     t_sweep: Tuple[int, ...] = field(default_factory=tuple)
+    n_group: int = 1            # group-limited select: expert groups (1: none)
+    topk_group: int = 1         # groups kept per token
 
     @property
     def P(self) -> int:
@@ -113,8 +115,15 @@ CONFIGS = {
 }
 
 
-def get_config(name: str, T: Optional[int] = None, dtype: Optional[str] = None) -> LayerConfig:
+def get_config(name: str, T: Optional[int] = None, dtype: Optional[str] = None, score: Optional[str] = None,
+               n_group: Optional[int] = None, topk_group: Optional[int] = None) -> LayerConfig:
+    """A named configuration; the optional arguments replace its token count,
+    operand mode, score function or group-limited select."""
     cfg = CONFIGS[name]
+    if score is not None:
+        cfg = replace(cfg, score=score)
+    if n_group is not None:
+        cfg = replace(cfg, n_group=n_group, topk_group=topk_group if topk_group is not None else n_group)
     if T is not None:
         cfg = replace(cfg, T=T)
     if dtype is not None:

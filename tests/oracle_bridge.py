@@ -21,4 +21,5 @@ def oracle_forward(inp: LayerInputs, tokens: Optional[np.ndarray] = None,
         bias=inp.bias, mask=mask,
         shared_gate_up=inp.w_gate_up_s, shared_down=inp.w_down_s,
         bf16_mode=(cfg.dtype == "bf16"), ids_override=ids_override,
+        n_group=cfg.n_group, topk_group=cfg.topk_group,
     )

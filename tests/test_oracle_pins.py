@@ -115,7 +115,89 @@ def test_scores_match_torch():
     np.testing.assert_allclose(sm, torch.softmax(torch.from_numpy(lg), dim=1).numpy(), rtol=1e-13, atol=0)
     np.testing.assert_allclose(sg, torch.sigmoid(torch.from_numpy(lg)).numpy(), rtol=1e-13, atol=0)
     with pytest.raises(ValueError):
-        oracle.scores(lg, "sqrtsoftplus")
+        oracle.scores(lg, "relu")
+
+
+def test_sqrtsoftplus_matches_torch_and_closed_forms():
+    # torch's softplus (library routine; a threshold beyond reach keeps its
+    # log1p(exp(l)) formula, which overflows past l ~ 709), then sqrt
+    lg = np.concatenate([np.linspace(-700, 700, 2801), np.random.default_rng(15).standard_normal(2000) * 4])[None, :]
+    ss = oracle.scores(lg, "sqrtsoftplus")
+    ref = torch.nn.functional.softplus(torch.from_numpy(lg), beta=1.0, threshold=1e300).sqrt().numpy()
+    np.testing.assert_allclose(ss, ref, rtol=1e-14, atol=1e-300)
+    # closed forms: sqrt(log 2) at 0; sqrt(l) up to e^-l / (2 sqrt(l)) for large l; sqrt(e^l) for very negative l
+    z = oracle.scores(np.array([[0.0, 60.0, -60.0, 1000.0]]), "sqrtsoftplus")[0]
+    assert abs(z[0] - np.sqrt(np.log(2.0))) <= 1e-16
+    assert abs(z[1] - np.sqrt(60.0)) <= 1e-15 * np.sqrt(60.0)
+    assert abs(z[2] - np.exp(-30.0)) <= 1e-14 * np.exp(-30.0)
+    assert z[3] == np.sqrt(1000.0)
+    assert np.all(np.diff(oracle.scores(np.linspace(-20, 20, 401)[None, :], "sqrtsoftplus")[0]) > 0)
+
+
+def _golden_grouped():
+    with open(os.path.join(GOLDEN, "grouped_select_examples.json")) as f:
+        return json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("case", range(3))
+def test_select_grouped_hand_examples(case):
+    c = _golden_grouped()[case]
+    choice = np.array([c["choice"]], dtype=np.float64)
+    ids, _ = oracle.select_grouped(choice, c["K"], c["n_group"], c["topk_group"])
+    assert list(ids[0]) == c["ids"]
+    ids0, _ = oracle.select_topk(choice, c["K"])
+    assert list(ids0[0]) == c["ungrouped_ids"]
+
+
+def _grouped_brute(row, K, G, TG):
+    """Plain Python lists: group scores, kept groups, then the dominance rule."""
+    E = len(row)
+    gs = E // G
+    gscore = []
+    for g in range(G):
+        vals = sorted(row[g * gs:(g + 1) * gs], reverse=True)
+        gscore.append(vals[0] + vals[1])
+    kept = sorted(range(G), key=lambda g: (-gscore[g], g))[:TG]
+    allowed = [e for e in range(E) if e // gs in kept]
+    picks = sorted(allowed, key=lambda e: (-row[e], e))[:K]
+    return sorted(picks), kept
+
+
+@pytest.mark.parametrize("E,G,TG,K", [(8, 4, 2, 3), (16, 4, 1, 2), (32, 8, 4, 6), (24, 3, 2, 5)])
+def test_select_grouped_matches_brute_force(E, G, TG, K):
+    rng = np.random.default_rng(E * 100 + G * 10 + TG)
+    c = rng.integers(-3, 4, size=(400, E)) / 4.0   # many exact ties, in groups and across them
+    ids, _ = oracle.select_grouped(c, K, G, TG)
+    for t in range(c.shape[0]):
+        picks, kept = _grouped_brute(list(c[t]), K, G, TG)
+        assert list(ids[t]) == picks
+        assert all(e // (E // G) in kept for e in ids[t])
+
+
+def test_select_grouped_reductions():
+    rng = np.random.default_rng(21)
+    c = rng.standard_normal((300, 64))
+    base, m0 = oracle.select_topk(c, 6)
+    for G, TG in ((1, 1), (8, 8), (4, 4)):
+        ids, m = oracle.select_grouped(c, 6, G, TG)
+        np.testing.assert_array_equal(ids, base)
+        np.testing.assert_array_equal(m, m0)
+    # one group kept: all picks inside the best group
+    ids, _ = oracle.select_grouped(c, 2, 8, 1)
+    assert np.all(ids[:, 0] // 8 == ids[:, 1] // 8)
+
+
+def test_select_grouped_margin_covers_group_ties():
+    # groups 1 and 3 tie exactly (0.9375): not exempt (an exact tie); raise
+    # group 3 by 2^-50 (the sum keeps it): exempt, and group 3 now wins
+    c = np.array([_golden_grouped()[0]["choice"]], dtype=np.float64)
+    _, m = oracle.select_grouped(c, 3, 4, 2)
+    assert m[0] == 0.0
+    c2 = c.copy()
+    c2[0, 6] = 0.25 + 2.0 ** -50
+    ids, m2 = oracle.select_grouped(c2, 3, 4, 2)
+    assert 0 < m2[0] < oracle.EXEMPT_REL_MARGIN
+    assert list(ids[0]) == [0, 6, 7]
 
 
 def test_silu_matches_torch():
