@@ -37,6 +37,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="dsv4", choices=["dsv4", "qnext", "q30", "dspark", "tiny"])
     ap.add_argument("--tokens", type=int, default=0, help="override T (0: the config's T)")
+    ap.add_argument("--score", default=None, choices=["softmax", "sigmoid", "sqrtsoftplus"],
+                    help="override the config's router score function")
+    ap.add_argument("--groups", type=int, default=0, help="group-limited select: expert groups (0: the config's)")
+    ap.add_argument("--topk-group", type=int, default=0, help="groups kept per token (with --groups)")
     ap.add_argument("--cpu-sample", type=int, default=384, help="tokens timed on the CPU oracle (0: skip)")
     ap.add_argument("--no-invariance", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -146,7 +150,8 @@ def main():
     import routing_grouped_gemm_gemv_amd as moe
     from synth import get_config, make_inputs
 
-    cfg = get_config(args.config, T=args.tokens or None)
+    cfg = get_config(args.config, T=args.tokens or None, score=args.score, n_group=args.groups or None,
+                     topk_group=args.topk_group or None)
     T = cfg.T
     t0 = time.time()
     inp = make_inputs(cfg)
@@ -162,7 +167,8 @@ def main():
 
     torch.cuda.set_device(0)
     shape = moe.Shape(T=T, D=cfg.D, E=cfg.E, K=cfg.K, I=cfg.I, Is=cfg.Is, score=cfg.score,
-                      renorm=cfg.renorm, route_scale=cfg.route_scale, dtype=cfg.dtype)
+                      renorm=cfg.renorm, route_scale=cfg.route_scale, dtype=cfg.dtype,
+                      n_group=cfg.n_group, topk_group=cfg.topk_group)
     x = dev(inp.x)
     layer = moe.MoeLayer(shape, dev(inp.w_router), dev(inp.w_gate_up), dev(inp.w_down),
                          dev(inp.w_gate_up_s), dev(inp.w_down_s), dev(inp.bias))
@@ -272,6 +278,7 @@ def main():
             "workload": f"{cfg.name}-like MoE layer forward",
             "T": T, "D": cfg.D, "E": cfg.E, "K": cfg.K, "I": cfg.I, "Is": cfg.Is,
             "score": cfg.score, "renorm": cfg.renorm, "route_scale": cfg.route_scale,
+            **({"n_group": cfg.n_group, "topk_group": cfg.topk_group} if cfg.n_group > 1 else {}),
             "selection_bias": cfg.bias is not None, "operands": cfg.dtype, "accumulate": "fp32",
             "parallelism": "single GPU",
         },
@@ -310,7 +317,8 @@ def cpu_baseline(cfg, inp, n):
     t0 = time.perf_counter()
     oracle.forward(inp.x[:n], inp.w_router, inp.w_gate_up, inp.w_down, K=cfg.K, score=cfg.score,
                    renorm=cfg.renorm, route_scale=cfg.route_scale, bias=inp.bias,
-                   shared_gate_up=inp.w_gate_up_s, shared_down=inp.w_down_s, bf16_mode=(cfg.dtype == "bf16"))
+                   shared_gate_up=inp.w_gate_up_s, shared_down=inp.w_down_s, bf16_mode=(cfg.dtype == "bf16"),
+                   n_group=cfg.n_group, topk_group=cfg.topk_group)
     dt = time.perf_counter() - t0
     model = ""
     try:

@@ -59,9 +59,11 @@ typedef enum {
 typedef enum { MOE_BF16 = 0, MOE_F32 = 1 } moe_dtype;
 
 /* Router score function (RL-Kernel roadmap, Problem 1: router softmax; SpecForge
- * pull request #1003 commit notes: sigmoid routers).  The score is computed in
- * float64 from float64-accumulated logits. */
-typedef enum { MOE_SOFTMAX = 0, MOE_SIGMOID = 1 } moe_score;
+ * pull request #1003 commit notes: sigmoid and sqrtsoftplus routers).  The
+ * score is computed in float64 from float64-accumulated logits.
+ * MOE_SQRTSOFTPLUS is read as sqrt(log(1 + e^l)) (the pages name it without a
+ * formula). */
+typedef enum { MOE_SOFTMAX = 0, MOE_SIGMOID = 1, MOE_SQRTSOFTPLUS = 2 } moe_score;
 
 /* Combine arithmetic (moe_combine, moe_forward).
  *   MOE_COMBINE_F32_FOLD: float32 left fold in ascending expert id (the
@@ -87,6 +89,16 @@ typedef struct {
     float route_scale;  /* multiplies the (renormalised) weights; finite, > 0 */
     int32_t dtype;      /* moe_dtype: operand dtype of x, weights, expert activations and outputs */
     int32_t combine;    /* moe_combine_mode */
+    /* Group-limited select (SpecForge pull request #1003 commit notes on select:
+     * DeepSeek-V3's group-limited routing, named without a formula; read as:
+     * experts form n_group groups of E/n_group consecutive ids, a group's
+     * score is the sum of its two largest choices, the topk_group best groups
+     * are kept, ties to the lower group id, and the K experts are chosen
+     * among the kept groups).  n_group 0 or 1: no grouping.  Otherwise E must
+     * be a multiple of n_group with at least 2 experts per group, n_group
+     * <= 64, 1 <= topk_group <= n_group and K <= topk_group * E / n_group. */
+    int32_t n_group;
+    int32_t topk_group;
 } moe_shape;
 
 /* Weights of one layer (device pointers, operand dtype unless noted).

@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(_PKG, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_BF16, MOE_F32 = 0, 1
-MOE_SOFTMAX, MOE_SIGMOID = 0, 1
+MOE_SOFTMAX, MOE_SIGMOID, MOE_SQRTSOFTPLUS = 0, 1, 2
 MOE_COMBINE_F32_FOLD, MOE_COMBINE_F64 = 0, 1
 
 EXPORTED = (
@@ -58,6 +58,8 @@ class _Shape(ctypes.Structure):
         ("route_scale", ctypes.c_float),
         ("dtype", ctypes.c_int32),
         ("combine", ctypes.c_int32),
+        ("n_group", ctypes.c_int32),
+        ("topk_group", ctypes.c_int32),
     ]
 
 
@@ -79,18 +81,22 @@ class Shape:
     K: int
     I: int
     Is: int = 0
-    score: str = "softmax"      # "softmax" | "sigmoid"
+    score: str = "softmax"      # "softmax" | "sigmoid" | "sqrtsoftplus"
     renorm: bool = True
     route_scale: float = 1.0
     dtype: str = "bf16"         # operand dtype: "bf16" | "f32"
     combine: str = "f32"        # combine arithmetic: "f32" (float32 fold) | "f64" (order-invariant sum)
+    n_group: int = 1            # group-limited select: expert groups (0 or 1: none)
+    topk_group: int = 1         # groups kept per token
 
     def c(self) -> _Shape:
         return _Shape(self.T, self.D, self.E, self.K, self.I, self.Is,
-                      {"softmax": MOE_SOFTMAX, "sigmoid": MOE_SIGMOID}.get(self.score, -1),
+                      {"softmax": MOE_SOFTMAX, "sigmoid": MOE_SIGMOID,
+                       "sqrtsoftplus": MOE_SQRTSOFTPLUS}.get(self.score, -1),
                       int(self.renorm), float(self.route_scale),
                       {"bf16": MOE_BF16, "f32": MOE_F32}.get(self.dtype, -1),
-                      {"f32": MOE_COMBINE_F32_FOLD, "f64": MOE_COMBINE_F64}.get(self.combine, -1))
+                      {"f32": MOE_COMBINE_F32_FOLD, "f64": MOE_COMBINE_F64}.get(self.combine, -1),
+                      int(self.n_group), int(self.topk_group))
 
     @property
     def torch_dtype(self) -> torch.dtype:

@@ -36,14 +36,30 @@ size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
 
 constexpr int64_t kMaxPairs = (static_cast<int64_t>(1) << 31) - 1;
 
+// 0 and 1 both mean: no group-limited select
+int n_group(const moe_shape* s) { return s->n_group > 1 ? s->n_group : 1; }
+
 moe_status check_shape(const moe_shape* s) {
     if (s == nullptr) return fail(MOE_ERR_INVALID, "shape is NULL");
     if (s->T < 0) return fail(MOE_ERR_INVALID, "T = %lld is negative", static_cast<long long>(s->T));
     if (s->D <= 0 || s->E <= 0 || s->K <= 0 || s->I <= 0 || s->Is < 0)
         return fail(MOE_ERR_INVALID, "D, E, K, I must be positive and Is non-negative (D=%d E=%d K=%d I=%d Is=%d)",
                     s->D, s->E, s->K, s->I, s->Is);
-    if (s->score != MOE_SOFTMAX && s->score != MOE_SIGMOID)
+    if (s->score != MOE_SOFTMAX && s->score != MOE_SIGMOID && s->score != MOE_SQRTSOFTPLUS)
         return fail(MOE_ERR_INVALID, "unknown score function %d", s->score);
+    if (s->n_group < 0 || s->topk_group < 0)
+        return fail(MOE_ERR_INVALID, "n_group = %d and topk_group = %d must be non-negative", s->n_group, s->topk_group);
+    if (s->n_group > 1) {
+        if (s->E % s->n_group != 0 || s->E / s->n_group < 2)
+            return fail(MOE_ERR_INVALID, "E = %d must split into n_group = %d groups of at least 2 experts", s->E,
+                        s->n_group);
+        if (s->topk_group < 1 || s->topk_group > s->n_group)
+            return fail(MOE_ERR_INVALID, "topk_group = %d must lie in [1, n_group = %d]", s->topk_group, s->n_group);
+        if (s->K > s->topk_group * (s->E / s->n_group))
+            return fail(MOE_ERR_INVALID, "K = %d exceeds the %d experts of the kept groups", s->K,
+                        s->topk_group * (s->E / s->n_group));
+        if (s->n_group > 64) return fail(MOE_ERR_UNSUPPORTED, "n_group = %d exceeds 64", s->n_group);
+    }
     if (s->dtype != MOE_BF16 && s->dtype != MOE_F32) return fail(MOE_ERR_INVALID, "unknown operand dtype %d", s->dtype);
     if (s->renorm != 0 && s->renorm != 1) return fail(MOE_ERR_INVALID, "renorm must be 0 or 1, got %d", s->renorm);
     if (s->combine != MOE_COMBINE_F32_FOLD && s->combine != MOE_COMBINE_F64)
@@ -162,8 +178,8 @@ moe_status moe_route(const moe_shape* shape, const void* x, const void* router, 
     if ((st = check_device()) != MOE_OK) return st;
     double* l64 = static_cast<double*>(ws);
     if ((st = hip_status(moe::launch_route(x, router, shape->T, shape->D, shape->E, shape->K, shape->dtype,
-                                           shape->score, shape->renorm, shape->route_scale, sel_bias, mask, l64,
-                                           logits, topk_ids, topk_w, stream),
+                                           shape->score, shape->renorm, shape->route_scale, n_group(shape),
+                                           shape->topk_group, sel_bias, mask, l64, logits, topk_ids, topk_w, stream),
                          "routing launch")) != MOE_OK)
         return st;
     return ok();
@@ -283,8 +299,8 @@ static moe_status forward_impl(const moe_shape* shape, const moe_weights* weight
                              "routing replay launch")) != MOE_OK)
             return st;
     } else if ((st = hip_status(moe::launch_route(x, weights->router, T, shape->D, shape->E, shape->K, shape->dtype,
-                                                  shape->score, shape->renorm, shape->route_scale, sel_bias, mask, l64,
-                                                  tr.logits, ids, tw, stream),
+                                                  shape->score, shape->renorm, shape->route_scale, n_group(shape),
+                                                  shape->topk_group, sel_bias, mask, l64, tr.logits, ids, tw, stream),
                                 "routing launch")) != MOE_OK) {
         return st;
     }

@@ -13,18 +13,20 @@ hipError_t launch_router_logits(const void* x, const void* router, int64_t T, in
                                 int dtype, double* logits64, hipStream_t stream);
 // scores, selection bias, top-k, weights; optional float32 logits export
 hipError_t launch_topk(const double* logits64, int64_t T, int E, int K, int score, int renorm,
-                       float route_scale, const float* bias, const uint8_t* mask,
+                       float route_scale, int n_group, int topk_group, const float* bias, const uint8_t* mask,
                        float* logits_out, int32_t* ids, float* w, hipStream_t stream,
                        const int32_t* given);
 // compute units of the current device
 int compute_units();
-// whether launch_route runs the single fused kernel (bf16 operands, E <= 512)
-bool route_fused(int E, int dtype);
+// whether launch_route runs the single fused kernel (bf16 operands, E <= 512,
+// no group-limited select)
+bool route_fused(int E, int dtype, int n_group);
 // logits + top-k: one fused kernel where route_fused(), else the two kernels
 // above through logits64 [T, E]; both give the same bits
 hipError_t launch_route(const void* x, const void* router, int64_t T, int D, int E, int K, int dtype,
-                        int score, int renorm, float route_scale, const float* bias, const uint8_t* mask,
-                        double* logits64, float* logits_out, int32_t* ids, float* w, hipStream_t stream);
+                        int score, int renorm, float route_scale, int n_group, int topk_group, const float* bias,
+                        const uint8_t* mask, double* logits64, float* logits_out, int32_t* ids, float* w,
+                        hipStream_t stream);
 // routing replay: logits through logits64, then the given ids with weights
 // from their scores (tokens with invalid given ids are treated as masked)
 hipError_t launch_route_replay(const void* x, const void* router, int64_t T, int D, int E, int K, int dtype,

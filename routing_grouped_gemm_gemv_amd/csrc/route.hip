@@ -206,11 +206,41 @@ __device__ __forceinline__ uint64_t choice_key(double c, int e) {
 // instead of the K largest choices (a token whose given ids are not K
 // distinct ids in [0, E) is treated as masked); the weights still come from
 // this token's scores.
+// Score of one logit, float64: the logistic sigmoid (score 1) or
+// sqrtsoftplus (score 2), sqrt(log(1 + e^l)) written as
+// sqrt(max(l, 0) + log1p(e^-|l|)), which does not overflow.
+__device__ __forceinline__ double elem_score(double l, int score) {
+    if (score == 2) return sqrt(fmax(l, 0.0) + log1p(exp(-fabs(l))));
+    return 1.0 / (1.0 + exp(-l));
+}
+
+// (a, b), a >= b: the two largest of this lane's and the other set's pair
+// (the sets are disjoint)
+__device__ __forceinline__ void top2_merge(double& a, double& b, double a2, double b2) {
+    const double lo = fmax(fmin(a, a2), fmax(b, b2));
+    a = fmax(a, a2);
+    b = lo;
+}
+// The two largest values over the wave (uniform result).  Every step pairs
+// lanes whose sets of values are disjoint, as a top-2 merge needs.
+__device__ __forceinline__ void wave_top2_f64(double& a, double& b) {
+    top2_merge(a, b, dpp_f64<0xB1>(a), dpp_f64<0xB1>(b));    // quad_perm(1,0,3,2)
+    top2_merge(a, b, dpp_f64<0x4E>(a), dpp_f64<0x4E>(b));    // quad_perm(2,3,0,1)
+    top2_merge(a, b, dpp_f64<0x141>(a), dpp_f64<0x141>(b));  // row_half_mirror
+    top2_merge(a, b, dpp_f64<0x140>(a), dpp_f64<0x140>(b));  // row_mirror
+    double ra = readlane_f64(a, 0), rb = readlane_f64(b, 0);
+    top2_merge(ra, rb, readlane_f64(a, 16), readlane_f64(b, 16));
+    top2_merge(ra, rb, readlane_f64(a, 32), readlane_f64(b, 32));
+    top2_merge(ra, rb, readlane_f64(a, 48), readlane_f64(b, 48));
+    a = ra;
+    b = rb;
+}
+
 template <int EPL>
 __device__ __forceinline__ void topk_token(const double (&lg)[EPL], int64_t t, int E, int K, int score,
                                            int renorm, double route_scale, const float* __restrict__ bias,
                                            bool kept, int32_t* __restrict__ ids_out, float* __restrict__ w_out,
-                                           const int32_t* __restrict__ given) {
+                                           const int32_t* __restrict__ given, int n_group, int topk_group) {
     const int lane = lane_id();
     if (given != nullptr && kept) {
         const int g = lane < K ? given[t * K + lane] : 0;
@@ -248,18 +278,57 @@ __device__ __forceinline__ void topk_token(const double (&lg)[EPL], int64_t t, i
         const double z = wave_sum_f64(part);
 #pragma unroll
         for (int i = 0; i < EPL; ++i) s[i] = s[i] / z;
-    } else {  // logistic sigmoid of each logit
+    } else {  // sigmoid or sqrtsoftplus of each logit
 #pragma unroll
-        for (int i = 0; i < EPL; ++i) s[i] = ok[i] ? 1.0 / (1.0 + exp(-lg[i])) : 0.0;
+        for (int i = 0; i < EPL; ++i) s[i] = ok[i] ? elem_score(lg[i], score) : 0.0;
     }
 
     uint64_t key[EPL];
+    double ch[EPL];
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
         const int e = lane + 64 * i;
         double c = s[i];
         if (bias != nullptr && ok[i]) c += static_cast<double>(bias[e]);
+        ch[i] = c;
         key[i] = ok[i] ? choice_key(c, e) : 0ull;
+    }
+
+    // Group-limited select: group g holds experts g*gs .. g*gs+gs-1; its
+    // score is the sum of its two largest choices; the topk_group best
+    // groups are kept (ties to the lower group id) and the others' experts
+    // leave the race.
+    if (given == nullptr && n_group > 1) {
+        const int gs = E / n_group;
+        double gsc = 0.0;  // lane g: the score of group g
+        for (int g = 0; g < n_group; ++g) {
+            double a = -INFINITY, b = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < EPL; ++i) {
+                if (ok[i] && (lane + 64 * i) / gs == g) {
+                    const double v = ch[i];
+                    if (v > a) {
+                        b = a;
+                        a = v;
+                    } else if (v > b) {
+                        b = v;
+                    }
+                }
+            }
+            wave_top2_f64(a, b);
+            if (lane == g) gsc = a + b;
+        }
+        uint64_t gkey = lane < n_group ? choice_key(gsc, lane) : 0ull;
+        uint64_t keep = 0ull;
+        for (int r = 0; r < topk_group; ++r) {
+            const uint64_t win = wave_max_u64(gkey);
+            const int g = 1023 - static_cast<int>(win & 0x3FFull);
+            keep |= 1ull << g;
+            if (lane == g) gkey = 0ull;
+        }
+#pragma unroll
+        for (int i = 0; i < EPL; ++i)
+            if (ok[i] && ((keep >> ((lane + 64 * i) / gs)) & 1ull) == 0ull) key[i] = 0ull;
     }
 
     // K rounds of wave argmax; lane r keeps the r-th pick
@@ -577,7 +646,7 @@ __device__ __forceinline__ void select_rows16(const double (&lg)[P][EPL16], int 
 #pragma unroll
         for (int p = 0; p < P; ++p)
 #pragma unroll
-            for (int i = 0; i < EPL16; ++i) s[p][i] = ok[i] ? 1.0 / (1.0 + exp(-lg[p][i])) : 0.0;
+            for (int i = 0; i < EPL16; ++i) s[p][i] = ok[i] ? elem_score(lg[p][i], score) : 0.0;
     }
 
     uint64_t key[P][EPL16];
@@ -647,7 +716,7 @@ __global__ __launch_bounds__(256) void topk_kernel(
     const double* __restrict__ logits, int64_t T, int E, int K, int score, int renorm,
     double route_scale, const float* __restrict__ bias, const uint8_t* __restrict__ mask,
     float* __restrict__ logits_out, int32_t* __restrict__ ids_out, float* __restrict__ w_out,
-    const int32_t* __restrict__ given) {
+    const int32_t* __restrict__ given, int n_group, int topk_group) {
     const int lane = lane_id();
     const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
     if (t >= T) return;  // uniform per wave
@@ -660,7 +729,7 @@ __global__ __launch_bounds__(256) void topk_kernel(
         if (logits_out && e < E) logits_out[t * E + e] = static_cast<float>(lg[i]);
     }
     const bool kept = (mask == nullptr) || (mask[t] != 0);
-    topk_token<EPL>(lg, t, E, K, score, renorm, route_scale, bias, kept, ids_out, w_out, given);
+    topk_token<EPL>(lg, t, E, K, score, renorm, route_scale, bias, kept, ids_out, w_out, given, n_group, topk_group);
 }
 
 // ---------------------------------------------------------------------------
@@ -751,7 +820,7 @@ __device__ __forceinline__ void route_topk_pass(const __attribute__((address_spa
                 if (logits_out && e < E) logits_out[t * E + e] = static_cast<float>(lg[i]);
             }
             const bool kept = (mask == nullptr) || (mask[t] != 0);
-            topk_token<RT::EPL>(lg, t, E, K, score, renorm, route_scale, bias, kept, ids_out, w_out, nullptr);
+            topk_token<RT::EPL>(lg, t, E, K, score, renorm, route_scale, bias, kept, ids_out, w_out, nullptr, 1, 1);
         }
     }
 }
@@ -920,13 +989,13 @@ hipError_t launch_router_logits(const void* x, const void* router, int64_t T, in
 }
 
 hipError_t launch_topk(const double* logits64, int64_t T, int E, int K, int score, int renorm,
-                       float route_scale, const float* bias, const uint8_t* mask,
+                       float route_scale, int n_group, int topk_group, const float* bias, const uint8_t* mask,
                        float* logits_out, int32_t* ids, float* w, hipStream_t stream, const int32_t* given) {
     const unsigned grid = static_cast<unsigned>((T + 3) / 4);
     const double rs = static_cast<double>(route_scale);
 #define MOE_TOPK(EPL)                                                                                   \
     topk_kernel<EPL><<<grid, 256, 0, stream>>>(logits64, T, E, K, score, renorm, rs, bias, mask, \
-                                                logits_out, ids, w, given)
+                                                logits_out, ids, w, given, n_group, topk_group)
     if (E <= 64) MOE_TOPK(1);
     else if (E <= 128) MOE_TOPK(2);
     else if (E <= 256) MOE_TOPK(4);
@@ -936,16 +1005,17 @@ hipError_t launch_topk(const double* logits64, int64_t T, int E, int K, int scor
     return hipGetLastError();
 }
 
-bool route_fused(int E, int dtype) { return dtype == 0 && E <= 512; }
+bool route_fused(int E, int dtype, int n_group) { return dtype == 0 && E <= 512 && n_group <= 1; }
 
 hipError_t launch_route(const void* x, const void* router, int64_t T, int D, int E, int K, int dtype,
-                        int score, int renorm, float route_scale, const float* bias, const uint8_t* mask,
-                        double* logits64, float* logits_out, int32_t* ids, float* w, hipStream_t stream) {
-    if (!route_fused(E, dtype)) {
+                        int score, int renorm, float route_scale, int n_group, int topk_group, const float* bias,
+                        const uint8_t* mask, double* logits64, float* logits_out, int32_t* ids, float* w,
+                        hipStream_t stream) {
+    if (!route_fused(E, dtype, n_group)) {
         hipError_t err = launch_router_logits(x, router, T, D, E, dtype, logits64, stream);
         if (err != hipSuccess) return err;
-        return launch_topk(logits64, T, E, K, score, renorm, route_scale, bias, mask, logits_out, ids, w, stream,
-                           nullptr);
+        return launch_topk(logits64, T, E, K, score, renorm, route_scale, n_group, topk_group, bias, mask,
+                           logits_out, ids, w, stream, nullptr);
     }
     const double rs = static_cast<double>(route_scale);
     const uint16_t* xb = static_cast<const uint16_t*>(x);
@@ -972,8 +1042,8 @@ hipError_t launch_route_replay(const void* x, const void* router, int64_t T, int
                                hipStream_t stream) {
     hipError_t err = launch_router_logits(x, router, T, D, E, dtype, logits64, stream);
     if (err != hipSuccess) return err;
-    return launch_topk(logits64, T, E, K, score, renorm, route_scale, nullptr, mask, logits_out, ids, w, stream,
-                       given);
+    return launch_topk(logits64, T, E, K, score, renorm, route_scale, 1, 1, nullptr, mask, logits_out, ids, w,
+                       stream, given);
 }
 
 }  // namespace moe

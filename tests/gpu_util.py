@@ -33,7 +33,8 @@ def make_layer(inp: LayerInputs):
     from routing_grouped_gemm_gemv_amd import MoeLayer, Shape
     cfg = inp.cfg
     shape = Shape(T=cfg.T, D=cfg.D, E=cfg.E, K=cfg.K, I=cfg.I, Is=cfg.Is, score=cfg.score,
-                  renorm=cfg.renorm, route_scale=cfg.route_scale, dtype=cfg.dtype)
+                  renorm=cfg.renorm, route_scale=cfg.route_scale, dtype=cfg.dtype,
+                  n_group=cfg.n_group, topk_group=cfg.topk_group)
     return MoeLayer(shape, to_dev(inp.w_router), to_dev(inp.w_gate_up), to_dev(inp.w_down),
                     to_dev(inp.w_gate_up_s), to_dev(inp.w_down_s), to_dev(inp.bias))
 

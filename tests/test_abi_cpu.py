@@ -33,10 +33,12 @@ def test_library_exports_every_declared_symbol():
 
 
 def _shape(**kw):
-    base = dict(T=64, D=128, E=8, K=2, I=256, Is=0, score=0, renorm=1, route_scale=1.0, dtype=0, combine=0)
+    base = dict(T=64, D=128, E=8, K=2, I=256, Is=0, score=0, renorm=1, route_scale=1.0, dtype=0, combine=0,
+                n_group=0, topk_group=0)
     base.update(kw)
     return B._Shape(base["T"], base["D"], base["E"], base["K"], base["I"], base["Is"], base["score"],
-                    base["renorm"], base["route_scale"], base["dtype"], base["combine"])
+                    base["renorm"], base["route_scale"], base["dtype"], base["combine"], base["n_group"],
+                    base["topk_group"])
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -44,7 +46,17 @@ def _shape(**kw):
     (dict(T=-1), B.MOE_ERR_INVALID),
     (dict(D=0), B.MOE_ERR_INVALID),
     (dict(K=9), B.MOE_ERR_INVALID),
-    (dict(score=2), B.MOE_ERR_INVALID),
+    (dict(score=2), B.MOE_OK),
+    (dict(score=3), B.MOE_ERR_INVALID),
+    (dict(n_group=1, topk_group=0), B.MOE_OK),
+    (dict(n_group=4, topk_group=2), B.MOE_OK),
+    (dict(n_group=4, topk_group=2, K=5), B.MOE_ERR_INVALID),
+    (dict(n_group=4, topk_group=0), B.MOE_ERR_INVALID),
+    (dict(n_group=4, topk_group=5), B.MOE_ERR_INVALID),
+    (dict(n_group=3, topk_group=1), B.MOE_ERR_INVALID),
+    (dict(n_group=8, topk_group=2), B.MOE_ERR_INVALID),
+    (dict(n_group=-1), B.MOE_ERR_INVALID),
+    (dict(E=256, n_group=128, topk_group=4), B.MOE_ERR_UNSUPPORTED),
     (dict(dtype=3), B.MOE_ERR_INVALID),
     (dict(renorm=2), B.MOE_ERR_INVALID),
     (dict(combine=2), B.MOE_ERR_INVALID),
