@@ -194,7 +194,7 @@ def main():
     stream = torch.cuda.current_stream()
     tr = layer.new_trace(shape)
     B = moe.binding
-    sh_shape = shape.replace(E=1, K=1, I=cfg.Is, Is=0) if cfg.Is else None
+    sh_shape = shape.replace(E=1, K=1, I=cfg.Is, Is=0, n_group=1, topk_group=1) if cfg.Is else None
     names = ["route", "permute", "experts_routed"] + (["experts_shared"] if cfg.Is else []) + ["combine"]
 
     def run_stages(evs):

@@ -480,10 +480,11 @@ __device__ __forceinline__ void write_picks16(const int (&my_e)[P], const double
     }
 }
 
-// Sigmoid scores, screened: the same picks and scores as select_rows16, with
-// float64 scores computed only for the few experts that can be picked.
-// Every choice c = sigmoid(l) + bias is first evaluated in float32 (c32,
-// within 1e-6 + 1e-7 |c| of the float64 value, far inside the margin below).
+// Elementwise scores (sigmoid, sqrtsoftplus), screened: the same picks and
+// scores as select_rows16, with float64 scores computed only for the few
+// experts that can be picked.  Every choice c = score(l) + bias is first
+// evaluated in float32 (c32, within about 1e-6 + 1e-7 |c| of the float64
+// value, far inside the margin below).
 // mu, the K-th largest of the 16 lanes' largest c32, is at most the K-th
 // largest c32 (K lanes hold a value >= mu), so every expert the float64
 // choice can pick has c32 >= mu - margin.  Those candidates are compacted
@@ -492,7 +493,7 @@ __device__ __forceinline__ void write_picks16(const int (&my_e)[P], const double
 // K rounds of row argmax pick among them.  Returns false, with no picks,
 // when a row of the wave has more than 16 candidates.
 template <int EPL16, int P>
-__device__ __forceinline__ bool select_rows16_screened(const double (&lg)[P][EPL16], int E, int K,
+__device__ __forceinline__ bool select_rows16_screened(const double (&lg)[P][EPL16], int E, int K, int score,
                                                        const float* __restrict__ bias, lds_u8* scr, int (&my_e)[P],
                                                        double (&my_s)[P]) {
     const int lane = lane_id();
@@ -513,8 +514,11 @@ __device__ __forceinline__ bool select_rows16_screened(const double (&lg)[P][EPL
         float c32[EPL16];
 #pragma unroll
         for (int i = 0; i < EPL16; ++i) {
-            const float e = __expf(-static_cast<float>(lg[p][i]));
-            c32[i] = ok[i] ? __builtin_amdgcn_rcpf(1.0f + e) + bv[i] : -INFINITY;
+            const float l = static_cast<float>(lg[p][i]);
+            float sc32;
+            if (score == 2) sc32 = sqrtf(fmaxf(l, 0.0f) + log1pf(__expf(-fabsf(l))));
+            else sc32 = __builtin_amdgcn_rcpf(1.0f + __expf(-l));
+            c32[i] = ok[i] ? sc32 + bv[i] : -INFINITY;
         }
         float m[EPL16];
 #pragma unroll
@@ -567,7 +571,7 @@ __device__ __forceinline__ bool select_rows16_screened(const double (&lg)[P][EPL
             const double l = *reinterpret_cast<const __attribute__((address_space(3))) double*>(sl);
             const int e = *reinterpret_cast<const __attribute__((address_space(3))) int*>(sl + 8);
             const float b = *reinterpret_cast<const __attribute__((address_space(3))) float*>(sl + 12);
-            sc[p] = 1.0 / (1.0 + exp(-l));
+            sc[p] = elem_score(l, score);
             double c = sc[p];
             if (bias != nullptr) c += static_cast<double>(b);
             key[p] = choice_key(c, e);
@@ -780,9 +784,11 @@ __device__ __forceinline__ void route_topk_pass(const __attribute__((address_spa
     const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
     const int64_t t0 = tp;
     if constexpr (RT::EMAX <= 256) {
-        // eight tokens per wave at a time: two per row of sixteen lanes
+        // P tokens per row of sixteen lanes at a time
         constexpr int EPL16 = RT::EMAX / 16;
-        constexpr int P = 2;
+        // two tokens per row where registers allow; the 128-token tile holds
+        // the other pass's logits in registers meanwhile
+        constexpr int P = RT::TB > RT::TBP ? 1 : 2;
         static_assert(RT::TBP % (16 * P) == 0, "tokens per wave pass");
         for (int tb = 4 * P * wv; tb < RT::TBP; tb += 16 * P) {
             double lg[P][EPL16];
@@ -804,7 +810,7 @@ __device__ __forceinline__ void route_topk_pass(const __attribute__((address_spa
             lds_u8* scr = scr_base + wv * (P * 64 * 16);
             int my_e[P];
             double my_s[P];
-            if (score != 1 || !select_rows16_screened<EPL16, P>(lg, E, K, bias, scr, my_e, my_s))
+            if (score == 0 || !select_rows16_screened<EPL16, P>(lg, E, K, score, bias, scr, my_e, my_s))
                 select_rows16<EPL16, P>(lg, E, K, score, bias, my_e, my_s);
             write_picks16<P>(my_e, my_s, t, live, kept, K, renorm, route_scale, ids_out, w_out);
         }

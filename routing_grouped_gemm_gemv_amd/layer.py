@@ -80,7 +80,7 @@ class MoeLayer:
                       tr["y"], ws)
         shared = None
         if shape.Is > 0:
-            sh_shape = shape.replace(E=1, K=1, I=shape.Is, Is=0)
+            sh_shape = shape.replace(E=1, K=1, I=shape.Is, Is=0, n_group=1, topk_group=1)
             B.moe_experts(sh_shape, x, None, None, self.weights["gate_up_shared"], self.weights["down_shared"],
                           tr["shared_out"], ws)
             shared = tr["shared_out"]
