@@ -29,9 +29,13 @@ Pins (the tests that tie each function to something other than itself):
                      720-order enumeration (360 classes) printed by the arXiv abstract
   combine_f64        exact rational sum rounded once (bf16 and float32); all 720
                      orders of six terms give one result
+  backward           torch.autograd in float64 of an independently written
+                     forward (straight-through bf16 rounding), every gradient;
+                     masked tokens get none
 No function is parity-unpinned.
 """
 
+from .backward import backward
 from .moe import (
     EXEMPT_REL_MARGIN,
     OracleResult,
@@ -54,6 +58,7 @@ from .moe import (
 
 __all__ = [
     "EXEMPT_REL_MARGIN",
+    "backward",
     "OracleResult",
     "bf16_bits_of",
     "combine_f64",

@@ -550,3 +550,109 @@ def test_combine_f64_masked_and_unit_weight():
     inv[3, 0] = -1
     out = oracle.combine_f64(y, inv, np.ones((10, 1), np.float32), out="f32")
     assert np.all(out[3] == 0)
+
+
+# ---------------------------------------------------------------- backward
+
+def _autograd_grads(x, wr, w1, w2, w1s, w2s, ids, G, score, renorm, rs, mask, bf16_mode):
+    """An independently written forward in float64 torch, differentiated by
+    autograd; bf16 rounding points pass the gradient straight through."""
+    F = torch.nn.functional
+    tt = lambda a: torch.tensor(oracle.widen(a), dtype=torch.float64, requires_grad=True)
+    X, Wr, W1, W2 = tt(x), tt(wr), tt(w1), tt(w2)
+    W1s = tt(w1s) if w1s is not None else None
+    W2s = tt(w2s) if w2s is not None else None
+
+    def rnd(v):
+        if not bf16_mode:
+            return v
+        r = torch.from_numpy(oracle.round_bf16(v.detach().numpy()))
+        return v + (r - v).detach()
+
+    logits = X @ Wr.T
+    if score == "softmax":
+        s = torch.softmax(logits, dim=1)
+    elif score == "sigmoid":
+        s = torch.sigmoid(logits)
+    else:
+        s = torch.sqrt(F.softplus(logits))
+    T, K = ids.shape
+    I = w2.shape[2]
+    out = []
+    for t in range(T):
+        if mask is not None and not mask[t]:
+            out.append(torch.zeros(X.shape[1], dtype=torch.float64))
+            continue
+        sel = torch.stack([s[t, int(e)] for e in ids[t]])
+        w = sel / sel.sum() * rs if renorm else sel * rs
+        o = 0.0
+        for j, e in enumerate(ids[t]):
+            h = W1[int(e)] @ X[t]
+            a = rnd(F.silu(h[:I]) * h[I:])
+            o = o + w[j] * rnd(W2[int(e)] @ a)
+        if W1s is not None:
+            Is = w2s.shape[1]
+            hs = W1s @ X[t]
+            o = o + rnd(W2s @ rnd(F.silu(hs[:Is]) * hs[Is:]))
+        out.append(o)
+    loss = (torch.stack(out) * torch.from_numpy(oracle.widen(G))).sum()
+    loss.backward()
+    g = {"dx": X.grad, "d_router": Wr.grad, "d_gate_up": W1.grad, "d_down": W2.grad}
+    if W1s is not None:
+        g.update({"d_gate_up_shared": W1s.grad, "d_down_shared": W2s.grad})
+    return {k: v.numpy() for k, v in g.items()}
+
+
+@pytest.mark.parametrize("score,renorm,bf16,shared,masked", [
+    ("softmax", True, False, False, False),
+    ("sigmoid", True, True, True, True),
+    ("sqrtsoftplus", False, False, True, False),
+    ("sigmoid", False, True, False, True),
+    ("sqrtsoftplus", True, True, True, True),
+])
+def test_backward_matches_torch_autograd(score, renorm, bf16, shared, masked):
+    rng = np.random.default_rng(31)
+    T, D, E, K, I, Is = 12, 32, 8, 3, 16, 16
+    f = (lambda a: oracle.round_bf16(a)) if bf16 else (lambda a: a)
+    x = f(rng.standard_normal((T, D)))
+    wr = f(rng.standard_normal((E, D)) * 0.3)
+    w1 = f(rng.standard_normal((E, 2 * I, D)) * 0.2)
+    w2 = f(rng.standard_normal((E, D, I)) * 0.2)
+    w1s = f(rng.standard_normal((2 * Is, D)) * 0.2) if shared else None
+    w2s = f(rng.standard_normal((D, Is)) * 0.2) if shared else None
+    G = f(rng.standard_normal((T, D)))
+    mask = (rng.random(T) > 0.25).astype(np.uint8) if masked else None
+    bias = rng.uniform(-0.05, 0.05, E).astype(np.float32)
+    fw = oracle.forward(x, wr, w1, w2, K=K, score=score, renorm=renorm, route_scale=1.5, bias=bias, mask=mask,
+                        shared_gate_up=w1s, shared_down=w2s, bf16_mode=bf16)
+    got = oracle.backward(x, wr, w1, w2, G, fw.ids, score=score, renorm=renorm, route_scale=1.5, mask=mask,
+                          shared_gate_up=w1s, shared_down=w2s, bf16_mode=bf16)
+    ids_full = np.where(fw.ids >= 0, fw.ids, 0)
+    ref = _autograd_grads(x, wr, w1, w2, w1s, w2s, ids_full, G, score, renorm, 1.5,
+                          None if mask is None else mask.astype(bool), bf16)
+    for k, v in ref.items():
+        scale = max(1e-300, float(np.abs(v).max()))
+        assert np.max(np.abs(got[k] - v)) <= 1e-11 * scale, k
+    if mask is not None:
+        assert np.all(got["dx"][~mask.astype(bool)] == 0)
+    # the weight gradient dw is the inner product of G with the bf16 expert output the combine used
+    t, j = np.argwhere(fw.ids >= 0)[0]
+    p = fw.inv_pos[t, j]
+    assert abs(got["dw"][t, j] - float(np.dot(oracle.widen(G)[t], fw.y[p]))) <= 1e-12 * (1 + abs(got["dw"][t, j]))
+
+
+def test_backward_of_unpicked_expert_is_zero():
+    rng = np.random.default_rng(32)
+    T, D, E, K, I = 6, 16, 8, 1, 8
+    x = rng.standard_normal((T, D))
+    wr = rng.standard_normal((E, D))
+    w1 = rng.standard_normal((E, 2 * I, D))
+    w2 = rng.standard_normal((E, D, I))
+    ids = np.array([[0], [0], [1], [1], [2], [0]], dtype=np.int32)
+    g = oracle.backward(x, wr, w1, w2, rng.standard_normal((T, D)), ids, score="sigmoid", renorm=False,
+                        route_scale=1.0, bf16_mode=False)
+    assert np.all(g["d_gate_up"][3:] == 0) and np.all(g["d_down"][3:] == 0)
+    # sigmoid scores: only the picked experts' logits receive a gradient
+    picked = np.zeros((T, E), bool)
+    picked[np.arange(T), ids[:, 0]] = True
+    assert np.all(g["dlogits"][~picked] == 0) and np.all(g["dlogits"][picked] != 0)
