@@ -15,6 +15,14 @@ hidden states and weights, given the gradient G of the layer output, with
     output y feeds the weight gradient;
   * masked tokens contributing nothing and receiving zero.
 
+With ``grad_bf16`` the gradient operands that a bf16 GEMM would consume are
+rounded to bf16 where they are formed: dY (the expert-output gradients), dH
+(the gradient of the gate/up projections) and dl (the logits' gradient).  The
+pages fix no precision for the backward; this option mirrors an
+implementation that feeds those operands to bf16 matrix products, so that a
+comparison with one isolates its accumulation order.  Without it every
+gradient is the exact float64 one.
+
 Everything is float64 (numpy matmul as the only library primitive).
 
 For a kept token t with picks j (expert e_j, pair row p_j, weight w_j):
@@ -94,7 +102,7 @@ def score_grad(logits: np.ndarray, s: np.ndarray, ds: np.ndarray, score: str) ->
 
 
 def expert_mlp_backward(x64: np.ndarray, w1: np.ndarray, w2: np.ndarray, dy: np.ndarray,
-                        bf16_mode: bool):
+                        bf16_mode: bool, grad_bf16: bool = False):
     """(dx [n, D], dW1 [2I, D], dW2 [D, I]) of one SwiGLU expert over the rows x64."""
     w1_64 = widen(w1)
     w2_64 = widen(w2)
@@ -109,6 +117,8 @@ def expert_mlp_backward(x64: np.ndarray, w1: np.ndarray, w2: np.ndarray, dy: np.
     dg = da * u * silu_grad(g)
     du = da * silu(g)
     dh = np.concatenate([dg, du], axis=1)
+    if grad_bf16:
+        dh = round_bf16(dh)
     return dh @ w1_64, dh.T @ x64, dW2
 
 
@@ -118,7 +128,7 @@ def backward(x: np.ndarray, w_router: np.ndarray,
              G: np.ndarray, ids: np.ndarray, *, score: str, renorm: bool, route_scale: float,
              mask: Optional[np.ndarray] = None,
              shared_gate_up: Optional[np.ndarray] = None, shared_down: Optional[np.ndarray] = None,
-             bf16_mode: bool) -> Dict[str, np.ndarray]:
+             bf16_mode: bool, grad_bf16: bool = False) -> Dict[str, np.ndarray]:
     """Gradients of the layer given the output gradient G [T, D] and the picks
     ``ids`` [T, K] (ascending, -1 for masked tokens).
 
@@ -160,19 +170,24 @@ def backward(x: np.ndarray, w_router: np.ndarray,
         xe = x64[t_rows]
         ye = expert_mlp(xe, get1(e), get2(e), bf16_mode)  # the y the combine used
         dy = w[t_rows, j_cols][:, None] * G64[t_rows]
+        if grad_bf16:
+            dy = round_bf16(dy)
         dw[t_rows, j_cols] = np.sum(G64[t_rows] * ye, axis=1)
-        dxe, d_gate_up[e], d_down[e] = expert_mlp_backward(xe, get1(e), get2(e), dy, bf16_mode)
+        dxe, d_gate_up[e], d_down[e] = expert_mlp_backward(xe, get1(e), get2(e), dy, bf16_mode, grad_bf16)
         np.add.at(dx, t_rows, dxe)
 
     d_gate_up_s = d_down_s = None
     if shared_gate_up is not None:
+        dys = round_bf16(G64[valid]) if grad_bf16 else G64[valid]
         dxs, d_gate_up_s, d_down_s = expert_mlp_backward(x64[valid], shared_gate_up, shared_down,
-                                                          G64[valid], bf16_mode)
+                                                          dys, bf16_mode, grad_bf16)
         dx[valid] += dxs
 
     ds = weights_grad(s, ids, dw, renorm, route_scale)
     dl = score_grad(logits, s, ds, score)
     dl[~valid] = 0.0
+    if grad_bf16:
+        dl = round_bf16(dl)
     dx += dl @ wr64
     d_router = dl.T @ x64
     dx[~valid] = 0.0

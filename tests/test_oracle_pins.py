@@ -554,10 +554,25 @@ def test_combine_f64_masked_and_unit_weight():
 
 # ---------------------------------------------------------------- backward
 
-def _autograd_grads(x, wr, w1, w2, w1s, w2s, ids, G, score, renorm, rs, mask, bf16_mode):
+class _RoundGrad(torch.autograd.Function):
+    """Identity whose backward rounds the incoming gradient to bf16."""
+
+    @staticmethod
+    def forward(ctx, v):
+        return v.view_as(v)
+
+    @staticmethod
+    def backward(ctx, g):
+        return torch.from_numpy(oracle.round_bf16(g.detach().numpy()))
+
+
+def _autograd_grads(x, wr, w1, w2, w1s, w2s, ids, G, score, renorm, rs, mask, bf16_mode, grad_bf16=False):
     """An independently written forward in float64 torch, differentiated by
-    autograd; bf16 rounding points pass the gradient straight through."""
+    autograd; bf16 rounding points pass the gradient straight through.  With
+    grad_bf16 the gradients arriving at the logits, at each expert's gate/up
+    projection and at each routed expert output are rounded to bf16."""
     F = torch.nn.functional
+    gr = _RoundGrad.apply if grad_bf16 else (lambda v: v)
     tt = lambda a: torch.tensor(oracle.widen(a), dtype=torch.float64, requires_grad=True)
     X, Wr, W1, W2 = tt(x), tt(wr), tt(w1), tt(w2)
     W1s = tt(w1s) if w1s is not None else None
@@ -569,7 +584,7 @@ def _autograd_grads(x, wr, w1, w2, w1s, w2s, ids, G, score, renorm, rs, mask, bf
         r = torch.from_numpy(oracle.round_bf16(v.detach().numpy()))
         return v + (r - v).detach()
 
-    logits = X @ Wr.T
+    logits = gr(X @ Wr.T)
     if score == "softmax":
         s = torch.softmax(logits, dim=1)
     elif score == "sigmoid":
@@ -587,12 +602,12 @@ def _autograd_grads(x, wr, w1, w2, w1s, w2s, ids, G, score, renorm, rs, mask, bf
         w = sel / sel.sum() * rs if renorm else sel * rs
         o = 0.0
         for j, e in enumerate(ids[t]):
-            h = W1[int(e)] @ X[t]
+            h = gr(W1[int(e)] @ X[t])
             a = rnd(F.silu(h[:I]) * h[I:])
-            o = o + w[j] * rnd(W2[int(e)] @ a)
+            o = o + w[j] * gr(rnd(W2[int(e)] @ a))
         if W1s is not None:
             Is = w2s.shape[1]
-            hs = W1s @ X[t]
+            hs = gr(W1s @ X[t])
             o = o + rnd(W2s @ rnd(F.silu(hs[:Is]) * hs[Is:]))
         out.append(o)
     loss = (torch.stack(out) * torch.from_numpy(oracle.widen(G))).sum()
@@ -603,14 +618,17 @@ def _autograd_grads(x, wr, w1, w2, w1s, w2s, ids, G, score, renorm, rs, mask, bf
     return {k: v.numpy() for k, v in g.items()}
 
 
-@pytest.mark.parametrize("score,renorm,bf16,shared,masked", [
-    ("softmax", True, False, False, False),
-    ("sigmoid", True, True, True, True),
-    ("sqrtsoftplus", False, False, True, False),
-    ("sigmoid", False, True, False, True),
-    ("sqrtsoftplus", True, True, True, True),
+@pytest.mark.parametrize("score,renorm,bf16,shared,masked,grad_bf16", [
+    ("softmax", True, False, False, False, False),
+    ("sigmoid", True, True, True, True, False),
+    ("sqrtsoftplus", False, False, True, False, False),
+    ("sigmoid", False, True, False, True, False),
+    ("sqrtsoftplus", True, True, True, True, False),
+    ("softmax", True, True, True, False, True),
+    ("sigmoid", True, True, True, True, True),
+    ("sqrtsoftplus", False, True, False, False, True),
 ])
-def test_backward_matches_torch_autograd(score, renorm, bf16, shared, masked):
+def test_backward_matches_torch_autograd(score, renorm, bf16, shared, masked, grad_bf16):
     rng = np.random.default_rng(31)
     T, D, E, K, I, Is = 12, 32, 8, 3, 16, 16
     f = (lambda a: oracle.round_bf16(a)) if bf16 else (lambda a: a)
@@ -626,15 +644,20 @@ def test_backward_matches_torch_autograd(score, renorm, bf16, shared, masked):
     fw = oracle.forward(x, wr, w1, w2, K=K, score=score, renorm=renorm, route_scale=1.5, bias=bias, mask=mask,
                         shared_gate_up=w1s, shared_down=w2s, bf16_mode=bf16)
     got = oracle.backward(x, wr, w1, w2, G, fw.ids, score=score, renorm=renorm, route_scale=1.5, mask=mask,
-                          shared_gate_up=w1s, shared_down=w2s, bf16_mode=bf16)
+                          shared_gate_up=w1s, shared_down=w2s, bf16_mode=bf16, grad_bf16=grad_bf16)
     ids_full = np.where(fw.ids >= 0, fw.ids, 0)
     ref = _autograd_grads(x, wr, w1, w2, w1s, w2s, ids_full, G, score, renorm, 1.5,
-                          None if mask is None else mask.astype(bool), bf16)
+                          None if mask is None else mask.astype(bool), bf16, grad_bf16)
     for k, v in ref.items():
         scale = max(1e-300, float(np.abs(v).max()))
         assert np.max(np.abs(got[k] - v)) <= 1e-11 * scale, k
     if mask is not None:
         assert np.all(got["dx"][~mask.astype(bool)] == 0)
+    if grad_bf16:  # the rounding is exercised: the exact gradients differ
+        exact = oracle.backward(x, wr, w1, w2, G, fw.ids, score=score, renorm=renorm, route_scale=1.5, mask=mask,
+                                shared_gate_up=w1s, shared_down=w2s, bf16_mode=bf16)
+        for k in ("dx", "d_router", "d_gate_up", "d_down"):
+            assert not np.array_equal(exact[k], got[k]), k
     # the weight gradient dw is the inner product of G with the bf16 expert output the combine used
     t, j = np.argwhere(fw.ids >= 0)[0]
     p = fw.inv_pos[t, j]
