@@ -147,8 +147,8 @@ moe_status moe_workspace_size(const moe_shape* shape, size_t* bytes);
 /* Routing (RL-Kernel roadmap, Problem 1 and the routing boundary of Problem 2;
  * SpecForge pull request #1003, commit notes on the router).
  *   logits[t,e] = sum_d x[t,d] * router[e,d], accumulated in float64 from
- *   float32 partial sums of 64 products each (bf16 mode) or in float64 (f32 mode);
- *   s = softmax over e, or sigmoid, in float64;
+ *   float32 partial sums of 128 products each (bf16 mode) or in float64 (f32 mode);
+ *   s = softmax over e, sigmoid or sqrtsoftplus, in float64;
  *   choice = s + sel_bias[e] (sel_bias may be NULL);
  *   the K experts with the largest choice are selected, ties to the lower id;
  *   topk_ids[t,:] lists them in ascending id order;
@@ -236,6 +236,54 @@ moe_status moe_route_replay(const moe_shape* shape, const void* x, const void* r
 moe_status moe_forward_replay(const moe_shape* shape, const moe_weights* weights, const void* x,
                               const int32_t* replay_ids, const uint8_t* mask, int32_t out_dtype, void* out,
                               const moe_trace* trace, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Gradients of one layer (device pointers, float32, row-major; the shared
+ * ones are used only when Is > 0).
+ *   dx               [T, D]
+ *   d_router         [E, D]
+ *   d_gate_up        [E, 2I, D]
+ *   d_down           [E, D, I]
+ *   d_gate_up_shared [2Is, D]
+ *   d_down_shared    [D, Is] */
+typedef struct {
+    float* dx;
+    float* d_router;
+    float* d_gate_up;
+    float* d_down;
+    float* d_gate_up_shared;
+    float* d_down_shared;
+} moe_grads;
+
+/* Workspace bytes moe_backward needs for this shape (host-only). */
+moe_status moe_backward_workspace_size(const moe_shape* shape, size_t* bytes);
+
+/* Backward of the layer (RL-Kernel roadmap: the scope list names forward +
+ * backward with a deterministic reduction order; the issue-bucket table asks
+ * for a single-GPU forward + backward).  Read as the gradients of moe_forward
+ * with the top-k selection fixed (the selection bias gets none) and the bf16
+ * rounding points passed straight through, given dout = dL/d(out) [T, D] in
+ * the operand dtype:
+ *   dY_p = bf16(w_j dout_t); dw_j = <dout_t, y_p> (float64);
+ *   per expert (gate_up rows H recomputed in float32):
+ *     dA = dY W2_e; dH = [dA u silu'(g), dA silu(g)] (bf16);
+ *     dW2_e = dY_e^T A_e (A: the forward's bf16 activation); dX_e = dH W1_e;
+ *     dW1_e = dH_e^T X_e;
+ *   the shared expert likewise with dY = dout on kept tokens;
+ *   router: the weights' gradient through renormalisation and route_scale,
+ *     then through the score function, to dl [T, E] (bf16 operand);
+ *     dx += dl W_r; d_router = dl^T x;
+ *   dx_t = sum of the token's routed dX rows in ascending expert id, then the
+ *     shared and the router terms, in float32; masked tokens get dx = 0.
+ * bf16 operands only, and T*K/128 + E <= 65535 (MOE_ERR_UNSUPPORTED
+ * otherwise); float32 accumulation.  Every reduction has a fixed order and no atomics: repeated calls give the
+ * same bits, and dx of a token does not depend on the other tokens.
+ * fwd: the trace of the moe_forward call being differentiated, with
+ * topk_ids, topk_w, offsets, perm_token, inv_pos and y set (the other fields
+ * are not read).  Every pointer of grads is written in full (experts no token
+ * picked get zero gradients).  ws: moe_backward_workspace_size() bytes. */
+moe_status moe_backward(const moe_shape* shape, const moe_weights* weights, const void* x, const uint8_t* mask,
+                        const moe_trace* fwd, const void* dout, const moe_grads* grads, void* ws, size_t ws_bytes,
+                        hipStream_t stream);
 
 /* Static text for a status code. */
 const char* moe_status_string(moe_status status);

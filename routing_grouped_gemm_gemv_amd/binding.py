@@ -34,6 +34,8 @@ EXPORTED = (
     "moe_forward",
     "moe_route_replay",
     "moe_forward_replay",
+    "moe_backward_workspace_size",
+    "moe_backward",
     "moe_status_string",
     "moe_last_error",
 )
@@ -65,6 +67,11 @@ class _Shape(ctypes.Structure):
 
 class _Weights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("router", "gate_up", "down", "gate_up_shared", "down_shared")]
+
+
+class _Grads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("dx", "d_router", "d_gate_up", "d_down", "d_gate_up_shared",
+                                                  "d_down_shared")]
 
 
 class _Trace(ctypes.Structure):
@@ -132,8 +139,11 @@ def lib() -> ctypes.CDLL:
     L.moe_route_replay.argtypes = [S, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     L.moe_forward_replay.argtypes = [S, ctypes.POINTER(_Weights), P, P, P, ctypes.c_int32, P,
                                      ctypes.POINTER(_Trace), P, ctypes.c_size_t, P]
+    L.moe_backward_workspace_size.argtypes = [S, ctypes.POINTER(ctypes.c_size_t)]
+    L.moe_backward.argtypes = [S, ctypes.POINTER(_Weights), P, P, ctypes.POINTER(_Trace), P,
+                               ctypes.POINTER(_Grads), P, ctypes.c_size_t, P]
     for fn in ("moe_workspace_size", "moe_route", "moe_permute", "moe_experts", "moe_combine", "moe_forward",
-               "moe_route_replay", "moe_forward_replay"):
+               "moe_route_replay", "moe_forward_replay", "moe_backward_workspace_size", "moe_backward"):
         getattr(L, fn).restype = ctypes.c_int
     L.moe_status_string.argtypes = [ctypes.c_int]
     L.moe_status_string.restype = ctypes.c_char_p
@@ -281,3 +291,50 @@ def moe_forward(shape: Shape, weights: dict, x, sel_bias, mask, out, ws, trace: 
         out_dtype, _ptr(out, "out", None, shape.T * shape.D),
         ctypes.byref(tr) if tr is not None else None,
         _ptr(ws, "ws", torch.uint8), ws.numel() if ws is not None else 0, _stream()), "moe_forward")
+
+
+def backward_workspace_size(shape: Shape) -> int:
+    n = ctypes.c_size_t(0)
+    s = shape.c()
+    _check(lib().moe_backward_workspace_size(ctypes.byref(s), ctypes.byref(n)), "moe_backward_workspace_size")
+    return int(n.value)
+
+
+def moe_backward(shape: Shape, weights: dict, x, mask, trace: dict, dout, grads: dict, ws) -> None:
+    """Gradients of the layer (moe_backward).  trace: the forward's boundary
+    tensors (topk_ids, topk_w, offsets, perm_token, inv_pos, y); grads: float32
+    tensors dx, d_router, d_gate_up, d_down[, d_gate_up_shared, d_down_shared]."""
+    s = shape.c()
+    od = shape.torch_dtype
+    P = shape.T * shape.K
+    f32 = torch.float32
+    w = _Weights(
+        _ptr(weights["router"], "router", od, shape.E * shape.D),
+        _ptr(weights["gate_up"], "gate_up", od, shape.E * 2 * shape.I * shape.D),
+        _ptr(weights["down"], "down", od, shape.E * shape.D * shape.I),
+        _ptr(weights.get("gate_up_shared"), "gate_up_shared", od, 2 * shape.Is * shape.D),
+        _ptr(weights.get("down_shared"), "down_shared", od, shape.D * shape.Is),
+    )
+    tr = _Trace(
+        None,
+        _ptr(trace["topk_ids"], "topk_ids", torch.int32, P),
+        _ptr(trace["topk_w"], "topk_w", f32, P),
+        None,
+        _ptr(trace["offsets"], "offsets", torch.int32, shape.E + 1),
+        _ptr(trace["perm_token"], "perm_token", torch.int32, P),
+        _ptr(trace["inv_pos"], "inv_pos", torch.int32, P),
+        _ptr(trace["y"], "y", od, P * shape.D),
+        None,
+    )
+    g = _Grads(
+        _ptr(grads["dx"], "dx", f32, shape.T * shape.D),
+        _ptr(grads["d_router"], "d_router", f32, shape.E * shape.D),
+        _ptr(grads["d_gate_up"], "d_gate_up", f32, shape.E * 2 * shape.I * shape.D),
+        _ptr(grads["d_down"], "d_down", f32, shape.E * shape.D * shape.I),
+        _ptr(grads.get("d_gate_up_shared"), "d_gate_up_shared", f32, 2 * shape.Is * shape.D),
+        _ptr(grads.get("d_down_shared"), "d_down_shared", f32, shape.D * shape.Is),
+    )
+    _check(lib().moe_backward(
+        ctypes.byref(s), ctypes.byref(w), _ptr(x, "x", od, shape.T * shape.D), _ptr(mask, "mask", torch.uint8, shape.T),
+        ctypes.byref(tr), _ptr(dout, "dout", od, shape.T * shape.D), ctypes.byref(g),
+        _ptr(ws, "ws", torch.uint8), ws.numel() if ws is not None else 0, _stream()), "moe_backward")

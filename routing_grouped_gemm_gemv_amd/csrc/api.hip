@@ -339,4 +339,74 @@ moe_status moe_forward_replay(const moe_shape* shape, const moe_weights* weights
     return forward_impl(shape, weights, x, nullptr, replay_ids, mask, out_dtype, out, trace, ws, ws_bytes, stream);
 }
 
+moe_status moe_backward_workspace_size(const moe_shape* shape, size_t* bytes) {
+    moe_status st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    if (bytes == nullptr) return fail(MOE_ERR_INVALID, "bytes is NULL");
+    *bytes = moe::backward_ws_bytes(shape->T, shape->D, shape->E, shape->K, shape->I, shape->Is);
+    return ok();
+}
+
+moe_status moe_backward(const moe_shape* shape, const moe_weights* weights, const void* x, const uint8_t* mask,
+                        const moe_trace* fwd, const void* dout, const moe_grads* grads, void* ws, size_t ws_bytes,
+                        hipStream_t stream) {
+    moe_status st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    if (shape->dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "moe_backward: bf16 operands only");
+    // the backward's GEMMs take their 128-row tiles from grid.y
+    if ((shape->T * shape->K + 127) / 128 + shape->E > 65535)
+        return fail(MOE_ERR_UNSUPPORTED, "moe_backward: T*K = %lld exceeds the tile grid",
+                    static_cast<long long>(shape->T * shape->K));
+    if (!weights || !weights->router || !weights->gate_up || !weights->down)
+        return fail(MOE_ERR_INVALID, "moe_backward: router, gate_up and down weights are required");
+    if (shape->Is > 0 && (!weights->gate_up_shared || !weights->down_shared))
+        return fail(MOE_ERR_INVALID, "moe_backward: Is > 0 needs gate_up_shared and down_shared");
+    if (!x || !dout) return fail(MOE_ERR_INVALID, "moe_backward: x and dout are required");
+    if (!fwd || !fwd->topk_ids || !fwd->topk_w || !fwd->offsets || !fwd->perm_token || !fwd->inv_pos || !fwd->y)
+        return fail(MOE_ERR_INVALID,
+                    "moe_backward: the forward trace needs topk_ids, topk_w, offsets, perm_token, inv_pos and y");
+    if (!grads || !grads->dx || !grads->d_router || !grads->d_gate_up || !grads->d_down)
+        return fail(MOE_ERR_INVALID, "moe_backward: dx, d_router, d_gate_up and d_down are required");
+    if (shape->Is > 0 && (!grads->d_gate_up_shared || !grads->d_down_shared))
+        return fail(MOE_ERR_INVALID, "moe_backward: Is > 0 needs d_gate_up_shared and d_down_shared");
+    if (shape->T == 0) return ok();
+    const size_t need = moe::backward_ws_bytes(shape->T, shape->D, shape->E, shape->K, shape->I, shape->Is);
+    if (!ws || ws_bytes < need)
+        return fail(MOE_ERR_WORKSPACE, "moe_backward needs %zu workspace bytes, got %zu", need, ws ? ws_bytes : 0);
+    if ((st = check_device()) != MOE_OK) return st;
+    moe::BwdArgs a{};
+    a.T = shape->T;
+    a.D = shape->D;
+    a.E = shape->E;
+    a.K = shape->K;
+    a.I = shape->I;
+    a.Is = shape->Is;
+    a.score = shape->score;
+    a.renorm = shape->renorm;
+    a.route_scale = shape->route_scale;
+    a.x = x;
+    a.router = weights->router;
+    a.gate_up = weights->gate_up;
+    a.down = weights->down;
+    a.gate_up_shared = weights->gate_up_shared;
+    a.down_shared = weights->down_shared;
+    a.dout = dout;
+    a.y = fwd->y;
+    a.topk_ids = fwd->topk_ids;
+    a.offsets = fwd->offsets;
+    a.perm_token = fwd->perm_token;
+    a.inv_pos = fwd->inv_pos;
+    a.topk_w = fwd->topk_w;
+    a.mask = mask;
+    a.dx = grads->dx;
+    a.d_router = grads->d_router;
+    a.d_gate_up = grads->d_gate_up;
+    a.d_down = grads->d_down;
+    a.d_gate_up_shared = grads->d_gate_up_shared;
+    a.d_down_shared = grads->d_down_shared;
+    a.ws = ws;
+    if ((st = hip_status(moe::launch_backward(a, stream), "backward launch")) != MOE_OK) return st;
+    return ok();
+}
+
 }  // extern "C"

@@ -29,6 +29,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 // v_mfma_f32_16x16x32_bf16: D[16x16] = A[16x32] * B[32x16] + C.
 // Lane l supplies row (l % 16) of A and column (l % 16) of B, each with the
 // eight k values 8*(l/16) .. 8*(l/16)+7; it receives D[4*(l/16) + i][l % 16].
+// silu(g) * u with the hardware exponential and reciprocal (about 2 ulp in
+// float32); used where the activation is then rounded to bf16 (the
+// gate_up epilogue, and the backward pass recomputing the same activation)
+__device__ __forceinline__ float silu_mul_fast(float g, float u) {
+    return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
+
 __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);

@@ -130,11 +130,6 @@ __device__ __forceinline__ int swz(int row, int chunk) { return row * kRowBytes 
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return (g / (1.0f + expf(-g))) * u; }
 
-// silu(g) * u with the hardware exponential and reciprocal (about 2 ulp in
-// float32); used where the activation is then rounded to bf16
-__device__ __forceinline__ float silu_mul_fast(float g, float u) {
-    return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
-}
 
 // two floats -> two bf16 (round to nearest even), low half first
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {

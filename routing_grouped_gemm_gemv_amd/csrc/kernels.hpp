@@ -59,4 +59,21 @@ hipError_t launch_combine(const void* y, const int32_t* inv_pos, const float* w,
                           int64_t T, int D, int K, int dtype, int out_dtype, int mode, void* out,
                           hipStream_t stream);
 
+
+// ---- backward ------------------------------------------------------------------
+struct BwdArgs {
+    int64_t T;
+    int D, E, K, I, Is, score, renorm;
+    float route_scale;
+    const void *x, *router, *gate_up, *down, *gate_up_shared, *down_shared;  // bf16
+    const void *dout, *y;                                                    // bf16 [T, D], [P, D]
+    const int32_t *topk_ids, *offsets, *perm_token, *inv_pos;
+    const float* topk_w;
+    const uint8_t* mask;
+    float *dx, *d_router, *d_gate_up, *d_down, *d_gate_up_shared, *d_down_shared;
+    void* ws;
+};
+size_t backward_ws_bytes(int64_t T, int D, int E, int K, int I, int Is);
+hipError_t launch_backward(const BwdArgs& a, hipStream_t stream);
+
 }  // namespace moe

@@ -87,3 +87,25 @@ class MoeLayer:
         out = torch.empty(shape.T, shape.D, dtype=out_dtype or torch.bfloat16, device="cuda")
         B.moe_combine(shape, tr["y"], tr["inv_pos"], tr["topk_w"], shared, out)
         return out, tr
+
+    def backward(self, x: torch.Tensor, dout: torch.Tensor, trace: Dict[str, torch.Tensor],
+                 mask: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+        """Gradients of the forward that produced ``trace`` (moe_backward), as
+        new float32 tensors."""
+        shape = self.with_tokens(x.shape[0])
+        dev = x.device
+        f32 = torch.float32
+        S = shape
+        grads = {
+            "dx": torch.empty(S.T, S.D, dtype=f32, device=dev),
+            "d_router": torch.empty(S.E, S.D, dtype=f32, device=dev),
+            "d_gate_up": torch.empty(S.E, 2 * S.I, S.D, dtype=f32, device=dev),
+            "d_down": torch.empty(S.E, S.D, S.I, dtype=f32, device=dev),
+        }
+        if S.Is > 0:
+            grads["d_gate_up_shared"] = torch.empty(2 * S.Is, S.D, dtype=f32, device=dev)
+            grads["d_down_shared"] = torch.empty(S.D, S.Is, dtype=f32, device=dev)
+        ws = torch.empty(B.backward_workspace_size(shape), dtype=torch.uint8, device=dev)
+        B.moe_backward(shape, self.weights, x, mask, trace, dout, grads, ws)
+        return grads
+

@@ -146,3 +146,34 @@ def test_binding_rejects_host_tensors():
     with pytest.raises(ValueError):
         B.moe_combine(shape, torch.zeros(8, 128), torch.zeros(4, 2, dtype=torch.int32),
                       torch.zeros(4, 2), None, torch.zeros(4, 128))
+
+
+def test_backward_validation_before_launch():
+    L = moe.lib()
+    one = ctypes.c_void_p(1)
+    n = ctypes.c_size_t(0)
+    s = _shape(dtype=0)
+    assert L.moe_backward_workspace_size(ctypes.byref(s), ctypes.byref(n)) == B.MOE_OK and n.value > 0
+    w = B._Weights(one, one, one, None, None)
+    tr = B._Trace(None, one, one, None, one, one, one, one, None)
+    g = B._Grads(one, one, one, one, None, None)
+    # fp32 operands: not supported by the backward
+    s32 = _shape(dtype=1)
+    assert L.moe_backward(ctypes.byref(s32), ctypes.byref(w), one, None, ctypes.byref(tr), one, ctypes.byref(g),
+                          one, 1 << 30, None) == B.MOE_ERR_UNSUPPORTED
+    # a forward trace without y
+    tr2 = B._Trace(None, one, one, None, one, one, one, None, None)
+    assert L.moe_backward(ctypes.byref(s), ctypes.byref(w), one, None, ctypes.byref(tr2), one, ctypes.byref(g),
+                          one, 1 << 30, None) == B.MOE_ERR_INVALID
+    # a shared expert needs its gradient buffers
+    s2 = _shape(Is=64)
+    w2 = B._Weights(one, one, one, one, one)
+    assert L.moe_backward(ctypes.byref(s2), ctypes.byref(w2), one, None, ctypes.byref(tr), one, ctypes.byref(g),
+                          one, 1 << 30, None) == B.MOE_ERR_INVALID
+    # too small a workspace
+    assert L.moe_backward(ctypes.byref(s), ctypes.byref(w), one, None, ctypes.byref(tr), one, ctypes.byref(g),
+                          one, 16, None) == B.MOE_ERR_WORKSPACE
+    # T = 0 launches nothing
+    s0 = _shape(T=0)
+    assert L.moe_backward(ctypes.byref(s0), ctypes.byref(w), one, None, ctypes.byref(tr), one, ctypes.byref(g),
+                          None, 0, None) == B.MOE_OK

@@ -1,0 +1,127 @@
+"""Backward of the layer against the CPU oracle, through the C ABI.
+
+The RL-Kernel roadmap ("DSV4 Flash MoE Train-Inference Consistency Roadmap":
+the scope list, forward + backward with a deterministic reduction order; the
+issue-bucket table, a single-GPU forward + backward).  The oracle's backward
+(float64, pinned to torch autograd) is fed the GPU's own picks, so the
+comparison isolates the gradient arithmetic.
+
+Acceptance.  The kernels feed three gradient operands to bf16 matrix
+products: dY (the expert-output gradients), dH (the gate/up gradients) and dl
+(the logits' gradient).  The oracle's grad_bf16 mode rounds at the same three
+points, so against it only the float32 accumulation order and the rare
+operand whose float32 and float64 values round to neighbouring bf16 values
+(a flip) remain.  Normwise ||gpu - oracle|| <= TOL_NORM ||oracle||: flips are
+sparse and the accumulation error is of order 2^-24 per term.  Elementwise
+max |gpu - oracle| <= TOL_MAX times the oracle's RMS: a flip moves one
+operand by one bf16 ulp (at most 2^-7 of it), and in a hot expert a single
+product can be several times the gradient's RMS (one flip in dH of the
+expert that holds every token of the softmax case is 3.3e-2 of the RMS, the
+whole gap at that element to 1e-6).  Against the exact float64
+gradient the three roundings (uniform over +-2^-9 relative, about 1.1e-3 rms
+each, chained) give about 2e-3 normwise; the bound TOL_EXACT is four times
+that.  Repeated calls must give the same bits, and a token's dx must not
+depend on the other tokens of the batch (bitwise).
+"""
+
+import json
+import sys
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import get_config, make_inputs
+from tests.gpu_util import make_layer, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+TOL_MAX = 5e-2
+TOL_NORM = 2 ** -10
+TOL_EXACT = 2 ** -7
+
+CASES = [
+    # config, reduced sizes, score override, masked
+    ("dsv4", dict(T=256, D=512, E=16, K=4, I=256, Is=256), None, False),   # sigmoid + bias, renorm x2.5, shared
+    ("dsv4", dict(T=160, D=512, E=16, K=4, I=256, Is=256), None, True),    # the same with masked tokens
+    ("qnext", dict(T=200, D=256, E=64, K=8, I=128, Is=128), None, False),  # softmax, Zipf skew, shared
+    ("q30", dict(T=130, D=256, E=16, K=4, I=192, Is=0), "sqrtsoftplus", False),  # N not a multiple of the tile
+    ("dspark", dict(T=96, D=256, E=8, K=1, I=128, Is=0), None, False),     # top-1, no renorm, E = 8
+]
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _case(name, dims, score, masked):
+    cfg = replace(get_config(name), **dims)
+    if score:
+        cfg = replace(cfg, score=score)
+    inp = make_inputs(cfg)
+    if masked:
+        rng = np.random.default_rng(5)
+        inp.mask = (rng.random(cfg.T) > 0.3).astype(np.uint8)
+    rng = np.random.default_rng(6)
+    g32 = rng.standard_normal((cfg.T, cfg.D)).astype(np.float32)
+    dout = (g32.view(np.uint32) + 0x7FFF + ((g32.view(np.uint32) >> 16) & 1)) >> 16
+    return cfg, inp, dout.astype(np.uint16)
+
+
+def _run(inp, dout):
+    layer = make_layer(inp)
+    x = to_dev(inp.x)
+    mask = to_dev(inp.mask)
+    _, tr = layer.forward(x, mask, trace=True)
+    grads = layer.backward(x, to_dev(dout), tr, mask)
+    torch.cuda.synchronize()
+    return layer, tr, grads
+
+
+@pytest.mark.parametrize("name,dims,score,masked", CASES)
+def test_backward_against_oracle(name, dims, score, masked):
+    cfg, inp, dout = _case(name, dims, score, masked)
+    _say(f"[backward] {name} {dims} score={cfg.score} masked={masked}")
+    layer, tr, grads = _run(inp, dout)
+    ids = to_host(tr["topk_ids"])
+    kw = dict(score=cfg.score, renorm=cfg.renorm, route_scale=cfg.route_scale, mask=inp.mask,
+              shared_gate_up=inp.w_gate_up_s, shared_down=inp.w_down_s, bf16_mode=True)
+    ref = oracle.backward(inp.x, inp.w_router, inp.w_gate_up, inp.w_down, dout, ids, grad_bf16=True, **kw)
+    exact = oracle.backward(inp.x, inp.w_router, inp.w_gate_up, inp.w_down, dout, ids, **kw)
+    rep = {}
+    for k, v in grads.items():
+        g = to_host(v).astype(np.float64)
+        r, ex = ref[k], exact[k]
+        rms = float(np.sqrt(np.mean(r * r)))
+        rep[k] = (float(np.max(np.abs(g - r)) / rms), float(np.linalg.norm(g - r) / np.linalg.norm(r)),
+                  float(np.linalg.norm(g - ex) / np.linalg.norm(ex)))
+    _say(f"[backward] max/rms, norm, norm vs exact: {json.dumps(rep)}")
+    for k, (emax, enorm, eexact) in rep.items():
+        assert emax <= TOL_MAX and enorm <= TOL_NORM and eexact <= TOL_EXACT, (k, rep[k])
+    if masked:
+        assert np.all(to_host(grads["dx"])[inp.mask == 0] == 0)
+    # experts no token picked get zero gradients
+    counts = to_host(tr["counts"])
+    for e in np.nonzero(counts == 0)[0]:
+        assert np.all(to_host(grads["d_gate_up"][e]) == 0) and np.all(to_host(grads["d_down"][e]) == 0)
+    # repeat: the same bits
+    g2 = layer.backward(to_dev(inp.x), to_dev(dout), tr, to_dev(inp.mask))
+    torch.cuda.synchronize()
+    for k in grads:
+        assert torch.equal(grads[k].view(torch.int32), g2[k].view(torch.int32)), k
+
+
+def test_backward_dx_is_batch_invariant():
+    """dx of a token is the same bits whether it is differentiated alone, in a
+    prefix, or in the full batch (the weight gradients sum over the batch by
+    definition and are only required to repeat)."""
+    cfg, inp, dout = _case("dsv4", dict(T=256, D=512, E=16, K=4, I=256, Is=256), None, False)
+    _, _, full = _run(inp, dout)
+    dx_full = to_host(full["dx"])
+    for T in (1, 37, 200):
+        sub = replace(inp, cfg=replace(cfg, T=T), x=inp.x[:T])
+        _, _, part = _run(sub, dout[:T])
+        assert np.array_equal(to_host(part["dx"]).view(np.uint32), dx_full[:T].view(np.uint32)), T
