@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--no-invariance", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 1 GiB buffer 5 times (reference kernel for the HBM byte counters)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time moe_backward (gradients of x and every weight) instead of the forward")
     ap.add_argument("--dense-reference", action="store_true",
                     help="only time the vendor dense bf16 GEMM (torch.mm) on the routed GEMMs' total shapes")
     return ap.parse_args()
@@ -177,6 +179,10 @@ def main():
     torch.cuda.synchronize()
     log(f"uploaded; workspace {ws.numel() / 2**30:.2f} GiB")
 
+    if args.backward:
+        bench_backward(args, cfg, inp, layer, shape, x)
+        return
+
     # ---- timed region 1: moe_forward, whole steps ---------------------------
     for _ in range(args.warmup):
         layer.forward(x, out=out)
@@ -302,6 +308,94 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def bench_backward(args, cfg, inp, layer, shape, x):
+    """One step = moe_backward over the trace of one forward: the gradients of
+    the hidden states, the router and every expert weight (float32), from a
+    seeded bf16 output gradient already resident in HBM."""
+    import numpy as np
+    import torch
+
+    import routing_grouped_gemm_gemv_amd as moe
+    B = moe.binding
+    T = shape.T
+    _, tr = layer.forward(x, trace=True)
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    dout = torch.randn(T, cfg.D, device="cuda", generator=gen).to(torch.bfloat16)
+    grads = layer.backward(x, dout, tr)  # allocates the gradients once
+    ws = torch.empty(B.backward_workspace_size(shape), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    log(f"backward workspace {ws.numel() / 2**30:.2f} GiB, gradients "
+        f"{sum(g.numel() for g in grads.values()) * 4 / 2**30:.2f} GiB")
+
+    def step():
+        B.moe_backward(shape, layer.weights, x, None, tr, dout, grads, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_start = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_per_step = wall / args.steps * 1e3
+    ev_ms = e0.elapsed_time(e1) / args.steps
+    log(f"moe_backward: {ms_per_step:.3f} ms/step (events {ev_ms:.3f})")
+    first = {k: v.clone() for k, v in grads.items()}
+    step()
+    torch.cuda.synchronize()
+    repeat_bitwise = all(torch.equal(first[k].view(torch.int32), grads[k].view(torch.int32)) for k in grads)
+
+    P = int(tr["counts"].sum().item())
+    # bf16 GEMM flops: H recomputed (2I x D), dA (I x D), dX (D x 2I), dW_down, dW_gate_up
+    routed = 16.0 * cfg.D * cfg.I * P
+    shared = 16.0 * cfg.D * cfg.Is * T
+    router = 2.0 * 2.0 * cfg.D * cfg.E * T  # dx_r and dW_r (the float64 logits recompute not counted)
+    flops = routed + shared + router
+    achieved = flops / (ev_ms * 1e-3) / 1e12
+    cpu = None
+    n = min(args.cpu_sample, 16, T)
+    if n > 0:
+        import oracle
+        ids = tr["topk_ids"][:n].cpu().numpy()
+        g = dout[:n].contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+        t0 = time.perf_counter()
+        oracle.backward(inp.x[:n], inp.w_router, inp.w_gate_up, inp.w_down, g, ids, score=cfg.score,
+                        renorm=cfg.renorm, route_scale=cfg.route_scale, shared_gate_up=inp.w_gate_up_s,
+                        shared_down=inp.w_down_s, bf16_mode=True)
+        dt = time.perf_counter() - t0
+        cpu = {"value": n / dt, "unit": "tokens/s", "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+               "sample": f"backward of the first {n} tokens of the same {cfg.name}-like layer, fp64 numpy "
+                         f"oracle, {dt:.1f} s"}
+    print(json.dumps({
+        "metric": "MoE-layer backward tokens/s @1 GPU (dx, d_router, d_gate_up, d_down, shared)",
+        "value": T / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded; random-init weights, seeded normal output gradient)",
+        "config": {"workload": f"{cfg.name}-like MoE layer backward", "T": T, "D": cfg.D, "E": cfg.E,
+                   "K": cfg.K, "I": cfg.I, "Is": cfg.Is, "score": cfg.score, "parallelism": "single GPU"},
+        "roofline": {"kernel": "whole backward (bf16 MFMA GEMMs dominate)", "bound": "mfma",
+                     "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None},
+        "gemm_flops": flops,
+        "repeat_bitwise": repeat_bitwise,
+        "routed_pairs": P,
+        "cpu_baseline": cpu,
+    }), flush=True)
 
 
 def cpu_baseline(cfg, inp, n):

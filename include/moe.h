@@ -274,8 +274,8 @@ moe_status moe_backward_workspace_size(const moe_shape* shape, size_t* bytes);
  *     dx += dl W_r; d_router = dl^T x;
  *   dx_t = sum of the token's routed dX rows in ascending expert id, then the
  *     shared and the router terms, in float32; masked tokens get dx = 0.
- * bf16 operands only, and T*K/128 + E <= 65535 (MOE_ERR_UNSUPPORTED
- * otherwise); float32 accumulation.  Every reduction has a fixed order and no atomics: repeated calls give the
+ * bf16 operands only, and 2*T*K*max(D, 2I) and 2*T*max(D, 2Is) below
+ * 4 GiB (MOE_ERR_UNSUPPORTED otherwise); float32 accumulation.  Every reduction has a fixed order and no atomics: repeated calls give the
  * same bits, and dx of a token does not depend on the other tokens.
  * fwd: the trace of the moe_forward call being differentiated, with
  * topk_ids, topk_w, offsets, perm_token, inv_pos and y set (the other fields

@@ -353,10 +353,8 @@ moe_status moe_backward(const moe_shape* shape, const moe_weights* weights, cons
     moe_status st = check_shape(shape);
     if (st != MOE_OK) return st;
     if (shape->dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "moe_backward: bf16 operands only");
-    // the backward's GEMMs take their 128-row tiles from grid.y
-    if ((shape->T * shape->K + 127) / 128 + shape->E > 65535)
-        return fail(MOE_ERR_UNSUPPORTED, "moe_backward: T*K = %lld exceeds the tile grid",
-                    static_cast<long long>(shape->T * shape->K));
+    if (!moe::backward_fits_dma(shape->T, shape->D, shape->K, shape->I, shape->Is))
+        return fail(MOE_ERR_UNSUPPORTED, "moe_backward: T*K*max(D, 2I) bf16 values must stay below 4 GiB");
     if (!weights || !weights->router || !weights->gate_up || !weights->down)
         return fail(MOE_ERR_INVALID, "moe_backward: router, gate_up and down weights are required");
     if (shape->Is > 0 && (!weights->gate_up_shared || !weights->down_shared))

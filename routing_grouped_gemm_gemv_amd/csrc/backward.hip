@@ -12,13 +12,14 @@
 // Steps (P routed pairs, rows in the forward's expert order; bf16 operands,
 // float32 accumulation):
 //   combine_bwd   dY[p] = bf16(w * G[t]);  dw[t, j] = <G[t], y[p]> (float64)
-//   gemm          H = X W1_e^T, rows gathered (float32, recomputed)
+//   gather        Xp = x[perm] (the routed rows in expert order)
+//   gemm          H = Xp W1_e^T (float32, recomputed)
 //   gemm          dA = dY W2_e (float32)
 //   swiglu_bwd    A = bf16(silu(g) u) as the forward formed it;
 //                 dH = bf16([dA u silu'(g), dA silu(g)])
 //   gemm          dW2_e = dY_e^T A_e, K-grouped (float32)
 //   gemm          dXp = dH W1_e (float32)
-//   gemm          dW1_e = dH_e^T X_e, K-grouped, rows gathered
+//   gemm          dW1_e = dH_e^T Xp_e, K-grouped
 //   (the same for the shared expert, with dY = G on every kept token)
 //   router_bwd    dl[t, e] from dw through the weights and the score (bf16)
 //   gemm          dx_r = dl W_r;  gemm  dW_r = dl^T x (K-grouped, one group)
@@ -31,31 +32,43 @@
 namespace moe {
 
 // ===========================================================================
-// Generic grouped GEMM for the backward: C[m][n] = sum_k A(m, k) B(k, n),
-// bf16 operands, float32 accumulation and output.
+// Grouped GEMM for the backward: C[m][n] = sum_k A(m, k) B(k, n), bf16
+// operands, float32 accumulation and output.
 //
 // A is stored [M rows][K] (K contiguous) or, AT, [K rows][M]; B is stored
 // [N rows][K] or, BT, [K rows][N].  Groups split either M (the routed rows of
 // an expert; B is the expert's matrix) or, GK, K (an expert's rows are the
-// reduction; C is the expert's matrix).  A 128 x 128 tile per 256-thread
-// workgroup, four waves of 64 x 64 (MFMA 16x16x32 bf16), 64-wide k stages
-// staged through registers into two LDS buffers laid out as the forward
-// kernels lay them out ([row][64 k], 16-byte chunk c of row r at c ^ (r % 8)).
-// An operand stored [K][X] is loaded as 8 k-rows x 4 columns per thread and
-// transposed in registers before its LDS write.  Each output element is one
-// MFMA chain over its k range in ascending order: no split-K, no atomics.
+// reduction; C is the expert's matrix).  256 x 256 tiles, four waves of
+// 128 x 128 (MFMA 16x16x32 bf16), 64-wide k stages moved global -> LDS by
+// DMA into two buffers, the next stage in flight over the current one's
+// MFMAs.  Each output element is one MFMA chain over its k range in
+// ascending order: no split-K, no atomics.
+//
+// LDS layouts of one operand's stage (32 KiB):
+//  * K-major: 256 rows of 64 k (128 B); 16-byte chunk c of row r at
+//    c ^ (r % 8).  A fragment (16 rows x 8 k per lane) is one 16-byte read.
+//  * [K][X]: 64 k-rows of 256 x-values (512 B); the 32-byte block of 16
+//    x-values p of k-row k at p ^ h(k), h(k) = (k % 4) + 4 ((k / 8) % 2), so
+//    that the 16 k-rows one transposed read touches fall on distinct banks.
+//    A fragment is two ds_read_b64_tr_b16: in each 16-lane block, lane i
+//    receives element i % 4 of the 8 bytes that lane 4j + i / 4 addresses, as
+//    its element j; a lane that addresses x-values 4 (s % 4) .. + 3 of k-row
+//    k0 + s / 4 (s its index in the block) hands lane i the four k of x-value
+//    i, which is the MFMA operand layout.
 // ===========================================================================
-constexpr int kBT = 128;                 // tile rows and columns
-constexpr int kBK = 64;                  // k per stage
-constexpr int kRowB = 128;               // LDS bytes per tile row (64 bf16)
-constexpr int kOpB = kBT * kRowB;        // one operand's stage: 16 KiB
-constexpr int kStageB = 2 * kOpB;        // 32 KiB
+constexpr int kT = 256;                  // tile rows and columns
+constexpr int kSK = 64;                  // k per stage
+constexpr int kOpB = 32768;              // one operand's stage
+constexpr int kStageB = 2 * kOpB;
+constexpr int kZeroTail = 1024;          // zero bytes after each K-grouped A operand
+
+typedef short bwd_v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bwd_v4s lds_v4s;
 
 struct BwdOperand {
     const uint16_t* base;    // bf16 elements
     int64_t ld;              // elements between stored rows
     int64_t gstride;         // elements between the groups' matrices (0: one matrix)
-    const int32_t* gather;   // index map of the stored rows (m rows of A; k rows of BT), or null
 };
 
 struct BwdGemm {
@@ -65,20 +78,21 @@ struct BwdGemm {
     int64_t c_gstride;          // GK: elements between the groups' outputs
     const int32_t* offsets;     // row ranges of the G groups [G + 1], or null: one group [0, rows)
     const int32_t* tile_start;  // !GK: m-tile prefix over the groups [G + 1] (null with one group)
+    const uint16_t* a_zero;     // GK: kZeroTail zero bytes after A's buffer (A's k-rows past a group read these)
     int G;
     int rows;                   // the one-group row count
     int M, N, K;                // !GK: N, K fixed (M from the groups); GK: M, N fixed
-    int kb_valid;               // !GK, BT: B rows k >= kb_valid read as zero
-    int m_valid;                // GK: output rows m >= m_valid are not stored (A may be wider)
+    int kb_valid;               // !GK: B k-rows >= kb_valid are clamped (A is zero there)
+    int m_valid;                // GK: output rows m >= m_valid are not stored
 };
 
-// m-tile prefix over groups of 128-row tiles (one workgroup of 1024 threads)
+// m-tile prefix over groups of kT-row tiles (one workgroup of 1024 threads)
 __global__ __launch_bounds__(1024) void bwd_tile_prefix_kernel(const int32_t* __restrict__ offsets, int G,
                                                                int32_t* __restrict__ ts) {
     __shared__ int part[1024];
     const int tid = threadIdx.x;
     int v = 0;
-    if (tid < G) v = (offsets[tid + 1] - offsets[tid] + kBT - 1) / kBT;
+    if (tid < G) v = (offsets[tid + 1] - offsets[tid] + kT - 1) / kT;
     part[tid] = v;
     __syncthreads();
     for (int d = 1; d < 1024; d <<= 1) {
@@ -91,210 +105,227 @@ __global__ __launch_bounds__(1024) void bwd_tile_prefix_kernel(const int32_t* __
     if (tid == 0) ts[0] = 0;
 }
 
-// 4 bf16 of 8 k-rows (v[r] = columns c..c+3 of row r) -> 8 k of each column
-__device__ __forceinline__ void transpose_8x4(const u32x2 (&v)[8], u32x4 (&t)[4]) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        uint32_t w[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const uint32_t lo = (c < 2) ? v[2 * q].x : v[2 * q].y;
-            const uint32_t hi = (c < 2) ? v[2 * q + 1].x : v[2 * q + 1].y;
-            w[q] = (c & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
-        }
-        t[c] = u32x4{w[0], w[1], w[2], w[3]};
-    }
-}
-
 template <bool AT, bool BT, bool GK>
 __global__ __launch_bounds__(256) void bwd_gemm_kernel(BwdGemm p) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[2 * kStageB];
     lds_u8* smem = (lds_u8*)(smem_raw);
+    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem));
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wv >> 1;
     const int wn = wv & 1;
 
-    // ---- the tile -------------------------------------------------------------
-    int g = 0;
-    int64_t m0 = 0;
-    int mrows = 0;
+    // ---- the tile (XCD-aware: consecutive tiles on one XCD) ---------------------
+    const int ntn = (p.N + kT - 1) / kT;
+    const int64_t L = xcd_remap(blockIdx.x, gridDim.x);
+    int g = 0, mt = 0, nt = 0;
+    int64_t m0 = 0;     // !GK: first row of the tile
+    int mrows = 0;      // !GK: valid rows of the tile
     int kbeg = 0, kend = p.K;
-    const int n0 = blockIdx.x * kBT;
-    const int ncols = min(kBT, p.N - n0);
     if (!GK) {
-        const int L = blockIdx.y;
         if (p.offsets == nullptr) {
-            m0 = static_cast<int64_t>(L) * kBT;
-            if (m0 >= p.rows) return;
-            mrows = min(kBT, p.rows - static_cast<int>(m0));
+            const int mtn = (p.rows + kT - 1) / kT;
+            if (L >= static_cast<int64_t>(mtn) * ntn) return;
+            nt = static_cast<int>(L / mtn);
+            mt = static_cast<int>(L % mtn);
+            m0 = static_cast<int64_t>(mt) * kT;
+            mrows = min(kT, p.rows - static_cast<int>(m0));
         } else {
-            if (L >= p.tile_start[p.G]) return;
+            if (L >= static_cast<int64_t>(p.tile_start[p.G]) * ntn) return;
             int lo = 0, hi = p.G - 1;  // last group whose first tile is <= L
             while (lo < hi) {
                 const int mid = (lo + hi + 1) >> 1;
-                if (p.tile_start[mid] <= L) lo = mid; else hi = mid - 1;
+                if (static_cast<int64_t>(p.tile_start[mid]) * ntn <= L) lo = mid; else hi = mid - 1;
             }
             g = lo;
-            m0 = p.offsets[g] + static_cast<int64_t>(L - p.tile_start[g]) * kBT;
-            mrows = min(static_cast<int64_t>(kBT), static_cast<int64_t>(p.offsets[g + 1]) - m0);
+            const int mtn = p.tile_start[g + 1] - p.tile_start[g];
+            const int loc = static_cast<int>(L - static_cast<int64_t>(p.tile_start[g]) * ntn);
+            nt = loc / mtn;
+            mt = loc % mtn;
+            m0 = p.offsets[g] + static_cast<int64_t>(mt) * kT;
+            mrows = min(static_cast<int64_t>(kT), static_cast<int64_t>(p.offsets[g + 1]) - m0);
         }
     } else {
-        g = blockIdx.z;
-        m0 = static_cast<int64_t>(blockIdx.y) * kBT;
-        mrows = min(kBT, p.m_valid - static_cast<int>(m0));
+        const int mtn = (p.M + kT - 1) / kT;
+        const int per = mtn * ntn;
+        if (L >= static_cast<int64_t>(per) * p.G) return;
+        g = static_cast<int>(L / per);
+        const int loc = static_cast<int>(L % per);
+        mt = loc / ntn;
+        nt = loc % ntn;
         kbeg = p.offsets ? p.offsets[g] : 0;
         kend = p.offsets ? p.offsets[g + 1] : p.rows;
     }
-    const int ns = (kend - kbeg + kBK - 1) / kBK;
+    const int n0 = nt * kT;
+    const int ns = (kend - kbeg + kSK - 1) / kSK;
 
-    const uint16_t* abase = p.a.base;
-    const uint16_t* bbase = p.b.base + (GK ? 0 : static_cast<int64_t>(g) * p.b.gstride);
-    const int kb_lim = GK ? kend : (BT ? p.kb_valid : kend);
-
-    // ---- staging: each thread's share of one stage ------------------------------
-    // K-major operand: rows (tid / 8) + 32 i, 16-byte chunk tid % 8.
-    // Stored [K][X]: k rows 8 (tid / 32) + r, columns 4 (tid % 32) .. + 3.
-    const int km_chunk = tid & 7;
-    const int km_row = tid >> 3;
-    const int tr_col = 4 * (tid & 31);
-    const int tr_ko = tid >> 5;
-    u32x4 ra[4], rb[4];
-    u32x2 ta[8], tb[8];
-
-    auto load_stage = [&](int s) {
-        const int k0 = kbeg + s * kBK;
-        if (!AT) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = km_row + 32 * i;
-                const int rr = r < mrows ? r : mrows - 1;  // rows past the tile repeat its last; never stored
-                int64_t row = m0 + rr;
-                if (p.a.gather) row = p.a.gather[row];
-                ra[i] = *reinterpret_cast<const u32x4*>(abase + row * p.a.ld + k0 + 8 * km_chunk);
-            }
-        } else {
-            const int col = static_cast<int>(m0) + tr_col < p.M ? static_cast<int>(m0) + tr_col : p.M - 4;
-#pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                const int k = k0 + 8 * tr_ko + r;
-                ta[r] = u32x2{0u, 0u};
-                if (k < kend) ta[r] = *reinterpret_cast<const u32x2*>(abase + static_cast<int64_t>(k) * p.a.ld + col);
-            }
-        }
-        if (!BT) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = km_row + 32 * i;
-                const int rr = r < ncols ? r : ncols - 1;
-                rb[i] = *reinterpret_cast<const u32x4*>(bbase + static_cast<int64_t>(n0 + rr) * p.b.ld + k0 +
-                                                        8 * km_chunk);
-            }
-        } else {
-            const int col = n0 + tr_col < p.N ? n0 + tr_col : p.N - 4;
-#pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                const int k = k0 + 8 * tr_ko + r;
-                tb[r] = u32x2{0u, 0u};
-                if (k < kb_lim && k < kend) {
-                    int64_t row = k;
-                    if (GK && p.b.gather) row = p.b.gather[k];
-                    tb[r] = *reinterpret_cast<const u32x2*>(bbase + row * p.b.ld + col);
-                }
-            }
-        }
+    // ---- operand bases (wave-uniform) and per-lane DMA offsets --------------------
+    // K-major: instruction q of wave w fills rows 64 w + 8 q + lane / 8 at
+    // physical chunk lane % 8 with logical chunk (lane % 8) ^ (lane / 8).
+    // [K][X]: instruction q of wave w fills k-rows 8 q + 2 w + lane / 32 at
+    // physical chunk lane % 32 (block (lane % 32) / 2).
+    const uint8_t* abase;
+    const uint8_t* bbase;
+    if (!GK) {
+        abase = reinterpret_cast<const uint8_t*>(p.a.base + m0 * p.a.ld);
+        bbase = reinterpret_cast<const uint8_t*>(p.b.base + static_cast<int64_t>(g) * p.b.gstride);
+    } else {
+        abase = reinterpret_cast<const uint8_t*>(p.a.base + static_cast<int64_t>(kbeg) * p.a.ld);
+        bbase = reinterpret_cast<const uint8_t*>(p.b.base + static_cast<int64_t>(kbeg) * p.b.ld);
+    }
+    const uint32_t lda2 = static_cast<uint32_t>(p.a.ld) * 2;
+    const uint32_t ldb2 = static_cast<uint32_t>(p.b.ld) * 2;
+    const int km_chunk = (lane & 7) ^ (lane >> 3);
+    const int km_row = 64 * wv + (lane >> 3);          // + 8 q
+    const int tx_row = 2 * wv + (lane >> 5);           // + 8 q
+    const int tx_pc = lane & 31;
+    // [K][X] x offset (bytes) of instruction parity qp, clamped to the operand's width
+    auto tx_x = [&](int qp, int x0, int xlim) -> uint32_t {
+        const int h = ((2 * wv + (lane >> 5)) & 3) | (qp << 2);
+        const int c = 2 * ((tx_pc >> 1) ^ h) + (tx_pc & 1);
+        int x = x0 + 8 * c;
+        if (x > xlim - 8) x = xlim - 8;
+        return static_cast<uint32_t>(x) * 2;
     };
-    auto store_stage = [&](int buf) {
-        lds_u8* sa = smem + buf * kStageB;
-        lds_u8* sb = sa + kOpB;
-        if (!AT) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = km_row + 32 * i;
-                *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(sa + r * kRowB +
-                                                                             ((km_chunk ^ (r & 7)) << 4)) = ra[i];
+    const int m_tile0 = GK ? mt * kT : 0;
+    const uint32_t ax0 = AT ? tx_x(0, m_tile0, p.M) : 0u, ax1 = AT ? tx_x(1, m_tile0, p.M) : 0u;
+    const uint32_t bx0 = BT ? tx_x(0, n0, p.N) : 0u, bx1 = BT ? tx_x(1, n0, p.N) : 0u;
+    const uint32_t a_zero_off =
+        GK ? static_cast<uint32_t>(reinterpret_cast<const uint8_t*>(p.a_zero) - abase) + 16 * tx_pc : 0u;
+    const int klen = kend - kbeg;
+    const int kb_lim = GK ? klen : p.kb_valid;
+    // K-major rows: lane base and the clamp to the last valid row (rows past
+    // the group repeat its last row and are never stored)
+    const uint32_t a_km = static_cast<uint32_t>(km_row) * lda2 + km_chunk * 16;
+    const uint32_t a_km_lim = static_cast<uint32_t>(mrows - 1) * lda2 + km_chunk * 16;
+    const uint32_t b_km = static_cast<uint32_t>(n0 + km_row) * ldb2 + km_chunk * 16;
+    const uint32_t b_km_lim = static_cast<uint32_t>(p.N - 1) * ldb2 + km_chunk * 16;
+
+    auto dma = [&](int st, uint32_t stage_off, int q) {
+        const int s = st < ns ? st : ns - 1;  // past the end: reload the last stage (never read)
+        if (q < 8) {  // A
+            const uint32_t dst = lds0 + stage_off + static_cast<uint32_t>(q * 4 + wv) * 1024u;
+            if (!AT) {
+                uint32_t v = a_km;
+                asm volatile("" : "+v"(v));  // recomputed per DMA, not held for every q
+                v = min(v + static_cast<uint32_t>(8 * q) * lda2, a_km_lim);
+                dma16(abase, v + static_cast<uint32_t>(s) * 128u,
+                      lds0 + stage_off + static_cast<uint32_t>(64 * wv + 8 * q) * 128u);
+            } else {
+                const int k = s * kSK + 8 * q + tx_row;
+                const uint32_t off = k < klen ? static_cast<uint32_t>(k) * lda2 + ((q & 1) ? ax1 : ax0) : a_zero_off;
+                dma16(abase, off, dst);
             }
-        } else {
-            u32x4 t[4];
-            transpose_8x4(ta, t);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int r = tr_col + c;
-                *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(sa + r * kRowB +
-                                                                             ((tr_ko ^ (r & 7)) << 4)) = t[c];
-            }
-        }
-        if (!BT) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = km_row + 32 * i;
-                *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(sb + r * kRowB +
-                                                                             ((km_chunk ^ (r & 7)) << 4)) = rb[i];
-            }
-        } else {
-            u32x4 t[4];
-            transpose_8x4(tb, t);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int r = tr_col + c;
-                *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(sb + r * kRowB +
-                                                                             ((tr_ko ^ (r & 7)) << 4)) = t[c];
+        } else {      // B
+            const int qb = q - 8;
+            const uint32_t dst = lds0 + stage_off + kOpB + static_cast<uint32_t>(qb * 4 + wv) * 1024u;
+            if (!BT) {
+                uint32_t v = b_km;
+                asm volatile("" : "+v"(v));
+                v = min(v + static_cast<uint32_t>(8 * qb) * ldb2, b_km_lim);
+                dma16(bbase, v + static_cast<uint32_t>(s) * 128u,
+                      lds0 + stage_off + kOpB + static_cast<uint32_t>(64 * wv + 8 * qb) * 128u);
+            } else {
+                int k = s * kSK + 8 * qb + tx_row;
+                if (k >= kb_lim) k = kb_lim - 1;  // A is zero there
+                dma16(bbase, static_cast<uint32_t>(k) * ldb2 + ((qb & 1) ? bx1 : bx0), dst);
             }
         }
     };
 
-    f32x4 acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    // fragment of half j of a stage: logical chunk 4j + lane/16 of row lane%16
-    // (+16 per block), at chunk ^ (lane % 8)
+    // ---- fragment reads ----------------------------------------------------------
+    // K-major: sub-step j reads logical chunk 4 j + lane / 16 of row lane % 16.
     const int xo0 = ((lane >> 4) ^ (lane & 7)) << 4;
     const int xo1 = ((4 + (lane >> 4)) ^ (lane & 7)) << 4;
-    const int a_frag = (wm * 64 + (lane & 15)) * kRowB;
-    const int b_frag = kOpB + (wn * 64 + (lane & 15)) * kRowB;
+    // [K][X]: lane (block b, index s) reads k-row 32 j + 8 b + 4 h + s / 4,
+    // x-values 16 t + 4 (s % 4) .. + 3, at block t ^ hl.
+    const int tb = lane >> 4, ts_ = lane & 15;
+    const int hl = (ts_ >> 2) | ((tb & 1) << 2);
+    const int tx_base = (8 * tb + (ts_ >> 2)) * 512 + 8 * (ts_ & 3);
+    auto frag = [&](uint32_t stage_off, int j, int op, int t) -> u32x4 {
+        // op 0: A block t (rows 16 t of the wave's 128), op 1: B block t
+        const int wblk = op == 0 ? wm * 8 + t : wn * 8 + t;
+        const lds_u8* st = smem + stage_off + (op == 0 ? 0 : kOpB);
+        const bool tr = op == 0 ? AT : BT;
+        if (!tr) {
+            return *reinterpret_cast<lds_u32x4*>(st + (wblk * 16 + (lane & 15)) * 128 + (j == 0 ? xo0 : xo1));
+        } else {
+            const lds_u8* q = st + tx_base + 32 * j * 512 + (((wblk & 8) | ((wblk & 7) ^ hl)) << 5);
+            const bwd_v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(q));
+            const bwd_v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(q + 4 * 512));
+            const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+            return u32x4{l2.x, l2.y, h2.x, h2.y};
+        }
+    };
+
+    f32x4 acc[8][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // f[0..7]: A blocks, f[8..15]: B blocks of one 32-wide sub-step.  One
+    // sub-step: 64 MFMAs, the next sub-step's 16 fragments read in its first
+    // half, and (do_dma) the 16 DMAs of stage dst spread over it.
+    auto sub = [&](const u32x4 (&f)[16], u32x4 (&nx)[16], uint32_t rs, int rj, bool do_dma, int dst, uint32_t ds) {
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+#pragma unroll
+                for (int nb = 4 * h; nb < 4 * h + 4; ++nb) acc[mb][nb] = mfma_bf16(f[8 + nb], f[mb], acc[mb][nb]);
+                const int q = 2 * mb + h;
+                if (q < 8) {
+                    nx[2 * q] = frag(rs, rj, (2 * q) >> 3, (2 * q) & 7);
+                    nx[2 * q + 1] = frag(rs, rj, (2 * q + 1) >> 3, (2 * q + 1) & 7);
+                }
+                if (do_dma) dma(dst, ds, q);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    };
 
     if (ns > 0) {
-        load_stage(0);
-        store_stage(0);
+#pragma unroll
+        for (int q = 0; q < 16; ++q) dma(0, 0, q);
+#pragma unroll
+        for (int q = 0; q < 16; ++q) dma(1, kStageB, q);
+        wait_vmem<16>();
         __syncthreads();
-        for (int s = 0; s < ns; ++s) {
-            if (s + 1 < ns) load_stage(s + 1);  // global loads in flight over this stage's MFMAs
-            const lds_u8* st = smem + (s & 1) * kStageB;
+        u32x4 f0[16], f1[16];
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int xo = j == 0 ? xo0 : xo1;
-                u32x4 af[4], bf[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    af[i] = *reinterpret_cast<lds_u32x4*>(st + a_frag + i * 16 * kRowB + xo);
-                    bf[i] = *reinterpret_cast<lds_u32x4*>(st + b_frag + i * 16 * kRowB + xo);
-                }
-#pragma unroll
-                for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-                    for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma_bf16(bf[nb], af[mb], acc[mb][nb]);
-            }
-            if (s + 1 < ns) store_stage((s + 1) & 1);  // that buffer was last read in stage s-1
+        for (int k = 0; k < 16; ++k) f0[k] = frag(0, 0, k >> 3, k & 7);
+        for (int st = 0; st < ns; ++st) {
+            const uint32_t cur = static_cast<uint32_t>(st & 1) * kStageB;
+            const uint32_t nxt = static_cast<uint32_t>((st + 1) & 1) * kStageB;
+            // first half: fragments of this stage's second half
+            sub(f0, f1, cur, 1, false, 0, 0);
+            // stage st+1 has landed and every wave is done with stage st
+            wait_vmem<0>();
             __syncthreads();
+            __builtin_amdgcn_sched_barrier(0);
+            // second half: fragments of the next stage's first half; stage st+2 into this buffer
+            sub(f1, f0, nxt, 0, true, st + 2, cur);
         }
+        wait_vmem<0>();
     }
 
-    // ---- output: lane holds row (lane % 16) x 4 consecutive columns per block ----
+    // ---- output: lane holds row (lane % 16) x 4 consecutive columns per block ------
     float* cb = p.c + (GK ? static_cast<int64_t>(g) * p.c_gstride : 0);
     const int c4 = 4 * (lane >> 4);
+    const int mlim = GK ? p.m_valid - mt * kT : mrows;
+    const int64_t row0 = GK ? static_cast<int64_t>(mt) * kT : m0;
+    const int ncols = min(kT, p.N - n0);
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-        const int m = wm * 64 + mb * 16 + (lane & 15);
-        if (m >= mrows) continue;
+    for (int mb = 0; mb < 8; ++mb) {
+        const int m = wm * 128 + mb * 16 + (lane & 15);
+        if (m >= mlim) continue;
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-            const int n = wn * 64 + nb * 16 + c4;
+        for (int nb = 0; nb < 8; ++nb) {
+            const int n = wn * 128 + nb * 16 + c4;
             if (n < ncols)
-                *reinterpret_cast<f32x4*>(cb + (m0 + m) * p.ldc + n0 + n) = acc[mb][nb];
+                __builtin_nontemporal_store(acc[mb][nb], reinterpret_cast<f32x4*>(cb + (row0 + m) * p.ldc + n0 + n));
         }
     }
 }
@@ -498,73 +529,123 @@ __global__ __launch_bounds__(kBwdThreads) void dx_assemble_kernel(
     }
 }
 
+// rows p < *count of x gathered by perm: xp[p] = x[perm[p]] (16 bytes per thread)
+__global__ __launch_bounds__(kBwdThreads) void gather_rows_kernel(const uint16_t* __restrict__ x,
+                                                                  const int32_t* __restrict__ perm,
+                                                                  const int32_t* __restrict__ count, int D,
+                                                                  uint16_t* __restrict__ xp) {
+    const int64_t p = blockIdx.x;
+    if (p >= *count) return;
+    const int64_t t = perm[p];
+    for (int d0 = threadIdx.x * 8; d0 < D; d0 += kBwdThreads * 8)
+        *reinterpret_cast<u32x4*>(xp + p * D + d0) = *reinterpret_cast<const u32x4*>(x + t * D + d0);
+}
+
+// n 16-byte words of zeros at each of up to four addresses
+__global__ void zero_tails_kernel(uint8_t* a, uint8_t* b, uint8_t* c, uint8_t* d, int n) {
+    const int i = threadIdx.x;
+    uint8_t* dst[4] = {a, b, c, d};
+    for (int k = 0; k < 4; ++k)
+        if (dst[k] != nullptr && i < n) reinterpret_cast<u32x4*>(dst[k])[i] = u32x4{0u, 0u, 0u, 0u};
+}
+
 // ===========================================================================
 // launcher
 // ===========================================================================
+// tiles: an upper bound of the tile count (padded to a multiple of 8 for the
+// XCD mapping; tiles past the real count exit at once)
 template <bool AT, bool BT, bool GK>
-static hipError_t gemm(const BwdGemm& p, int m_tiles, int groups_z, hipStream_t stream) {
-    dim3 grid(static_cast<unsigned>((p.N + kBT - 1) / kBT), static_cast<unsigned>(m_tiles),
-              static_cast<unsigned>(groups_z));
-    bwd_gemm_kernel<AT, BT, GK><<<grid, 256, 0, stream>>>(p);
+static hipError_t gemm(const BwdGemm& p, int64_t tiles, hipStream_t stream) {
+    if (tiles <= 0) return hipSuccess;
+    const int64_t n = (tiles + 7) / 8 * 8;
+    bwd_gemm_kernel<AT, BT, GK><<<dim3(static_cast<unsigned>(n)), 256, 0, stream>>>(p);
     return hipGetLastError();
 }
 
-static BwdOperand op(const void* base, int64_t ld, int64_t gstride = 0, const int32_t* gather = nullptr) {
-    return BwdOperand{static_cast<const uint16_t*>(base), ld, gstride, gather};
+static BwdOperand op(const void* base, int64_t ld, int64_t gstride = 0) {
+    return BwdOperand{static_cast<const uint16_t*>(base), ld, gstride};
 }
 
-size_t backward_ws_bytes(int64_t T, int D, int E, int K, int I, int Is) {
+static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+namespace {
+struct BwdLayout {
+    size_t logits, dw, dY, dYs, H, dA, dH, Aact, xp, dXp, dXs, dxr, dl, ts, total;
+};
+BwdLayout bwd_layout(int64_t T, int D, int E, int K, int I, int Is) {
     const int64_t P = T * K;
     const int64_t rows2 = P * 2 * I > T * 2 * static_cast<int64_t>(Is) ? P * 2 * I : T * 2 * static_cast<int64_t>(Is);
     const int64_t rows1 = P * I > T * static_cast<int64_t>(Is) ? P * I : T * static_cast<int64_t>(Is);
     const int64_t Epad = (E + 63) / 64 * 64;
+    BwdLayout l{};
     size_t b = 0;
-    auto take = [&](size_t n) { b += (n + 255) & ~static_cast<size_t>(255); };
-    take(sizeof(double) * T * E);        // logits
-    take(sizeof(double) * P);            // dw
-    take(2 * static_cast<size_t>(P) * D);  // dY
-    take(2 * static_cast<size_t>(T) * D);  // dYs
-    take(4 * static_cast<size_t>(rows2));  // H
-    take(4 * static_cast<size_t>(rows1));  // dA
-    take(2 * static_cast<size_t>(rows2));  // dH
-    take(2 * static_cast<size_t>(rows1));  // A
-    take(4 * static_cast<size_t>(P) * D);  // dXp
-    take(4 * static_cast<size_t>(T) * D);  // dXs
-    take(4 * static_cast<size_t>(T) * D);  // dxr
-    take(2 * static_cast<size_t>(T) * Epad);  // dl
-    take(sizeof(int32_t) * (E + 1));     // tile prefix
-    return b;
+    auto take = [&](size_t n) {
+        const size_t at = b;
+        b += (n + 255) & ~static_cast<size_t>(255);
+        return at;
+    };
+    l.logits = take(sizeof(double) * T * E);
+    l.dw = take(sizeof(double) * P);
+    l.dY = take(2 * static_cast<size_t>(P) * D + kZeroTail);      // zero tail: K-grouped A operand
+    l.dYs = take(2 * static_cast<size_t>(T) * D + kZeroTail);
+    l.H = take(4 * static_cast<size_t>(rows2));
+    l.dA = take(4 * static_cast<size_t>(rows1));
+    l.dH = take(2 * static_cast<size_t>(rows2) + kZeroTail);
+    l.Aact = take(2 * static_cast<size_t>(rows1));
+    l.xp = take(2 * static_cast<size_t>(P) * D);
+    l.dXp = take(4 * static_cast<size_t>(P) * D);
+    l.dXs = take(4 * static_cast<size_t>(T) * D);
+    l.dxr = take(4 * static_cast<size_t>(T) * D);
+    l.dl = take(2 * static_cast<size_t>(T) * Epad + kZeroTail);
+    l.ts = take(sizeof(int32_t) * (E + 1));
+    l.total = b;
+    return l;
+}
+}  // namespace
+
+size_t backward_ws_bytes(int64_t T, int D, int E, int K, int I, int Is) { return bwd_layout(T, D, E, K, I, Is).total; }
+
+bool backward_fits_dma(int64_t T, int D, int K, int I, int Is) {
+    // every DMA-staged buffer (and its zero tail) spans less than 4 GiB: the
+    // GEMMs address it with 32-bit offsets from a group's first row
+    const int64_t P = T * K;
+    const int64_t lim = (int64_t{1} << 32) - 2 * kZeroTail;
+    const int64_t w = 2 * I > D ? 2 * I : D;
+    const int64_t ws = 2 * Is > D ? 2 * Is : D;
+    return 2 * P * w < lim && 2 * T * ws < lim;
 }
 
 hipError_t launch_backward(const BwdArgs& a, hipStream_t stream) {
     const int64_t T = a.T;
     const int D = a.D, E = a.E, K = a.K, I = a.I, Is = a.Is;
     const int64_t P = T * K;
-    const int64_t rows2 = P * 2 * I > T * 2 * static_cast<int64_t>(Is) ? P * 2 * I : T * 2 * static_cast<int64_t>(Is);
-    const int64_t rows1 = P * I > T * static_cast<int64_t>(Is) ? P * I : T * static_cast<int64_t>(Is);
     const int Epad = (E + 63) / 64 * 64;
+    const BwdLayout lo = bwd_layout(T, D, E, K, I, Is);
     uint8_t* w = static_cast<uint8_t*>(a.ws);
-    size_t off = 0;
-    auto take = [&](size_t n) {
-        void* q = w + off;
-        off += (n + 255) & ~static_cast<size_t>(255);
-        return q;
-    };
-    double* logits = static_cast<double*>(take(sizeof(double) * T * E));
-    double* dw = static_cast<double*>(take(sizeof(double) * P));
-    uint16_t* dY = static_cast<uint16_t*>(take(2 * static_cast<size_t>(P) * D));
-    uint16_t* dYs = static_cast<uint16_t*>(take(2 * static_cast<size_t>(T) * D));
-    float* H = static_cast<float*>(take(4 * static_cast<size_t>(rows2)));
-    float* dA = static_cast<float*>(take(4 * static_cast<size_t>(rows1)));
-    uint16_t* dH = static_cast<uint16_t*>(take(2 * static_cast<size_t>(rows2)));
-    uint16_t* Aact = static_cast<uint16_t*>(take(2 * static_cast<size_t>(rows1)));
-    float* dXp = static_cast<float*>(take(4 * static_cast<size_t>(P) * D));
-    float* dXs = static_cast<float*>(take(4 * static_cast<size_t>(T) * D));
-    float* dxr = static_cast<float*>(take(4 * static_cast<size_t>(T) * D));
-    uint16_t* dl = static_cast<uint16_t*>(take(2 * static_cast<size_t>(T) * Epad));
-    int32_t* ts = static_cast<int32_t*>(take(sizeof(int32_t) * (E + 1)));
+    double* logits = reinterpret_cast<double*>(w + lo.logits);
+    double* dw = reinterpret_cast<double*>(w + lo.dw);
+    uint16_t* dY = reinterpret_cast<uint16_t*>(w + lo.dY);
+    uint16_t* dYs = reinterpret_cast<uint16_t*>(w + lo.dYs);
+    float* H = reinterpret_cast<float*>(w + lo.H);
+    float* dA = reinterpret_cast<float*>(w + lo.dA);
+    uint16_t* dH = reinterpret_cast<uint16_t*>(w + lo.dH);
+    uint16_t* Aact = reinterpret_cast<uint16_t*>(w + lo.Aact);
+    uint16_t* xp = reinterpret_cast<uint16_t*>(w + lo.xp);
+    float* dXp = reinterpret_cast<float*>(w + lo.dXp);
+    float* dXs = reinterpret_cast<float*>(w + lo.dXs);
+    float* dxr = reinterpret_cast<float*>(w + lo.dxr);
+    uint16_t* dl = reinterpret_cast<uint16_t*>(w + lo.dl);
+    int32_t* ts = reinterpret_cast<int32_t*>(w + lo.ts);
+    const int64_t rows2 = P * 2 * I > T * 2 * static_cast<int64_t>(Is) ? P * 2 * I : T * 2 * static_cast<int64_t>(Is);
+    // the zero tails sit right after each buffer's rows
+    uint8_t* z_dY = reinterpret_cast<uint8_t*>(dY) + 2 * static_cast<size_t>(P) * D;
+    uint8_t* z_dYs = reinterpret_cast<uint8_t*>(dYs) + 2 * static_cast<size_t>(T) * D;
+    uint8_t* z_dH = reinterpret_cast<uint8_t*>(dH) + 2 * static_cast<size_t>(rows2);
+    uint8_t* z_dl = reinterpret_cast<uint8_t*>(dl) + 2 * static_cast<size_t>(T) * Epad;
 
     hipError_t err;
+    zero_tails_kernel<<<1, kZeroTail / 16, 0, stream>>>(z_dY, z_dYs, z_dH, z_dl, kZeroTail / 16);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
     if ((err = launch_router_logits(a.x, a.router, T, D, E, 0, logits, stream)) != hipSuccess) return err;
     combine_bwd_kernel<<<static_cast<unsigned>(T), kBwdThreads, 0, stream>>>(
         static_cast<const uint16_t*>(a.dout), static_cast<const uint16_t*>(a.y), a.inv_pos, a.topk_w, a.mask, T, D,
@@ -572,23 +653,26 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t stream) {
     if ((err = hipGetLastError()) != hipSuccess) return err;
     bwd_tile_prefix_kernel<<<1, 1024, 0, stream>>>(a.offsets, E, ts);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    const int mt_routed = static_cast<int>((P + kBT - 1) / kBT) + E;
+    gather_rows_kernel<<<static_cast<unsigned>(P), kBwdThreads, 0, stream>>>(
+        static_cast<const uint16_t*>(a.x), a.perm_token, a.offsets + E, D, xp);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    const int64_t mt_routed = cdiv(P, kT) + E;  // bound on the routed m-tiles
 
     // routed experts
     BwdGemm g{};
     g.offsets = a.offsets;
     g.tile_start = ts;
     g.G = E;
-    // H = X_e W1_e^T (rows gathered)
-    g.a = op(a.x, D, 0, a.perm_token);
+    // H = Xp W1_e^T
+    g.a = op(xp, D);
     g.b = op(a.gate_up, D, static_cast<int64_t>(2) * I * D);
     g.c = H; g.ldc = 2 * I; g.N = 2 * I; g.K = D; g.kb_valid = D;
-    if ((err = gemm<false, false, false>(g, mt_routed, 1, stream)) != hipSuccess) return err;
+    if ((err = gemm<false, false, false>(g, mt_routed * cdiv(g.N, kT), stream)) != hipSuccess) return err;
     // dA = dY W2_e
     g.a = op(dY, D);
     g.b = op(a.down, I, static_cast<int64_t>(D) * I);
     g.c = dA; g.ldc = I; g.N = I; g.K = D; g.kb_valid = D;
-    if ((err = gemm<false, true, false>(g, mt_routed, 1, stream)) != hipSuccess) return err;
+    if ((err = gemm<false, true, false>(g, mt_routed * cdiv(g.N, kT), stream)) != hipSuccess) return err;
     {
         dim3 grid(static_cast<unsigned>(P), static_cast<unsigned>((I / 8 + kBwdThreads - 1) / kBwdThreads));
         swiglu_bwd_kernel<<<grid, kBwdThreads, 0, stream>>>(H, dA, a.offsets + E, P, I, dH, Aact);
@@ -598,54 +682,57 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t stream) {
     g.a = op(dH, 2 * I);
     g.b = op(a.gate_up, D, static_cast<int64_t>(2) * I * D);
     g.c = dXp; g.ldc = D; g.N = D; g.K = 2 * I; g.kb_valid = 2 * I;
-    if ((err = gemm<false, true, false>(g, mt_routed, 1, stream)) != hipSuccess) return err;
+    if ((err = gemm<false, true, false>(g, mt_routed * cdiv(g.N, kT), stream)) != hipSuccess) return err;
     // dW2_e = dY_e^T A_e
     BwdGemm k{};
     k.offsets = a.offsets;
     k.G = E;
     k.a = op(dY, D);
+    k.a_zero = reinterpret_cast<const uint16_t*>(z_dY);
     k.b = op(Aact, I);
     k.c = a.d_down; k.ldc = I; k.c_gstride = static_cast<int64_t>(D) * I; k.M = D; k.N = I; k.m_valid = D;
-    if ((err = gemm<true, true, true>(k, (D + kBT - 1) / kBT, E, stream)) != hipSuccess) return err;
-    // dW1_e = dH_e^T X_e (rows gathered)
+    if ((err = gemm<true, true, true>(k, E * cdiv(k.M, kT) * cdiv(k.N, kT), stream)) != hipSuccess) return err;
+    // dW1_e = dH_e^T Xp_e
     k.a = op(dH, 2 * I);
-    k.b = op(a.x, D, 0, a.perm_token);
+    k.a_zero = reinterpret_cast<const uint16_t*>(z_dH);
+    k.b = op(xp, D);
     k.c = a.d_gate_up; k.ldc = D; k.c_gstride = static_cast<int64_t>(2) * I * D; k.M = 2 * I; k.N = D;
     k.m_valid = 2 * I;
-    if ((err = gemm<true, true, true>(k, (2 * I + kBT - 1) / kBT, E, stream)) != hipSuccess) return err;
+    if ((err = gemm<true, true, true>(k, E * cdiv(k.M, kT) * cdiv(k.N, kT), stream)) != hipSuccess) return err;
 
     // shared expert: one group of T rows, dY = G on kept tokens
     if (Is > 0) {
-        const int mt = static_cast<int>((T + kBT - 1) / kBT);
         BwdGemm s{};
         s.G = 1;
         s.rows = static_cast<int>(T);
         s.a = op(a.x, D);
         s.b = op(a.gate_up_shared, D);
         s.c = H; s.ldc = 2 * Is; s.N = 2 * Is; s.K = D; s.kb_valid = D;
-        if ((err = gemm<false, false, false>(s, mt, 1, stream)) != hipSuccess) return err;
+        if ((err = gemm<false, false, false>(s, cdiv(T, kT) * cdiv(s.N, kT), stream)) != hipSuccess) return err;
         s.a = op(dYs, D);
         s.b = op(a.down_shared, Is);
         s.c = dA; s.ldc = Is; s.N = Is; s.K = D; s.kb_valid = D;
-        if ((err = gemm<false, true, false>(s, mt, 1, stream)) != hipSuccess) return err;
+        if ((err = gemm<false, true, false>(s, cdiv(T, kT) * cdiv(s.N, kT), stream)) != hipSuccess) return err;
         dim3 grid(static_cast<unsigned>(T), static_cast<unsigned>((Is / 8 + kBwdThreads - 1) / kBwdThreads));
         swiglu_bwd_kernel<<<grid, kBwdThreads, 0, stream>>>(H, dA, nullptr, T, Is, dH, Aact);
         if ((err = hipGetLastError()) != hipSuccess) return err;
         s.a = op(dH, 2 * Is);
         s.b = op(a.gate_up_shared, D);
         s.c = dXs; s.ldc = D; s.N = D; s.K = 2 * Is; s.kb_valid = 2 * Is;
-        if ((err = gemm<false, true, false>(s, mt, 1, stream)) != hipSuccess) return err;
+        if ((err = gemm<false, true, false>(s, cdiv(T, kT) * cdiv(s.N, kT), stream)) != hipSuccess) return err;
         BwdGemm sk{};
         sk.G = 1;
         sk.rows = static_cast<int>(T);
         sk.a = op(dYs, D);
+        sk.a_zero = reinterpret_cast<const uint16_t*>(z_dYs);
         sk.b = op(Aact, Is);
         sk.c = a.d_down_shared; sk.ldc = Is; sk.M = D; sk.N = Is; sk.m_valid = D;
-        if ((err = gemm<true, true, true>(sk, (D + kBT - 1) / kBT, 1, stream)) != hipSuccess) return err;
+        if ((err = gemm<true, true, true>(sk, cdiv(sk.M, kT) * cdiv(sk.N, kT), stream)) != hipSuccess) return err;
         sk.a = op(dH, 2 * Is);
+        sk.a_zero = reinterpret_cast<const uint16_t*>(z_dH);
         sk.b = op(a.x, D);
         sk.c = a.d_gate_up_shared; sk.ldc = D; sk.M = 2 * Is; sk.N = D; sk.m_valid = 2 * Is;
-        if ((err = gemm<true, true, true>(sk, (2 * Is + kBT - 1) / kBT, 1, stream)) != hipSuccess) return err;
+        if ((err = gemm<true, true, true>(sk, cdiv(sk.M, kT) * cdiv(sk.N, kT), stream)) != hipSuccess) return err;
     }
 
     // router
@@ -653,21 +740,21 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t stream) {
         logits, a.topk_ids, dw, a.mask, T, E, K, a.score, a.renorm, static_cast<double>(a.route_scale), dl, Epad);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     {
-        const int mt = static_cast<int>((T + kBT - 1) / kBT);
         BwdGemm r{};
         r.G = 1;
         r.rows = static_cast<int>(T);
         r.a = op(dl, Epad);
         r.b = op(a.router, D);
         r.c = dxr; r.ldc = D; r.N = D; r.K = Epad; r.kb_valid = E;
-        if ((err = gemm<false, true, false>(r, mt, 1, stream)) != hipSuccess) return err;
+        if ((err = gemm<false, true, false>(r, cdiv(T, kT) * cdiv(r.N, kT), stream)) != hipSuccess) return err;
         BwdGemm rk{};
         rk.G = 1;
         rk.rows = static_cast<int>(T);
         rk.a = op(dl, Epad);
+        rk.a_zero = reinterpret_cast<const uint16_t*>(z_dl);
         rk.b = op(a.x, D);
         rk.c = a.d_router; rk.ldc = D; rk.M = Epad; rk.N = D; rk.m_valid = E;
-        if ((err = gemm<true, true, true>(rk, (E + kBT - 1) / kBT, 1, stream)) != hipSuccess) return err;
+        if ((err = gemm<true, true, true>(rk, cdiv(rk.M, kT) * cdiv(rk.N, kT), stream)) != hipSuccess) return err;
     }
     dx_assemble_kernel<<<static_cast<unsigned>(T), kBwdThreads, 0, stream>>>(dXp, a.inv_pos, Is > 0 ? dXs : nullptr,
                                                                              dxr, a.mask, T, D, K, a.dx);
