@@ -35,7 +35,7 @@ Pins (the tests that tie each function to something other than itself):
 No function is parity-unpinned.
 """
 
-from .backward import backward
+from .backward import backward, backward_expert
 from .moe import (
     EXEMPT_REL_MARGIN,
     OracleResult,
@@ -59,6 +59,7 @@ from .moe import (
 __all__ = [
     "EXEMPT_REL_MARGIN",
     "backward",
+    "backward_expert",
     "OracleResult",
     "bf16_bits_of",
     "combine_f64",

@@ -42,7 +42,7 @@ For a kept token t with picks j (expert e_j, pair row p_j, weight w_j):
 
 from __future__ import annotations
 
-from typing import Callable, Dict, Optional
+from typing import Callable, Dict, Optional, Tuple
 
 import numpy as np
 
@@ -122,6 +122,50 @@ def expert_mlp_backward(x64: np.ndarray, w1: np.ndarray, w2: np.ndarray, dy: np.
     return dh @ w1_64, dh.T @ x64, dW2
 
 
+def _routing_weights(x64, wr64, ids, score, renorm, route_scale):
+    """Logits, scores and the routing weights [T, K] of the given picks."""
+    logits = router_logits(x64, wr64)
+    s = scores(logits, score)
+    sp = np.where(ids >= 0, np.take_along_axis(s, np.maximum(ids, 0), axis=1), 0.0)
+    if renorm:
+        den = sp.sum(axis=1, keepdims=True)
+        w = np.divide(sp, den, out=np.zeros_like(sp), where=den > 0) * route_scale
+    else:
+        w = sp * route_scale
+    return logits, s, w
+
+
+def _expert_step(x64, G64, w, tj, w1, w2, bf16_mode, grad_bf16):
+    """(dX rows, dW1, dW2) of one expert over its picks tj = (token, slot)
+    pairs in token order: dY = w G per pick, then the SwiGLU backward."""
+    t_rows, j_cols = tj[:, 0], tj[:, 1]
+    dy = w[t_rows, j_cols][:, None] * G64[t_rows]
+    if grad_bf16:
+        dy = round_bf16(dy)
+    return expert_mlp_backward(x64[t_rows], w1, w2, dy, bf16_mode, grad_bf16)
+
+
+def backward_expert(e: int, x: np.ndarray, w_router: np.ndarray, gate_up_e: np.ndarray, down_e: np.ndarray,
+                    G: np.ndarray, ids: np.ndarray, *, score: str, renorm: bool, route_scale: float,
+                    mask: Optional[np.ndarray] = None, bf16_mode: bool,
+                    grad_bf16: bool = False) -> Tuple[np.ndarray, np.ndarray]:
+    """(d_gate_up[e], d_down[e]) alone: the same steps as ``backward`` for the
+    one expert, without the other experts, the router or dx (for sampling one
+    expert's weight gradients at sizes where the full backward is too slow)."""
+    x64 = widen(x)
+    G64 = widen(G)
+    valid = np.ones(x64.shape[0], dtype=bool) if mask is None else np.asarray(mask).astype(bool)
+    ids = np.where(valid[:, None], ids, -1)
+    G64 = np.where(valid[:, None], G64, 0.0)
+    _, _, w = _routing_weights(x64, widen(w_router), ids, score, renorm, route_scale)
+    tj = np.argwhere(ids == e)
+    I = widen(down_e).shape[1]
+    if tj.size == 0:
+        return np.zeros((2 * I, x64.shape[1])), np.zeros((x64.shape[1], I))
+    _, dw1, dw2 = _expert_step(x64, G64, w, tj, gate_up_e, down_e, bf16_mode, grad_bf16)
+    return dw1, dw2
+
+
 def backward(x: np.ndarray, w_router: np.ndarray,
              gate_up: Callable[[int], np.ndarray] | np.ndarray,
              down: Callable[[int], np.ndarray] | np.ndarray,
@@ -146,14 +190,7 @@ def backward(x: np.ndarray, w_router: np.ndarray,
     ids = np.where(valid[:, None], ids, -1)
     G64 = np.where(valid[:, None], G64, 0.0)
 
-    logits = router_logits(x64, wr64)
-    s = scores(logits, score)
-    sp = np.where(ids >= 0, np.take_along_axis(s, np.maximum(ids, 0), axis=1), 0.0)
-    if renorm:
-        den = sp.sum(axis=1, keepdims=True)
-        w = np.divide(sp, den, out=np.zeros_like(sp), where=den > 0) * route_scale
-    else:
-        w = sp * route_scale
+    logits, s, w = _routing_weights(x64, wr64, ids, score, renorm, route_scale)
 
     get1 = gate_up if callable(gate_up) else (lambda e: gate_up[e])
     get2 = down if callable(down) else (lambda e: down[e])
@@ -169,11 +206,8 @@ def backward(x: np.ndarray, w_router: np.ndarray,
         t_rows, j_cols = tj[:, 0], tj[:, 1]
         xe = x64[t_rows]
         ye = expert_mlp(xe, get1(e), get2(e), bf16_mode)  # the y the combine used
-        dy = w[t_rows, j_cols][:, None] * G64[t_rows]
-        if grad_bf16:
-            dy = round_bf16(dy)
         dw[t_rows, j_cols] = np.sum(G64[t_rows] * ye, axis=1)
-        dxe, d_gate_up[e], d_down[e] = expert_mlp_backward(xe, get1(e), get2(e), dy, bf16_mode, grad_bf16)
+        dxe, d_gate_up[e], d_down[e] = _expert_step(x64, G64, w, tj, get1(e), get2(e), bf16_mode, grad_bf16)
         np.add.at(dx, t_rows, dxe)
 
     d_gate_up_s = d_down_s = None

@@ -125,3 +125,57 @@ def test_backward_dx_is_batch_invariant():
         sub = replace(inp, cfg=replace(cfg, T=T), x=inp.x[:T])
         _, _, part = _run(sub, dout[:T])
         assert np.array_equal(to_host(part["dx"]).view(np.uint32), dx_full[:T].view(np.uint32)), T
+
+
+def _grad_report(g, r, ex):
+    g = np.asarray(g, dtype=np.float64)
+    rms = float(np.sqrt(np.mean(r * r)))
+    return (float(np.max(np.abs(g - r)) / rms), float(np.linalg.norm(g - r) / np.linalg.norm(r)),
+            float(np.linalg.norm(g - ex) / np.linalg.norm(ex)))
+
+
+def test_backward_full_size_dsv4_sampled():
+    """The DeepSeek-V4-Flash-like layer at full size (T=32768, D=4096, 256
+    experts, top-6 sigmoid with selection bias, I=2048, one shared expert of
+    2048), moe_backward over the whole batch as the benchmark times it.  dx of
+    sampled tokens (a token's dx depends on that token alone) and the complete
+    weight gradients of the most and the least loaded expert, against the
+    oracle; the repeat is bitwise."""
+    cfg = get_config("dsv4")
+    _say(f"[backward-full] drawing inputs T={cfg.T}")
+    inp = make_inputs(cfg)
+    rng = np.random.default_rng(7)
+    g32 = rng.standard_normal((cfg.T, cfg.D), dtype=np.float32)
+    u = g32.view(np.uint32)
+    dout = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    del g32, u
+    layer, tr, grads = _run(inp, dout)
+    _say("[backward-full] forward + backward done")
+    ids = to_host(tr["topk_ids"])
+    counts = to_host(tr["counts"])
+    kw = dict(score=cfg.score, renorm=cfg.renorm, route_scale=cfg.route_scale, bf16_mode=True)
+
+    tok = np.sort(rng.choice(cfg.T, 8, replace=False))
+    args = (inp.x[tok], inp.w_router, inp.w_gate_up, inp.w_down, dout[tok], ids[tok])
+    sh = dict(shared_gate_up=inp.w_gate_up_s, shared_down=inp.w_down_s)
+    ref = oracle.backward(*args, grad_bf16=True, **sh, **kw)["dx"]
+    exact = oracle.backward(*args, **sh, **kw)["dx"]
+    rep = {"dx_sampled": _grad_report(to_host(grads["dx"])[tok], ref, exact)}
+    _say(f"[backward-full] dx of tokens {tok.tolist()}: {rep['dx_sampled']}")
+
+    nz = np.nonzero(counts)[0]
+    for e in (int(np.argmax(counts)), int(nz[np.argmin(counts[nz])])):
+        ea = (e, inp.x, inp.w_router, inp.w_gate_up[e], inp.w_down[e], dout, ids)
+        r1, r2 = oracle.backward_expert(*ea, grad_bf16=True, **kw)
+        x1, x2 = oracle.backward_expert(*ea, **kw)
+        rep[f"d_gate_up[{e}] rows={counts[e]}"] = _grad_report(to_host(grads["d_gate_up"][e]), r1, x1)
+        rep[f"d_down[{e}] rows={counts[e]}"] = _grad_report(to_host(grads["d_down"][e]), r2, x2)
+        _say(f"[backward-full] expert {e} ({counts[e]} rows) done")
+    _say(f"[backward-full] max/rms, norm, norm vs exact: {json.dumps(rep)}")
+    for k, (emax, enorm, eexact) in rep.items():
+        assert emax <= TOL_MAX and enorm <= TOL_NORM and eexact <= TOL_EXACT, (k, rep[k])
+
+    g2 = layer.backward(to_dev(inp.x), to_dev(dout), tr)
+    torch.cuda.synchronize()
+    for k in grads:
+        assert torch.equal(grads[k].view(torch.int32), g2[k].view(torch.int32)), k

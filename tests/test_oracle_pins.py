@@ -679,3 +679,23 @@ def test_backward_of_unpicked_expert_is_zero():
     picked = np.zeros((T, E), bool)
     picked[np.arange(T), ids[:, 0]] = True
     assert np.all(g["dlogits"][~picked] == 0) and np.all(g["dlogits"][picked] != 0)
+
+
+def test_backward_expert_equals_the_full_backward():
+    """The one-expert entry takes the same steps as the full backward."""
+    rng = np.random.default_rng(33)
+    T, D, E, K, I = 20, 32, 8, 3, 16
+    r = oracle.round_bf16
+    x, wr = r(rng.standard_normal((T, D))), r(rng.standard_normal((E, D)) * 0.3)
+    w1, w2 = r(rng.standard_normal((E, 2 * I, D)) * 0.2), r(rng.standard_normal((E, D, I)) * 0.2)
+    G = r(rng.standard_normal((T, D)))
+    mask = (rng.random(T) > 0.2).astype(np.uint8)
+    for score, renorm, gb in (("sigmoid", True, True), ("softmax", False, False)):
+        fw = oracle.forward(x, wr, w1, w2, K=K, score=score, renorm=renorm, route_scale=2.0, mask=mask,
+                            bf16_mode=True)
+        full = oracle.backward(x, wr, w1, w2, G, fw.ids, score=score, renorm=renorm, route_scale=2.0, mask=mask,
+                               bf16_mode=True, grad_bf16=gb)
+        for e in range(E):
+            d1, d2 = oracle.backward_expert(e, x, wr, w1[e], w2[e], G, fw.ids, score=score, renorm=renorm,
+                                            route_scale=2.0, mask=mask, bf16_mode=True, grad_bf16=gb)
+            assert np.array_equal(d1, full["d_gate_up"][e]) and np.array_equal(d2, full["d_down"][e]), e
