@@ -107,7 +107,7 @@ __global__ __launch_bounds__(1024) void bwd_tile_prefix_kernel(const int32_t* __
 
 template <bool AT, bool BT, bool GK>
 __global__ __launch_bounds__(256) void bwd_gemm_kernel(BwdGemm p) {
-    __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[2 * kStageB];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[2 * kStageB + 8192];  // stages; the output staging needs 128 x 1040 B
     lds_u8* smem = (lds_u8*)(smem_raw);
     const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem));
     const int tid = threadIdx.x;
@@ -311,21 +311,31 @@ __global__ __launch_bounds__(256) void bwd_gemm_kernel(BwdGemm p) {
         wait_vmem<0>();
     }
 
-    // ---- output: lane holds row (lane % 16) x 4 consecutive columns per block ------
+    // ---- output: through LDS, 128 rows at a time (row stride padded by 16
+    // bytes against bank conflicts), so that each store writes one whole
+    // 1 KiB output row; streaming (non-temporal) stores ---------------------------
     float* cb = p.c + (GK ? static_cast<int64_t>(g) * p.c_gstride : 0);
     const int c4 = 4 * (lane >> 4);
     const int mlim = GK ? p.m_valid - mt * kT : mrows;
     const int64_t row0 = GK ? static_cast<int64_t>(mt) * kT : m0;
     const int ncols = min(kT, p.N - n0);
+    constexpr int kOR = 1040;
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb) {
-        const int m = wm * 128 + mb * 16 + (lane & 15);
-        if (m >= mlim) continue;
+    for (int half = 0; half < 2; ++half) {
+        __syncthreads();
+        if (wm == half) {
 #pragma unroll
-        for (int nb = 0; nb < 8; ++nb) {
-            const int n = wn * 128 + nb * 16 + c4;
-            if (n < ncols)
-                __builtin_nontemporal_store(acc[mb][nb], reinterpret_cast<f32x4*>(cb + (row0 + m) * p.ldc + n0 + n));
+            for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < 8; ++nb)
+                    *reinterpret_cast<__attribute__((address_space(3))) f32x4*>(
+                        smem + (mb * 16 + (lane & 15)) * kOR + (wn * 128 + nb * 16 + c4) * 4) = acc[mb][nb];
+        }
+        __syncthreads();
+        for (int r = wv; r < 128; r += 4) {
+            const int row = half * 128 + r;
+            const f32x4 v = *reinterpret_cast<__attribute__((address_space(3))) f32x4*>(smem + r * kOR + lane * 16);
+            if (row < mlim && 4 * lane < ncols) __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(cb + (row0 + row) * p.ldc + n0 + 4 * lane));
         }
     }
 }
