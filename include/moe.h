@@ -147,7 +147,7 @@ moe_status moe_workspace_size(const moe_shape* shape, size_t* bytes);
 /* Routing (RL-Kernel roadmap, Problem 1 and the routing boundary of Problem 2;
  * SpecForge pull request #1003, commit notes on the router).
  *   logits[t,e] = sum_d x[t,d] * router[e,d], accumulated in float64 from
- *   float32 partial sums of 128 products each (bf16 mode) or in float64 (f32 mode);
+ *   float32 partial sums of 256 products each (bf16 mode) or in float64 (f32 mode);
  *   s = softmax over e, sigmoid or sqrtsoftplus, in float64;
  *   choice = s + sel_bias[e] (sel_bias may be NULL);
  *   the K experts with the largest choice are selected, ties to the lower id;

@@ -10,8 +10,9 @@
 //
 // Precision: a top-k decision is discrete, so the logits are accumulated far
 // more accurately than the score margins that decide it.  In bf16 mode the
-// GEMM runs on MFMA with fp32 accumulation over chunks of 128 products (the
-// last chunk may hold 64), and the chunk sums are added in float64; in fp32
+// GEMM runs on MFMA with fp32 accumulation over chunks of 256 products (the
+// last chunk may hold 64, 128 or 192), and the chunk sums are added in
+// float64; in fp32
 // mode each logit is a float64 FMA chain (the fp32 x fp32 products are exact
 // in float64).  Scores, choices and weights are then float64; the weights are
 // rounded once to float32.
@@ -25,7 +26,7 @@ namespace moe {
 // ---------------------------------------------------------------------------
 constexpr int kRtTok = 64;
 constexpr int kRtExp = 64;
-constexpr int kRtK = 64;  // k per LDS stage; fp32 partial sums span two stages (128 products)
+constexpr int kRtK = 64;  // k per LDS stage; fp32 partial sums span four stages (256 products)
 
 __global__ __launch_bounds__(256) void router_logits_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int64_t T, int D, int E,
@@ -61,7 +62,7 @@ __global__ __launch_bounds__(256) void router_logits_bf16_kernel(
             *reinterpret_cast<u32x4*>(sw + off) = vw;
         }
         __syncthreads();
-        if ((k0 & 127) == 0) {
+        if ((k0 & 255) == 0) {
 #pragma unroll
             for (int nb = 0; nb < 4; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
@@ -77,7 +78,7 @@ __global__ __launch_bounds__(256) void router_logits_bf16_kernel(
                 acc[nb] = mfma_bf16(a, b, acc[nb]);
             }
         }
-        if ((k0 & 127) == 64 || k0 + kRtK == D) {
+        if ((k0 & 255) == 192 || k0 + kRtK == D) {
 #pragma unroll
             for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
@@ -741,7 +742,7 @@ __global__ __launch_bounds__(256) void topk_kernel(
 // workgroup, kept in LDS as float64, then top-k per token from LDS.
 // The hidden rows are read from memory once and the logits never leave the
 // chip.  Each logit is computed exactly as router_logits_bf16_kernel does
-// (MFMA k=32 steps into an fp32 accumulator zeroed every 128 k, the 128-wide
+// (MFMA k=32 steps into an fp32 accumulator zeroed every 256 k, the 256-wide
 // partial sums added in float64 in k order), so both paths give the same bits.
 // The chunks stream through two LDS stages filled by global_load_lds_dwordx4
 // (8 rows x 128 bytes per instruction, the 16-byte chunks of a row XOR-
@@ -937,14 +938,16 @@ __global__ __launch_bounds__(256) void route_fused_bf16_kernel(
             }
         }
     };
-    // 128-wide partial sums: two stages per fp32 accumulation, then float64
-    for (int st = 0; st < ns; st += 2) {
+    // 256-wide partial sums: four stages per fp32 accumulation, then float64
+    for (int st = 0; st < ns; st += 4) {
 #pragma unroll
         for (int a = 0; a < TBB; ++a)
 #pragma unroll
             for (int b = 0; b < NBW; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
         stage(st);
         if (st + 1 < ns) stage(st + 1);
+        if (st + 2 < ns) stage(st + 2);
+        if (st + 3 < ns) stage(st + 3);
 #pragma unroll
         for (int a = 0; a < TBB; ++a)
 #pragma unroll
