@@ -134,14 +134,17 @@ def _grad_report(g, r, ex):
             float(np.linalg.norm(g - ex) / np.linalg.norm(ex)))
 
 
-def test_backward_full_size_dsv4_sampled():
-    """The DeepSeek-V4-Flash-like layer at full size (T=32768, D=4096, 256
-    experts, top-6 sigmoid with selection bias, I=2048, one shared expert of
-    2048), moe_backward over the whole batch as the benchmark times it.  dx of
-    sampled tokens (a token's dx depends on that token alone) and the complete
-    weight gradients of the most and the least loaded expert, against the
-    oracle; the repeat is bitwise."""
-    cfg = get_config("dsv4")
+@pytest.mark.parametrize("name", ["dsv4", "qnext"])
+def test_backward_full_size_sampled(name):
+    """A workload at full size — the DeepSeek-V4-Flash-like layer (T=32768,
+    D=4096, 256 experts, top-6 sigmoid with selection bias, I=2048, one shared
+    expert of 2048), as the benchmark times it, and the Qwen3-Next-like one
+    (T=16384, D=2048, 512 experts, top-10 softmax with Zipf skew, I=512, shared
+    512) — moe_backward over the whole batch.  dx of sampled tokens (a token's
+    dx depends on that token alone) and the complete weight gradients of the
+    most and the least loaded expert, against the oracle; the repeat is
+    bitwise."""
+    cfg = get_config(name)
     _say(f"[backward-full] drawing inputs T={cfg.T}")
     inp = make_inputs(cfg)
     rng = np.random.default_rng(7)
