@@ -551,6 +551,24 @@ __global__ __launch_bounds__(kBwdThreads) void gather_rows_kernel(const uint16_t
         *reinterpret_cast<u32x4*>(xp + p * D + d0) = *reinterpret_cast<const u32x4*>(x + t * D + d0);
 }
 
+// K-slices of a single-group weight-gradient GEMM: off[i] = min(i * len, rows)
+__global__ void split_bounds_kernel(int32_t* __restrict__ off, int S, int rows, int len) {
+    const int i = threadIdx.x;
+    if (i <= S) off[i] = min(i * len, rows);
+}
+
+// out[m][n] = sum over s = 0..S-1, in that order, of part[s][m][n] (float32);
+// m < M rows of N columns, four columns per thread
+__global__ __launch_bounds__(kBwdThreads) void sum_slices_kernel(const float* __restrict__ part, int S, int64_t M,
+                                                                 int N, float* __restrict__ out) {
+    const int64_t i = (static_cast<int64_t>(blockIdx.x) * kBwdThreads + threadIdx.x) * 4;
+    const int64_t mn = M * N;
+    if (i >= mn) return;
+    f32x4 a = *reinterpret_cast<const f32x4*>(part + i);
+    for (int s = 1; s < S; ++s) a = a + *reinterpret_cast<const f32x4*>(part + s * mn + i);
+    __builtin_nontemporal_store(a, reinterpret_cast<f32x4*>(out + i));
+}
+
 // n 16-byte words of zeros at each of up to four addresses
 __global__ void zero_tails_kernel(uint8_t* a, uint8_t* b, uint8_t* c, uint8_t* d, int n) {
     const int i = threadIdx.x;
@@ -580,8 +598,20 @@ static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 namespace {
 struct BwdLayout {
-    size_t logits, dw, dY, dYs, H, dA, dH, Aact, xp, dXp, dXs, dxr, dl, ts, total;
+    size_t logits, dw, dY, dYs, H, dA, dH, Aact, xp, dXp, dXs, dxr, dl, ts, slices, bounds, total;
 };
+
+// K-slices of a single-group weight-gradient GEMM with `tiles` output tiles
+// over `rows` rows: enough slices to give 256 workgroups, each slice at least
+// 1024 rows, at most 64.  A function of the shape only, so the summation
+// order (and the bits) never depend on the device.
+int wgrad_slices(int64_t tiles, int64_t rows) {
+    int64_t s = (256 + tiles - 1) / tiles;
+    const int64_t by_rows = rows / 1024;
+    if (s > by_rows) s = by_rows;
+    if (s > 64) s = 64;
+    return s < 1 ? 1 : static_cast<int>(s);
+}
 BwdLayout bwd_layout(int64_t T, int D, int E, int K, int I, int Is) {
     const int64_t P = T * K;
     const int64_t rows2 = P * 2 * I > T * 2 * static_cast<int64_t>(Is) ? P * 2 * I : T * 2 * static_cast<int64_t>(Is);
@@ -608,6 +638,19 @@ BwdLayout bwd_layout(int64_t T, int D, int E, int K, int I, int Is) {
     l.dxr = take(4 * static_cast<size_t>(T) * D);
     l.dl = take(2 * static_cast<size_t>(T) * Epad + kZeroTail);
     l.ts = take(sizeof(int32_t) * (E + 1));
+    // partial sums of the sliced weight gradients (shared down, shared gate_up, router)
+    size_t sl = 0;
+    auto need = [&](int64_t M, int64_t N) {
+        const int S = wgrad_slices(cdiv(M, kT) * cdiv(N, kT), T);
+        if (S > 1) sl = std::max(sl, static_cast<size_t>(S) * M * N * 4);
+    };
+    if (Is > 0) {
+        need(D, Is);
+        need(2 * static_cast<int64_t>(Is), D);
+    }
+    need(E, D);
+    l.slices = take(sl);
+    l.bounds = take(sizeof(int32_t) * 65);
     l.total = b;
     return l;
 }
@@ -646,6 +689,8 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t stream) {
     float* dxr = reinterpret_cast<float*>(w + lo.dxr);
     uint16_t* dl = reinterpret_cast<uint16_t*>(w + lo.dl);
     int32_t* ts = reinterpret_cast<int32_t*>(w + lo.ts);
+    float* slices = reinterpret_cast<float*>(w + lo.slices);
+    int32_t* bounds = reinterpret_cast<int32_t*>(w + lo.bounds);
     const int64_t rows2 = P * 2 * I > T * 2 * static_cast<int64_t>(Is) ? P * 2 * I : T * 2 * static_cast<int64_t>(Is);
     // the zero tails sit right after each buffer's rows
     uint8_t* z_dY = reinterpret_cast<uint8_t*>(dY) + 2 * static_cast<size_t>(P) * D;
@@ -654,6 +699,32 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t stream) {
     uint8_t* z_dl = reinterpret_cast<uint8_t*>(dl) + 2 * static_cast<size_t>(T) * Epad;
 
     hipError_t err;
+    // A single-group weight gradient (K = the T rows).  With few output tiles
+    // its rows are cut into wgrad_slices() slices of a multiple of 64 rows,
+    // each slice's float32 partial written on its own, then summed in slice
+    // order: a fixed order for a given shape.
+    auto wgrad = [&](BwdGemm k1, float* out) -> hipError_t {
+        const int64_t tiles = cdiv(k1.M, kT) * cdiv(k1.N, kT);
+        const int S = wgrad_slices(tiles, k1.rows);
+        if (S == 1) {
+            k1.c = out;
+            return gemm<true, true, true>(k1, tiles, stream);
+        }
+        const int len = static_cast<int>(cdiv(cdiv(k1.rows, S), kSK) * kSK);
+        split_bounds_kernel<<<1, 65, 0, stream>>>(bounds, S, k1.rows, len);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        k1.offsets = bounds;
+        k1.G = S;
+        k1.c = slices;
+        k1.ldc = k1.N;
+        k1.c_gstride = static_cast<int64_t>(k1.m_valid) * k1.N;
+        if ((e = gemm<true, true, true>(k1, tiles * S, stream)) != hipSuccess) return e;
+        const int64_t mn4 = static_cast<int64_t>(k1.m_valid) * k1.N / 4;
+        sum_slices_kernel<<<static_cast<unsigned>(cdiv(mn4, kBwdThreads)), kBwdThreads, 0, stream>>>(
+            slices, S, k1.m_valid, k1.N, out);
+        return hipGetLastError();
+    };
     zero_tails_kernel<<<1, kZeroTail / 16, 0, stream>>>(z_dY, z_dYs, z_dH, z_dl, kZeroTail / 16);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if ((err = launch_router_logits(a.x, a.router, T, D, E, 0, logits, stream)) != hipSuccess) return err;
@@ -736,13 +807,13 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t stream) {
         sk.a = op(dYs, D);
         sk.a_zero = reinterpret_cast<const uint16_t*>(z_dYs);
         sk.b = op(Aact, Is);
-        sk.c = a.d_down_shared; sk.ldc = Is; sk.M = D; sk.N = Is; sk.m_valid = D;
-        if ((err = gemm<true, true, true>(sk, cdiv(sk.M, kT) * cdiv(sk.N, kT), stream)) != hipSuccess) return err;
+        sk.ldc = Is; sk.M = D; sk.N = Is; sk.m_valid = D;
+        if ((err = wgrad(sk, a.d_down_shared)) != hipSuccess) return err;
         sk.a = op(dH, 2 * Is);
         sk.a_zero = reinterpret_cast<const uint16_t*>(z_dH);
         sk.b = op(a.x, D);
-        sk.c = a.d_gate_up_shared; sk.ldc = D; sk.M = 2 * Is; sk.N = D; sk.m_valid = 2 * Is;
-        if ((err = gemm<true, true, true>(sk, cdiv(sk.M, kT) * cdiv(sk.N, kT), stream)) != hipSuccess) return err;
+        sk.ldc = D; sk.M = 2 * Is; sk.N = D; sk.m_valid = 2 * Is;
+        if ((err = wgrad(sk, a.d_gate_up_shared)) != hipSuccess) return err;
     }
 
     // router
@@ -763,8 +834,8 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t stream) {
         rk.a = op(dl, Epad);
         rk.a_zero = reinterpret_cast<const uint16_t*>(z_dl);
         rk.b = op(a.x, D);
-        rk.c = a.d_router; rk.ldc = D; rk.M = Epad; rk.N = D; rk.m_valid = E;
-        if ((err = gemm<true, true, true>(rk, cdiv(rk.M, kT) * cdiv(rk.N, kT), stream)) != hipSuccess) return err;
+        rk.ldc = D; rk.M = Epad; rk.N = D; rk.m_valid = E;
+        if ((err = wgrad(rk, a.d_router)) != hipSuccess) return err;
     }
     dx_assemble_kernel<<<static_cast<unsigned>(T), kBwdThreads, 0, stream>>>(dXp, a.inv_pos, Is > 0 ? dXs : nullptr,
                                                                              dxr, a.mask, T, D, K, a.dx);

@@ -49,6 +49,9 @@ CASES = [
     ("qnext", dict(T=200, D=256, E=64, K=8, I=128, Is=128), None, False),  # softmax, Zipf skew, shared
     ("q30", dict(T=130, D=256, E=16, K=4, I=192, Is=0), "sqrtsoftplus", False),  # N not a multiple of the tile
     ("dspark", dict(T=96, D=256, E=8, K=1, I=128, Is=0), None, False),     # top-1, no renorm, E = 8
+    # 3000 rows: the router's and the shared expert's weight gradients are cut
+    # into two K-slices (1536 + 1464 rows) summed in order
+    ("dsv4", dict(T=3000, D=256, E=16, K=2, I=128, Is=128), None, False),
 ]
 
 
