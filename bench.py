@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--no-invariance", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 1 GiB buffer 5 times (reference kernel for the HBM byte counters)")
+    ap.add_argument("--ep-shard", type=int, default=0,
+                    help="time moe_experts on the expert share of one of this many expert-parallel ranks")
     ap.add_argument("--backward", action="store_true",
                     help="time moe_backward (gradients of x and every weight) instead of the forward")
     ap.add_argument("--dense-reference", action="store_true",
@@ -182,17 +184,25 @@ def main():
     if args.backward:
         bench_backward(args, cfg, inp, layer, shape, x)
         return
+    if args.ep_shard > 1:
+        bench_ep_shard(args, cfg, layer, shape, x)
+        return
 
     # ---- timed region 1: moe_forward, whole steps ---------------------------
     for _ in range(args.warmup):
         layer.forward(x, out=out)
     torch.cuda.synchronize()
+    stream0 = torch.cuda.current_stream()
+    step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t_start = time.perf_counter()
-    for _ in range(args.steps):
+    step_ev[0].record(stream0)
+    for i in range(args.steps):
         layer.forward(x, out=out)
+        step_ev[i + 1].record(stream0)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     ms_per_step = wall / args.steps * 1e3
+    step_ms = [step_ev[i].elapsed_time(step_ev[i + 1]) for i in range(args.steps)]
     log(f"moe_forward: {ms_per_step:.3f} ms/step")
 
     # ---- timed region 2: the same layer through the stage entry points, with
@@ -275,6 +285,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
+        "ms_per_step_median": float(np.median(step_ms)),
+        "ms_per_step_min": float(np.min(step_ms)),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -308,6 +320,74 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def bench_ep_shard(args, cfg, layer, shape, x):
+    """moe_experts on the experts one of P expert-parallel ranks would own
+    (E/P experts, rank 0) with the rows the layer's routing sends them: the
+    part of an expert-parallel layer one GPU runs, at its real shape.  Its
+    rows are bitwise the full layer's (tests/test_gpu_ep_shard.py)."""
+    import numpy as np
+    import torch
+
+    import routing_grouped_gemm_gemv_amd as moe
+    B = moe.binding
+    P = args.ep_shard
+    if cfg.E % P:
+        raise SystemExit(f"E = {cfg.E} does not split over {P} ranks")
+    T = shape.T
+    _, tr = layer.forward(x, trace=True)
+    torch.cuda.synchronize()
+    Es = cfg.E // P
+    offs = tr["offsets"].cpu().numpy()
+    rows = int(offs[Es])
+    o_r = tr["offsets"][:Es + 1].contiguous()
+    sh = shape.replace(E=Es, Is=0, n_group=1, topk_group=1)
+    ws = layer.workspace(sh)
+    y = torch.empty(T * cfg.K, cfg.D, dtype=torch.bfloat16, device="cuda")
+    gu, dn = layer.weights["gate_up"][:Es], layer.weights["down"][:Es]
+
+    def step():
+        B.moe_experts(sh, x, tr["perm_token"], o_r, gu, dn, y, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    t_start = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(args.steps):
+        step()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
+    ms = float(np.mean(per))
+    same = bool(torch.equal(y[:rows].view(torch.int16), tr["y"][:rows].view(torch.int16)))
+    flops = 6.0 * cfg.D * cfg.I * rows
+    achieved = flops / (ms * 1e-3) / 1e12
+    print(json.dumps({
+        "metric": f"expert GEMMs of one of {P} expert-parallel ranks: TFLOP/s",
+        "value": achieved,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "ms_per_step_median": float(np.median(per)),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded; the rows the layer's routing sends to rank 0's experts)",
+        "config": {"workload": f"{cfg.name}-like layer, rank 0 of {P}: moe_experts", "T_total": T,
+                   "experts": Es, "rows": rows, "D": cfg.D, "I": cfg.I, "parallelism": f"ep{P} (one rank)"},
+        "roofline": {"kernel": "moe_experts (grouped gate_up+SwiGLU, grouped down)", "bound": "mfma",
+                     "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None},
+        "rows_bitwise_equal_full_layer": same,
+    }), flush=True)
 
 
 def bench_backward(args, cfg, inp, layer, shape, x):
