@@ -13,10 +13,10 @@
 // float32 accumulation):
 //   combine_bwd   dY[p] = bf16(w * G[t]);  dw[t, j] = <G[t], y[p]> (float64)
 //   gather        Xp = x[perm] (the routed rows in expert order)
-//   gemm          H = Xp W1_e^T (float32, recomputed)
 //   gemm          dA = dY W2_e (float32)
-//   swiglu_bwd    A = bf16(silu(g) u) as the forward formed it;
-//                 dH = bf16([dA u silu'(g), dA silu(g)])
+//   gemm          H = Xp W1_e^T recomputed in float32, never stored: its
+//                 epilogue forms A = bf16(silu(g) u) as the forward formed it
+//                 and dH = bf16([dA u silu'(g), dA silu(g)])
 //   gemm          dW2_e = dY_e^T A_e, K-grouped (float32)
 //   gemm          dXp = dH W1_e (float32)
 //   gemm          dW1_e = dH_e^T Xp_e, K-grouped
@@ -84,7 +84,31 @@ struct BwdGemm {
     int M, N, K;                // !GK: N, K fixed (M from the groups); GK: M, N fixed
     int kb_valid;               // !GK: B k-rows >= kb_valid are clamped (A is zero there)
     int m_valid;                // GK: output rows m >= m_valid are not stored
+    // SW (gate/up recompute with the SwiGLU backward in the epilogue): B is
+    // the expert's W1 [2I][D]; a tile takes gate rows c and up rows I + c of
+    // 128 columns c; dA [rows][I] float32 in, dH [rows][2I] and A [rows][I] bf16 out
+    int I;
+    const float* da;
+    uint16_t* dh;
+    uint16_t* act;
 };
+
+// two floats -> two bf16 (round to nearest even) in one word, low first
+__device__ __forceinline__ uint32_t bwd_pack_bf16(float lo, float hi) {
+    return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+// SwiGLU backward of one element: the forward's activation a = bf16(silu(g) u)
+// (the same expression the forward's epilogue evaluates) and the gate and up
+// gradients dg = dA u silu'(g), du = dA silu(g), float32.
+__device__ __forceinline__ void swiglu_grad(float g, float u, float d, float& dg, float& du, float& a) {
+    const float sg = 1.0f / (1.0f + expf(-g));
+    const float silu = g * sg;
+    const float dsilu = sg * (1.0f + g * (1.0f - sg));
+    dg = d * u * dsilu;
+    du = d * silu;
+    a = silu_mul_fast(g, u);
+}
 
 // m-tile prefix over groups of kT-row tiles (one workgroup of 1024 threads)
 __global__ __launch_bounds__(1024) void bwd_tile_prefix_kernel(const int32_t* __restrict__ offsets, int G,
@@ -105,8 +129,9 @@ __global__ __launch_bounds__(1024) void bwd_tile_prefix_kernel(const int32_t* __
     if (tid == 0) ts[0] = 0;
 }
 
-template <bool AT, bool BT, bool GK>
+template <bool AT, bool BT, bool GK, bool SW = false>
 __global__ __launch_bounds__(256) void bwd_gemm_kernel(BwdGemm p) {
+    static_assert(!SW || (!AT && !BT && !GK), "the SwiGLU epilogue is for the M-grouped K-major gate/up GEMM");
     __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[2 * kStageB + 8192];  // stages; the output staging needs 128 x 1040 B
     lds_u8* smem = (lds_u8*)(smem_raw);
     const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem));
@@ -117,7 +142,7 @@ __global__ __launch_bounds__(256) void bwd_gemm_kernel(BwdGemm p) {
     const int wn = wv & 1;
 
     // ---- the tile (XCD-aware: consecutive tiles on one XCD) ---------------------
-    const int ntn = (p.N + kT - 1) / kT;
+    const int ntn = SW ? (p.I + 127) / 128 : (p.N + kT - 1) / kT;
     const int64_t L = xcd_remap(blockIdx.x, gridDim.x);
     int g = 0, mt = 0, nt = 0;
     int64_t m0 = 0;     // !GK: first row of the tile
@@ -199,8 +224,12 @@ __global__ __launch_bounds__(256) void bwd_gemm_kernel(BwdGemm p) {
     // the group repeat its last row and are never stored)
     const uint32_t a_km = static_cast<uint32_t>(km_row) * lda2 + km_chunk * 16;
     const uint32_t a_km_lim = static_cast<uint32_t>(mrows - 1) * lda2 + km_chunk * 16;
-    const uint32_t b_km = static_cast<uint32_t>(n0 + km_row) * ldb2 + km_chunk * 16;
-    const uint32_t b_km_lim = static_cast<uint32_t>(p.N - 1) * ldb2 + km_chunk * 16;
+    // SW: tile row r of B is gate row c = 128 nt + r % 128 (waves 0, 1) or the
+    // matching up row I + c (waves 2, 3); columns past I repeat I - 1 (never stored)
+    const int b_row0 = SW ? (wv < 2 ? 0 : p.I) + nt * 128 + 64 * (wv & 1) + (lane >> 3) : n0 + km_row;
+    const int b_rowlim = SW ? (wv < 2 ? p.I : 2 * p.I) - 1 : p.N - 1;
+    const uint32_t b_km = static_cast<uint32_t>(b_row0) * ldb2 + km_chunk * 16;
+    const uint32_t b_km_lim = static_cast<uint32_t>(b_rowlim) * ldb2 + km_chunk * 16;
 
     auto dma = [&](int st, uint32_t stage_off, int q) {
         const int s = st < ns ? st : ns - 1;  // past the end: reload the last stage (never read)
@@ -245,7 +274,8 @@ __global__ __launch_bounds__(256) void bwd_gemm_kernel(BwdGemm p) {
     const int tx_base = (8 * tb + (ts_ >> 2)) * 512 + 8 * (ts_ & 3);
     auto frag = [&](uint32_t stage_off, int j, int op, int t) -> u32x4 {
         // op 0: A block t (rows 16 t of the wave's 128), op 1: B block t
-        const int wblk = op == 0 ? wm * 8 + t : wn * 8 + t;
+        // (SW: gate blocks 4 wn + t, then the matching up blocks 8 + 4 wn + t)
+        const int wblk = op == 0 ? wm * 8 + t : (SW ? (t < 4 ? 4 * wn + t : 4 + 4 * wn + t) : wn * 8 + t);
         const lds_u8* st = smem + stage_off + (op == 0 ? 0 : kOpB);
         const bool tr = op == 0 ? AT : BT;
         if (!tr) {
@@ -309,6 +339,58 @@ __global__ __launch_bounds__(256) void bwd_gemm_kernel(BwdGemm p) {
             sub(f1, f0, nxt, 0, true, st + 2, cur);
         }
         wait_vmem<0>();
+    }
+
+    if constexpr (SW) {
+        // ---- SwiGLU backward epilogue: acc[mb][nb] (gate) and acc[mb][nb + 4]
+        // (up) hold the same (row, column); dH gate and up halves, then A, each
+        // staged through LDS (256 rows x 272 B) and stored as whole 256-byte rows.
+        constexpr int kSR = 272;
+        const int c4 = 4 * (lane >> 4);
+        const int cl0 = 64 * wn + c4;  // tile column of block 0
+        auto put = [&](int buf, int mb, int nb, uint32_t lo, uint32_t hi) {
+            *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(
+                smem + buf * 256 * kSR + (wm * 128 + mb * 16 + (lane & 15)) * kSR + (cl0 + nb * 16) * 2) = u32x2{lo, hi};
+        };
+        auto drain = [&](int buf, uint16_t* base, int64_t ld) {
+            const int cc = nt * 128 + 8 * (lane & 15);
+            for (int r = 4 * wv + (lane >> 4); r < kT; r += 16) {
+                const u32x4 v = *reinterpret_cast<lds_u32x4*>(smem + buf * 256 * kSR + r * kSR + 16 * (lane & 15));
+                if (r < mrows && cc < p.I)
+                    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(base + (m0 + r) * ld + cc));
+            }
+        };
+        __syncthreads();  // every wave is done with the stages
+        uint32_t apk[8][4][2];  // A, packed, until the dH tiles have left LDS
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb) {
+            const int m = wm * 128 + mb * 16 + (lane & 15);
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) {
+                const int c = nt * 128 + cl0 + nb * 16;
+                f32x4 d = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (m < mrows && c < p.I) d = *reinterpret_cast<const f32x4*>(p.da + (m0 + m) * p.I + c);
+                float dg[4], du[4], av[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) swiglu_grad(acc[mb][nb][i], acc[mb][nb + 4][i], d[i], dg[i], du[i], av[i]);
+                put(0, mb, nb, bwd_pack_bf16(dg[0], dg[1]), bwd_pack_bf16(dg[2], dg[3]));
+                put(1, mb, nb, bwd_pack_bf16(du[0], du[1]), bwd_pack_bf16(du[2], du[3]));
+                apk[mb][nb][0] = bwd_pack_bf16(av[0], av[1]);
+                apk[mb][nb][1] = bwd_pack_bf16(av[2], av[3]);
+            }
+            __builtin_amdgcn_sched_barrier(0);  // one row block's dA loads live at a time
+        }
+        __syncthreads();
+        drain(0, p.dh, 2 * static_cast<int64_t>(p.I));
+        drain(1, p.dh + p.I, 2 * static_cast<int64_t>(p.I));
+        __syncthreads();
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) put(0, mb, nb, apk[mb][nb][0], apk[mb][nb][1]);
+        __syncthreads();
+        drain(0, p.act, p.I);
+        return;
     }
 
     // ---- output: through LDS, 128 rows at a time (row stride padded by 16
@@ -396,43 +478,6 @@ __global__ __launch_bounds__(kBwdThreads) void combine_bwd_kernel(
             *reinterpret_cast<u32x4*>(gs + t * D + d0) = gv;
         }
     }
-}
-
-// SwiGLU backward over rows [0, *rows_dev or rows): H [rows, 2I] float32 (gate
-// columns, then up), dA [rows, I] float32 -> dH [rows, 2I] bf16 and the
-// forward's activation A [rows, I] bf16.  Eight columns per thread.
-__global__ __launch_bounds__(kBwdThreads) void swiglu_bwd_kernel(
-    const float* __restrict__ H, const float* __restrict__ dA, const int32_t* __restrict__ rows_dev, int64_t rows,
-    int I, uint16_t* __restrict__ dH, uint16_t* __restrict__ A) {
-    const int64_t r = blockIdx.x;
-    const int64_t nrows = rows_dev ? *rows_dev : rows;
-    if (r >= nrows) return;
-    const int i0 = (blockIdx.y * kBwdThreads + threadIdx.x) * 8;
-    if (i0 >= I) return;
-    const float* hg = H + r * 2 * I + i0;
-    const float* hu = hg + I;
-    const float* da = dA + r * I + i0;
-    uint32_t og[4], ou[4], oa[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        float vg[2], vu[2], va[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const float g = hg[2 * q + h], u = hu[2 * q + h], d = da[2 * q + h];
-            const float sg = 1.0f / (1.0f + expf(-g));
-            const float silu = g * sg;
-            const float dsilu = sg * (1.0f + g * (1.0f - sg));
-            vg[h] = d * u * dsilu;
-            vu[h] = d * silu;
-            va[h] = silu_mul_fast(g, u);
-        }
-        og[q] = static_cast<uint32_t>(f32_to_bf16(vg[0])) | (static_cast<uint32_t>(f32_to_bf16(vg[1])) << 16);
-        ou[q] = static_cast<uint32_t>(f32_to_bf16(vu[0])) | (static_cast<uint32_t>(f32_to_bf16(vu[1])) << 16);
-        oa[q] = static_cast<uint32_t>(f32_to_bf16(va[0])) | (static_cast<uint32_t>(f32_to_bf16(va[1])) << 16);
-    }
-    *reinterpret_cast<u32x4*>(dH + r * 2 * I + i0) = u32x4{og[0], og[1], og[2], og[3]};
-    *reinterpret_cast<u32x4*>(dH + r * 2 * I + I + i0) = u32x4{ou[0], ou[1], ou[2], ou[3]};
-    *reinterpret_cast<u32x4*>(A + r * I + i0) = u32x4{oa[0], oa[1], oa[2], oa[3]};
 }
 
 // float64 score of one logit (softmax handled by the caller)
@@ -582,11 +627,11 @@ __global__ void zero_tails_kernel(uint8_t* a, uint8_t* b, uint8_t* c, uint8_t* d
 // ===========================================================================
 // tiles: an upper bound of the tile count (padded to a multiple of 8 for the
 // XCD mapping; tiles past the real count exit at once)
-template <bool AT, bool BT, bool GK>
+template <bool AT, bool BT, bool GK, bool SW = false>
 static hipError_t gemm(const BwdGemm& p, int64_t tiles, hipStream_t stream) {
     if (tiles <= 0) return hipSuccess;
     const int64_t n = (tiles + 7) / 8 * 8;
-    bwd_gemm_kernel<AT, BT, GK><<<dim3(static_cast<unsigned>(n)), 256, 0, stream>>>(p);
+    bwd_gemm_kernel<AT, BT, GK, SW><<<dim3(static_cast<unsigned>(n)), 256, 0, stream>>>(p);
     return hipGetLastError();
 }
 
@@ -598,7 +643,7 @@ static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 namespace {
 struct BwdLayout {
-    size_t logits, dw, dY, dYs, H, dA, dH, Aact, xp, dXp, dXs, dxr, dl, ts, slices, bounds, total;
+    size_t logits, dw, dY, dYs, dA, dH, Aact, xp, dXp, dXs, dxr, dl, ts, slices, bounds, total;
 };
 
 // K-slices of a single-group weight-gradient GEMM with `tiles` output tiles
@@ -628,7 +673,6 @@ BwdLayout bwd_layout(int64_t T, int D, int E, int K, int I, int Is) {
     l.dw = take(sizeof(double) * P);
     l.dY = take(2 * static_cast<size_t>(P) * D + kZeroTail);      // zero tail: K-grouped A operand
     l.dYs = take(2 * static_cast<size_t>(T) * D + kZeroTail);
-    l.H = take(4 * static_cast<size_t>(rows2));
     l.dA = take(4 * static_cast<size_t>(rows1));
     l.dH = take(2 * static_cast<size_t>(rows2) + kZeroTail);
     l.Aact = take(2 * static_cast<size_t>(rows1));
@@ -679,7 +723,6 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t stream) {
     double* dw = reinterpret_cast<double*>(w + lo.dw);
     uint16_t* dY = reinterpret_cast<uint16_t*>(w + lo.dY);
     uint16_t* dYs = reinterpret_cast<uint16_t*>(w + lo.dYs);
-    float* H = reinterpret_cast<float*>(w + lo.H);
     float* dA = reinterpret_cast<float*>(w + lo.dA);
     uint16_t* dH = reinterpret_cast<uint16_t*>(w + lo.dH);
     uint16_t* Aact = reinterpret_cast<uint16_t*>(w + lo.Aact);
@@ -744,21 +787,17 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t stream) {
     g.offsets = a.offsets;
     g.tile_start = ts;
     g.G = E;
-    // H = Xp W1_e^T
-    g.a = op(xp, D);
-    g.b = op(a.gate_up, D, static_cast<int64_t>(2) * I * D);
-    g.c = H; g.ldc = 2 * I; g.N = 2 * I; g.K = D; g.kb_valid = D;
-    if ((err = gemm<false, false, false>(g, mt_routed * cdiv(g.N, kT), stream)) != hipSuccess) return err;
     // dA = dY W2_e
     g.a = op(dY, D);
     g.b = op(a.down, I, static_cast<int64_t>(D) * I);
     g.c = dA; g.ldc = I; g.N = I; g.K = D; g.kb_valid = D;
     if ((err = gemm<false, true, false>(g, mt_routed * cdiv(g.N, kT), stream)) != hipSuccess) return err;
-    {
-        dim3 grid(static_cast<unsigned>(P), static_cast<unsigned>((I / 8 + kBwdThreads - 1) / kBwdThreads));
-        swiglu_bwd_kernel<<<grid, kBwdThreads, 0, stream>>>(H, dA, a.offsets + E, P, I, dH, Aact);
-        if ((err = hipGetLastError()) != hipSuccess) return err;
-    }
+    // H = Xp W1_e^T recomputed, and from it and dA: dH and A
+    g.a = op(xp, D);
+    g.b = op(a.gate_up, D, static_cast<int64_t>(2) * I * D);
+    g.c = nullptr; g.N = 2 * I; g.K = D; g.kb_valid = D;
+    g.I = I; g.da = dA; g.dh = dH; g.act = Aact;
+    if ((err = gemm<false, false, false, true>(g, mt_routed * cdiv(I, 128), stream)) != hipSuccess) return err;
     // dXp = dH W1_e
     g.a = op(dH, 2 * I);
     g.b = op(a.gate_up, D, static_cast<int64_t>(2) * I * D);
@@ -786,17 +825,15 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t stream) {
         BwdGemm s{};
         s.G = 1;
         s.rows = static_cast<int>(T);
-        s.a = op(a.x, D);
-        s.b = op(a.gate_up_shared, D);
-        s.c = H; s.ldc = 2 * Is; s.N = 2 * Is; s.K = D; s.kb_valid = D;
-        if ((err = gemm<false, false, false>(s, cdiv(T, kT) * cdiv(s.N, kT), stream)) != hipSuccess) return err;
         s.a = op(dYs, D);
         s.b = op(a.down_shared, Is);
         s.c = dA; s.ldc = Is; s.N = Is; s.K = D; s.kb_valid = D;
         if ((err = gemm<false, true, false>(s, cdiv(T, kT) * cdiv(s.N, kT), stream)) != hipSuccess) return err;
-        dim3 grid(static_cast<unsigned>(T), static_cast<unsigned>((Is / 8 + kBwdThreads - 1) / kBwdThreads));
-        swiglu_bwd_kernel<<<grid, kBwdThreads, 0, stream>>>(H, dA, nullptr, T, Is, dH, Aact);
-        if ((err = hipGetLastError()) != hipSuccess) return err;
+        s.a = op(a.x, D);
+        s.b = op(a.gate_up_shared, D);
+        s.c = nullptr; s.N = 2 * Is; s.K = D; s.kb_valid = D;
+        s.I = Is; s.da = dA; s.dh = dH; s.act = Aact;
+        if ((err = gemm<false, false, false, true>(s, cdiv(T, kT) * cdiv(Is, 128), stream)) != hipSuccess) return err;
         s.a = op(dH, 2 * Is);
         s.b = op(a.gate_up_shared, D);
         s.c = dXs; s.ldc = D; s.N = D; s.K = 2 * Is; s.kb_valid = 2 * Is;
