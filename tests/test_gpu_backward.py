@@ -185,3 +185,31 @@ def test_backward_full_size_sampled(name):
     torch.cuda.synchronize()
     for k in grads:
         assert torch.equal(grads[k].view(torch.int32), g2[k].view(torch.int32)), k
+
+
+def test_backward_dx_shuffle_and_padding_invariant():
+    """dx of a token is the same bits when the batch is shuffled and when it is
+    padded with masked rows; the routed experts' weight gradients (each a sum
+    over the expert's rows in token order, masked rows never among them) are
+    the same bits under padding too."""
+    cfg, inp, dout = _case("dsv4", dict(T=192, D=512, E=16, K=4, I=256, Is=256), None, False)
+    _, _, base = _run(inp, dout)
+    dx0 = to_host(base["dx"])
+    # shuffle
+    perm = np.random.default_rng(9).permutation(cfg.T)
+    sh = replace(inp, x=inp.x[perm])
+    _, _, g = _run(sh, dout[perm])
+    assert np.array_equal(to_host(g["dx"]).view(np.uint32), dx0[perm].view(np.uint32))
+    # padding: 64 extra rows (other hidden states, other output gradients), masked
+    pad = 64
+    rng = np.random.default_rng(10)
+    xp = np.concatenate([inp.x, inp.x[rng.integers(0, cfg.T, pad)][:, ::-1].copy()])
+    gp = np.concatenate([dout, dout[rng.integers(0, cfg.T, pad)]])
+    mask = np.concatenate([np.ones(cfg.T, np.uint8), np.zeros(pad, np.uint8)])
+    pd = replace(inp, cfg=replace(cfg, T=cfg.T + pad), x=xp, mask=mask)
+    _, _, gpad = _run(pd, gp)
+    dxp = to_host(gpad["dx"])
+    assert np.array_equal(dxp[:cfg.T].view(np.uint32), dx0.view(np.uint32))
+    assert np.all(dxp[cfg.T:] == 0)
+    for k in ("d_gate_up", "d_down"):
+        assert torch.equal(gpad[k].view(torch.int32), base[k].view(torch.int32)), k
