@@ -144,7 +144,7 @@ def main():
         dense_reference(cfg, cfg.T * cfg.K)
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1 "
+        print(json.dumps({"error": "the layer is measured on exactly one GPU; --gpus must be 1 "
                                    "(the multi-GPU expert-parallel design is described, not built)"}))
         sys.exit(2)
 

@@ -79,20 +79,20 @@ moe_status check_shape(const moe_shape* s) {
 // gfx950 only; the answer is cached per device
 moe_status check_device() {
     static std::mutex mu;
-    static int verdict[64];  // 0 unknown, 1 ok, 2 unsupported
+    static int arch_ok[64];  // 0 unknown, 1 ok, 2 unsupported
     int dev = -1;
     hipError_t err = hipGetDevice(&dev);
     if (err != hipSuccess) return fail(MOE_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(err));
     if (dev < 0 || dev >= 64) return fail(MOE_ERR_UNSUPPORTED, "device index %d out of range", dev);
     std::lock_guard<std::mutex> lock(mu);
-    if (verdict[dev] == 0) {
+    if (arch_ok[dev] == 0) {
         hipDeviceProp_t prop;
         err = hipGetDeviceProperties(&prop, dev);
         if (err != hipSuccess) return fail(MOE_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(err));
-        verdict[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
-        if (verdict[dev] == 2) return fail(MOE_ERR_UNSUPPORTED, "device %d is %s, not gfx950", dev, prop.gcnArchName);
+        arch_ok[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        if (arch_ok[dev] == 2) return fail(MOE_ERR_UNSUPPORTED, "device %d is %s, not gfx950", dev, prop.gcnArchName);
     }
-    if (verdict[dev] == 2) return fail(MOE_ERR_UNSUPPORTED, "device %d is not gfx950", dev);
+    if (arch_ok[dev] == 2) return fail(MOE_ERR_UNSUPPORTED, "device %d is not gfx950", dev);
     return MOE_OK;
 }
 
