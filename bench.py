@@ -41,7 +41,7 @@ def parse():
                     help="override the config's router score function")
     ap.add_argument("--groups", type=int, default=0, help="group-limited select: expert groups (0: the config's)")
     ap.add_argument("--topk-group", type=int, default=0, help="groups kept per token (with --groups)")
-    ap.add_argument("--cpu-sample", type=int, default=384, help="tokens timed on the CPU oracle (0: skip)")
+    ap.add_argument("--cpu-sample", type=int, default=2048, help="tokens timed on the CPU oracle (0: skip)")
     ap.add_argument("--no-invariance", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 1 GiB buffer 5 times (reference kernel for the HBM byte counters)")
@@ -203,6 +203,20 @@ def main():
     wall = time.perf_counter() - t_start
     ms_per_step = wall / args.steps * 1e3
     step_ms = [step_ev[i].elapsed_time(step_ev[i + 1]) for i in range(args.steps)]
+
+    # cold caches: a 1 GiB write between steps evicts the L2s and the 256 MB
+    # last-level cache; each step timed alone with HIP events on its stream
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    cold_ms = []
+    for _ in range(min(args.steps, 10)):
+        flush.fill_(1.0)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream0)
+        layer.forward(x, out=out)
+        e1.record(stream0)
+        torch.cuda.synchronize()
+        cold_ms.append(e0.elapsed_time(e1))
+    del flush
     log(f"moe_forward: {ms_per_step:.3f} ms/step")
 
     # ---- timed region 2: the same layer through the stage entry points, with
@@ -287,6 +301,7 @@ def main():
         "ms_per_step": ms_per_step,
         "ms_per_step_median": float(np.median(step_ms)),
         "ms_per_step_min": float(np.min(step_ms)),
+        "ms_per_step_cold_median": float(np.median(cold_ms)),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
