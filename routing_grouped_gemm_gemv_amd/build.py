@@ -12,7 +12,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
-SOURCES = ["api.hip", "route.hip", "permute.hip", "experts.hip", "combine.hip", "backward.hip"]
+SOURCES = ["api.hip", "route.hip", "permute.hip", "experts.hip", "skinny.hip", "combine.hip", "backward.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

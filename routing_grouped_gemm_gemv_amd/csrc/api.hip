@@ -223,6 +223,18 @@ moe_status moe_permute(const moe_shape* shape, const int32_t* topk_ids, int32_t*
     return ok();
 }
 
+// The routed-expert MLP: the skinny kernels when groups hold few rows on
+// average (decode-sized batches), the tiled persistent kernels otherwise.
+// Both compute every element by the same MFMA chain and rounding, so the
+// choice never changes a result.
+static hipError_t run_experts(const void* x, int64_t x_rows, const int32_t* perm, const int32_t* offsets, int G,
+                              int64_t rows, int D, int I, int dtype, const void* gate_up, const void* down, void* y,
+                              void* ws, hipStream_t stream) {
+    if (moe::experts_use_skinny(rows, G, dtype))
+        return moe::launch_experts_skinny(x, perm, offsets, G, rows, D, I, gate_up, down, y, ws, stream);
+    return moe::launch_experts(x, x_rows, perm, offsets, G, rows, D, I, dtype, gate_up, down, y, ws, stream);
+}
+
 moe_status moe_experts(const moe_shape* shape, const void* x, const int32_t* perm_token, const int32_t* offsets,
                        const void* gate_up, const void* down, void* y, void* ws, size_t ws_bytes,
                        hipStream_t stream) {
@@ -237,7 +249,7 @@ moe_status moe_experts(const moe_shape* shape, const void* x, const int32_t* per
     if ((st = check_device()) != MOE_OK) return st;
     const int64_t rows = shape->T * shape->K;
     const int64_t x_rows = perm_token != nullptr ? shape->T : rows;
-    if ((st = hip_status(moe::launch_experts(x, x_rows, perm_token, offsets, shape->E, rows, shape->D, shape->I,
+    if ((st = hip_status(run_experts(x, x_rows, perm_token, offsets, shape->E, rows, shape->D, shape->I,
                                              shape->dtype, gate_up, down, y, ws, stream),
                          "experts launch")) != MOE_OK)
         return st;
@@ -308,12 +320,12 @@ static moe_status forward_impl(const moe_shape* shape, const moe_weights* weight
                                              counts, offsets, perm, inv, stream),
                          "permute launch")) != MOE_OK)
         return st;
-    if ((st = hip_status(moe::launch_experts(x, T, perm, offsets, shape->E, T * shape->K, shape->D, shape->I,
+    if ((st = hip_status(run_experts(x, T, perm, offsets, shape->E, T * shape->K, shape->D, shape->I,
                                              shape->dtype, weights->gate_up, weights->down, y, exw, stream),
                          "routed experts launch")) != MOE_OK)
         return st;
     if (sh != nullptr) {
-        if ((st = hip_status(moe::launch_experts(x, T, nullptr, nullptr, 1, T, shape->D, shape->Is, shape->dtype,
+        if ((st = hip_status(run_experts(x, T, nullptr, nullptr, 1, T, shape->D, shape->Is, shape->dtype,
                                                  weights->gate_up_shared, weights->down_shared, sh, exw, stream),
                              "shared expert launch")) != MOE_OK)
             return st;

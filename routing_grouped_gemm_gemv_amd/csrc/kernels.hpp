@@ -52,6 +52,13 @@ size_t experts_ws_bytes(int64_t rows_max, int G, int D, int I, int dtype);
 hipError_t launch_experts(const void* x, int64_t x_rows, const int32_t* perm_token, const int32_t* offsets,
                           int G, int64_t rows_max, int D, int I, int dtype, const void* gate_up,
                           const void* down, void* y, void* ws, hipStream_t stream);
+// few rows per group (decode-sized batches): one wave per 16-row block and
+// 16-column weight slice, the same bits as launch_experts; bf16 only, the
+// same workspace
+bool experts_use_skinny(int64_t rows_max, int G, int dtype);
+hipError_t launch_experts_skinny(const void* x, const int32_t* perm_token, const int32_t* offsets, int G,
+                                 int64_t rows_max, int D, int I, const void* gate_up, const void* down, void* y,
+                                 void* ws, hipStream_t stream);
 
 // ---- combine -----------------------------------------------------------------
 // mode 0: float32 fold; mode 1: float64 sum rounded once
