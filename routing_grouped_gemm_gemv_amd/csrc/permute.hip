@@ -208,11 +208,96 @@ __global__ __launch_bounds__(256) void permute_scatter_kernel(
     }
 }
 
+// All three passes in one workgroup when every pair fits one block (the
+// block's base rows are zero), for decode-sized batches: one launch instead
+// of three, the same rows.
+__global__ __launch_bounds__(256) void permute_single_kernel(
+    const int32_t* __restrict__ ids, int64_t P, int K, int E, int ppb, int id_bits, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm_token, int32_t* __restrict__ inv_pos) {
+    __shared__ int hist[kPermWaves][kMaxExperts];
+    __shared__ int offs[kMaxExperts + 1];
+    __shared__ int part[256];
+    const int tid = threadIdx.x;
+    const int wv = tid >> 6;
+    const int lane = lane_id();
+    for (int i = tid; i < kPermWaves * E; i += 256) hist[i / E][i % E] = 0;
+    __syncthreads();
+    const int per_wave = ppb / kPermWaves;
+    const int64_t w_begin = static_cast<int64_t>(wv) * per_wave;
+    const int64_t w_end = w_begin + per_wave;
+    wave_histogram(ids, P, w_begin, w_end, id_bits, hist[wv]);
+    __syncthreads();
+    // counts, then their exclusive scan into offs[0..E]
+    int v[4];
+    int sum = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int e = 4 * tid + j;
+        v[j] = e < E ? hist[0][e] + hist[1][e] + hist[2][e] + hist[3][e] : 0;
+        if (e < E) counts[e] = v[j];
+        sum += v[j];
+    }
+    part[tid] = sum;
+    __syncthreads();
+    for (int d = 1; d < 256; d <<= 1) {
+        const int u = tid >= d ? part[tid - d] : 0;
+        __syncthreads();
+        part[tid] += u;
+        __syncthreads();
+    }
+    int run = part[tid] - sum;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int e = 4 * tid + j;
+        if (e < E) offs[e] = run;
+        run += v[j];
+    }
+    if (tid == 255) offs[E] = part[255];
+    __syncthreads();
+    for (int e = tid; e <= E; e += 256) offsets[e] = offs[e];
+    // per-wave base rows, then the scatter of the three-kernel path
+    for (int e = tid; e < E; e += 256) {
+        int r = offs[e];
+#pragma unroll
+        for (int w = 0; w < kPermWaves; ++w) {
+            const int h = hist[w][e];
+            hist[w][e] = r;
+            r += h;
+        }
+    }
+    __syncthreads();
+    const uint64_t lt = (1ull << lane) - 1ull;
+    int* row = hist[wv];
+    for (int64_t seg = w_begin; seg < w_end; seg += 64) {
+        const int64_t p = seg + lane;
+        const bool in = p < w_end && p < P;
+        int e = -1;
+        if (in) e = ids[p];
+        const bool valid = e >= 0;
+        const uint64_t m = match_mask(valid ? e : 0, valid, id_bits);
+        if (valid) {
+            const int pos = row[e] + __popcll(m & lt);
+            perm_token[pos] = static_cast<int32_t>(p / K);
+            inv_pos[p] = pos;
+        } else if (in) {
+            inv_pos[p] = -1;
+        }
+        __builtin_amdgcn_wave_barrier();
+        if (valid && (m & lt) == 0ull) row[e] += __popcll(m);
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
 hipError_t launch_permute(const int32_t* ids, int64_t T, int K, int E, int32_t* ws_i32,
                           int32_t* counts, int32_t* offsets, int32_t* perm_token, int32_t* inv_pos,
                           hipStream_t stream) {
     const int64_t P = T * K;
     const PermutePlan pl = permute_plan(P, E);
+    if (pl.blocks == 1) {
+        permute_single_kernel<<<1, 256, 0, stream>>>(ids, P, K, E, pl.pairs_per_block, pl.id_bits, counts, offsets,
+                                                     perm_token, inv_pos);
+        return hipGetLastError();
+    }
     int32_t* block_hist = ws_i32;
     int32_t* block_base = ws_i32 + static_cast<int64_t>(E) * pl.blocks;
     permute_count_kernel<<<pl.blocks, 256, 0, stream>>>(ids, P, E, pl.pairs_per_block, pl.blocks, pl.id_bits,

@@ -27,6 +27,7 @@ namespace moe {
 constexpr int kRtTok = 64;
 constexpr int kRtExp = 64;
 constexpr int kRtK = 64;  // k per LDS stage; fp32 partial sums span four stages (256 products)
+constexpr int64_t kRouteSmallT = 64;  // at most this many tokens: the decode-sized router
 
 __global__ __launch_bounds__(256) void router_logits_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int64_t T, int D, int E,
@@ -983,8 +984,68 @@ __global__ __launch_bounds__(256) void route_fused_bf16_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// router logits for decode-sized batches: one wave per 16 tokens x 16 experts,
+// operand fragments loaded straight from memory with kRdU 32-wide k steps in
+// flight.  The same MFMA chain, chunking (float32 over 256 products, then
+// float64 in k order) and 16-aligned token and expert blocks as the kernels
+// above, so the same bits.
+// ---------------------------------------------------------------------------
+constexpr int kRdU = 8;
+
+__global__ __launch_bounds__(64) void router_logits_small_kernel(const uint16_t* __restrict__ x,
+                                                                 const uint16_t* __restrict__ w, int64_t T, int D,
+                                                                 int E, double* __restrict__ out) {
+    const int lane = threadIdx.x;
+    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * 16;
+    const int e0 = blockIdx.y * 16;
+    int64_t tr = t0 + (lane & 15);
+    if (tr > T - 1) tr = T - 1;  // rows past T repeat row T-1; never stored
+    int er = e0 + (lane & 15);
+    if (er > E - 1) er = E - 1;
+    const int kq = 8 * (lane >> 4);
+    const uint16_t* xp = x + tr * D + kq;
+    const uint16_t* wp = w + static_cast<int64_t>(er) * D + kq;
+    double acc64[4] = {0.0, 0.0, 0.0, 0.0};
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int S = D / 32;
+    for (int s0 = 0; s0 < S; s0 += kRdU) {  // kRdU = 8 steps = one 256-product chunk
+        u32x4 a[kRdU], b[kRdU];
+#pragma unroll
+        for (int u = 0; u < kRdU; ++u) {
+            const int s = s0 + u < S ? s0 + u : S - 1;
+            a[u] = *reinterpret_cast<const u32x4*>(xp + 32 * s);
+            b[u] = *reinterpret_cast<const u32x4*>(wp + 32 * s);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // the chunk's loads all in flight before its MFMAs
+        acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < kRdU; ++u) {
+            if (s0 + u >= S) break;  // uniform
+            acc = mfma_bf16(a[u], b[u], acc);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc64[i] += static_cast<double>(acc[i]);
+    }
+    const int e = e0 + (lane & 15);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t t = t0 + 4 * (lane >> 4) + i;
+        if (t < T && e < E) out[t * E + e] = acc64[i];
+    }
+}
+
+// whether the decode-sized router (small logits kernel + top-k kernel) runs
+static bool route_small(int64_t T, int dtype) { return dtype == 0 && T <= kRouteSmallT; }
+
 hipError_t launch_router_logits(const void* x, const void* router, int64_t T, int D, int E,
                                 int dtype, double* logits64, hipStream_t stream) {
+    if (route_small(T, dtype)) {
+        dim3 grid(static_cast<unsigned>((T + 15) / 16), static_cast<unsigned>((E + 15) / 16));
+        router_logits_small_kernel<<<grid, 64, 0, stream>>>(static_cast<const uint16_t*>(x),
+                                                            static_cast<const uint16_t*>(router), T, D, E, logits64);
+        return hipGetLastError();
+    }
     if (dtype == 0) {
         dim3 grid(static_cast<unsigned>((T + kRtTok - 1) / kRtTok), static_cast<unsigned>((E + kRtExp - 1) / kRtExp));
         router_logits_bf16_kernel<<<grid, 256, 0, stream>>>(static_cast<const uint16_t*>(x),
@@ -1020,7 +1081,7 @@ hipError_t launch_route(const void* x, const void* router, int64_t T, int D, int
                         int score, int renorm, float route_scale, int n_group, int topk_group, const float* bias,
                         const uint8_t* mask, double* logits64, float* logits_out, int32_t* ids, float* w,
                         hipStream_t stream) {
-    if (!route_fused(E, dtype, n_group)) {
+    if (!route_fused(E, dtype, n_group) || route_small(T, dtype)) {
         hipError_t err = launch_router_logits(x, router, T, D, E, dtype, logits64, stream);
         if (err != hipSuccess) return err;
         return launch_topk(logits64, T, E, K, score, renorm, route_scale, n_group, topk_group, bias, mask,
