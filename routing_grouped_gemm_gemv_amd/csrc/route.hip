@@ -27,7 +27,10 @@ namespace moe {
 constexpr int kRtTok = 64;
 constexpr int kRtExp = 64;
 constexpr int kRtK = 64;  // k per LDS stage; fp32 partial sums span four stages (256 products)
-constexpr int64_t kRouteSmallT = 64;  // at most this many tokens: the decode-sized router
+// the small-batch router runs while T * E is at most this (each of its waves
+// re-reads 16 hidden rows and 16 router rows, so its traffic grows with T * E;
+// measured crossover with the fused router on the Qwen3-30B- and DSV4-like layers)
+constexpr int64_t kRouteSmallTE = int64_t{1} << 18;
 
 __global__ __launch_bounds__(256) void router_logits_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int64_t T, int D, int E,
@@ -1036,11 +1039,11 @@ __global__ __launch_bounds__(64) void router_logits_small_kernel(const uint16_t*
 }
 
 // whether the decode-sized router (small logits kernel + top-k kernel) runs
-static bool route_small(int64_t T, int dtype) { return dtype == 0 && T <= kRouteSmallT; }
+static bool route_small(int64_t T, int E, int dtype) { return dtype == 0 && T * E <= kRouteSmallTE; }
 
 hipError_t launch_router_logits(const void* x, const void* router, int64_t T, int D, int E,
                                 int dtype, double* logits64, hipStream_t stream) {
-    if (route_small(T, dtype)) {
+    if (route_small(T, E, dtype)) {
         dim3 grid(static_cast<unsigned>((T + 15) / 16), static_cast<unsigned>((E + 15) / 16));
         router_logits_small_kernel<<<grid, 64, 0, stream>>>(static_cast<const uint16_t*>(x),
                                                             static_cast<const uint16_t*>(router), T, D, E, logits64);
@@ -1081,7 +1084,7 @@ hipError_t launch_route(const void* x, const void* router, int64_t T, int D, int
                         int score, int renorm, float route_scale, int n_group, int topk_group, const float* bias,
                         const uint8_t* mask, double* logits64, float* logits_out, int32_t* ids, float* w,
                         hipStream_t stream) {
-    if (!route_fused(E, dtype, n_group) || route_small(T, dtype)) {
+    if (!route_fused(E, dtype, n_group) || route_small(T, E, dtype)) {
         hipError_t err = launch_router_logits(x, router, T, D, E, dtype, logits64, stream);
         if (err != hipSuccess) return err;
         return launch_topk(logits64, T, E, K, score, renorm, route_scale, n_group, topk_group, bias, mask,
