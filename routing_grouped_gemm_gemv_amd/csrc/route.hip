@@ -1039,7 +1039,9 @@ __global__ __launch_bounds__(64) void router_logits_small_kernel(const uint16_t*
 }
 
 // whether the decode-sized router (small logits kernel + top-k kernel) runs
-static bool route_small(int64_t T, int E, int dtype) { return dtype == 0 && T * E <= kRouteSmallTE; }
+static bool route_small(int64_t T, int E, int dtype) {
+    return dtype == 0 && T <= 1024 && T * E <= kRouteSmallTE;
+}
 
 hipError_t launch_router_logits(const void* x, const void* router, int64_t T, int D, int E,
                                 int dtype, double* logits64, hipStream_t stream) {
