@@ -41,7 +41,7 @@ def parse():
                     help="override the config's router score function")
     ap.add_argument("--groups", type=int, default=0, help="group-limited select: expert groups (0: the config's)")
     ap.add_argument("--topk-group", type=int, default=0, help="groups kept per token (with --groups)")
-    ap.add_argument("--cpu-sample", type=int, default=2048, help="tokens timed on the CPU oracle (0: skip)")
+    ap.add_argument("--cpu-sample", type=int, default=4096, help="tokens timed on the CPU oracle (0: skip)")
     ap.add_argument("--no-invariance", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 1 GiB buffer 5 times (reference kernel for the HBM byte counters)")
