@@ -93,3 +93,24 @@ def test_token_shuffles(pool, k):
     assert np.array_equal(o, ref["out"][perm])
     assert np.array_equal(i, ref["ids"][perm])
     assert np.array_equal(w, ref["w"][perm])
+
+
+@pytest.mark.parametrize("name", ["dsv4", "qnext"])
+def test_prefixes_across_the_decode_paths(name):
+    """The small-batch paths (skinny experts, the shared expert's skinny path
+    up to 64 rows, the small-batch router, the one-workgroup permute) give
+    each token the same bits as the tiled paths: prefixes on both sides of
+    every switch, against the 2048-token batch (DeepSeek-V4- and
+    Qwen3-Next-like layers, both with a shared expert)."""
+    cfg = get_config(name, T=2048)
+    inp = make_inputs(cfg)
+    layer = make_layer(inp)
+    x = to_dev(inp.x)
+    full, trf = layer.forward(x, trace=True)
+    torch.cuda.synchronize()
+    for T in (1, 2, 15, 16, 17, 63, 64, 65, 100, 200, 341, 342, 1000):
+        sub, trs = layer.forward(x[:T].contiguous(), trace=True)
+        torch.cuda.synchronize()
+        assert torch.equal(sub.view(torch.int16), full[:T].view(torch.int16)), T
+        assert torch.equal(trs["topk_ids"], trf["topk_ids"][:T]), T
+        assert torch.equal(trs["topk_w"].view(torch.int32), trf["topk_w"][:T].view(torch.int32)), T
