@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--no-invariance", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 1 GiB buffer 5 times (reference kernel for the HBM byte counters)")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of moe_forward captured in a HIP graph (launch overhead removed)")
     ap.add_argument("--ep-shard", type=int, default=0,
                     help="time moe_experts on the expert share of one of this many expert-parallel ranks")
     ap.add_argument("--backward", action="store_true",
@@ -186,6 +188,9 @@ def main():
         return
     if args.ep_shard > 1:
         bench_ep_shard(args, cfg, layer, shape, x)
+        return
+    if args.graph:
+        bench_graph(args, cfg, layer, x, out)
         return
 
     # ---- timed region 1: moe_forward, whole steps ---------------------------
@@ -335,6 +340,55 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def bench_graph(args, cfg, layer, x, out):
+    """moe_forward captured once in a HIP graph and replayed: the layer
+    without host launch overhead (decode-sized batches are launch-bound).
+    Every replay gives the eager bits (tests/test_gpu_graph.py)."""
+    import numpy as np
+    import torch
+
+    layer.forward(x, out=out)  # the workspace exists before the capture
+    torch.cuda.synchronize()
+    ref = out.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer.forward(x, out=out)
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    t_start = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(args.steps):
+        g.replay()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
+    same = bool(torch.equal(out.view(torch.int16), ref.view(torch.int16)))
+    ms = wall / args.steps * 1e3
+    print(json.dumps({
+        "metric": "MoE-layer tokens/s @1 GPU, moe_forward replayed from a HIP graph",
+        "value": cfg.T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "ms_per_step_median": float(np.median(per)),
+        "ms_per_step_min": float(np.min(per)),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded; shapes and value distributions of the configs, random-init weights)",
+        "config": {"workload": f"{cfg.name}-like MoE layer forward, HIP graph replay", "T": cfg.T, "D": cfg.D,
+                   "E": cfg.E, "K": cfg.K, "I": cfg.I, "Is": cfg.Is, "parallelism": "single GPU"},
+        "replay_bitwise_equal_eager": same,
+    }), flush=True)
 
 
 def bench_ep_shard(args, cfg, layer, shape, x):
