@@ -24,7 +24,13 @@
  *     kernel runs, outputs are untouched and the status says why; the text of
  *     the last error of the calling thread is in moe_last_error().  There is
  *     no fallback to other numerics (fail closed: RL-Kernel roadmap, issue
- *     buckets).  T == 0 returns MOE_OK and launches nothing.
+ *     buckets).  T == 0 returns MOE_OK and launches nothing (moe_backward
+ *     then zeroes the weight gradients: sums over no tokens); buffers of T
+ *     rows (x, out, dout, dx, the trace) and the workspace may then be NULL.
+ *   - Alignment: activations, weights, outputs, gradients, y, shared_out and
+ *     the workspace are moved in 16-byte vectors and must start on a 16-byte
+ *     boundary; the int32 arrays, the per-token float32 arrays, logits and
+ *     sel_bias on a 4-byte one.  Any other pointer is MOE_ERR_INVALID.
  *   - Kernel faults surface at the caller's next synchronisation; launch
  *     errors return MOE_ERR_HIP.
  *   - Supported shapes: D, I (and Is when non-zero) multiples of 64;
@@ -280,7 +286,8 @@ moe_status moe_backward_workspace_size(const moe_shape* shape, size_t* bytes);
  * fwd: the trace of the moe_forward call being differentiated, with
  * topk_ids, topk_w, offsets, perm_token, inv_pos and y set (the other fields
  * are not read).  Every pointer of grads is written in full (experts no token
- * picked get zero gradients).  ws: moe_backward_workspace_size() bytes. */
+ * picked get zero gradients; with T == 0 every weight gradient is zero and
+ * ws may be NULL).  ws: moe_backward_workspace_size() bytes. */
 moe_status moe_backward(const moe_shape* shape, const moe_weights* weights, const void* x, const uint8_t* mask,
                         const moe_trace* fwd, const void* dout, const moe_grads* grads, void* ws, size_t ws_bytes,
                         hipStream_t stream);

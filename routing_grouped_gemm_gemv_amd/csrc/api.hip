@@ -7,6 +7,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <initializer_list>
 #include <mutex>
 #include <string>
 
@@ -103,6 +104,15 @@ moe_status hip_status(hipError_t err, const char* what) {
 
 size_t elem_bytes(int dtype) { return dtype == MOE_BF16 ? 2 : 4; }
 
+// Whether every non-NULL pointer is a multiple of `align` bytes.  The kernels
+// move activations, weights, outputs, gradients and workspace in 16-byte
+// vectors and index arrays and per-token floats as 4-byte words.
+bool aligned(size_t align, std::initializer_list<const void*> ptrs) {
+    for (const void* p : ptrs)
+        if (p != nullptr && reinterpret_cast<uintptr_t>(p) % align != 0) return false;
+    return true;
+}
+
 size_t route_ws(const moe_shape* s) { return align256(sizeof(double) * static_cast<size_t>(s->T) * s->E); }
 size_t permute_ws(const moe_shape* s) { return align256(moe::permute_ws_bytes(s->T * s->K, s->E)); }
 size_t experts_ws(const moe_shape* s) { return align256(moe::experts_ws_bytes(s->T * s->K, s->E, s->D, s->I, s->dtype)); }
@@ -171,8 +181,10 @@ moe_status moe_route(const moe_shape* shape, const void* x, const void* router, 
                      size_t ws_bytes, hipStream_t stream) {
     moe_status st = check_shape(shape);
     if (st != MOE_OK) return st;
-    if (!x || !router || !topk_ids || !topk_w) return fail(MOE_ERR_INVALID, "moe_route: x, router, topk_ids and topk_w are required");
+    if (!aligned(16, {x, router, ws}) || !aligned(4, {sel_bias, logits, topk_ids, topk_w}))
+        return fail(MOE_ERR_INVALID, "moe_route: x, router and ws must be 16-byte aligned, the other arrays 4-byte");
     if (shape->T == 0) return ok();
+    if (!x || !router || !topk_ids || !topk_w) return fail(MOE_ERR_INVALID, "moe_route: x, router, topk_ids and topk_w are required");
     if (!ws || ws_bytes < route_ws(shape))
         return fail(MOE_ERR_WORKSPACE, "moe_route needs %zu workspace bytes, got %zu", route_ws(shape), ws ? ws_bytes : 0);
     if ((st = check_device()) != MOE_OK) return st;
@@ -190,9 +202,11 @@ moe_status moe_route_replay(const moe_shape* shape, const void* x, const void* r
                             size_t ws_bytes, hipStream_t stream) {
     moe_status st = check_shape(shape);
     if (st != MOE_OK) return st;
+    if (!aligned(16, {x, router, ws}) || !aligned(4, {replay_ids, logits, topk_ids, topk_w}))
+        return fail(MOE_ERR_INVALID, "moe_route_replay: x, router and ws must be 16-byte aligned, the other arrays 4-byte");
+    if (shape->T == 0) return ok();
     if (!x || !router || !replay_ids || !topk_ids || !topk_w)
         return fail(MOE_ERR_INVALID, "moe_route_replay: x, router, replay_ids, topk_ids and topk_w are required");
-    if (shape->T == 0) return ok();
     if (!ws || ws_bytes < route_ws(shape))
         return fail(MOE_ERR_WORKSPACE, "moe_route_replay needs %zu workspace bytes, got %zu", route_ws(shape),
                     ws ? ws_bytes : 0);
@@ -210,9 +224,11 @@ moe_status moe_permute(const moe_shape* shape, const int32_t* topk_ids, int32_t*
                        int32_t* perm_token, int32_t* inv_pos, void* ws, size_t ws_bytes, hipStream_t stream) {
     moe_status st = check_shape(shape);
     if (st != MOE_OK) return st;
+    if (!aligned(16, {ws}) || !aligned(4, {topk_ids, counts, offsets, perm_token, inv_pos}))
+        return fail(MOE_ERR_INVALID, "moe_permute: ws must be 16-byte aligned, the int32 arrays 4-byte");
+    if (shape->T == 0) return ok();
     if (!topk_ids || !counts || !offsets || !perm_token || !inv_pos)
         return fail(MOE_ERR_INVALID, "moe_permute: topk_ids, counts, offsets, perm_token and inv_pos are required");
-    if (shape->T == 0) return ok();
     if (!ws || ws_bytes < permute_ws(shape))
         return fail(MOE_ERR_WORKSPACE, "moe_permute needs %zu workspace bytes, got %zu", permute_ws(shape), ws ? ws_bytes : 0);
     if ((st = check_device()) != MOE_OK) return st;
@@ -240,10 +256,12 @@ moe_status moe_experts(const moe_shape* shape, const void* x, const int32_t* per
                        hipStream_t stream) {
     moe_status st = check_shape(shape);
     if (st != MOE_OK) return st;
+    if (!aligned(16, {x, gate_up, down, y, ws}) || !aligned(4, {perm_token, offsets}))
+        return fail(MOE_ERR_INVALID, "moe_experts: x, gate_up, down, y and ws must be 16-byte aligned, the int32 arrays 4-byte");
+    if (shape->T == 0) return ok();
     if (!x || !gate_up || !down || !y) return fail(MOE_ERR_INVALID, "moe_experts: x, gate_up, down and y are required");
     if (offsets == nullptr && shape->E != 1)
         return fail(MOE_ERR_INVALID, "moe_experts: offsets may be NULL only for a single group (E == 1)");
-    if (shape->T == 0) return ok();
     if (!ws || ws_bytes < experts_ws(shape))
         return fail(MOE_ERR_WORKSPACE, "moe_experts needs %zu workspace bytes, got %zu", experts_ws(shape), ws ? ws_bytes : 0);
     if ((st = check_device()) != MOE_OK) return st;
@@ -260,9 +278,11 @@ moe_status moe_combine(const moe_shape* shape, const void* y, const int32_t* inv
                        const void* shared_out, int32_t out_dtype, void* out, hipStream_t stream) {
     moe_status st = check_shape(shape);
     if (st != MOE_OK) return st;
-    if (!y || !inv_pos || !topk_w || !out) return fail(MOE_ERR_INVALID, "moe_combine: y, inv_pos, topk_w and out are required");
+    if (!aligned(16, {y, shared_out, out}) || !aligned(4, {inv_pos, topk_w}))
+        return fail(MOE_ERR_INVALID, "moe_combine: y, shared_out and out must be 16-byte aligned, inv_pos and topk_w 4-byte");
     if (out_dtype != MOE_BF16 && out_dtype != MOE_F32) return fail(MOE_ERR_INVALID, "unknown out_dtype %d", out_dtype);
     if (shape->T == 0) return ok();
+    if (!y || !inv_pos || !topk_w || !out) return fail(MOE_ERR_INVALID, "moe_combine: y, inv_pos, topk_w and out are required");
     if ((st = check_device()) != MOE_OK) return st;
     if ((st = hip_status(moe::launch_combine(y, inv_pos, topk_w, shared_out, shape->T, shape->D, shape->K, shape->dtype,
                                              out_dtype, shape->combine, out, stream),
@@ -277,13 +297,25 @@ static moe_status forward_impl(const moe_shape* shape, const moe_weights* weight
                                hipStream_t stream) {
     moe_status st = check_shape(shape);
     if (st != MOE_OK) return st;
-    if (!weights || !x || !out) return fail(MOE_ERR_INVALID, "moe_forward: weights, x and out are required");
+    if (!weights) return fail(MOE_ERR_INVALID, "moe_forward: weights are required");
     if (!weights->router || !weights->gate_up || !weights->down)
         return fail(MOE_ERR_INVALID, "moe_forward: router, gate_up and down weights are required");
     if (shape->Is > 0 && (!weights->gate_up_shared || !weights->down_shared))
         return fail(MOE_ERR_INVALID, "moe_forward: Is > 0 needs gate_up_shared and down_shared");
     if (out_dtype != MOE_BF16 && out_dtype != MOE_F32) return fail(MOE_ERR_INVALID, "unknown out_dtype %d", out_dtype);
+    {
+        moe_trace t{};
+        if (trace) t = *trace;
+        if (!aligned(16, {x, out, ws, weights->router, weights->gate_up, weights->down, weights->gate_up_shared,
+                          weights->down_shared, t.y, t.shared_out}) ||
+            !aligned(4, {sel_bias, replay_ids, t.logits, t.topk_ids, t.topk_w, t.counts, t.offsets, t.perm_token,
+                         t.inv_pos}))
+            return fail(MOE_ERR_INVALID,
+                        "moe_forward: x, out, ws, the weights and the trace's y and shared_out must be 16-byte "
+                        "aligned, the other arrays 4-byte");
+    }
     if (shape->T == 0) return ok();
+    if (!x || !out) return fail(MOE_ERR_INVALID, "moe_forward: x and out are required");
     const ForwardLayout L = forward_layout(shape);
     if (!ws || ws_bytes < L.total)
         return fail(MOE_ERR_WORKSPACE, "moe_forward needs %zu workspace bytes, got %zu", L.total, ws ? ws_bytes : 0);
@@ -371,18 +403,28 @@ moe_status moe_backward(const moe_shape* shape, const moe_weights* weights, cons
         return fail(MOE_ERR_INVALID, "moe_backward: router, gate_up and down weights are required");
     if (shape->Is > 0 && (!weights->gate_up_shared || !weights->down_shared))
         return fail(MOE_ERR_INVALID, "moe_backward: Is > 0 needs gate_up_shared and down_shared");
-    if (!x || !dout) return fail(MOE_ERR_INVALID, "moe_backward: x and dout are required");
-    if (!fwd || !fwd->topk_ids || !fwd->topk_w || !fwd->offsets || !fwd->perm_token || !fwd->inv_pos || !fwd->y)
-        return fail(MOE_ERR_INVALID,
-                    "moe_backward: the forward trace needs topk_ids, topk_w, offsets, perm_token, inv_pos and y");
-    if (!grads || !grads->dx || !grads->d_router || !grads->d_gate_up || !grads->d_down)
-        return fail(MOE_ERR_INVALID, "moe_backward: dx, d_router, d_gate_up and d_down are required");
+    if (!grads || !grads->d_router || !grads->d_gate_up || !grads->d_down)
+        return fail(MOE_ERR_INVALID, "moe_backward: d_router, d_gate_up and d_down are required");
     if (shape->Is > 0 && (!grads->d_gate_up_shared || !grads->d_down_shared))
         return fail(MOE_ERR_INVALID, "moe_backward: Is > 0 needs d_gate_up_shared and d_down_shared");
-    if (shape->T == 0) return ok();
-    const size_t need = moe::backward_ws_bytes(shape->T, shape->D, shape->E, shape->K, shape->I, shape->Is);
-    if (!ws || ws_bytes < need)
-        return fail(MOE_ERR_WORKSPACE, "moe_backward needs %zu workspace bytes, got %zu", need, ws ? ws_bytes : 0);
+    moe_trace t{};
+    if (fwd) t = *fwd;
+    if (!aligned(16, {x, dout, ws, weights->router, weights->gate_up, weights->down, weights->gate_up_shared,
+                      weights->down_shared, t.y, grads->dx, grads->d_router, grads->d_gate_up, grads->d_down,
+                      grads->d_gate_up_shared, grads->d_down_shared}) ||
+        !aligned(4, {t.topk_ids, t.topk_w, t.offsets, t.perm_token, t.inv_pos}))
+        return fail(MOE_ERR_INVALID,
+                    "moe_backward: x, dout, ws, the weights, the trace's y and the gradients must be 16-byte "
+                    "aligned, the trace's index and weight arrays 4-byte");
+    if (shape->T > 0) {
+        if (!x || !dout || !grads->dx) return fail(MOE_ERR_INVALID, "moe_backward: x, dout and dx are required");
+        if (!fwd || !t.topk_ids || !t.topk_w || !t.offsets || !t.perm_token || !t.inv_pos || !t.y)
+            return fail(MOE_ERR_INVALID,
+                        "moe_backward: the forward trace needs topk_ids, topk_w, offsets, perm_token, inv_pos and y");
+        const size_t need = moe::backward_ws_bytes(shape->T, shape->D, shape->E, shape->K, shape->I, shape->Is);
+        if (!ws || ws_bytes < need)
+            return fail(MOE_ERR_WORKSPACE, "moe_backward needs %zu workspace bytes, got %zu", need, ws ? ws_bytes : 0);
+    }
     if ((st = check_device()) != MOE_OK) return st;
     moe::BwdArgs a{};
     a.T = shape->T;
@@ -401,12 +443,12 @@ moe_status moe_backward(const moe_shape* shape, const moe_weights* weights, cons
     a.gate_up_shared = weights->gate_up_shared;
     a.down_shared = weights->down_shared;
     a.dout = dout;
-    a.y = fwd->y;
-    a.topk_ids = fwd->topk_ids;
-    a.offsets = fwd->offsets;
-    a.perm_token = fwd->perm_token;
-    a.inv_pos = fwd->inv_pos;
-    a.topk_w = fwd->topk_w;
+    a.y = t.y;
+    a.topk_ids = t.topk_ids;
+    a.offsets = t.offsets;
+    a.perm_token = t.perm_token;
+    a.inv_pos = t.inv_pos;
+    a.topk_w = t.topk_w;
     a.mask = mask;
     a.dx = grads->dx;
     a.d_router = grads->d_router;
@@ -415,6 +457,10 @@ moe_status moe_backward(const moe_shape* shape, const moe_weights* weights, cons
     a.d_gate_up_shared = grads->d_gate_up_shared;
     a.d_down_shared = grads->d_down_shared;
     a.ws = ws;
+    if (shape->T == 0) {
+        if ((st = hip_status(moe::launch_backward_empty(a, stream), "backward launch")) != MOE_OK) return st;
+        return ok();
+    }
     if ((st = hip_status(moe::launch_backward(a, stream), "backward launch")) != MOE_OK) return st;
     return ok();
 }

@@ -622,6 +622,13 @@ __global__ void zero_tails_kernel(uint8_t* a, uint8_t* b, uint8_t* c, uint8_t* d
         if (dst[k] != nullptr && i < n) reinterpret_cast<u32x4*>(dst[k])[i] = u32x4{0u, 0u, 0u, 0u};
 }
 
+// n4 groups of four float32 zeros
+__global__ __launch_bounds__(256) void zero_f32x4_kernel(float* __restrict__ p, int64_t n4) {
+    const int64_t step = static_cast<int64_t>(gridDim.x) * 256;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n4; i += step)
+        reinterpret_cast<f32x4*>(p)[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
 // ===========================================================================
 // launcher
 // ===========================================================================
@@ -877,6 +884,27 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t stream) {
     dx_assemble_kernel<<<static_cast<unsigned>(T), kBwdThreads, 0, stream>>>(dXp, a.inv_pos, Is > 0 ? dXs : nullptr,
                                                                              dxr, a.mask, T, D, K, a.dx);
     return hipGetLastError();
+}
+
+// An empty batch: every weight gradient is a sum over no tokens, so zeros.
+hipError_t launch_backward_empty(const BwdArgs& a, hipStream_t stream) {
+    const int64_t D = a.D;
+    struct { float* p; int64_t n; } bufs[5] = {
+        {a.d_router, a.E * D},
+        {a.d_gate_up, a.E * 2 * a.I * D},
+        {a.d_down, a.E * D * a.I},
+        {a.Is > 0 ? a.d_gate_up_shared : nullptr, 2 * a.Is * D},
+        {a.Is > 0 ? a.d_down_shared : nullptr, D * a.Is},
+    };
+    for (const auto& b : bufs) {
+        if (b.p == nullptr || b.n == 0) continue;
+        const int64_t n4 = b.n / 4;  // D is a multiple of 64
+        const int64_t blocks = (n4 + 255) / 256;
+        zero_f32x4_kernel<<<static_cast<unsigned>(blocks < 4096 ? blocks : 4096), 256, 0, stream>>>(b.p, n4);
+        const hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    return hipSuccess;
 }
 
 }  // namespace moe

@@ -84,5 +84,7 @@ size_t backward_ws_bytes(int64_t T, int D, int E, int K, int I, int Is);
 // whether every buffer the backward's GEMMs stage spans less than 4 GiB
 bool backward_fits_dma(int64_t T, int D, int K, int I, int Is);
 hipError_t launch_backward(const BwdArgs& a, hipStream_t stream);
+// T == 0: zeroes the weight gradients (dx has no elements)
+hipError_t launch_backward_empty(const BwdArgs& a, hipStream_t stream);
 
 }  // namespace moe

@@ -150,7 +150,7 @@ def test_binding_rejects_host_tensors():
 
 def test_backward_validation_before_launch():
     L = moe.lib()
-    one = ctypes.c_void_p(1)
+    one = ctypes.c_void_p(16)  # never dereferenced: validation fails first
     n = ctypes.c_size_t(0)
     s = _shape(dtype=0)
     assert L.moe_backward_workspace_size(ctypes.byref(s), ctypes.byref(n)) == B.MOE_OK and n.value > 0
@@ -173,7 +173,37 @@ def test_backward_validation_before_launch():
     # too small a workspace
     assert L.moe_backward(ctypes.byref(s), ctypes.byref(w), one, None, ctypes.byref(tr), one, ctypes.byref(g),
                           one, 16, None) == B.MOE_ERR_WORKSPACE
-    # T = 0 launches nothing
+    # a misaligned gradient buffer
+    g2 = B._Grads(one, ctypes.c_void_p(20), one, one, None, None)
+    assert L.moe_backward(ctypes.byref(s), ctypes.byref(w), one, None, ctypes.byref(tr), one, ctypes.byref(g2),
+                          one, 1 << 30, None) == B.MOE_ERR_INVALID
+
+
+def test_misaligned_pointers_are_rejected_before_launch():
+    """Activations, weights, outputs and workspace move in 16-byte vectors,
+    index arrays and per-token floats in 4-byte words: a pointer off that
+    alignment is an argument error, found before anything is launched."""
+    L = moe.lib()
+    a16 = ctypes.c_void_p(256)
+    odd8 = ctypes.c_void_p(264)   # 8-byte aligned only
+    odd2 = ctypes.c_void_p(258)
+    n = ctypes.c_size_t(1 << 30)
+    s = _shape()
+    INV = B.MOE_ERR_INVALID
+    # route: x off 16 bytes; topk_ids off 4 bytes
+    assert L.moe_route(ctypes.byref(s), odd8, a16, None, None, None, a16, a16, a16, n.value, None) == INV
+    assert L.moe_route(ctypes.byref(s), a16, a16, None, None, None, odd2, a16, a16, n.value, None) == INV
+    # permute: the workspace off 16 bytes
+    assert L.moe_permute(ctypes.byref(s), a16, a16, a16, a16, a16, odd8, n.value, None) == INV
+    # experts: y off 16 bytes
+    assert L.moe_experts(ctypes.byref(s), a16, a16, a16, a16, a16, odd8, a16, n.value, None) == INV
+    # combine: out off 16 bytes
+    assert L.moe_combine(ctypes.byref(s), a16, a16, a16, None, 0, odd8, None) == INV
+    # forward: a weight off 16 bytes; a trace array off 4 bytes (also with T = 0)
+    w = B._Weights(a16, odd8, a16, None, None)
+    assert L.moe_forward(ctypes.byref(s), ctypes.byref(w), a16, None, None, 0, a16, None, a16, n.value, None) == INV
+    w = B._Weights(a16, a16, a16, None, None)
+    tr = B._Trace(None, odd2, None, None, None, None, None, None, None)
     s0 = _shape(T=0)
-    assert L.moe_backward(ctypes.byref(s0), ctypes.byref(w), one, None, ctypes.byref(tr), one, ctypes.byref(g),
-                          None, 0, None) == B.MOE_OK
+    assert L.moe_forward(ctypes.byref(s0), ctypes.byref(w), a16, None, None, 0, a16, ctypes.byref(tr), a16,
+                         n.value, None) == INV

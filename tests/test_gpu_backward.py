@@ -213,3 +213,33 @@ def test_backward_dx_shuffle_and_padding_invariant():
     assert np.all(dxp[cfg.T:] == 0)
     for k in ("d_gate_up", "d_down"):
         assert torch.equal(gpad[k].view(torch.int32), base[k].view(torch.int32)), k
+
+
+def test_empty_batch():
+    """T = 0: the forward succeeds and writes nothing; the backward's weight
+    gradients are sums over no tokens, so zeros, written over whatever the
+    buffers held (here NaN)."""
+    import routing_grouped_gemm_gemv_amd.binding as B
+
+    cfg, inp, _ = _case("dsv4", dict(T=8, D=256, E=16, K=4, I=128, Is=128), None, False)
+    _say("[backward] empty batch")
+    layer = make_layer(inp)
+    x = torch.empty(0, cfg.D, dtype=torch.bfloat16, device="cuda")
+    out, tr = layer.forward(x, trace=True)
+    assert out.shape == (0, cfg.D)
+    shape = layer.with_tokens(0)
+    nan = float("nan")
+    f32 = torch.float32
+    grads = {
+        "dx": torch.empty(0, cfg.D, dtype=f32, device="cuda"),
+        "d_router": torch.full((cfg.E, cfg.D), nan, dtype=f32, device="cuda"),
+        "d_gate_up": torch.full((cfg.E, 2 * cfg.I, cfg.D), nan, dtype=f32, device="cuda"),
+        "d_down": torch.full((cfg.E, cfg.D, cfg.I), nan, dtype=f32, device="cuda"),
+        "d_gate_up_shared": torch.full((2 * cfg.Is, cfg.D), nan, dtype=f32, device="cuda"),
+        "d_down_shared": torch.full((cfg.D, cfg.Is), nan, dtype=f32, device="cuda"),
+    }
+    B.moe_backward(shape, layer.weights, x, None, tr, torch.empty(0, cfg.D, dtype=torch.bfloat16, device="cuda"),
+                   grads, torch.empty(0, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    for k, v in grads.items():
+        assert torch.equal(v, torch.zeros_like(v)), k
