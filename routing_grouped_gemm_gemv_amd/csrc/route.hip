@@ -988,18 +988,29 @@ __global__ __launch_bounds__(256) void route_fused_bf16_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// router logits for decode-sized batches: one wave per 16 tokens x 16 experts,
-// operand fragments loaded straight from memory with kRdU 32-wide k steps in
-// flight.  The same MFMA chain, chunking (float32 over 256 products, then
-// float64 in k order) and 16-aligned token and expert blocks as the kernels
-// above, so the same bits.
+// router logits for decode-sized batches: one workgroup per 16 tokens x 16
+// experts, operand fragments loaded straight from memory, kRdU 32-wide k
+// steps (one 256-product chunk) in flight per wave.  The same MFMA chain,
+// chunking (float32 over 256 products, then float64 in k order) and
+// 16-aligned token and expert blocks as the kernels above, so the same bits.
 // ---------------------------------------------------------------------------
 constexpr int kRdU = 8;
 
-__global__ __launch_bounds__(64) void router_logits_small_kernel(const uint16_t* __restrict__ x,
-                                                                 const uint16_t* __restrict__ w, int64_t T, int D,
-                                                                 int E, double* __restrict__ out) {
-    const int lane = threadIdx.x;
+// The chunks of a 16 x 16 block are spread over kSplitW waves: each wave
+// computes one 256-product chunk per round (all of its loads in flight, the
+// float32 MFMA chain from zero), the chunks meet in LDS, and each output adds
+// them in float64 in chunk order.  A decode-sized batch has few blocks, so a
+// wave per block walking the chunks one after another would wait for D/256
+// dependent memory round trips; here there are D/2048.
+constexpr int kSplitW = 8;
+
+__global__ __launch_bounds__(64 * kSplitW) void router_logits_split_kernel(const uint16_t* __restrict__ x,
+                                                                        const uint16_t* __restrict__ w, int64_t T,
+                                                                        int D, int E, double* __restrict__ out) {
+    __shared__ __attribute__((aligned(16))) float part[kSplitW][64][4];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t t0 = static_cast<int64_t>(blockIdx.x) * 16;
     const int e0 = blockIdx.y * 16;
     int64_t tr = t0 + (lane & 15);
@@ -1009,32 +1020,45 @@ __global__ __launch_bounds__(64) void router_logits_small_kernel(const uint16_t*
     const int kq = 8 * (lane >> 4);
     const uint16_t* xp = x + tr * D + kq;
     const uint16_t* wp = w + static_cast<int64_t>(er) * D + kq;
-    double acc64[4] = {0.0, 0.0, 0.0, 0.0};
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
     const int S = D / 32;
-    for (int s0 = 0; s0 < S; s0 += kRdU) {  // kRdU = 8 steps = one 256-product chunk
-        u32x4 a[kRdU], b[kRdU];
+    const int nc = (S + kRdU - 1) / kRdU;  // 256-product chunks (the last may be short)
+    double acc64 = 0.0;                    // output (tid / 4, element tid % 4) of the MFMA layout
+    for (int c0 = 0; c0 < nc; c0 += kSplitW) {
+        const int c = c0 + wv;
+        if (c < nc) {  // uniform per wave
+            const int s0 = c * kRdU;
+            f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (s0 + kRdU <= S) {
+                // a full chunk: no branch between the loads and their MFMAs,
+                // so the compiler cannot sink a load down to its use
+                u32x4 a[kRdU], b[kRdU];
 #pragma unroll
-        for (int u = 0; u < kRdU; ++u) {
-            const int s = s0 + u < S ? s0 + u : S - 1;
-            a[u] = *reinterpret_cast<const u32x4*>(xp + 32 * s);
-            b[u] = *reinterpret_cast<const u32x4*>(wp + 32 * s);
+                for (int u = 0; u < kRdU; ++u) {
+                    a[u] = *reinterpret_cast<const u32x4*>(xp + 32 * (s0 + u));
+                    b[u] = *reinterpret_cast<const u32x4*>(wp + 32 * (s0 + u));
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int u = 0; u < kRdU; ++u) acc = mfma_bf16(a[u], b[u], acc);
+            } else {
+                for (int st = s0; st < S; ++st)  // the short last chunk when D % 256 != 0
+                    acc = mfma_bf16(*reinterpret_cast<const u32x4*>(xp + 32 * st),
+                                    *reinterpret_cast<const u32x4*>(wp + 32 * st), acc);
+            }
+            *reinterpret_cast<f32x4*>(&part[wv][lane][0]) = acc;
         }
-        __builtin_amdgcn_sched_barrier(0);  // the chunk's loads all in flight before its MFMAs
-        acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int u = 0; u < kRdU; ++u) {
-            if (s0 + u >= S) break;  // uniform
-            acc = mfma_bf16(a[u], b[u], acc);
+        __syncthreads();
+        if (tid < 256) {
+            const int n = nc - c0 < kSplitW ? nc - c0 : kSplitW;
+            for (int j = 0; j < n; ++j) acc64 += static_cast<double>(part[j][tid >> 2][tid & 3]);
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc64[i] += static_cast<double>(acc[i]);
+        __syncthreads();
     }
-    const int e = e0 + (lane & 15);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int64_t t = t0 + 4 * (lane >> 4) + i;
-        if (t < T && e < E) out[t * E + e] = acc64[i];
+    if (tid < 256) {
+        const int l = tid >> 2;
+        const int e = e0 + (l & 15);
+        const int64_t t = t0 + 4 * (l >> 4) + (tid & 3);
+        if (t < T && e < E) out[t * E + e] = acc64;
     }
 }
 
@@ -1047,8 +1071,8 @@ hipError_t launch_router_logits(const void* x, const void* router, int64_t T, in
                                 int dtype, double* logits64, hipStream_t stream) {
     if (route_small(T, E, dtype)) {
         dim3 grid(static_cast<unsigned>((T + 15) / 16), static_cast<unsigned>((E + 15) / 16));
-        router_logits_small_kernel<<<grid, 64, 0, stream>>>(static_cast<const uint16_t*>(x),
-                                                            static_cast<const uint16_t*>(router), T, D, E, logits64);
+        router_logits_split_kernel<<<grid, 64 * kSplitW, 0, stream>>>(
+            static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(router), T, D, E, logits64);
         return hipGetLastError();
     }
     if (dtype == 0) {
