@@ -55,6 +55,40 @@ struct Vec8<float> {
     }
 };
 
+// Eight consecutive elements loaded raw, so that the loads of all K rows can
+// be in flight together, and widened to float32 where they are used.
+template <typename Tin>
+struct Raw8;
+template <>
+struct Raw8<uint16_t> {
+    u32x4 u;
+    static __device__ __forceinline__ Raw8 load(const uint16_t* p) {
+        return Raw8{__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p))};
+    }
+    static __device__ __forceinline__ Raw8 zero() { return Raw8{u32x4{0u, 0u, 0u, 0u}}; }
+    __device__ __forceinline__ void widen(float* v) const {
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = __uint_as_float(w[i] << 16);
+            v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+        }
+    }
+};
+template <>
+struct Raw8<float> {
+    f32x4 a, b;
+    static __device__ __forceinline__ Raw8 load(const float* p) {
+        return Raw8{__builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p)),
+                    __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + 4))};
+    }
+    static __device__ __forceinline__ Raw8 zero() { return Raw8{f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}}; }
+    __device__ __forceinline__ void widen(float* v) const {
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+};
+
 // float64 -> bf16 with one rounding (nearest-even): the float64 value is first
 // narrowed to float32 rounding to odd (truncate, then set the last bit if
 // anything was dropped), which keeps enough bits that the final float32 ->
@@ -152,12 +186,90 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     }
 }
 
+// The same fold for small batches (fewer than kCombineSmallT tokens), where
+// each wave's memory latency shows: all K row loads of a 16-byte chunk are
+// issued before the first is used (the kernel above waits for each row in
+// turn, which at large T keeps more waves resident and streams faster).  The
+// fold runs over KC slots, K rounded up to a compiled size, with weight +0
+// and zero data past K: that adds +0 to an accumulator that cannot be -0 (it
+// starts at +0, and round-to-nearest returns +0, not -0, for +0 + -0 and for
+// two terms that cancel), so every bit is the same as the kernel above.
+constexpr int64_t kCombineSmallT = 1024;
+
+template <typename Tin, bool OUT_BF16, typename Acc, int KC>
+__global__ __launch_bounds__(kCombineThreads) void combine_small_kernel(
+    const Tin* __restrict__ y, const int32_t* __restrict__ inv_pos, const float* __restrict__ w,
+    const Tin* __restrict__ shared, int64_t T, int D, int K, void* __restrict__ out) {
+    const int64_t t = blockIdx.x;
+    int64_t pos[KC];
+    float wt[KC];
+    bool kept = false;
+#pragma unroll
+    for (int j = 0; j < KC; ++j) {
+        pos[j] = -1;
+        wt[j] = 0.0f;
+        if (j < K) {
+            pos[j] = inv_pos[t * K + j];
+            wt[j] = w[t * K + j];
+            kept = kept || pos[j] >= 0;
+        }
+    }
+    for (int d0 = threadIdx.x * 8; d0 < D; d0 += kCombineThreads * 8) {
+        Acc acc[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = Acc(0);
+        if (kept) {  // every pick of a kept token has a row
+            Raw8<Tin> r[KC];
+#pragma unroll
+            for (int j = 0; j < KC; ++j) r[j] = j < K ? Raw8<Tin>::load(y + pos[j] * D + d0) : Raw8<Tin>::zero();
+            const Raw8<Tin> rs = shared != nullptr ? Raw8<Tin>::load(shared + t * D + d0) : Raw8<Tin>::zero();
+#pragma unroll
+            for (int j = 0; j < KC; ++j) {
+                float v[8];
+                r[j].widen(v);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const Acc prod = static_cast<Acc>(wt[j]) * static_cast<Acc>(v[i]);
+                    acc[i] = acc[i] + prod;
+                }
+            }
+            if (shared != nullptr) {
+                float v[8];
+                rs.widen(v);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[i] = acc[i] + static_cast<Acc>(v[i]);
+            }
+        }
+        store8<OUT_BF16>(out, t * D + d0, acc);
+    }
+}
+
+template <typename Tin, bool OUT_BF16, typename Acc>
+static void launch_combine_t(const void* y, const int32_t* inv_pos, const float* w, const void* shared, int64_t T,
+                             int D, int K, void* out, hipStream_t stream) {
+    const unsigned grid = static_cast<unsigned>(T);
+    const Tin* yy = static_cast<const Tin*>(y);
+    const Tin* ss = static_cast<const Tin*>(shared);
+    if (T >= kCombineSmallT) {
+        combine_kernel<Tin, OUT_BF16, Acc><<<grid, kCombineThreads, 0, stream>>>(yy, inv_pos, w, ss, T, D, K, out);
+        return;
+    }
+#define MOE_COMBINE_SMALL(KC) \
+    combine_small_kernel<Tin, OUT_BF16, Acc, KC><<<grid, kCombineThreads, 0, stream>>>(yy, inv_pos, w, ss, T, D, K, out)
+    if (K <= 1) MOE_COMBINE_SMALL(1);
+    else if (K <= 2) MOE_COMBINE_SMALL(2);
+    else if (K <= 4) MOE_COMBINE_SMALL(4);
+    else if (K <= 6) MOE_COMBINE_SMALL(6);
+    else if (K <= 8) MOE_COMBINE_SMALL(8);
+    else if (K <= 10) MOE_COMBINE_SMALL(10);
+    else if (K <= 12) MOE_COMBINE_SMALL(12);
+    else MOE_COMBINE_SMALL(kMaxK);
+#undef MOE_COMBINE_SMALL
+}
+
 hipError_t launch_combine(const void* y, const int32_t* inv_pos, const float* w, const void* shared,
                           int64_t T, int D, int K, int dtype, int out_dtype, int mode, void* out, hipStream_t stream) {
-    const unsigned grid = static_cast<unsigned>(T);
-#define MOE_COMBINE(TIN, BF16OUT, ACC)                                                                   \
-    combine_kernel<TIN, BF16OUT, ACC><<<grid, kCombineThreads, 0, stream>>>(                          \
-        static_cast<const TIN*>(y), inv_pos, w, static_cast<const TIN*>(shared), T, D, K, out)
+#define MOE_COMBINE(TIN, BF16OUT, ACC) launch_combine_t<TIN, BF16OUT, ACC>(y, inv_pos, w, shared, T, D, K, out, stream)
     if (dtype == 0) {
         if (mode == 0) {
             if (out_dtype == 0) MOE_COMBINE(uint16_t, true, float);
