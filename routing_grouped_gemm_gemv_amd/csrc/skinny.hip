@@ -25,8 +25,7 @@ struct SkinnyParams {
     const uint16_t* a;          // rows: x (gathered through perm) or the activations
     const int32_t* perm;        // row -> x row, or null (identity)
     const int32_t* offsets;     // [G + 1] row ranges, or null: one group of ident_rows rows
-    const int32_t* u_start;     // [G + 1] prefix of the groups' 64-row units
-    int G;
+    int G;                      // at most 1024
     int ident_rows;
     int Kd;                     // reduction length (D for gate_up, I for down)
     const uint16_t* w;          // the groups' weight matrices [.][Kd], w_group_stride apart
@@ -36,26 +35,81 @@ struct SkinnyParams {
     uint16_t* out;              // [rows][N] bf16
 };
 
-// u_start[g] = sum over earlier groups of ceil(rows / 64); u_start[G] = total
-__global__ __launch_bounds__(1024) void skinny_prefix_kernel(const int32_t* __restrict__ offsets, int G,
-                                                             int ident_rows, int32_t* __restrict__ u_start) {
-    __shared__ int part[1024];
-    const int tid = threadIdx.x;
-    int v = 0;
-    if (tid < G) {
-        const int c = offsets ? offsets[tid + 1] - offsets[tid] : ident_rows;
-        v = (c + kSkRows - 1) / kSkRows;
+// Work item L of a launch: unit `unit` (64 rows) of group g against column
+// slice `slice`, items in group order, the units of a slice consecutive.  The
+// wave finds it from the offsets alone, with one round of loads: lane l holds
+// the row counts of groups [l*gpl, (l+1)*gpl), a wave scan of their unit
+// counts gives each group's first item, and the lane whose range holds L
+// hands (g, rows of g) to the others.  Returns false when L is past the last
+// item.
+__device__ __forceinline__ bool skinny_locate(const SkinnyParams& p, int64_t L, int ns, int& g, int& o0, int& o1,
+                                              int& slice, int& unit) {
+    const int lane = lane_id();
+    if (p.offsets == nullptr) {  // one group of ident_rows rows
+        const int nu = (p.ident_rows + kSkRows - 1) / kSkRows;
+        if (L >= static_cast<int64_t>(nu) * ns) return false;
+        g = 0;
+        o0 = 0;
+        o1 = p.ident_rows;
+        slice = static_cast<int>(L / nu);
+        unit = static_cast<int>(L % nu);
+        return true;
     }
-    part[tid] = v;
-    __syncthreads();
-    for (int d = 1; d < 1024; d <<= 1) {
-        const int u = tid >= d ? part[tid - d] : 0;
-        __syncthreads();
-        part[tid] += u;
-        __syncthreads();
+    constexpr int kMaxPer = 16;  // groups per lane: G <= 1024
+    const int gpl = (p.G + 63) / 64;
+    const int ga = lane * gpl;
+    int beg[kMaxPer], cnt[kMaxPer];
+#pragma unroll
+    for (int k = 0; k < kMaxPer; ++k) {
+        // every load in bounds (a clamped group) and unconditional, so all of
+        // them are in flight together
+        int gi = ga + k;
+        if (gi > p.G - 1) gi = p.G - 1;
+        beg[k] = p.offsets[gi];
+        cnt[k] = p.offsets[gi + 1];
     }
-    if (tid < G) u_start[tid + 1] = part[tid];
-    if (tid == 0) u_start[0] = 0;
+    int local = 0;
+#pragma unroll
+    for (int k = 0; k < kMaxPer; ++k) {
+        const bool own = k < gpl && ga + k < p.G;
+        cnt[k] = own ? cnt[k] - beg[k] : 0;
+        local += (cnt[k] + kSkRows - 1) / kSkRows;
+    }
+    int incl = local;  // inclusive wave scan of the unit counts
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int v = __shfl_up(incl, d);
+        if (lane >= d) incl += v;
+    }
+    const int total = __shfl(incl, 63);
+    if (L >= static_cast<int64_t>(total) * ns) return false;
+    int u0 = incl - local;  // first unit of this lane's first group
+    bool found = false;
+    int fg = 0, fb = 0, fc = 0, floc = 0, fnu = 1;
+#pragma unroll
+    for (int k = 0; k < kMaxPer; ++k) {
+        const int nu = (cnt[k] + kSkRows - 1) / kSkRows;
+        const int64_t first = static_cast<int64_t>(u0) * ns;
+        if (nu > 0 && L >= first && L < first + static_cast<int64_t>(nu) * ns) {
+            found = true;
+            fg = ga + k;
+            fb = beg[k];
+            fc = cnt[k];
+            floc = static_cast<int>(L - first);
+            fnu = nu;
+        }
+        u0 += nu;
+    }
+    const uint64_t who = __ballot(found);
+    const int src = __builtin_ctzll(who);  // exactly one lane: L < total
+    g = __shfl(fg, src);
+    o0 = __shfl(fb, src);
+    o1 = o0 + __shfl(fc, src);
+    const int loc = __shfl(floc, src);
+    const int nu = __shfl(fnu, src);
+    slice = loc / nu;
+    unit = loc % nu;
+    return true;
 }
 
 // The k loop of one wave over RB row blocks (nb of them valid, uniform) with
@@ -94,20 +148,8 @@ template <bool GATE_UP>
 __global__ __launch_bounds__(64) void skinny_kernel(SkinnyParams p) {
     const int lane = threadIdx.x;
     const int ns = p.N / 16;  // column slices
-    const int64_t L = blockIdx.x;
-    if (L >= static_cast<int64_t>(p.u_start[p.G]) * ns) return;
-    int lo = 0, hi = p.G - 1;  // last group whose first unit is <= L
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (static_cast<int64_t>(p.u_start[mid]) * ns <= L) lo = mid; else hi = mid - 1;
-    }
-    const int g = lo;
-    const int nu = p.u_start[g + 1] - p.u_start[g];
-    const int loc = static_cast<int>(L - static_cast<int64_t>(p.u_start[g]) * ns);
-    const int slice = loc / nu;
-    const int unit = loc % nu;
-    const int o0 = p.offsets ? p.offsets[g] : 0;
-    const int o1 = p.offsets ? p.offsets[g + 1] : p.ident_rows;
+    int g, o0, o1, slice, unit;
+    if (!skinny_locate(p, blockIdx.x, ns, g, o0, o1, slice, unit)) return;
     const int r0 = o0 + kSkRows * unit;               // first row of the unit
     const int nb = min(4, (o1 - r0 + 15) / 16);      // valid 16-row blocks (uniform)
 
@@ -161,23 +203,20 @@ bool experts_use_skinny(int64_t rows_max, int G, int dtype) {
 hipError_t launch_experts_skinny(const void* x, const int32_t* perm_token, const int32_t* offsets, int G,
                                  int64_t rows_max, int D, int I, const void* gate_up, const void* down, void* y,
                                  void* ws, hipStream_t stream) {
-    // the workspace of launch_experts: u_start in its table area at the
-    // front, the activations [rows_max][I] where the tiled path keeps them
+    // the workspace of launch_experts: the activations [rows_max][I] where
+    // the tiled path keeps them
     const size_t ws_total = experts_ws_bytes(rows_max, G, D, I, 0);
     const size_t act_bytes = (static_cast<size_t>(rows_max) * I * 2 + 255) & ~static_cast<size_t>(255);
-    int32_t* u_start = static_cast<int32_t*>(ws);
     uint16_t* act = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(ws) + (ws_total - act_bytes));
     const int ident_rows = static_cast<int>(rows_max);
-    skinny_prefix_kernel<<<1, 1024, 0, stream>>>(offsets, G, ident_rows, u_start);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    // units: at most ceil(rows / 64) + G, times the column slices
-    const int64_t blocks = (rows_max + kSkRows - 1) / kSkRows + G;
+    // units: a group of c rows has ceil(c / 64) <= c / 64 + 1 of them, and at
+    // most min(G, rows) groups are non-empty
+    const int64_t groups = offsets ? (rows_max < G ? rows_max : G) : 1;
+    const int64_t blocks = (rows_max + kSkRows - 1) / kSkRows + groups;
     SkinnyParams p{};
     p.perm = perm_token;
     p.offsets = offsets;
-    p.u_start = u_start;
-    p.G = G;
+    p.G = offsets ? G : 1;
     p.ident_rows = ident_rows;
     p.a = static_cast<const uint16_t*>(x);
     p.Kd = D;
@@ -187,7 +226,8 @@ hipError_t launch_experts_skinny(const void* x, const int32_t* perm_token, const
     p.N = I;
     p.out = act;
     skinny_kernel<true><<<static_cast<unsigned>(blocks * (I / 16)), 64, 0, stream>>>(p);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
     p.a = act;
     p.perm = nullptr;
     p.Kd = I;
