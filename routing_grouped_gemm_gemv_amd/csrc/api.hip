@@ -120,8 +120,14 @@ size_t experts_ws(const moe_shape* s) { return align256(moe::experts_ws_bytes(s-
 // Workspace of moe_forward, in order: logits64, ids, weights, counts, offsets,
 // perm_token, inv_pos, permute scratch, expert scratch, y, shared_out.
 struct ForwardLayout {
-    size_t logits64, ids, w, counts, offsets, perm, inv, perm_ws, exp_ws, y, shared, total;
+    size_t logits64, ids, w, counts, offsets, perm, inv, perm_ws, exp_ws, y, shared, shared_act, total;
 };
+
+// whether moe_forward runs the shared expert in the routed experts' launches
+bool shared_with_routed(const moe_shape* s) {
+    return s->Is > 0 && moe::experts_use_skinny(s->T * s->K, s->E, s->dtype) &&
+           moe::experts_use_skinny(s->T, 1, s->dtype);
+}
 
 ForwardLayout forward_layout(const moe_shape* s) {
     ForwardLayout L;
@@ -147,6 +153,9 @@ ForwardLayout forward_layout(const moe_shape* s) {
     L.exp_ws = take(ex_routed > ex_shared ? ex_routed : ex_shared);
     L.y = take(eb * P * s->D);
     L.shared = take(s->Is > 0 ? eb * T * s->D : 0);
+    // both expert MLPs on the skinny path run in shared launches: the shared
+    // expert's activations then need a place of their own
+    L.shared_act = take(shared_with_routed(s) ? sizeof(uint16_t) * T * s->Is : 0);
     L.total = off;
     return L;
 }
@@ -352,11 +361,19 @@ static moe_status forward_impl(const moe_shape* shape, const moe_weights* weight
                                              counts, offsets, perm, inv, stream),
                          "permute launch")) != MOE_OK)
         return st;
-    if ((st = hip_status(run_experts(x, T, perm, offsets, shape->E, T * shape->K, shape->D, shape->I,
-                                             shape->dtype, weights->gate_up, weights->down, y, exw, stream),
-                         "routed experts launch")) != MOE_OK)
+    if (shared_with_routed(shape)) {
+        if ((st = hip_status(moe::launch_experts_skinny_pair(
+                                 x, perm, offsets, shape->E, T * shape->K, shape->D, shape->I, weights->gate_up,
+                                 weights->down, y, exw, T, shape->Is, weights->gate_up_shared, weights->down_shared,
+                                 sh, base + L.shared_act, stream),
+                             "experts launch")) != MOE_OK)
+            return st;
+    } else if ((st = hip_status(run_experts(x, T, perm, offsets, shape->E, T * shape->K, shape->D, shape->I,
+                                            shape->dtype, weights->gate_up, weights->down, y, exw, stream),
+                                "routed experts launch")) != MOE_OK) {
         return st;
-    if (sh != nullptr) {
+    }
+    if (sh != nullptr && !shared_with_routed(shape)) {
         if ((st = hip_status(run_experts(x, T, nullptr, nullptr, 1, T, shape->D, shape->Is, shape->dtype,
                                                  weights->gate_up_shared, weights->down_shared, sh, exw, stream),
                              "shared expert launch")) != MOE_OK)

@@ -59,6 +59,13 @@ bool experts_use_skinny(int64_t rows_max, int G, int dtype);
 hipError_t launch_experts_skinny(const void* x, const int32_t* perm_token, const int32_t* offsets, int G,
                                  int64_t rows_max, int D, int I, const void* gate_up, const void* down, void* y,
                                  void* ws, hipStream_t stream);
+// the routed experts (as launch_experts_skinny) and a shared expert of rows_s
+// identity rows in the same two launches; act_s: its activations
+// [rows_s][Is] bf16
+hipError_t launch_experts_skinny_pair(const void* x, const int32_t* perm_token, const int32_t* offsets, int G,
+                                      int64_t rows_max, int D, int I, const void* gate_up, const void* down, void* y,
+                                      void* ws, int64_t rows_s, int Is, const void* gate_up_s, const void* down_s,
+                                      void* y_s, void* act_s, hipStream_t stream);
 
 // ---- combine -----------------------------------------------------------------
 // mode 0: float32 fold; mode 1: float64 sum rounded once

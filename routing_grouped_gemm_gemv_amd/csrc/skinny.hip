@@ -144,12 +144,18 @@ __device__ __forceinline__ void skinny_loop(const uint16_t* const (&ap)[4], cons
 
 // One wave per (group, 16-column slice, 64-row unit); the units and slices of
 // a group run on consecutive workgroups.
+// Blocks below `split` work on problem p0, the others on p1 (the routed
+// experts and the shared expert of one layer in one launch: both are weight
+// streams too short to fill the chip on their own).
 template <bool GATE_UP>
-__global__ __launch_bounds__(64) void skinny_kernel(SkinnyParams p) {
+__global__ __launch_bounds__(64) void skinny_kernel(SkinnyParams p0, SkinnyParams p1, int64_t split) {
     const int lane = threadIdx.x;
+    const bool second = static_cast<int64_t>(blockIdx.x) >= split;
+    const SkinnyParams p = second ? p1 : p0;
+    const int64_t L = second ? static_cast<int64_t>(blockIdx.x) - split : static_cast<int64_t>(blockIdx.x);
     const int ns = p.N / 16;  // column slices
     int g, o0, o1, slice, unit;
-    if (!skinny_locate(p, blockIdx.x, ns, g, o0, o1, slice, unit)) return;
+    if (!skinny_locate(p, L, ns, g, o0, o1, slice, unit)) return;
     const int r0 = o0 + kSkRows * unit;               // first row of the unit
     const int nb = min(4, (o1 - r0 + 15) / 16);      // valid 16-row blocks (uniform)
 
@@ -200,24 +206,25 @@ bool experts_use_skinny(int64_t rows_max, int G, int dtype) {
     return G > 1 ? rows_max <= static_cast<int64_t>(4) * G : rows_max <= 64;
 }
 
-hipError_t launch_experts_skinny(const void* x, const int32_t* perm_token, const int32_t* offsets, int G,
-                                 int64_t rows_max, int D, int I, const void* gate_up, const void* down, void* y,
-                                 void* ws, hipStream_t stream) {
-    // the workspace of launch_experts: the activations [rows_max][I] where
-    // the tiled path keeps them
-    const size_t ws_total = experts_ws_bytes(rows_max, G, D, I, 0);
-    const size_t act_bytes = (static_cast<size_t>(rows_max) * I * 2 + 255) & ~static_cast<size_t>(255);
-    uint16_t* act = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(ws) + (ws_total - act_bytes));
-    const int ident_rows = static_cast<int>(rows_max);
-    // units: a group of c rows has ceil(c / 64) <= c / 64 + 1 of them, and at
-    // most min(G, rows) groups are non-empty
+// The two products of one expert MLP problem and their grid bounds.
+struct SkinnyProblem {
+    SkinnyParams gu, dn;
+    int64_t units;  // upper bound of the 64-row units
+};
+
+static SkinnyProblem skinny_problem(const void* x, const int32_t* perm_token, const int32_t* offsets, int G,
+                                    int64_t rows_max, int D, int I, const void* gate_up, const void* down, void* y,
+                                    uint16_t* act) {
+    SkinnyProblem pr;
+    // a group of c rows has ceil(c / 64) <= c / 64 + 1 units, and at most
+    // min(G, rows) groups are non-empty
     const int64_t groups = offsets ? (rows_max < G ? rows_max : G) : 1;
-    const int64_t blocks = (rows_max + kSkRows - 1) / kSkRows + groups;
+    pr.units = (rows_max + kSkRows - 1) / kSkRows + groups;
     SkinnyParams p{};
     p.perm = perm_token;
     p.offsets = offsets;
     p.G = offsets ? G : 1;
-    p.ident_rows = ident_rows;
+    p.ident_rows = static_cast<int>(rows_max);
     p.a = static_cast<const uint16_t*>(x);
     p.Kd = D;
     p.w = static_cast<const uint16_t*>(gate_up);
@@ -225,9 +232,7 @@ hipError_t launch_experts_skinny(const void* x, const int32_t* perm_token, const
     p.I = I;
     p.N = I;
     p.out = act;
-    skinny_kernel<true><<<static_cast<unsigned>(blocks * (I / 16)), 64, 0, stream>>>(p);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
+    pr.gu = p;
     p.a = act;
     p.perm = nullptr;
     p.Kd = I;
@@ -235,7 +240,45 @@ hipError_t launch_experts_skinny(const void* x, const int32_t* perm_token, const
     p.w_group_stride = static_cast<int64_t>(D) * I;
     p.N = D;
     p.out = static_cast<uint16_t*>(y);
-    skinny_kernel<false><<<static_cast<unsigned>(blocks * (D / 16)), 64, 0, stream>>>(p);
+    pr.dn = p;
+    return pr;
+}
+
+static uint16_t* skinny_act(void* ws, int64_t rows_max, int G, int D, int I) {
+    // the workspace of launch_experts: the activations [rows_max][I] where
+    // the tiled path keeps them
+    const size_t ws_total = experts_ws_bytes(rows_max, G, D, I, 0);
+    const size_t act_bytes = (static_cast<size_t>(rows_max) * I * 2 + 255) & ~static_cast<size_t>(255);
+    return reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(ws) + (ws_total - act_bytes));
+}
+
+hipError_t launch_experts_skinny(const void* x, const int32_t* perm_token, const int32_t* offsets, int G,
+                                 int64_t rows_max, int D, int I, const void* gate_up, const void* down, void* y,
+                                 void* ws, hipStream_t stream) {
+    const SkinnyProblem a = skinny_problem(x, perm_token, offsets, G, rows_max, D, I, gate_up, down, y,
+                                           skinny_act(ws, rows_max, G, D, I));
+    const int64_t b1 = a.units * (I / 16), b2 = a.units * (D / 16);
+    skinny_kernel<true><<<static_cast<unsigned>(b1), 64, 0, stream>>>(a.gu, a.gu, b1);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    skinny_kernel<false><<<static_cast<unsigned>(b2), 64, 0, stream>>>(a.dn, a.dn, b2);
+    return hipGetLastError();
+}
+
+hipError_t launch_experts_skinny_pair(const void* x, const int32_t* perm_token, const int32_t* offsets, int G,
+                                      int64_t rows_max, int D, int I, const void* gate_up, const void* down, void* y,
+                                      void* ws, int64_t rows_s, int Is, const void* gate_up_s, const void* down_s,
+                                      void* y_s, void* act_s, hipStream_t stream) {
+    const SkinnyProblem a = skinny_problem(x, perm_token, offsets, G, rows_max, D, I, gate_up, down, y,
+                                           skinny_act(ws, rows_max, G, D, I));
+    const SkinnyProblem b = skinny_problem(x, nullptr, nullptr, 1, rows_s, D, Is, gate_up_s, down_s, y_s,
+                                           static_cast<uint16_t*>(act_s));
+    const int64_t a1 = a.units * (I / 16), a2 = a.units * (D / 16);
+    const int64_t n1 = a1 + b.units * (Is / 16), n2 = a2 + b.units * (D / 16);
+    skinny_kernel<true><<<static_cast<unsigned>(n1), 64, 0, stream>>>(a.gu, b.gu, a1);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    skinny_kernel<false><<<static_cast<unsigned>(n2), 64, 0, stream>>>(a.dn, b.dn, a2);
     return hipGetLastError();
 }
 
