@@ -763,11 +763,12 @@ struct RouteTile {
     static constexpr int EPL = EMAX / 64;      // experts per lane in the top-k
     static constexpr int XSTAGE = TB * 128;    // bytes of hidden rows per 64-wide k chunk
     static constexpr int WSTAGE = EMAX * 128;  // bytes of router rows per chunk
-    static constexpr int XS = TB >= 128 ? 4 : 8;
+    static constexpr int XS = (TB >= 128 || EMAX > 256) ? 4 : 8;
     static constexpr int WS = (3 * WSTAGE + XS * XSTAGE <= 160 * 1024) ? 3 : 2;
     static constexpr int WOFF = XS * XSTAGE;   // LDS offset of the router ring
     static constexpr int RING = WOFF + WS * WSTAGE;
-    static constexpr int TBP = TB < 64 ? TB : 64;  // tokens whose logits are in LDS at a time
+    static constexpr int TBP_MAX = EMAX > 256 ? 32 : 64;
+    static constexpr int TBP = TB < TBP_MAX ? TB : TBP_MAX;  // tokens whose logits are in LDS at a time
     static constexpr int LOGB = TBP * EMAX * 8; // float64 logits of one pass
     static constexpr int SCRB = 4 * 2 * 64 * 16;  // top-k candidate slots: 4 waves x 2 passes x 64
     static constexpr int SMEM = RING > LOGB + SCRB ? RING : LOGB + SCRB;
@@ -1130,6 +1131,7 @@ hipError_t launch_route(const void* x, const void* router, int64_t T, int D, int
     else if (E <= 128) MOE_ROUTE(4, 2);
     else if (E <= 256 && T >= 128 * static_cast<int64_t>(compute_units())) MOE_ROUTE(8, 4);
     else if (E <= 256) MOE_ROUTE(4, 4);
+    else if (T >= 64 * static_cast<int64_t>(compute_units())) MOE_ROUTE(4, 8);
     else MOE_ROUTE(2, 8);
 #undef MOE_ROUTE
     return hipGetLastError();
