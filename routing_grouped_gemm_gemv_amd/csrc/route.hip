@@ -1124,11 +1124,15 @@ hipError_t launch_route(const void* x, const void* router, int64_t T, int D, int
     route_fused_bf16_kernel<TBB, NBW><<<static_cast<unsigned>((T + 16 * TBB - 1) / (16 * TBB)), 256, 0, \
                                          stream>>>(xb, wb, T, D, E, K, score, renorm, rs, bias, mask,      \
                                                    logits_out, ids, w)
-    // 128-token tiles halve the router-matrix traffic per token once there
-    // are enough of them to give every CU one; the logits and picks do not
-    // depend on the tile
-    if (E <= 64) MOE_ROUTE(4, 1);
-    else if (E <= 128) MOE_ROUTE(4, 2);
+    // Larger token tiles cut the router-matrix traffic per token once there
+    // are enough of them to give every CU one; smaller ones keep every CU
+    // busy on shorter batches.  The logits and picks do not depend on the
+    // tile.
+    const bool wide = T >= 64 * static_cast<int64_t>(compute_units());
+    if (E <= 64 && wide) MOE_ROUTE(4, 1);
+    else if (E <= 64) MOE_ROUTE(2, 1);
+    else if (E <= 128 && wide) MOE_ROUTE(4, 2);
+    else if (E <= 128) MOE_ROUTE(2, 2);
     else if (E <= 256 && T >= 128 * static_cast<int64_t>(compute_units())) MOE_ROUTE(8, 4);
     else if (E <= 256) MOE_ROUTE(4, 4);
     else if (T >= 64 * static_cast<int64_t>(compute_units())) MOE_ROUTE(4, 8);

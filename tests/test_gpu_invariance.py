@@ -114,3 +114,35 @@ def test_prefixes_across_the_decode_paths(name):
         assert torch.equal(sub.view(torch.int16), full[:T].view(torch.int16)), T
         assert torch.equal(trs["topk_ids"], trf["topk_ids"][:T]), T
         assert torch.equal(trs["topk_w"].view(torch.int32), trf["topk_w"][:T].view(torch.int32)), T
+
+
+@pytest.mark.parametrize("name", ["q30", "qnext", "dsv4"])
+def test_router_tiles_give_the_same_bits(name):
+    """The fused router picks its token tile from T and the CU count (larger
+    tiles once every CU gets one).  A batch exactly at the switch runs the
+    larger tile, the same batch without its last token the smaller one: the
+    float32 logits, ids and weights of every common token are the same
+    bits."""
+    import routing_grouped_gemm_gemv_amd.binding as B
+    from tests.gpu_util import make_layer
+
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    per_cu = {"q30": 64, "qnext": 64, "dsv4": 128}[name]
+    T = per_cu * cus
+    cfg = get_config(name)
+    inp = make_inputs(cfg, T=T)
+    layer = make_layer(inp)
+    x = to_dev(inp.x)
+    print(f"[router tiles] {name} T={T} and {T - 1}", flush=True)
+    res = []
+    for n in (T, T - 1):
+        shape = layer.with_tokens(n)
+        ws = layer.workspace(shape)
+        lg = torch.empty(n, cfg.E, dtype=torch.float32, device="cuda")
+        ids = torch.empty(n, cfg.K, dtype=torch.int32, device="cuda")
+        w = torch.empty(n, cfg.K, dtype=torch.float32, device="cuda")
+        B.moe_route(shape, x[:n], layer.weights["router"], layer.sel_bias, None, lg, ids, w, ws)
+        torch.cuda.synchronize()
+        res.append((lg, ids, w))
+    for a, b in zip(res[0], res[1]):
+        assert torch.equal(a[: T - 1].view(torch.int32), b.view(torch.int32))
