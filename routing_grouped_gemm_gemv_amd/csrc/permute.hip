@@ -60,18 +60,70 @@ __device__ __forceinline__ uint64_t match_mask(int e, bool valid, int id_bits) {
     return m;
 }
 
+// A wave walks its sub-range in 64-pair segments, kSegBatch of them per
+// round of loads: the ids of a round are loaded at once (clamped, in-bounds,
+// unconditional loads, so all of them are in flight together) and then the
+// segments are taken one after another as before.  Sub-ranges are multiples
+// of 64 * kSegBatch pairs.
+constexpr int kSegBatch = 8;
+
+__device__ __forceinline__ void load_segments(const int32_t* __restrict__ ids, int64_t P, int64_t seg0,
+                                              int (&ev)[kSegBatch]) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int s = 0; s < kSegBatch; ++s) {
+        const int64_t p = seg0 + 64 * s + lane;
+        ev[s] = ids[p < P ? p : P - 1];  // pairs past P are never used
+    }
+}
+
 // Fill hist[w][*] with the per-expert pair counts of wave w's sub-range.
 __device__ __forceinline__ void wave_histogram(const int32_t* __restrict__ ids, int64_t P, int64_t w_begin,
                                                int64_t w_end, int id_bits, int* hist_row) {
     const int lane = lane_id();
     const uint64_t lt = (1ull << lane) - 1ull;
-    for (int64_t seg = w_begin; seg < w_end; seg += 64) {
-        const int64_t p = seg + lane;
-        int e = -1;
-        if (p < w_end && p < P) e = ids[p];
-        const bool valid = e >= 0;
-        const uint64_t m = match_mask(valid ? e : 0, valid, id_bits);
-        if (valid && (m & lt) == 0ull) hist_row[e] += __popcll(m);
+    for (int64_t seg0 = w_begin; seg0 < w_end; seg0 += 64 * kSegBatch) {
+        int ev[kSegBatch];
+        load_segments(ids, P, seg0, ev);
+#pragma unroll
+        for (int s = 0; s < kSegBatch; ++s) {
+            const int64_t p = seg0 + 64 * s + lane;
+            const int e = (p < w_end && p < P) ? ev[s] : -1;
+            const bool valid = e >= 0;
+            const uint64_t m = match_mask(valid ? e : 0, valid, id_bits);
+            if (valid && (m & lt) == 0ull) hist_row[e] += __popcll(m);
+        }
+    }
+}
+
+// The scatter of wave w's sub-range: row[e] holds the next row of expert e
+// for this wave.
+__device__ __forceinline__ void wave_scatter(const int32_t* __restrict__ ids, int64_t P, int K, int64_t w_begin,
+                                             int64_t w_end, int id_bits, int* row, int32_t* __restrict__ perm_token,
+                                             int32_t* __restrict__ inv_pos) {
+    const int lane = lane_id();
+    const uint64_t lt = (1ull << lane) - 1ull;
+    for (int64_t seg0 = w_begin; seg0 < w_end; seg0 += 64 * kSegBatch) {
+        int ev[kSegBatch];
+        load_segments(ids, P, seg0, ev);
+#pragma unroll
+        for (int s = 0; s < kSegBatch; ++s) {
+            const int64_t p = seg0 + 64 * s + lane;
+            const bool in = p < w_end && p < P;
+            const int e = in ? ev[s] : -1;
+            const bool valid = e >= 0;
+            const uint64_t m = match_mask(valid ? e : 0, valid, id_bits);
+            if (valid) {
+                const int pos = row[e] + __popcll(m & lt);
+                perm_token[pos] = static_cast<int32_t>(p / K);
+                inv_pos[p] = pos;
+            } else if (in) {
+                inv_pos[p] = -1;
+            }
+            __builtin_amdgcn_wave_barrier();
+            if (valid && (m & lt) == 0ull) row[e] += __popcll(m);
+            __builtin_amdgcn_wave_barrier();
+        }
     }
 }
 
@@ -164,7 +216,6 @@ __global__ __launch_bounds__(256) void permute_scatter_kernel(
     __shared__ int part[256];
     const int tid = threadIdx.x;
     const int wv = tid >> 6;
-    const int lane = lane_id();
     for (int i = tid; i < kPermWaves * E; i += 256) hist[i / E][i % E] = 0;
     scan_counts(counts, E, offs, part);
     if (blockIdx.x == 0)
@@ -186,26 +237,7 @@ __global__ __launch_bounds__(256) void permute_scatter_kernel(
         }
     }
     __syncthreads();
-    const uint64_t lt = (1ull << lane) - 1ull;
-    int* row = hist[wv];
-    for (int64_t seg = w_begin; seg < w_end; seg += 64) {
-        const int64_t p = seg + lane;
-        const bool in = p < w_end && p < P;
-        int e = -1;
-        if (in) e = ids[p];
-        const bool valid = e >= 0;
-        const uint64_t m = match_mask(valid ? e : 0, valid, id_bits);
-        if (valid) {
-            const int pos = row[e] + __popcll(m & lt);
-            perm_token[pos] = static_cast<int32_t>(p / K);
-            inv_pos[p] = pos;
-        } else if (in) {
-            inv_pos[p] = -1;
-        }
-        __builtin_amdgcn_wave_barrier();
-        if (valid && (m & lt) == 0ull) row[e] += __popcll(m);
-        __builtin_amdgcn_wave_barrier();
-    }
+    wave_scatter(ids, P, K, w_begin, w_end, id_bits, hist[wv], perm_token, inv_pos);
 }
 
 // All three passes in one workgroup when every pair fits one block (the
@@ -219,7 +251,6 @@ __global__ __launch_bounds__(256) void permute_single_kernel(
     __shared__ int part[256];
     const int tid = threadIdx.x;
     const int wv = tid >> 6;
-    const int lane = lane_id();
     for (int i = tid; i < kPermWaves * E; i += 256) hist[i / E][i % E] = 0;
     __syncthreads();
     const int per_wave = ppb / kPermWaves;
@@ -266,26 +297,7 @@ __global__ __launch_bounds__(256) void permute_single_kernel(
         }
     }
     __syncthreads();
-    const uint64_t lt = (1ull << lane) - 1ull;
-    int* row = hist[wv];
-    for (int64_t seg = w_begin; seg < w_end; seg += 64) {
-        const int64_t p = seg + lane;
-        const bool in = p < w_end && p < P;
-        int e = -1;
-        if (in) e = ids[p];
-        const bool valid = e >= 0;
-        const uint64_t m = match_mask(valid ? e : 0, valid, id_bits);
-        if (valid) {
-            const int pos = row[e] + __popcll(m & lt);
-            perm_token[pos] = static_cast<int32_t>(p / K);
-            inv_pos[p] = pos;
-        } else if (in) {
-            inv_pos[p] = -1;
-        }
-        __builtin_amdgcn_wave_barrier();
-        if (valid && (m & lt) == 0ull) row[e] += __popcll(m);
-        __builtin_amdgcn_wave_barrier();
-    }
+    wave_scatter(ids, P, K, w_begin, w_end, id_bits, hist[wv], perm_token, inv_pos);
 }
 
 hipError_t launch_permute(const int32_t* ids, int64_t T, int K, int E, int32_t* ws_i32,
