@@ -345,22 +345,35 @@ static moe_status forward_impl(const moe_shape* shape, const moe_weights* weight
     void* exw = base + L.exp_ws;
     const int64_t T = shape->T;
 
-    if (replay_ids != nullptr) {
-        if ((st = hip_status(moe::launch_route_replay(x, weights->router, T, shape->D, shape->E, shape->K,
-                                                      shape->dtype, shape->score, shape->renorm, shape->route_scale,
-                                                      replay_ids, mask, l64, tr.logits, ids, tw, stream),
-                             "routing replay launch")) != MOE_OK)
+    if (moe::route_permute_fused(T)) {
+        // decode-sized batch: top-k and the permutation in one launch (a
+        // replay takes the given ids, no selection bias and no groups)
+        const bool rp = replay_ids != nullptr;
+        if ((st = hip_status(moe::launch_route_permute(
+                                 x, weights->router, T, shape->D, shape->E, shape->K, shape->dtype, shape->score,
+                                 shape->renorm, shape->route_scale, rp ? 1 : n_group(shape), rp ? 1 : shape->topk_group,
+                                 rp ? nullptr : sel_bias, replay_ids, mask, l64, tr.logits, ids, tw, counts, offsets,
+                                 perm, inv, stream),
+                             "routing launch")) != MOE_OK)
             return st;
-    } else if ((st = hip_status(moe::launch_route(x, weights->router, T, shape->D, shape->E, shape->K, shape->dtype,
-                                                  shape->score, shape->renorm, shape->route_scale, n_group(shape),
-                                                  shape->topk_group, sel_bias, mask, l64, tr.logits, ids, tw, stream),
-                                "routing launch")) != MOE_OK) {
-        return st;
+    } else {
+        if (replay_ids != nullptr) {
+            if ((st = hip_status(moe::launch_route_replay(x, weights->router, T, shape->D, shape->E, shape->K,
+                                                          shape->dtype, shape->score, shape->renorm, shape->route_scale,
+                                                          replay_ids, mask, l64, tr.logits, ids, tw, stream),
+                                 "routing replay launch")) != MOE_OK)
+                return st;
+        } else if ((st = hip_status(moe::launch_route(x, weights->router, T, shape->D, shape->E, shape->K, shape->dtype,
+                                                      shape->score, shape->renorm, shape->route_scale, n_group(shape),
+                                                      shape->topk_group, sel_bias, mask, l64, tr.logits, ids, tw, stream),
+                                    "routing launch")) != MOE_OK) {
+            return st;
+        }
+        if ((st = hip_status(moe::launch_permute(ids, T, shape->K, shape->E, reinterpret_cast<int32_t*>(base + L.perm_ws),
+                                                 counts, offsets, perm, inv, stream),
+                             "permute launch")) != MOE_OK)
+            return st;
     }
-    if ((st = hip_status(moe::launch_permute(ids, T, shape->K, shape->E, reinterpret_cast<int32_t*>(base + L.perm_ws),
-                                             counts, offsets, perm, inv, stream),
-                         "permute launch")) != MOE_OK)
-        return st;
     if (shared_with_routed(shape)) {
         if ((st = hip_status(moe::launch_experts_skinny_pair(
                                  x, perm, offsets, shape->E, T * shape->K, shape->D, shape->I, weights->gate_up,

@@ -21,6 +21,15 @@ int compute_units();
 // whether launch_route runs the single fused kernel (bf16 operands, E <= 512,
 // no group-limited select)
 bool route_fused(int E, int dtype, int n_group);
+// decode-sized batches in moe_forward: logits, then top-k and the dispatch
+// permutation in one kernel (given: replayed ids or null); the same picks and
+// rows as launch_route (or launch_route_replay) followed by launch_permute
+bool route_permute_fused(int64_t T);
+hipError_t launch_route_permute(const void* x, const void* router, int64_t T, int D, int E, int K, int dtype,
+                                int score, int renorm, float route_scale, int n_group, int topk_group,
+                                const float* bias, const int32_t* given, const uint8_t* mask, double* logits64,
+                                float* logits_out, int32_t* ids, float* w, int32_t* counts, int32_t* offsets,
+                                int32_t* perm_token, int32_t* inv_pos, hipStream_t stream);
 // logits + top-k: one fused kernel where route_fused(), else the two kernels
 // above through logits64 [T, E]; both give the same bits
 hipError_t launch_route(const void* x, const void* router, int64_t T, int D, int E, int K, int dtype,

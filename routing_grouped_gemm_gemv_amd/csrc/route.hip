@@ -18,6 +18,7 @@
 // rounded once to float32.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "permute_block.hpp"
 
 namespace moe {
 
@@ -31,6 +32,7 @@ constexpr int kRtK = 64;  // k per LDS stage; fp32 partial sums span four stages
 // re-reads 16 hidden rows and 16 router rows, so its traffic grows with T * E;
 // measured crossover with the fused router on the Qwen3-30B- and DSV4-like layers)
 constexpr int64_t kRouteSmallTE = int64_t{1} << 18;
+constexpr int64_t kTopkPermuteT = 8;  // moe_forward fuses top-k and permute up to this many tokens
 
 __global__ __launch_bounds__(256) void router_logits_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int64_t T, int D, int E,
@@ -741,6 +743,36 @@ __global__ __launch_bounds__(256) void topk_kernel(
     topk_token<EPL>(lg, t, E, K, score, renorm, route_scale, bias, kept, ids_out, w_out, given, n_group, topk_group);
 }
 
+// Decode-sized batches in moe_forward: the top-k of every token and the
+// dispatch permutation in one workgroup, one launch instead of two.  Wave w
+// takes tokens w, w + 4, ... and picks exactly as topk_kernel does; the
+// barrier makes the ids visible to the workgroup, and the permutation
+// follows as permute_single_kernel computes it.
+template <int EPL>
+__global__ __launch_bounds__(256) void topk_permute_kernel(
+    const double* __restrict__ logits, int64_t T, int E, int K, int score, int renorm, double route_scale,
+    const float* __restrict__ bias, const uint8_t* __restrict__ mask, float* __restrict__ logits_out,
+    int32_t* __restrict__ ids_out, float* __restrict__ w_out, const int32_t* __restrict__ given, int n_group,
+    int topk_group, int ppb, int id_bits, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ perm_token, int32_t* __restrict__ inv_pos) {
+    const int lane = lane_id();
+    const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+    for (int64_t t = wv; t < T; t += 4) {
+        double lg[EPL];
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+            const int e = lane + 64 * i;
+            lg[i] = e < E ? logits[t * E + e] : 0.0;
+            if (logits_out && e < E) logits_out[t * E + e] = static_cast<float>(lg[i]);
+        }
+        const bool kept = (mask == nullptr) || (mask[t] != 0);
+        topk_token<EPL>(lg, t, E, K, score, renorm, route_scale, bias, kept, ids_out, w_out, given, n_group,
+                        topk_group);
+    }
+    __syncthreads();  // every token's ids written and visible to the workgroup
+    permute_one_block(ids_out, T * K, K, E, ppb, id_bits, counts, offsets, perm_token, inv_pos);
+}
+
 // ---------------------------------------------------------------------------
 // fused routing, bf16 operands: logits of TB tokens x all experts in one
 // workgroup, kept in LDS as float64, then top-k per token from LDS.
@@ -1102,6 +1134,31 @@ hipError_t launch_topk(const double* logits64, int64_t T, int E, int K, int scor
     else if (E <= 512) MOE_TOPK(8);
     else MOE_TOPK(16);
 #undef MOE_TOPK
+    return hipGetLastError();
+}
+
+bool route_permute_fused(int64_t T) { return T >= 1 && T <= kTopkPermuteT; }
+
+hipError_t launch_route_permute(const void* x, const void* router, int64_t T, int D, int E, int K, int dtype,
+                                int score, int renorm, float route_scale, int n_group, int topk_group,
+                                const float* bias, const int32_t* given, const uint8_t* mask, double* logits64,
+                                float* logits_out, int32_t* ids, float* w, int32_t* counts, int32_t* offsets,
+                                int32_t* perm_token, int32_t* inv_pos, hipStream_t stream) {
+    hipError_t err = launch_router_logits(x, router, T, D, E, dtype, logits64, stream);
+    if (err != hipSuccess) return err;
+    const PermutePlan pl = permute_plan(T * K, E);  // one block: T * K <= 8 * 16 pairs
+    const double rs = static_cast<double>(route_scale);
+#define MOE_TOPK_PERMUTE(EPL)                                                                               \
+    topk_permute_kernel<EPL><<<1, 256, 0, stream>>>(logits64, T, E, K, score, renorm, rs, bias, mask,      \
+                                                    logits_out, ids, w, given, n_group, topk_group,         \
+                                                    pl.pairs_per_block, pl.id_bits, counts, offsets, perm_token, \
+                                                    inv_pos)
+    if (E <= 64) MOE_TOPK_PERMUTE(1);
+    else if (E <= 128) MOE_TOPK_PERMUTE(2);
+    else if (E <= 256) MOE_TOPK_PERMUTE(4);
+    else if (E <= 512) MOE_TOPK_PERMUTE(8);
+    else MOE_TOPK_PERMUTE(16);
+#undef MOE_TOPK_PERMUTE
     return hipGetLastError();
 }
 
