@@ -21,6 +21,8 @@ Pins (the tests that tie each function to something other than itself):
                      topk_group = n_group reduce to select_topk; brute-force
                      group ranking with plain Python lists
   topk_weights       sum = route_scale, top-1 renorm = 1, zero row = 1/K
+  route              the routing half of forward (logits .. weights) on its own;
+                     equal to forward's routing fields (its pins are theirs)
   permute            numpy stable argsort; bijection and segment invariants
   expert_mlp         dense all-experts formulation with torch.nn.functional.silu;
                      E=1, K=1 reduces to a dense SwiGLU MLP
@@ -39,6 +41,7 @@ from .backward import backward, backward_expert
 from .moe import (
     EXEMPT_REL_MARGIN,
     OracleResult,
+    RouteResult,
     bf16_bits_of,
     combine_f64,
     combine_fp32,
@@ -47,6 +50,7 @@ from .moe import (
     forward,
     permute,
     round_bf16,
+    route,
     router_logits,
     scores,
     select_grouped,
@@ -61,6 +65,7 @@ __all__ = [
     "backward",
     "backward_expert",
     "OracleResult",
+    "RouteResult",
     "bf16_bits_of",
     "combine_f64",
     "combine_fp32",
@@ -69,6 +74,7 @@ __all__ = [
     "forward",
     "permute",
     "round_bf16",
+    "route",
     "router_logits",
     "scores",
     "select_grouped",

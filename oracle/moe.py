@@ -383,6 +383,45 @@ def combine_orders(y: np.ndarray, inv_pos: np.ndarray, w32: np.ndarray,
 # ----------------------------------------------------------------------------
 
 @dataclass
+class RouteResult:
+    logits: np.ndarray        # [T, E] float64
+    scores: np.ndarray        # [T, E] float64
+    choice: np.ndarray        # [T, E] float64
+    ids: np.ndarray           # [T, K] int32, ascending, -1 masked
+    weights: np.ndarray       # [T, K] float64
+    rel_margin: np.ndarray    # [T] float64
+    exempt: np.ndarray        # [T] bool: 0 < rel_margin < EXEMPT_REL_MARGIN
+
+
+def route(x: np.ndarray, w_router: np.ndarray, *, K: int, score: str, renorm: bool, route_scale: float,
+          bias: Optional[np.ndarray] = None, mask: Optional[np.ndarray] = None,
+          ids_override: Optional[np.ndarray] = None, n_group: int = 1, topk_group: int = 1) -> RouteResult:
+    """The routing boundary alone [RLK, Problem 1]: logits, scores, choice,
+    top-K ids (ascending, -1 for masked tokens), weights and the near-tie
+    margin, exactly as ``forward`` computes them.  ``ids_override`` replays
+    given ids [RLK, "R3 Should Not Be A Prerequisite"]; the weights then come
+    from the scores of those ids."""
+    x64 = widen(x)
+    wr64 = widen(w_router)
+    T = x64.shape[0]
+    valid = np.ones(T, dtype=bool) if mask is None else np.asarray(mask).astype(bool)
+
+    logits = router_logits(x64, wr64)
+    s = scores(logits, score)
+    c = s + widen(bias)[None, :] if bias is not None else s
+    if n_group > 1:
+        ids, margin = select_grouped(c, K, n_group, topk_group, valid)
+    else:
+        ids, margin = select_topk(c, K, valid)
+    if ids_override is not None:
+        ids = np.asarray(ids_override, dtype=np.int32).copy()
+        ids[~valid] = -1
+    w = topk_weights(s, ids, renorm, route_scale)
+    exempt = (margin > 0) & (margin < EXEMPT_REL_MARGIN)
+    return RouteResult(logits, s, c, ids, w, margin, exempt)
+
+
+@dataclass
 class OracleResult:
     logits: np.ndarray        # [T, E] float64
     scores: np.ndarray        # [T, E] float64
@@ -421,23 +460,13 @@ def forward(x: np.ndarray, w_router: np.ndarray,
     with select_grouped.
     """
     x64 = widen(x)
-    wr64 = widen(w_router)
     T = x64.shape[0]
-    E = wr64.shape[0]
+    E = np.asarray(w_router).shape[0]
     valid = np.ones(T, dtype=bool) if mask is None else np.asarray(mask).astype(bool)
-
-    logits = router_logits(x64, wr64)
-    s = scores(logits, score)
-    c = s + widen(bias)[None, :] if bias is not None else s
-    if n_group > 1:
-        ids, margin = select_grouped(c, K, n_group, topk_group, valid)
-    else:
-        ids, margin = select_topk(c, K, valid)
-    if ids_override is not None:
-        ids = np.asarray(ids_override, dtype=np.int32).copy()
-        ids[~valid] = -1
-    w = topk_weights(s, ids, renorm, route_scale)
-    exempt = (margin > 0) & (margin < EXEMPT_REL_MARGIN)
+    rt = route(x64, w_router, K=K, score=score, renorm=renorm, route_scale=route_scale, bias=bias, mask=mask,
+               ids_override=ids_override, n_group=n_group, topk_group=topk_group)
+    logits, s, c, ids, w, margin, exempt = (rt.logits, rt.scores, rt.choice, rt.ids, rt.weights,
+                                            rt.rel_margin, rt.exempt)
 
     pm = permute(ids, E)
     offsets = pm["offsets"]

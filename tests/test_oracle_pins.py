@@ -307,6 +307,18 @@ def test_no_renorm_weight_is_the_softmax_probability():
     assert not np.array_equal(np.argmax(res.scores, axis=1), res.ids[:, 0])
 
 
+def test_route_is_the_routing_half_of_forward():
+    from dataclasses import replace
+    # the tiny layer (softmax, ties) and a reduced DSV4-like one (sigmoid, bias, route_scale 2.5)
+    for cfg in (get_config("tiny"), replace(get_config("dsv4", T=64), D=256, I=64, Is=0)):
+        inp = make_inputs(cfg)
+        full = oracle_forward(inp)
+        rt = oracle.route(inp.x, inp.w_router, K=cfg.K, score=cfg.score, renorm=cfg.renorm,
+                          route_scale=cfg.route_scale, bias=inp.bias)
+        for f in ("logits", "scores", "choice", "ids", "weights", "rel_margin", "exempt"):
+            assert np.array_equal(getattr(rt, f), getattr(full, f)), (cfg.name, f)
+
+
 # ---------------------------------------------------------------- dispatch
 
 def test_permutation_matches_stable_argsort_and_invariants():
