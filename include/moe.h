@@ -177,7 +177,10 @@ moe_status moe_route(const moe_shape* shape, const void* x, const void* router,
  *   perm_token[p]    token of row p of the expert-sorted order; within one
  *                    expert the tokens ascend
  *   inv_pos[t,j]     row of pair (t,j) in that order, -1 for skipped slots
- * topk_ids int32 [T,K] (ids in [0,E) or -1); outputs as above (device). */
+ * topk_ids int32 [T,K]: ids in [0,E), or -1 for a slot without an expert; a
+ * slot holding any other value (< -1 or >= E) is skipped like -1.  A token
+ * is expected to list distinct ids (tokens then ascend within an expert);
+ * the kernels do not check it.  Outputs as above (device). */
 moe_status moe_permute(const moe_shape* shape, const int32_t* topk_ids, int32_t* counts,
                        int32_t* offsets, int32_t* perm_token, int32_t* inv_pos,
                        void* ws, size_t ws_bytes, hipStream_t stream);
@@ -206,8 +209,9 @@ moe_status moe_experts(const moe_shape* shape, const void* x, const int32_t* per
  *   out[t] = acc rounded to bf16 nearest-even (out_dtype MOE_BF16) or acc (MOE_F32)
  * No fused multiply-add.  With shape->combine == MOE_COMBINE_F64 the same
  * terms are formed and summed in float64 and the sum is rounded once (to bf16
- * or float32, nearest-even).  A token whose inv_pos slots are all -1 gets a +0
- * row.
+ * or float32, nearest-even).  A slot whose inv_pos is -1 contributes nothing
+ * (its weight is not read); a token whose inv_pos slots are all -1 gets a +0
+ * row.  inv_pos entries other than -1 must be rows of y.
  * y [T*K,D] and shared_out [T,D] (or NULL) in operand dtype; inv_pos int32
  * [T,K]; topk_w float [T,K]; out [T,D] in out_dtype. */
 moe_status moe_combine(const moe_shape* shape, const void* y, const int32_t* inv_pos,

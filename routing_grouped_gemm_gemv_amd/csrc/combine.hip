@@ -191,9 +191,10 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
 // issued before the first is used (the kernel above waits for each row in
 // turn, which at large T keeps more waves resident and streams faster).  The
 // fold runs over KC slots, K rounded up to a compiled size, with weight +0
-// and zero data past K: that adds +0 to an accumulator that cannot be -0 (it
-// starts at +0, and round-to-nearest returns +0, not -0, for +0 + -0 and for
-// two terms that cancel), so every bit is the same as the kernel above.
+// and zero data past K and in slots without a row: that adds +0 to an
+// accumulator that cannot be -0 (it starts at +0, and round-to-nearest
+// returns +0, not -0, for +0 + -0 and for two terms that cancel), so every
+// bit is the same as the kernel above, which skips those slots.
 constexpr int64_t kCombineSmallT = 1024;
 
 template <typename Tin, bool OUT_BF16, typename Acc, int KC>
@@ -210,7 +211,9 @@ __global__ __launch_bounds__(kCombineThreads) void combine_small_kernel(
         wt[j] = 0.0f;
         if (j < K) {
             pos[j] = inv_pos[t * K + j];
-            wt[j] = w[t * K + j];
+            // a slot without a row (-1) takes weight +0 and zero data below:
+            // it adds +0, which leaves the bits of skipping it
+            wt[j] = pos[j] >= 0 ? w[t * K + j] : 0.0f;
             kept = kept || pos[j] >= 0;
         }
     }
@@ -218,10 +221,11 @@ __global__ __launch_bounds__(kCombineThreads) void combine_small_kernel(
         Acc acc[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] = Acc(0);
-        if (kept) {  // every pick of a kept token has a row
+        if (kept) {
             Raw8<Tin> r[KC];
 #pragma unroll
-            for (int j = 0; j < KC; ++j) r[j] = j < K ? Raw8<Tin>::load(y + pos[j] * D + d0) : Raw8<Tin>::zero();
+            for (int j = 0; j < KC; ++j)
+                r[j] = pos[j] >= 0 ? Raw8<Tin>::load(y + pos[j] * D + d0) : Raw8<Tin>::zero();
             const Raw8<Tin> rs = shared != nullptr ? Raw8<Tin>::load(shared + t * D + d0) : Raw8<Tin>::zero();
 #pragma unroll
             for (int j = 0; j < KC; ++j) {

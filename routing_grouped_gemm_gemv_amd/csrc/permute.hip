@@ -60,7 +60,7 @@ __global__ __launch_bounds__(256) void permute_count_kernel(
     __syncthreads();
     const int64_t base = static_cast<int64_t>(blockIdx.x) * ppb;
     const int per_wave = ppb / kPermWaves;
-    wave_histogram(ids, P, base + wv * per_wave, base + (wv + 1) * per_wave, id_bits, hist[wv]);
+    wave_histogram(ids, P, E, base + wv * per_wave, base + (wv + 1) * per_wave, id_bits, hist[wv]);
     __syncthreads();
     for (int e = tid; e < E; e += 256)
         block_hist[static_cast<int64_t>(e) * nblocks + blockIdx.x] = hist[0][e] + hist[1][e] + hist[2][e] + hist[3][e];
@@ -147,7 +147,7 @@ __global__ __launch_bounds__(256) void permute_scatter_kernel(
     const int per_wave = ppb / kPermWaves;
     const int64_t w_begin = base + wv * per_wave;
     const int64_t w_end = w_begin + per_wave;
-    wave_histogram(ids, P, w_begin, w_end, id_bits, hist[wv]);
+    wave_histogram(ids, P, E, w_begin, w_end, id_bits, hist[wv]);
     __syncthreads();
     // per-wave base rows: block base of the expert plus earlier waves' pairs
     for (int e = tid; e < E; e += 256) {
@@ -160,7 +160,7 @@ __global__ __launch_bounds__(256) void permute_scatter_kernel(
         }
     }
     __syncthreads();
-    wave_scatter(ids, P, K, w_begin, w_end, id_bits, hist[wv], perm_token, inv_pos);
+    wave_scatter(ids, P, K, E, w_begin, w_end, id_bits, hist[wv], perm_token, inv_pos);
 }
 
 // All three passes in one workgroup when every pair fits one block (the

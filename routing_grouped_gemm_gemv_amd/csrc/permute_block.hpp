@@ -38,8 +38,10 @@ __device__ __forceinline__ void load_segments(const int32_t* __restrict__ ids, i
     }
 }
 
-// Fill hist[w][*] with the per-expert pair counts of wave w's sub-range.
-__device__ __forceinline__ void wave_histogram(const int32_t* __restrict__ ids, int64_t P, int64_t w_begin,
+// Fill hist[w][*] with the per-expert pair counts of wave w's sub-range.  An
+// id outside [0, E) (the -1 of a masked slot, or a caller's out-of-range id)
+// marks a slot without a row.
+__device__ __forceinline__ void wave_histogram(const int32_t* __restrict__ ids, int64_t P, int E, int64_t w_begin,
                                                int64_t w_end, int id_bits, int* hist_row) {
     const int lane = lane_id();
     const uint64_t lt = (1ull << lane) - 1ull;
@@ -50,7 +52,7 @@ __device__ __forceinline__ void wave_histogram(const int32_t* __restrict__ ids, 
         for (int s = 0; s < kSegBatch; ++s) {
             const int64_t p = seg0 + 64 * s + lane;
             const int e = (p < w_end && p < P) ? ev[s] : -1;
-            const bool valid = e >= 0;
+            const bool valid = e >= 0 && e < E;
             const uint64_t m = match_mask(valid ? e : 0, valid, id_bits);
             if (valid && (m & lt) == 0ull) hist_row[e] += __popcll(m);
         }
@@ -59,7 +61,7 @@ __device__ __forceinline__ void wave_histogram(const int32_t* __restrict__ ids, 
 
 // The scatter of wave w's sub-range: row[e] holds the next row of expert e
 // for this wave.
-__device__ __forceinline__ void wave_scatter(const int32_t* __restrict__ ids, int64_t P, int K, int64_t w_begin,
+__device__ __forceinline__ void wave_scatter(const int32_t* __restrict__ ids, int64_t P, int K, int E, int64_t w_begin,
                                              int64_t w_end, int id_bits, int* row, int32_t* __restrict__ perm_token,
                                              int32_t* __restrict__ inv_pos) {
     const int lane = lane_id();
@@ -72,7 +74,7 @@ __device__ __forceinline__ void wave_scatter(const int32_t* __restrict__ ids, in
             const int64_t p = seg0 + 64 * s + lane;
             const bool in = p < w_end && p < P;
             const int e = in ? ev[s] : -1;
-            const bool valid = e >= 0;
+            const bool valid = e >= 0 && e < E;
             const uint64_t m = match_mask(valid ? e : 0, valid, id_bits);
             if (valid) {
                 const int pos = row[e] + __popcll(m & lt);
@@ -105,7 +107,7 @@ __device__ __forceinline__ void permute_one_block(const int32_t* __restrict__ id
     const int per_wave = ppb / kPermWaves;
     const int64_t w_begin = static_cast<int64_t>(wv) * per_wave;
     const int64_t w_end = w_begin + per_wave;
-    wave_histogram(ids, P, w_begin, w_end, id_bits, hist[wv]);
+    wave_histogram(ids, P, E, w_begin, w_end, id_bits, hist[wv]);
     __syncthreads();
     // counts, then their exclusive scan into offs[0..E]
     int v[4];
@@ -146,7 +148,7 @@ __device__ __forceinline__ void permute_one_block(const int32_t* __restrict__ id
         }
     }
     __syncthreads();
-    wave_scatter(ids, P, K, w_begin, w_end, id_bits, hist[wv], perm_token, inv_pos);
+    wave_scatter(ids, P, K, E, w_begin, w_end, id_bits, hist[wv], perm_token, inv_pos);
 }
 
 }  // namespace moe

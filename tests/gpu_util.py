@@ -77,3 +77,88 @@ def routing_check(gpu_ids: np.ndarray, ref) -> Dict[str, object]:
         "mismatch_count": int(bad.size),
         "mismatch_tokens": bad.tolist()[:20],
     }
+
+
+def bf16_ulp(v: np.ndarray) -> np.ndarray:
+    """Spacing of the bf16 grid (8 significant bits) at |v|; 2^-133 at 0."""
+    _, e = np.frexp(np.asarray(v, dtype=np.float64))   # v = m * 2^e, 0.5 <= |m| < 1
+    return np.ldexp(1.0, np.where(v == 0, -133, e - 8))
+
+
+def bf16_output_report(gout_bits: np.ndarray, ref64: np.ndarray, kept: Optional[np.ndarray],
+                       rms: float, tol: float) -> Dict[str, float]:
+    """The delivered bf16 layer output against the unrounded float64 reference.
+
+    Counts the elements whose error exceeds ``tol * rms`` and gives the worst
+    error in units of ``rms``; for every element, the distance to the
+    reference rounded once to bf16 (RNE_bf16(out64)) in units of the bf16
+    spacing there.  Final rounding alone can move an element by half a bf16
+    ulp of its magnitude, which exceeds ``tol * rms`` only for elements of
+    several RMS, so a breach that comes from the rounding sits within one ulp
+    of RNE_bf16(out64); the caller asserts that.
+    """
+    g = as_f64(gout_bits)
+    r = ref64
+    if kept is not None:
+        g, r = g[kept], r[kept]
+    err = np.abs(g - r)
+    rne = oracle.round_bf16(r)
+    ulp = np.maximum(bf16_ulp(rne), bf16_ulp(g))
+    dist = np.abs(g - rne) / ulp
+    over = err > tol * rms
+    return {
+        "bf16_out_max_rel_rms": float(err.max() / rms) if err.size and rms > 0 else 0.0,
+        "bf16_out_over_tol_count": int(over.sum()),
+        "bf16_out_over_tol_max_dist_ulp": float(dist[over].max()) if over.any() else 0.0,
+        "bf16_out_over_tol_min_abs_ref_rms": float(np.abs(r[over]).min() / rms) if over.any() else 0.0,
+        "bf16_out_elements": int(err.size),
+        "bf16_out_share_equal_rne": float(np.mean(dist == 0)) if err.size else 1.0,
+        "bf16_out_share_within_1ulp_rne": float(np.mean(dist <= 1.0)) if err.size else 1.0,
+        "bf16_out_max_dist_ulp": float(dist.max()) if err.size else 0.0,
+    }
+
+
+def check_layer_output(shape, tr: dict, gout: np.ndarray, ref64: np.ndarray, kept: Optional[np.ndarray],
+                       tol: float, report: Optional[dict] = None,
+                       tokens: Optional[np.ndarray] = None) -> Dict[str, float]:
+    """Parity (c) of one layer call, both sides of the final downcast.
+
+    The combine is run again on the call's own trace with a float32 output:
+    the delivered output must be exactly that value (rounded to nearest even
+    when it is bf16), and that value must lie within ``tol`` of the RMS of
+    the float64 reference, with no widening.  For a bf16 output the breaches
+    of ``tol * RMS`` are reported with their magnitude and each must lie
+    within one bf16 ulp of the reference rounded once to bf16.  With
+    ``tokens``, ``ref64`` (and ``kept``) hold those tokens only, while the
+    downcast is checked on every token of ``gout``.
+    """
+    from routing_grouped_gemm_gemv_amd import binding as B
+    T, D = gout.shape
+    out32 = torch.empty(T, D, dtype=torch.float32, device="cuda")
+    B.moe_combine(shape, tr["y"], tr["inv_pos"], tr["topk_w"], tr.get("shared_out"), out32)
+    torch.cuda.synchronize()
+    o32 = to_host(out32)
+    if gout.dtype == np.uint16:
+        assert np.array_equal(gout, oracle.bf16_bits_of(o32)), "bf16 output is not RNE of the float32 combine"
+    else:
+        assert np.array_equal(gout.view(np.uint32), o32.view(np.uint32))
+    if tokens is not None:
+        o32, gout = o32[tokens], gout[tokens]
+    pr = dict(report or {})
+    pr.update(parity_report(o32, ref64, kept))
+    if gout.dtype == np.uint16:
+        pr.update(bf16_output_report(gout, ref64, kept, pr["rms"], tol))
+    assert pr["max_rel_rms"] <= tol, pr
+    if gout.dtype == np.uint16:
+        assert pr["bf16_out_over_tol_max_dist_ulp"] <= 1.0, pr
+    return pr
+
+
+def f32_layer(layer_bf16):
+    """The same layer in the fp32-operand mode: every weight widened exactly
+    from its bf16 value on the device."""
+    from routing_grouped_gemm_gemv_amd import MoeLayer
+    s = layer_bf16.shape.replace(dtype="f32")
+    W = {k: v.float() for k, v in layer_bf16.weights.items()}
+    return MoeLayer(s, W["router"], W["gate_up"], W["down"], W.get("gate_up_shared"), W.get("down_shared"),
+                    layer_bf16.sel_bias)

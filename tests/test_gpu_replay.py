@@ -17,7 +17,7 @@ import torch
 
 import oracle
 from synth import get_config, make_inputs
-from tests.gpu_util import make_layer, parity_report, to_dev, to_host
+from tests.gpu_util import check_layer_output, make_layer, to_dev, to_host
 from tests.oracle_bridge import oracle_forward
 
 pytestmark = pytest.mark.gpu
@@ -70,12 +70,11 @@ def test_replay_of_other_ids_matches_the_oracle(name, T):
     emu = oracle.combine_fp32(to_host(tr["y"]), to_host(tr["inv_pos"]), to_host(tr["topk_w"]),
                               to_host(tr["shared_out"]) if cfg.Is > 0 else None,
                               out="f32" if od == torch.float32 else "bf16")
-    assert np.array_equal(to_host(out), emu)
-    g = oracle.widen(to_host(out))
-    pr = parity_report(g, rep.out)
-    _say(f"[replay] {name}-T{T} {json.dumps(pr)}")
+    gout = to_host(out)
+    assert np.array_equal(gout, emu)
     tol = 1e-5 if cfg.dtype == "f32" else 2e-2
-    assert np.all(np.abs(g - rep.out) <= tol * pr["rms"] + (0 if od == torch.float32 else 2.0 ** -8 * np.abs(rep.out)))
+    pr = check_layer_output(layer.with_tokens(T), tr, gout, rep.out, None, tol)
+    _say(f"[replay] {name}-T{T} {json.dumps(pr)}")
 
 
 def test_invalid_replayed_ids_are_masked():
