@@ -227,6 +227,30 @@ moe_status moe_forward(const moe_shape* shape, const moe_weights* weights, const
                        void* out, const moe_trace* trace, void* ws, size_t ws_bytes,
                        hipStream_t stream);
 
+/* Bytes of the fixed device scratch of moe_forward_noalloc (64 MiB per device). */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* moe_forward without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts that
+ * forbid allocation during the forward).  It runs exactly the kernels of
+ * moe_forward, with the same results bit for bit, on a scratch array that the
+ * library holds in device memory: MOE_NOALLOC_SCRATCH_BYTES per device, set
+ * aside when the library's device code is loaded on that device and kept
+ * until the process ends.  The call allocates nothing and frees nothing.
+ * Shapes whose moe_workspace_size() exceeds MOE_NOALLOC_SCRATCH_BYTES return
+ * MOE_ERR_UNSUPPORTED before anything runs (at 64 MiB: decode and moderate
+ * prefill batches, e.g. up to 796 tokens of a 4096-wide, 256-expert, top-6
+ * layer with a 2048-wide routed and shared expert).  Every call on one device uses the same
+ * scratch, which keeps what the last call left there; the forward needs no
+ * zeroed memory (it issues no memset), and no value left by an earlier call
+ * reaches an output, exactly as for moe_forward's workspace.  Calls that
+ * overlap on one device (two streams, or two host threads, without ordering
+ * between them) race on the scratch and give undefined results.  Arguments
+ * otherwise as in moe_forward. */
+moe_status moe_forward_noalloc(const moe_shape* shape, const moe_weights* weights, const void* x,
+                               const float* sel_bias, const uint8_t* mask, int32_t out_dtype, void* out,
+                               const moe_trace* trace, hipStream_t stream);
+
 /* Routing replay (RL-Kernel roadmap, "R3 Should Not Be A Prerequisite": the
  * experts a token used in another run are replayed, the router still scores
  * them).  The router logits and scores are computed as in moe_route, but the

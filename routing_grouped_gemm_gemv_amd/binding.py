@@ -32,6 +32,7 @@ EXPORTED = (
     "moe_experts",
     "moe_combine",
     "moe_forward",
+    "moe_forward_noalloc",
     "moe_route_replay",
     "moe_forward_replay",
     "moe_backward_workspace_size",
@@ -136,6 +137,8 @@ def lib() -> ctypes.CDLL:
     L.moe_combine.argtypes = [S, P, P, P, P, ctypes.c_int32, P, P]
     L.moe_forward.argtypes = [S, ctypes.POINTER(_Weights), P, P, P, ctypes.c_int32, P,
                               ctypes.POINTER(_Trace), P, ctypes.c_size_t, P]
+    L.moe_forward_noalloc.argtypes = [S, ctypes.POINTER(_Weights), P, P, P, ctypes.c_int32, P,
+                                      ctypes.POINTER(_Trace), P]
     L.moe_route_replay.argtypes = [S, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     L.moe_forward_replay.argtypes = [S, ctypes.POINTER(_Weights), P, P, P, ctypes.c_int32, P,
                                      ctypes.POINTER(_Trace), P, ctypes.c_size_t, P]
@@ -143,7 +146,7 @@ def lib() -> ctypes.CDLL:
     L.moe_backward.argtypes = [S, ctypes.POINTER(_Weights), P, P, ctypes.POINTER(_Trace), P,
                                ctypes.POINTER(_Grads), P, ctypes.c_size_t, P]
     for fn in ("moe_workspace_size", "moe_route", "moe_permute", "moe_experts", "moe_combine", "moe_forward",
-               "moe_route_replay", "moe_forward_replay", "moe_backward_workspace_size", "moe_backward"):
+               "moe_forward_noalloc", "moe_route_replay", "moe_forward_replay", "moe_backward_workspace_size", "moe_backward"):
         getattr(L, fn).restype = ctypes.c_int
     L.moe_status_string.argtypes = [ctypes.c_int]
     L.moe_status_string.restype = ctypes.c_char_p
@@ -248,11 +251,24 @@ def moe_combine(shape: Shape, y, inv_pos, topk_w, shared_out, out) -> None:
         out_dtype, _ptr(out, "out", None, shape.T * shape.D), _stream()), "moe_combine")
 
 
+NOALLOC_SCRATCH_BYTES = 64 << 20  # MOE_NOALLOC_SCRATCH_BYTES
+
+
+def moe_forward_noalloc(shape: Shape, weights: dict, x, sel_bias, mask, out, trace: Optional[dict] = None) -> None:
+    """moe_forward on the library's fixed device scratch (no workspace argument)."""
+    _forward_call(shape, weights, x, sel_bias, mask, out, None, trace, None, noalloc=True)
+
+
 def moe_forward(shape: Shape, weights: dict, x, sel_bias, mask, out, ws, trace: Optional[dict] = None,
                 replay_ids=None) -> None:
     """weights: router, gate_up, down[, gate_up_shared, down_shared]; trace: optional
     dict of preallocated boundary tensors keyed like moe_trace's fields.  With
     ``replay_ids`` ([T, K] int32) this calls moe_forward_replay instead."""
+    _forward_call(shape, weights, x, sel_bias, mask, out, ws, trace, replay_ids)
+
+
+def _forward_call(shape: Shape, weights: dict, x, sel_bias, mask, out, ws, trace, replay_ids,
+                  noalloc: bool = False) -> None:
     s = shape.c()
     od = shape.torch_dtype
     w = _Weights(
@@ -284,6 +300,13 @@ def moe_forward(shape: Shape, weights: dict, x, sel_bias, mask, out, ws, trace: 
             out_dtype, _ptr(out, "out", None, shape.T * shape.D),
             ctypes.byref(tr) if tr is not None else None,
             _ptr(ws, "ws", torch.uint8), ws.numel() if ws is not None else 0, _stream()), "moe_forward_replay")
+        return
+    if noalloc:
+        _check(lib().moe_forward_noalloc(
+            ctypes.byref(s), ctypes.byref(w), _ptr(x, "x", od, shape.T * shape.D),
+            _ptr(sel_bias, "sel_bias", torch.float32, shape.E), _ptr(mask, "mask", torch.uint8, shape.T),
+            out_dtype, _ptr(out, "out", None, shape.T * shape.D),
+            ctypes.byref(tr) if tr is not None else None, _stream()), "moe_forward_noalloc")
         return
     _check(lib().moe_forward(
         ctypes.byref(s), ctypes.byref(w), _ptr(x, "x", od, shape.T * shape.D),

@@ -37,6 +37,9 @@ size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
 
 constexpr int64_t kMaxPairs = (static_cast<int64_t>(1) << 31) - 1;
 
+// size of the fixed scratch of moe_forward_noalloc (MOE_NOALLOC_SCRATCH_BYTES)
+constexpr size_t kScratchBytes = MOE_NOALLOC_SCRATCH_BYTES;
+
 // 0 and 1 both mean: no group-limited select
 int n_group(const moe_shape* s) { return s->n_group > 1 ? s->n_group : 1; }
 
@@ -300,10 +303,10 @@ moe_status moe_combine(const moe_shape* shape, const void* y, const int32_t* inv
     return ok();
 }
 
-static moe_status forward_impl(const moe_shape* shape, const moe_weights* weights, const void* x,
-                               const float* sel_bias, const int32_t* replay_ids, const uint8_t* mask,
-                               int32_t out_dtype, void* out, const moe_trace* trace, void* ws, size_t ws_bytes,
-                               hipStream_t stream) {
+// The argument checks of the forward entry points, before any device call.
+static moe_status check_forward_args(const moe_shape* shape, const moe_weights* weights, const void* x,
+                                     const float* sel_bias, const int32_t* replay_ids, int32_t out_dtype,
+                                     const void* out, const moe_trace* trace, const void* ws) {
     moe_status st = check_shape(shape);
     if (st != MOE_OK) return st;
     if (!weights) return fail(MOE_ERR_INVALID, "moe_forward: weights are required");
@@ -323,8 +326,17 @@ static moe_status forward_impl(const moe_shape* shape, const moe_weights* weight
                         "moe_forward: x, out, ws, the weights and the trace's y and shared_out must be 16-byte "
                         "aligned, the other arrays 4-byte");
     }
+    if (shape->T > 0 && (!x || !out)) return fail(MOE_ERR_INVALID, "moe_forward: x and out are required");
+    return MOE_OK;
+}
+
+static moe_status forward_impl(const moe_shape* shape, const moe_weights* weights, const void* x,
+                               const float* sel_bias, const int32_t* replay_ids, const uint8_t* mask,
+                               int32_t out_dtype, void* out, const moe_trace* trace, void* ws, size_t ws_bytes,
+                               hipStream_t stream) {
+    moe_status st = check_forward_args(shape, weights, x, sel_bias, replay_ids, out_dtype, out, trace, ws);
+    if (st != MOE_OK) return st;
     if (shape->T == 0) return ok();
-    if (!x || !out) return fail(MOE_ERR_INVALID, "moe_forward: x and out are required");
     const ForwardLayout L = forward_layout(shape);
     if (!ws || ws_bytes < L.total)
         return fail(MOE_ERR_WORKSPACE, "moe_forward needs %zu workspace bytes, got %zu", L.total, ws ? ws_bytes : 0);
@@ -403,6 +415,50 @@ moe_status moe_forward(const moe_shape* shape, const moe_weights* weights, const
                        const uint8_t* mask, int32_t out_dtype, void* out, const moe_trace* trace, void* ws,
                        size_t ws_bytes, hipStream_t stream) {
     return forward_impl(shape, weights, x, sel_bias, nullptr, mask, out_dtype, out, trace, ws, ws_bytes, stream);
+}
+
+// Scratch of moe_forward_noalloc: one fixed array per device, part of the
+// library's device code, so that the call needs no allocation.  Host code
+// never uses the array's name as an address (on the host it is a stand-in):
+// the device address comes from hipGetSymbolAddress, once per device, with
+// that device current.
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+static moe_status scratch_address(void** out) {
+    static std::mutex mu;
+    static void* ptrs[64];
+    int dev = -1;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return fail(MOE_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(err));
+    if (dev < 0 || dev >= 64) return fail(MOE_ERR_UNSUPPORTED, "device index %d out of range", dev);
+    std::lock_guard<std::mutex> lock(mu);
+    if (ptrs[dev] == nullptr) {
+        void* p = nullptr;
+        err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (err != hipSuccess) return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(err));
+        if (p == nullptr) return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+        ptrs[dev] = p;
+    }
+    *out = ptrs[dev];
+    return MOE_OK;
+}
+
+moe_status moe_forward_noalloc(const moe_shape* shape, const moe_weights* weights, const void* x,
+                               const float* sel_bias, const uint8_t* mask, int32_t out_dtype, void* out,
+                               const moe_trace* trace, hipStream_t stream) {
+    moe_status st = check_forward_args(shape, weights, x, sel_bias, nullptr, out_dtype, out, trace, nullptr);
+    if (st != MOE_OK) return st;
+    const size_t need = forward_layout(shape).total;
+    if (need > kScratchBytes)
+        return fail(MOE_ERR_UNSUPPORTED,
+                    "moe_forward_noalloc: this shape needs %zu bytes of scratch, above the fixed %zu; "
+                    "call moe_forward with a workspace instead",
+                    need, kScratchBytes);
+    if (shape->T == 0) return ok();
+    if ((st = check_device()) != MOE_OK) return st;
+    void* ws = nullptr;
+    if ((st = scratch_address(&ws)) != MOE_OK) return st;
+    return forward_impl(shape, weights, x, sel_bias, nullptr, mask, out_dtype, out, trace, ws, kScratchBytes, stream);
 }
 
 moe_status moe_forward_replay(const moe_shape* shape, const moe_weights* weights, const void* x,

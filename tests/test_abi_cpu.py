@@ -207,3 +207,23 @@ def test_misaligned_pointers_are_rejected_before_launch():
     s0 = _shape(T=0)
     assert L.moe_forward(ctypes.byref(s0), ctypes.byref(w), a16, None, None, 0, a16, ctypes.byref(tr), a16,
                          n.value, None) == INV
+
+
+def test_noalloc_forward_host_checks():
+    """moe_forward_noalloc refuses shapes whose workspace exceeds its fixed
+    scratch, and validates like moe_forward, before touching a device."""
+    L = moe.lib()
+    one = ctypes.c_void_p(16)
+    w = B._Weights(16, 16, 16, None, None)
+    big = _shape(T=8192, D=2048, E=128, K=8, I=768)
+    n = ctypes.c_size_t(0)
+    assert L.moe_workspace_size(ctypes.byref(big), ctypes.byref(n)) == B.MOE_OK
+    assert n.value > B.NOALLOC_SCRATCH_BYTES
+    assert L.moe_forward_noalloc(ctypes.byref(big), ctypes.byref(w), one, None, None, 0, one, None, None) \
+        == B.MOE_ERR_UNSUPPORTED
+    assert "scratch" in L.moe_last_error().decode()
+    s0 = _shape(T=0)
+    assert L.moe_forward_noalloc(ctypes.byref(s0), ctypes.byref(w), one, None, None, 0, one, None, None) == B.MOE_OK
+    wbad = B._Weights(16, None, 16, None, None)
+    assert L.moe_forward_noalloc(ctypes.byref(_shape()), ctypes.byref(wbad), one, None, None, 0, one, None, None) \
+        == B.MOE_ERR_INVALID
