@@ -186,16 +186,19 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     }
 }
 
-// The same fold for small batches (fewer than kCombineSmallT tokens), where
-// each wave's memory latency shows: all K row loads of a 16-byte chunk are
-// issued before the first is used (the kernel above waits for each row in
-// turn, which at large T keeps more waves resident and streams faster).  The
+// The same fold for batches of fewer than kCombineLargeT tokens: all K row
+// loads of a 16-byte chunk are issued before the first is used (the kernel
+// above waits for each row in turn).  Measured on the workloads' shapes: this
+// kernel is faster up to 16384 tokens (4096 x 4096, top-1: 18.5 -> 13.7 us;
+// 8192 x 2048, top-8: 56 -> 53 us; 16384 x 2048, top-10: 144 -> 142 us) and
+// 2% slower at 32768 x 4096, top-6 (378 -> 386 us), where the kernel above
+// stays.  The
 // fold runs over KC slots, K rounded up to a compiled size, with weight +0
 // and zero data past K and in slots without a row: that adds +0 to an
 // accumulator that cannot be -0 (it starts at +0, and round-to-nearest
 // returns +0, not -0, for +0 + -0 and for two terms that cancel), so every
 // bit is the same as the kernel above, which skips those slots.
-constexpr int64_t kCombineSmallT = 1024;
+constexpr int64_t kCombineLargeT = 16385;
 
 template <typename Tin, bool OUT_BF16, typename Acc, int KC>
 __global__ __launch_bounds__(kCombineThreads) void combine_small_kernel(
@@ -254,7 +257,7 @@ static void launch_combine_t(const void* y, const int32_t* inv_pos, const float*
     const unsigned grid = static_cast<unsigned>(T);
     const Tin* yy = static_cast<const Tin*>(y);
     const Tin* ss = static_cast<const Tin*>(shared);
-    if (T >= kCombineSmallT) {
+    if (T >= kCombineLargeT) {
         combine_kernel<Tin, OUT_BF16, Acc><<<grid, kCombineThreads, 0, stream>>>(yy, inv_pos, w, ss, T, D, K, out);
         return;
     }

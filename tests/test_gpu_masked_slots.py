@@ -8,8 +8,8 @@ and its reduction boundary (Problem 3) are checked here on ids the caller
 makes, not the router's: the permutation against the oracle's counting sort,
 the combine bit for bit against the oracle's float32 fold (and the float64
 mode against the oracle's once-rounded sum), below and above the batch size
-at which the combine switches kernels, and the common tokens of the two
-batches bitwise equal.
+at which the combine switches kernels (16385 tokens), and the common tokens
+of the two batches bitwise equal.
 """
 
 import numpy as np
@@ -22,7 +22,7 @@ from tests.gpu_util import to_dev, to_host
 pytestmark = pytest.mark.gpu
 
 E, K, D = 64, 6, 512
-T_BIG = 2048     # above the small-batch combine switch (1024 tokens)
+T_BIG = 16448    # above the combine kernel switch (16385 tokens)
 T_SMALL = 100    # below it; the first T_SMALL tokens of the big batch
 
 
@@ -35,7 +35,7 @@ def _ids(T):
     bad = rng.random((T, K)) < 0.04
     ids[hole] = -1
     ids[bad & ~hole] = rng.choice(np.array([E, E + 3, 1 << 20, -2, -77], np.int32), int((bad & ~hole).sum()))
-    for t in (3, 50, 1500):
+    for t in (3, 50, 1500, 16400):
         if t < T:
             ids[t] = -1
     return ids
