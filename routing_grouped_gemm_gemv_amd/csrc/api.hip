@@ -225,7 +225,8 @@ moe_status moe_route_replay(const moe_shape* shape, const void* x, const void* r
     if ((st = check_device()) != MOE_OK) return st;
     double* l64 = static_cast<double*>(ws);
     if ((st = hip_status(moe::launch_route_replay(x, router, shape->T, shape->D, shape->E, shape->K, shape->dtype,
-                                                  shape->score, shape->renorm, shape->route_scale, replay_ids, mask,
+                                                  shape->score, shape->renorm, shape->route_scale, n_group(shape),
+                                                  replay_ids, mask,
                                                   l64, logits, topk_ids, topk_w, stream),
                          "routing replay launch")) != MOE_OK)
         return st;
@@ -359,11 +360,12 @@ static moe_status forward_impl(const moe_shape* shape, const moe_weights* weight
 
     if (moe::route_permute_fused(T)) {
         // decode-sized batch: top-k and the permutation in one launch (a
-        // replay takes the given ids, no selection bias and no groups)
+        // replay takes the given ids and no selection bias; the layer's
+        // n_group still selects the top-k code of its forward)
         const bool rp = replay_ids != nullptr;
         if ((st = hip_status(moe::launch_route_permute(
                                  x, weights->router, T, shape->D, shape->E, shape->K, shape->dtype, shape->score,
-                                 shape->renorm, shape->route_scale, rp ? 1 : n_group(shape), rp ? 1 : shape->topk_group,
+                                 shape->renorm, shape->route_scale, n_group(shape), shape->topk_group,
                                  rp ? nullptr : sel_bias, replay_ids, mask, l64, tr.logits, ids, tw, counts, offsets,
                                  perm, inv, stream),
                              "routing launch")) != MOE_OK)
@@ -372,7 +374,7 @@ static moe_status forward_impl(const moe_shape* shape, const moe_weights* weight
         if (replay_ids != nullptr) {
             if ((st = hip_status(moe::launch_route_replay(x, weights->router, T, shape->D, shape->E, shape->K,
                                                           shape->dtype, shape->score, shape->renorm, shape->route_scale,
-                                                          replay_ids, mask, l64, tr.logits, ids, tw, stream),
+                                                          n_group(shape), replay_ids, mask, l64, tr.logits, ids, tw, stream),
                                  "routing replay launch")) != MOE_OK)
                 return st;
         } else if ((st = hip_status(moe::launch_route(x, weights->router, T, shape->D, shape->E, shape->K, shape->dtype,

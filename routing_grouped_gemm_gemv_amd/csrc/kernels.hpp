@@ -37,9 +37,10 @@ hipError_t launch_route(const void* x, const void* router, int64_t T, int D, int
                         const uint8_t* mask, double* logits64, float* logits_out, int32_t* ids, float* w,
                         hipStream_t stream);
 // routing replay: logits through logits64, then the given ids with weights
-// from their scores (tokens with invalid given ids are treated as masked)
+// from their scores (tokens with invalid given ids are treated as masked);
+// n_group is the layer's, which selects the same top-k code as its forward
 hipError_t launch_route_replay(const void* x, const void* router, int64_t T, int D, int E, int K, int dtype,
-                               int score, int renorm, float route_scale, const int32_t* given,
+                               int score, int renorm, float route_scale, int n_group, const int32_t* given,
                                const uint8_t* mask, double* logits64, float* logits_out, int32_t* ids, float* w,
                                hipStream_t stream);
 

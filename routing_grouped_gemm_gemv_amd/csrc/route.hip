@@ -14,8 +14,9 @@
 // last chunk may hold 64, 128 or 192), and the chunk sums are added in
 // float64; in fp32
 // mode each logit is a float64 FMA chain (the fp32 x fp32 products are exact
-// in float64).  Scores, choices and weights are then float64; the weights are
-// rounded once to float32.
+// in float64).  Scores, choices and weights are then float64 (the softmax
+// normaliser sums float32 exponentials in float64); the weights are rounded
+// once to float32.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "permute_block.hpp"
@@ -487,54 +488,146 @@ __device__ __forceinline__ void write_picks16(const int (&my_e)[P], const double
     }
 }
 
-// Elementwise scores (sigmoid, sqrtsoftplus), screened: the same picks and
-// scores as select_rows16, with float64 scores computed only for the few
-// experts that can be picked.  Every choice c = score(l) + bias is first
-// evaluated in float32 (c32, within about 1e-6 + 1e-7 |c| of the float64
-// value, far inside the margin below).
-// mu, the K-th largest of the 16 lanes' largest c32, is at most the K-th
-// largest c32 (K lanes hold a value >= mu), so every expert the float64
-// choice can pick has c32 >= mu - margin.  Those candidates are compacted
-// one per lane through the wave's LDS scratch (16 bytes per slot, P x 64
-// slots), get their float64 choice exactly as select_rows16 computes it, and
-// K rounds of row argmax pick among them.  Returns false, with no picks,
-// when a row of the wave has more than 16 candidates.
-template <int EPL16, int P>
-__device__ __forceinline__ bool select_rows16_screened(const double (&lg)[P][EPL16], int E, int K, int score,
-                                                       const float* __restrict__ bias, lds_u8* scr, int (&my_e)[P],
-                                                       double (&my_s)[P]) {
+// ---- top-k of one token per row of sixteen lanes ------------------------------
+// Every routing path of a layer without group-limited select and with at most
+// 512 experts selects through the functions below (the fused router, the
+// top-k kernel, the decode top-k + permute kernel and replay), so a token's
+// ids and weights are the same bits whichever kernel runs and whatever the
+// batch.  Row r of a wave (lanes 16r .. 16r+15) takes one token; lane j of
+// the row covers experts j, j + 16, ... (EPL16 slots, those past E unused).
+// The float64 logits are read through lg_of(p, e): the logit of expert e of
+// the row's p-th token, from LDS or from memory.
+//
+// Scores: sigmoid and sqrtsoftplus per logit in float64 (elem_score).
+// Softmax: m = the token's largest logit; z = the sum over its experts of
+// float64(expf(float32(l - m))), each lane adding its slots in order and the
+// row then adding the lanes in a fixed pairwise tree; an expert's score is
+// exp(l - m) / z in float64.  The float32 exponentials put z within about
+// 1e-7 relative of the float64 sum; z scales every score of the token alike,
+// so it moves a weight by at most that much and decides no pick whose choice
+// margin is larger.
+template <int EPL16, typename LG>
+__device__ __forceinline__ void row_softmax(LG lg_of, int p, int E, double& m, double& z) {
+    const int j = lane_id() & 15;
+    double mx = -1.7976931348623157e308;
+#pragma unroll 4
+    for (int i = 0; i < EPL16; ++i)
+        if (j + 16 * i < E) mx = fmax(mx, lg_of(p, j + 16 * i));
+    m = row_max_f64(mx);
+    double part = 0.0;
+#pragma unroll 4
+    for (int i = 0; i < EPL16; ++i)
+        if (j + 16 * i < E) part += static_cast<double>(__expf(static_cast<float>(lg_of(p, j + 16 * i) - m)));
+    z = row_sum_f64(part);
+}
+
+__device__ __forceinline__ double row_score(double l, int score, double m, double z) {
+    return score == 0 ? exp(l - m) / z : elem_score(l, score);
+}
+
+// Rank of key a among the 2 x 16 keys (k0, k1) of this lane's row: how many
+// of them are larger.  The keys of a row are distinct or zero.
+template <int S>
+__device__ __forceinline__ void rank_step(uint64_t k0, uint64_t k1, int& r0, int& r1) {
+    const uint64_t o0 = dpp_u64<0x120 + S>(k0);  // row_ror:S
+    const uint64_t o1 = dpp_u64<0x120 + S>(k1);
+    r0 += (o0 > k0 ? 1 : 0) + (o1 > k0 ? 1 : 0);
+    r1 += (o0 > k1 ? 1 : 0) + (o1 > k1 ? 1 : 0);
+}
+__device__ __forceinline__ void row_ranks(uint64_t k0, uint64_t k1, int& r0, int& r1) {
+    r0 = k1 > k0 ? 1 : 0;
+    r1 = k0 > k1 ? 1 : 0;
+    rank_step<1>(k0, k1, r0, r1);
+    rank_step<2>(k0, k1, r0, r1);
+    rank_step<3>(k0, k1, r0, r1);
+    rank_step<4>(k0, k1, r0, r1);
+    rank_step<5>(k0, k1, r0, r1);
+    rank_step<6>(k0, k1, r0, r1);
+    rank_step<7>(k0, k1, r0, r1);
+    rank_step<8>(k0, k1, r0, r1);
+    rank_step<9>(k0, k1, r0, r1);
+    rank_step<10>(k0, k1, r0, r1);
+    rank_step<11>(k0, k1, r0, r1);
+    rank_step<12>(k0, k1, r0, r1);
+    rank_step<13>(k0, k1, r0, r1);
+    rank_step<14>(k0, k1, r0, r1);
+    rank_step<15>(k0, k1, r0, r1);
+}
+
+// The K largest choices (score + bias, ties to the lower id) of the P tokens
+// of this lane's row; lane r < K of the row receives one pick and its score
+// (the picks in descending choice order).  Every choice is first evaluated in
+// float32 (within about 1e-6 + 1e-7 |c| of its float64 value, far inside the
+// margin below).  mu, the K-th largest of the 16 lanes' largest float32
+// choices, is at most the K-th largest float32 choice (K lanes hold one
+// >= mu), so every expert the float64 choice can pick has a float32 choice
+// >= mu - margin.  Those candidates (at most 32 per row) are compacted
+// through the wave's LDS scratch (16 bytes per slot: logit, id, bias; P x 4
+// rows x 32 slots), get their float64 choice key, and each candidate's rank
+// among its row's candidates (how many keys are larger) places the K best.
+// A wave with a live row of more than 32 candidates (or K > 32) runs K rounds
+// of row argmax over every expert's float64 choice instead, rereading the
+// logits through lg_of; both give the same bits.  Every lane of the wave must
+// call this.
+template <int EPL16, int P, typename LG>
+__device__ __forceinline__ void rows16_select(LG lg_of, const bool (&live)[P], int E, int K, int score,
+                                              const float* __restrict__ bias, lds_u8* scr, int (&my_e)[P],
+                                              double (&my_s)[P]) {
     const int lane = lane_id();
     const int j = lane & 15;
     const int row = lane >> 4;
-    bool ok[EPL16];
-    float bv[EPL16];
+    float bv[EPL16];  // the selection bias of this lane's experts (all tokens alike)
 #pragma unroll
-    for (int i = 0; i < EPL16; ++i) {
-        ok[i] = j + 16 * i < E;
-        bv[i] = (bias != nullptr && ok[i]) ? bias[j + 16 * i] : 0.0f;
-    }
-    uint32_t cm[P];  // candidate bits over i
+    for (int i = 0; i < EPL16; ++i) bv[i] = (bias != nullptr && j + 16 * i < E) ? bias[j + 16 * i] : 0.0f;
+    double lg[P][EPL16];
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+#pragma unroll
+        for (int i = 0; i < EPL16; ++i) lg[p][i] = j + 16 * i < E ? lg_of(p, j + 16 * i) : 0.0;
+
+    double m[P], z[P];
+    uint32_t cm[P];  // candidate slots of this lane, one bit per slot
     int off[P], n_row[P];
-    bool over = false;
+    bool over = K > 32;
 #pragma unroll
     for (int p = 0; p < P; ++p) {
         float c32[EPL16];
+        m[p] = 0.0;
+        z[p] = 1.0;
+        if (score == 0) {
+            // the softmax of row_softmax, from registers
+            double mx = -1.7976931348623157e308;
 #pragma unroll
-        for (int i = 0; i < EPL16; ++i) {
-            const float l = static_cast<float>(lg[p][i]);
-            float sc32;
-            if (score == 2) sc32 = sqrtf(fmaxf(l, 0.0f) + log1pf(__expf(-fabsf(l))));
-            else sc32 = __builtin_amdgcn_rcpf(1.0f + __expf(-l));
-            c32[i] = ok[i] ? sc32 + bv[i] : -INFINITY;
+            for (int i = 0; i < EPL16; ++i)
+                if (j + 16 * i < E) mx = fmax(mx, lg[p][i]);
+            m[p] = row_max_f64(mx);
+            double part = 0.0;
+#pragma unroll
+            for (int i = 0; i < EPL16; ++i) {
+                c32[i] = 0.0f;
+                if (j + 16 * i < E) {
+                    c32[i] = __expf(static_cast<float>(lg[p][i] - m[p]));
+                    part += static_cast<double>(c32[i]);
+                }
+            }
+            z[p] = row_sum_f64(part);
+            const float rz = static_cast<float>(1.0 / z[p]);
+#pragma unroll
+            for (int i = 0; i < EPL16; ++i) c32[i] = j + 16 * i < E ? c32[i] * rz + bv[i] : -INFINITY;
+        } else {
+#pragma unroll
+            for (int i = 0; i < EPL16; ++i) {
+                const float l = static_cast<float>(lg[p][i]);
+                float sc32;
+                if (score == 2) sc32 = sqrtf(fmaxf(l, 0.0f) + log1pf(__expf(-fabsf(l))));
+                else sc32 = __builtin_amdgcn_rcpf(1.0f + __expf(-l));
+                c32[i] = j + 16 * i < E ? sc32 + bv[i] : -INFINITY;
+            }
         }
-        float m[EPL16];
+        float v = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < EPL16; ++i) m[i] = c32[i];
-#pragma unroll
-        for (int w = EPL16 / 2; w >= 1; w /= 2)
-#pragma unroll
-            for (int i = 0; i < w; ++i) m[i] = fmaxf(m[i], m[i + w]);
-        float v = m[0], mu = -INFINITY;
+        for (int i = 0; i < EPL16; ++i) v = fmaxf(v, c32[i]);
+        float mu = -INFINITY;
         for (int r = 0; r < K; ++r) {
             mu = row_max_f32(v);
             v = v == mu ? -INFINITY : v;  // equal lane maxima go together: mu only gets smaller
@@ -543,183 +636,145 @@ __device__ __forceinline__ bool select_rows16_screened(const double (&lg)[P][EPL
         cm[p] = 0u;
 #pragma unroll
         for (int i = 0; i < EPL16; ++i)
-            if (ok[i] && c32[i] >= thr) cm[p] |= 1u << i;
+            if (live[p] && c32[i] >= thr) cm[p] |= 1u << i;
         const int nl = __builtin_popcount(cm[p]);
         const int incl = row_scan_i32(nl);
         off[p] = incl - nl;
         n_row[p] = row_max_i32(incl);
-        over = over || n_row[p] > 16;
-    }
-    if (__ballot(over) != 0) return false;
-
-    // compaction: candidate k of row r of pass p at slot (p, r, k)
-#pragma unroll
-    for (int p = 0; p < P; ++p) {
-        int k = off[p];
-#pragma unroll
-        for (int i = 0; i < EPL16; ++i) {
-            if ((cm[p] >> i) & 1u) {
-                lds_u8* sl = scr + ((p * 4 + row) * 16 + k) * 16;
-                *reinterpret_cast<__attribute__((address_space(3))) double*>(sl) = lg[p][i];
-                *reinterpret_cast<__attribute__((address_space(3))) int*>(sl + 8) = j + 16 * i;
-                *reinterpret_cast<__attribute__((address_space(3))) float*>(sl + 12) = bv[i];
-                ++k;
-            }
-        }
-    }
-    uint64_t key[P];
-    double sc[P];
-#pragma unroll
-    for (int p = 0; p < P; ++p) {
-        key[p] = 0ull;
-        sc[p] = 0.0;
-        if (j < n_row[p]) {
-            const lds_u8* sl = scr + ((p * 4 + row) * 16 + j) * 16;
-            const double l = *reinterpret_cast<const __attribute__((address_space(3))) double*>(sl);
-            const int e = *reinterpret_cast<const __attribute__((address_space(3))) int*>(sl + 8);
-            const float b = *reinterpret_cast<const __attribute__((address_space(3))) float*>(sl + 12);
-            sc[p] = elem_score(l, score);
-            double c = sc[p];
-            if (bias != nullptr) c += static_cast<double>(b);
-            key[p] = choice_key(c, e);
-        }
+        over = over || n_row[p] > 32;
     }
 
-    // K rounds of row argmax over the candidates; lane r keeps the r-th pick
-#pragma unroll
-    for (int p = 0; p < P; ++p) {
-        my_e[p] = -1;
-        my_s[p] = 0.0;
-    }
-    for (int r = 0; r < K; ++r) {
-        uint64_t win[P];
-#pragma unroll
-        for (int p = 0; p < P; ++p) win[p] = row_max_u64(key[p]);
+    if (__ballot(over) == 0ull) {
+        // candidate k of row r of token p at slot (p, r, k): logit, id, bias
 #pragma unroll
         for (int p = 0; p < P; ++p) {
-            const bool mine = key[p] == win[p];
-            const double sw = row_max_f64(mine ? sc[p] : -1.0);
-            if (mine) key[p] = 0ull;
-            if (j == r) {
-                my_e[p] = 1023 - static_cast<int>(win[p] & 0x3FFull);
-                my_s[p] = sw;
-            }
-        }
-    }
-    return true;
-}
-
-// P tokens per row of 16 lanes: token t[p] of this lane's row, whose float64
-// logits the row holds (EPL16 per lane: experts j, j + 16, ... for lane j of
-// the row).  The P tokens are independent and handled side by side, so their
-// dependent chains (row reductions, K argmax rounds) overlap.  Every lane of
-// the wave must call it (rows whose token does not exist pass live = false
-// and write nothing).  Same arithmetic as topk_token except the order of the
-// softmax sums across lanes.
-template <int EPL16, int P>
-__device__ __forceinline__ void select_rows16(const double (&lg)[P][EPL16], int E, int K, int score,
-                                              const float* __restrict__ bias, int (&my_e)[P], double (&my_s)[P]) {
-    const int lane = lane_id();
-    const int j = lane & 15;
-    bool ok[EPL16];
-#pragma unroll
-    for (int i = 0; i < EPL16; ++i) ok[i] = j + 16 * i < E;
-
-    double s[P][EPL16];
-    if (score == 0) {
-        double m[P];
-#pragma unroll
-        for (int p = 0; p < P; ++p) {
-            m[p] = -1.7976931348623157e308;
-#pragma unroll
-            for (int i = 0; i < EPL16; ++i)
-                if (ok[i]) m[p] = fmax(m[p], lg[p][i]);
-        }
-#pragma unroll
-        for (int p = 0; p < P; ++p) m[p] = row_max_f64(m[p]);
-        double part[P];
-#pragma unroll
-        for (int p = 0; p < P; ++p) {
-            part[p] = 0.0;
+            int k = off[p];
 #pragma unroll
             for (int i = 0; i < EPL16; ++i) {
-                s[p][i] = ok[i] ? exp(lg[p][i] - m[p]) : 0.0;
-                part[p] += s[p][i];
-            }
-        }
-#pragma unroll
-        for (int p = 0; p < P; ++p) {
-            const double z = row_sum_f64(part[p]);
-#pragma unroll
-            for (int i = 0; i < EPL16; ++i) s[p][i] = s[p][i] / z;
-        }
-    } else {
-#pragma unroll
-        for (int p = 0; p < P; ++p)
-#pragma unroll
-            for (int i = 0; i < EPL16; ++i) s[p][i] = ok[i] ? elem_score(lg[p][i], score) : 0.0;
-    }
-
-    uint64_t key[P][EPL16];
-#pragma unroll
-    for (int i = 0; i < EPL16; ++i) {
-        const int e = j + 16 * i;
-        const double b = (bias != nullptr && ok[i]) ? static_cast<double>(bias[e]) : 0.0;
-#pragma unroll
-        for (int p = 0; p < P; ++p) {
-            double c = s[p][i];
-            if (bias != nullptr && ok[i]) c += b;
-            key[p][i] = ok[i] ? choice_key(c, e) : 0ull;
-        }
-    }
-
-    // K rounds of row argmax; lane r of the row keeps the r-th pick
-#pragma unroll
-    for (int p = 0; p < P; ++p) {
-        my_e[p] = -1;
-        my_s[p] = 0.0;
-    }
-    for (int r = 0; r < K; ++r) {
-        uint64_t win[P];
-#pragma unroll
-        for (int p = 0; p < P; ++p) {
-            uint64_t m[EPL16];  // the lane's largest key, as a tree
-#pragma unroll
-            for (int i = 0; i < EPL16; ++i) m[i] = key[p][i];
-#pragma unroll
-            for (int w = EPL16 / 2; w >= 1; w /= 2)
-#pragma unroll
-                for (int i = 0; i < w; ++i) m[i] = umax64(m[i], m[i + w]);
-            win[p] = m[0];
-        }
-#pragma unroll
-        for (int p = 0; p < P; ++p) win[p] = row_max_u64(win[p]);
-        double sw[P];
-        int ew[P];
-#pragma unroll
-        for (int p = 0; p < P; ++p) {
-            ew[p] = 1023 - static_cast<int>(win[p] & 0x3FFull);
-            const int owner = ew[p] & 15;
-            const int slot = ew[p] >> 4;
-            sw[p] = -1.0;  // scores are >= 0: the row max picks the owner's value
-#pragma unroll
-            for (int i = 0; i < EPL16; ++i) {
-                if (j == owner && i == slot) {
-                    sw[p] = s[p][i];
-                    key[p][i] = 0ull;
+                if ((cm[p] >> i) & 1u) {
+                    const uint64_t lb = static_cast<uint64_t>(__double_as_longlong(lg[p][i]));
+                    const u32x4 rec = {static_cast<uint32_t>(lb), static_cast<uint32_t>(lb >> 32),
+                                       static_cast<uint32_t>(j + 16 * i), __float_as_uint(bv[i])};
+                    *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(scr + ((p * 4 + row) * 32 + k) * 16) =
+                        rec;
+                    ++k;
                 }
             }
         }
+        __builtin_amdgcn_wave_barrier();
+        uint64_t key[P][2];
+        double sc[P][2];
+        int ce[P][2];
+#pragma unroll
+        for (int p = 0; p < P; ++p)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                key[p][h] = 0ull;
+                sc[p][h] = 0.0;
+                ce[p][h] = 0;
+                const int slot = j + 16 * h;
+                if (slot < n_row[p]) {
+                    const u32x4 rec = *reinterpret_cast<lds_u32x4*>(scr + ((p * 4 + row) * 32 + slot) * 16);
+                    const double l =
+                        __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(rec[1]) << 32) | rec[0]));
+                    ce[p][h] = static_cast<int>(rec[2]);
+                    sc[p][h] = row_score(l, score, m[p], z[p]);
+                    const double c = sc[p][h] + static_cast<double>(__uint_as_float(rec[3]));
+                    key[p][h] = choice_key(c, ce[p][h]);
+                }
+            }
+        __builtin_amdgcn_wave_barrier();
+        // the K best of each row to slots 0 .. K-1 of its scratch (by rank)
 #pragma unroll
         for (int p = 0; p < P; ++p) {
-            sw[p] = row_max_f64(sw[p]);
-            if (j == r) {
-                my_e[p] = ew[p];
-                my_s[p] = sw[p];
+            int r0, r1;
+            row_ranks(key[p][0], key[p][1], r0, r1);
+            const int rk[2] = {r0, r1};
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                if (j + 16 * h < n_row[p] && rk[h] < K) {
+                    const uint64_t sb = static_cast<uint64_t>(__double_as_longlong(sc[p][h]));
+                    const u32x4 rec = {static_cast<uint32_t>(sb), static_cast<uint32_t>(sb >> 32),
+                                       static_cast<uint32_t>(ce[p][h]), 0u};
+                    *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(scr + ((p * 4 + row) * 32 + rk[h]) *
+                                                                                        16) = rec;
+                }
             }
         }
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            my_e[p] = -1;
+            my_s[p] = 0.0;
+            if (j < K && live[p]) {
+                const u32x4 rec = *reinterpret_cast<lds_u32x4*>(scr + ((p * 4 + row) * 32 + j) * 16);
+                my_s[p] = __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(rec[1]) << 32) | rec[0]));
+                my_e[p] = static_cast<int>(rec[2]);
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+        return;
     }
 
+    // round r picks the largest key below the previous pick's (keys are
+    // distinct: their low bits hold the id)
+    auto key_of = [&](int p, int e) {
+        const double c = row_score(lg_of(p, e), score, m[p], z[p]) +
+                         (bias != nullptr ? static_cast<double>(bias[e]) : 0.0);
+        return choice_key(c, e);
+    };
+#pragma unroll 1
+    for (int p = 0; p < P; ++p) {
+        my_e[p] = -1;
+        uint64_t prev = ~0ull;
+        for (int r = 0; r < K; ++r) {
+            uint64_t best = 0ull;
+#pragma unroll 1
+            for (int i = 0; i < EPL16; ++i) {
+                if (j + 16 * i < E) {
+                    const uint64_t k = key_of(p, j + 16 * i);
+                    if (k < prev) best = umax64(best, k);
+                }
+            }
+            prev = row_max_u64(best);
+            if (j == r) my_e[p] = 1023 - static_cast<int>(prev & 0x3FFull);
+        }
+        // rows past the batch pick nothing meaningful and read expert 0
+        const int e = (live[p] && my_e[p] >= 0 && my_e[p] < E) ? my_e[p] : 0;
+        my_s[p] = j < K ? row_score(lg_of(p, e), score, m[p], z[p]) : 0.0;
+    }
+}
+
+// Replay: lane j < K of the row takes the given id given[t * K + j]; a token
+// whose K given ids are not distinct ids in [0, E) is dropped (kept false).
+// The scores are those of rows16_select.  Every lane of the wave must call
+// this.
+template <int EPL16, int P, typename LG>
+__device__ __forceinline__ void rows16_given(LG lg_of, const int64_t (&t)[P], const bool (&live)[P], int E, int K,
+                                             int score, const int32_t* __restrict__ given, bool (&kept)[P],
+                                             int (&my_e)[P], double (&my_s)[P]) {
+    const int lane = lane_id();
+    const int j = lane & 15;
+    const int rbase = lane & 48;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        double m = 0.0, z = 1.0;
+        if (score == 0) row_softmax<EPL16>(lg_of, p, E, m, z);
+        const bool mine = live[p] && j < K;
+        const int g = mine ? given[t[p] * K + j] : 0;
+        bool bad = mine && (g < 0 || g >= E);
+        for (int i = 0; i < K; ++i) {
+            const int gi = lane_get(g, rbase + i);
+            bad = bad || (mine && i != j && gi == g);
+        }
+        kept[p] = kept[p] && ((__ballot(bad) >> rbase) & 0xFFFFull) == 0ull;
+        my_e[p] = -1;
+        my_s[p] = 0.0;
+        if (kept[p] && j < K) {
+            my_e[p] = g;
+            my_s[p] = row_score(lg_of(p, g), score, m, z);
+        }
+    }
 }
 
 template <int EPL>
@@ -773,6 +828,73 @@ __global__ __launch_bounds__(256) void topk_permute_kernel(
     permute_one_block(ids_out, T * K, K, E, ppb, id_bits, counts, offsets, perm_token, inv_pos);
 }
 
+// scratch of rows16_select per wave: 4 rows x 32 slots x 16 bytes, for each
+// of the P tokens per row
+constexpr int kRowScr = 4 * 32 * 16;
+
+// The top-k of 16 tokens per 256-thread workgroup, one per row of sixteen
+// lanes (layers without group-limited select, E <= 512).
+template <int EPL16>
+__global__ __launch_bounds__(256) void topk_rows16_kernel(
+    const double* __restrict__ logits, int64_t T, int E, int K, int score, int renorm, double route_scale,
+    const float* __restrict__ bias, const uint8_t* __restrict__ mask, float* __restrict__ logits_out,
+    int32_t* __restrict__ ids_out, float* __restrict__ w_out, const int32_t* __restrict__ given) {
+    __shared__ __attribute__((aligned(16))) uint8_t scr_raw[4 * kRowScr];
+    const int j = lane_id() & 15;
+    const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+    int64_t t[1];
+    bool live[1], kept[1];
+    t[0] = static_cast<int64_t>(blockIdx.x) * 16 + (threadIdx.x >> 4);
+    live[0] = t[0] < T;
+    // rows past T read token T-1 (their picks are not written)
+    const double* row_lg = logits + (live[0] ? t[0] : T - 1) * E;
+    auto lg_of = [&](int, int e) { return row_lg[e]; };
+    if (logits_out && live[0])
+        for (int e = j; e < E; e += 16) logits_out[t[0] * E + e] = static_cast<float>(row_lg[e]);
+    kept[0] = live[0] && ((mask == nullptr) || (mask[t[0]] != 0));
+    int my_e[1];
+    double my_s[1];
+    if (given != nullptr)
+        rows16_given<EPL16, 1>(lg_of, t, live, E, K, score, given, kept, my_e, my_s);
+    else
+        rows16_select<EPL16, 1>(lg_of, live, E, K, score, bias, (lds_u8*)(scr_raw) + wv * kRowScr, my_e, my_s);
+    write_picks16<1>(my_e, my_s, t, live, kept, K, renorm, route_scale, ids_out, w_out);
+}
+
+// topk_permute_kernel for layers whose top-k runs in rows of sixteen lanes:
+// 16 tokens per pass, then the permutation of every pair.
+template <int EPL16>
+__global__ __launch_bounds__(256) void topk_permute_rows16_kernel(
+    const double* __restrict__ logits, int64_t T, int E, int K, int score, int renorm, double route_scale,
+    const float* __restrict__ bias, const uint8_t* __restrict__ mask, float* __restrict__ logits_out,
+    int32_t* __restrict__ ids_out, float* __restrict__ w_out, const int32_t* __restrict__ given, int ppb,
+    int id_bits, int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm_token,
+    int32_t* __restrict__ inv_pos) {
+    __shared__ __attribute__((aligned(16))) uint8_t scr_raw[4 * kRowScr];
+    const int j = lane_id() & 15;
+    const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+    for (int64_t tb = 0; tb < T; tb += 16) {
+        int64_t t[1];
+        bool live[1], kept[1];
+        t[0] = tb + (threadIdx.x >> 4);
+        live[0] = t[0] < T;
+        const double* row_lg = logits + (live[0] ? t[0] : T - 1) * E;
+        auto lg_of = [&](int, int e) { return row_lg[e]; };
+        if (logits_out && live[0])
+            for (int e = j; e < E; e += 16) logits_out[t[0] * E + e] = static_cast<float>(row_lg[e]);
+        kept[0] = live[0] && ((mask == nullptr) || (mask[t[0]] != 0));
+        int my_e[1];
+        double my_s[1];
+        if (given != nullptr)
+            rows16_given<EPL16, 1>(lg_of, t, live, E, K, score, given, kept, my_e, my_s);
+        else
+            rows16_select<EPL16, 1>(lg_of, live, E, K, score, bias, (lds_u8*)(scr_raw) + wv * kRowScr, my_e, my_s);
+        write_picks16<1>(my_e, my_s, t, live, kept, K, renorm, route_scale, ids_out, w_out);
+    }
+    __syncthreads();  // every token's ids written and visible to the workgroup
+    permute_one_block(ids_out, T * K, K, E, ppb, id_bits, counts, offsets, perm_token, inv_pos);
+}
+
 // ---------------------------------------------------------------------------
 // fused routing, bf16 operands: logits of TB tokens x all experts in one
 // workgroup, kept in LDS as float64, then top-k per token from LDS.
@@ -802,7 +924,7 @@ struct RouteTile {
     static constexpr int TBP_MAX = EMAX > 256 ? 32 : 64;
     static constexpr int TBP = TB < TBP_MAX ? TB : TBP_MAX;  // tokens whose logits are in LDS at a time
     static constexpr int LOGB = TBP * EMAX * 8; // float64 logits of one pass
-    static constexpr int SCRB = 4 * 2 * 64 * 16;  // top-k candidate slots: 4 waves x 2 passes x 64
+    static constexpr int SCRB = 4 * 2 * 4 * 32 * 16;  // top-k candidate slots: 4 waves x 2 tokens x 4 rows x 32
     static constexpr int SMEM = RING > LOGB + SCRB ? RING : LOGB + SCRB;
     static constexpr int XPER = TB / 32;       // 8-row DMA instructions per wave per chunk
     static constexpr int WPER = EMAX / 32;
@@ -821,51 +943,30 @@ __device__ __forceinline__ void route_topk_pass(const __attribute__((address_spa
     const int lane = lane_id();
     const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
     const int64_t t0 = tp;
-    if constexpr (RT::EMAX <= 256) {
-        // P tokens per row of sixteen lanes at a time
-        constexpr int EPL16 = RT::EMAX / 16;
-        // two tokens per row where registers allow; the 128-token tile holds
-        // the other pass's logits in registers meanwhile
-        constexpr int P = RT::TB > RT::TBP ? 1 : 2;
-        static_assert(RT::TBP % (16 * P) == 0, "tokens per wave pass");
-        for (int tb = 4 * P * wv; tb < RT::TBP; tb += 16 * P) {
-            double lg[P][EPL16];
-            int64_t t[P];
-            bool live[P], kept[P];
+    // P tokens per row of sixteen lanes at a time: two where registers allow
+    // (the 128-token tile holds the other pass's logits in registers meanwhile)
+    constexpr int EPL16 = RT::EMAX / 16;
+    constexpr int P = (RT::TB > RT::TBP || EPL16 > 16) ? 1 : 2;
+    static_assert(RT::TBP % (16 * P) == 0, "tokens per wave pass");
+    for (int tb = 4 * P * wv; tb < RT::TBP; tb += 16 * P) {
+        int64_t t[P];
+        int tl[P];
+        bool live[P], kept[P];
 #pragma unroll
-            for (int p = 0; p < P; ++p) {
-                const int tl = tb + 4 * p + (lane >> 4);
-                t[p] = t0 + tl;
-                live[p] = t[p] < T;
-#pragma unroll
-                for (int i = 0; i < EPL16; ++i) {
-                    const int e = (lane & 15) + 16 * i;
-                    lg[p][i] = lgs[tl * RT::EMAX + e];
-                    if (logits_out && live[p] && e < E) logits_out[t[p] * E + e] = static_cast<float>(lg[p][i]);
-                }
-                kept[p] = live[p] && ((mask == nullptr) || (mask[t[p]] != 0));
-            }
-            lds_u8* scr = scr_base + wv * (P * 64 * 16);
-            int my_e[P];
-            double my_s[P];
-            if (score == 0 || !select_rows16_screened<EPL16, P>(lg, E, K, score, bias, scr, my_e, my_s))
-                select_rows16<EPL16, P>(lg, E, K, score, bias, my_e, my_s);
-            write_picks16<P>(my_e, my_s, t, live, kept, K, renorm, route_scale, ids_out, w_out);
+        for (int p = 0; p < P; ++p) {
+            tl[p] = tb + 4 * p + (lane >> 4);
+            t[p] = t0 + tl[p];
+            live[p] = t[p] < T;
+            if (logits_out && live[p])
+                for (int e = lane & 15; e < E; e += 16)
+                    logits_out[t[p] * E + e] = static_cast<float>(lgs[tl[p] * RT::EMAX + e]);
+            kept[p] = live[p] && ((mask == nullptr) || (mask[t[p]] != 0));
         }
-    } else {
-        for (int tl = wv; tl < RT::TBP; tl += 4) {
-            const int64_t t = t0 + tl;
-            if (t >= T) break;  // uniform per wave
-            double lg[RT::EPL];
-#pragma unroll
-            for (int i = 0; i < RT::EPL; ++i) {
-                const int e = lane + 64 * i;
-                lg[i] = lgs[tl * RT::EMAX + e];
-                if (logits_out && e < E) logits_out[t * E + e] = static_cast<float>(lg[i]);
-            }
-            const bool kept = (mask == nullptr) || (mask[t] != 0);
-            topk_token<RT::EPL>(lg, t, E, K, score, renorm, route_scale, bias, kept, ids_out, w_out, nullptr, 1, 1);
-        }
+        auto lg_of = [&](int p, int e) { return lgs[tl[p] * RT::EMAX + e]; };
+        int my_e[P];
+        double my_s[P];
+        rows16_select<EPL16, P>(lg_of, live, E, K, score, bias, scr_base + wv * (P * kRowScr), my_e, my_s);
+        write_picks16<P>(my_e, my_s, t, live, kept, K, renorm, route_scale, ids_out, w_out);
     }
 }
 
@@ -1120,11 +1221,27 @@ hipError_t launch_router_logits(const void* x, const void* router, int64_t T, in
     return hipGetLastError();
 }
 
+// whether a layer's top-k runs in rows of sixteen lanes (rows16_select and
+// rows16_given) on every path, or one token per wave (topk_token) on every path
+static bool topk_rows16(int E, int n_group) { return E <= 512 && n_group <= 1; }
+
 hipError_t launch_topk(const double* logits64, int64_t T, int E, int K, int score, int renorm,
                        float route_scale, int n_group, int topk_group, const float* bias, const uint8_t* mask,
                        float* logits_out, int32_t* ids, float* w, hipStream_t stream, const int32_t* given) {
-    const unsigned grid = static_cast<unsigned>((T + 3) / 4);
     const double rs = static_cast<double>(route_scale);
+    if (topk_rows16(E, n_group)) {
+        const unsigned grid = static_cast<unsigned>((T + 15) / 16);
+#define MOE_TOPK16(EPL16)                                                                                    \
+    topk_rows16_kernel<EPL16><<<grid, 256, 0, stream>>>(logits64, T, E, K, score, renorm, rs, bias, mask, \
+                                                         logits_out, ids, w, given)
+        if (E <= 64) MOE_TOPK16(4);
+        else if (E <= 128) MOE_TOPK16(8);
+        else if (E <= 256) MOE_TOPK16(16);
+        else MOE_TOPK16(32);
+#undef MOE_TOPK16
+        return hipGetLastError();
+    }
+    const unsigned grid = static_cast<unsigned>((T + 3) / 4);
 #define MOE_TOPK(EPL)                                                                                   \
     topk_kernel<EPL><<<grid, 256, 0, stream>>>(logits64, T, E, K, score, renorm, rs, bias, mask, \
                                                 logits_out, ids, w, given, n_group, topk_group)
@@ -1148,6 +1265,18 @@ hipError_t launch_route_permute(const void* x, const void* router, int64_t T, in
     if (err != hipSuccess) return err;
     const PermutePlan pl = permute_plan(T * K, E);  // one block: T * K <= 8 * 16 pairs
     const double rs = static_cast<double>(route_scale);
+    if (topk_rows16(E, n_group)) {
+#define MOE_TOPK16_PERMUTE(EPL16)                                                                              \
+    topk_permute_rows16_kernel<EPL16><<<1, 256, 0, stream>>>(logits64, T, E, K, score, renorm, rs, bias, mask,  \
+                                                             logits_out, ids, w, given, pl.pairs_per_block,   \
+                                                             pl.id_bits, counts, offsets, perm_token, inv_pos)
+        if (E <= 64) MOE_TOPK16_PERMUTE(4);
+        else if (E <= 128) MOE_TOPK16_PERMUTE(8);
+        else if (E <= 256) MOE_TOPK16_PERMUTE(16);
+        else MOE_TOPK16_PERMUTE(32);
+#undef MOE_TOPK16_PERMUTE
+        return hipGetLastError();
+    }
 #define MOE_TOPK_PERMUTE(EPL)                                                                               \
     topk_permute_kernel<EPL><<<1, 256, 0, stream>>>(logits64, T, E, K, score, renorm, rs, bias, mask,      \
                                                     logits_out, ids, w, given, n_group, topk_group,         \
@@ -1199,12 +1328,15 @@ hipError_t launch_route(const void* x, const void* router, int64_t T, int D, int
 }
 
 hipError_t launch_route_replay(const void* x, const void* router, int64_t T, int D, int E, int K, int dtype,
-                               int score, int renorm, float route_scale, const int32_t* given,
+                               int score, int renorm, float route_scale, int n_group, const int32_t* given,
                                const uint8_t* mask, double* logits64, float* logits_out, int32_t* ids, float* w,
                                hipStream_t stream) {
     hipError_t err = launch_router_logits(x, router, T, D, E, dtype, logits64, stream);
     if (err != hipSuccess) return err;
-    return launch_topk(logits64, T, E, K, score, renorm, route_scale, 1, 1, nullptr, mask, logits_out, ids, w,
+    // n_group only picks the top-k code the layer's forward runs (so a
+    // replayed token gets the forward's weight bits); given ids skip the
+    // group-limited select itself
+    return launch_topk(logits64, T, E, K, score, renorm, route_scale, n_group, 1, nullptr, mask, logits_out, ids, w,
                        stream, given);
 }
 
