@@ -292,9 +292,18 @@ def main():
     torch.cuda.synchronize()
 
     # ---- CPU oracle on a bounded sample of the same workload ---------------
+    # (timed, then compared with this run's GPU routing and output for the
+    # same tokens: the parity fields of the line)
     cpu = None
+    parity = None
     if args.cpu_sample > 0:
-        cpu = cpu_baseline(cfg, inp, min(args.cpu_sample, T))
+        n = min(args.cpu_sample, T)
+        fwd = layer.forward(x[:n].contiguous(), trace=True)
+        torch.cuda.synchronize()
+        g_out, g_tr = fwd
+        gpu = {"ids": g_tr["topk_ids"].cpu().numpy(), "w": g_tr["topk_w"].cpu().numpy(),
+               "out": g_out.view(torch.int16).cpu().numpy().view(np.uint16)}
+        cpu, parity = cpu_baseline(cfg, inp, n, gpu)
 
     line = {
         "metric": METRIC,
@@ -337,6 +346,9 @@ def main():
         "batch_invariant_prefix_check": invariant,
         "routed_pairs": P,
         "expert_load_max_over_mean": float(counts.max() / max(1e-9, counts.mean())),
+        "expert_load": {"counts": [int(c) for c in counts], "min": int(counts.min()), "max": int(counts.max()),
+                        "mean": float(counts.mean()), "empty_experts": int((counts == 0).sum())},
+        "parity": parity,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
@@ -547,8 +559,16 @@ def bench_backward(args, cfg, inp, layer, shape, x):
     }), flush=True)
 
 
-def cpu_baseline(cfg, inp, n):
-    """The oracle, as it stands, on the first n tokens of the same layer."""
+def cpu_baseline(cfg, inp, n, gpu):
+    """The oracle, as it stands, on the first n tokens of the same layer.
+
+    Returns the timing record and the parity of this run's GPU results for
+    those tokens (gpu: their ids, weights and bf16 output bits from
+    moe_forward on the same n tokens) against the oracle's: routing ids
+    bit-exact except near ties (RL-Kernel roadmap, Problem 1: any mismatch
+    reported), weights, and the layer output against the unrounded float64
+    oracle in units of its RMS.
+    """
     import numpy as np
 
     import oracle
@@ -558,10 +578,10 @@ def cpu_baseline(cfg, inp, n):
     cores = len(os.sched_getaffinity(0))
     log(f"cpu oracle on {n} tokens ({threads} BLAS threads, {cores} cores in affinity)")
     t0 = time.perf_counter()
-    oracle.forward(inp.x[:n], inp.w_router, inp.w_gate_up, inp.w_down, K=cfg.K, score=cfg.score,
-                   renorm=cfg.renorm, route_scale=cfg.route_scale, bias=inp.bias,
-                   shared_gate_up=inp.w_gate_up_s, shared_down=inp.w_down_s, bf16_mode=(cfg.dtype == "bf16"),
-                   n_group=cfg.n_group, topk_group=cfg.topk_group)
+    ref = oracle.forward(inp.x[:n], inp.w_router, inp.w_gate_up, inp.w_down, K=cfg.K, score=cfg.score,
+                         renorm=cfg.renorm, route_scale=cfg.route_scale, bias=inp.bias,
+                         shared_gate_up=inp.w_gate_up_s, shared_down=inp.w_down_s, bf16_mode=(cfg.dtype == "bf16"),
+                         n_group=cfg.n_group, topk_group=cfg.topk_group)
     dt = time.perf_counter() - t0
     model = ""
     try:
@@ -572,7 +592,7 @@ def cpu_baseline(cfg, inp, n):
                     break
     except OSError:
         pass
-    return {
+    timing = {
         "value": n / dt,
         "unit": "tokens/s",
         "cores": threads,
@@ -580,6 +600,28 @@ def cpu_baseline(cfg, inp, n):
         "sample": f"first {n} tokens of the same {cfg.name}-like layer (all experts' weights), "
                   f"fp64 numpy oracle, {dt:.1f} s, {model}",
     }
+
+    same = np.all(gpu["ids"] == ref.ids, axis=1)
+    ok_w = np.abs(gpu["w"][same].astype(np.float64) - ref.weights[same]) <= 2e-6 * np.abs(ref.weights[same]) + 1e-7
+    out32 = (gpu["out"].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    cmp = same  # tokens routed alike: their outputs are comparable with the oracle's
+    diff = np.abs(out32[cmp] - ref.out[cmp])
+    rms = float(np.sqrt(np.mean(ref.out[cmp] ** 2))) if cmp.any() else 0.0
+    rel = diff / rms if rms > 0 else diff
+    parity = {
+        "token_count": int(n),
+        "mismatch_count": int((~same & ~ref.exempt).sum()),
+        "exempt_count": int(ref.exempt.sum()),
+        "exempt_differing": int((~same & ref.exempt).sum()),
+        "weights_outside_rtol_2e-6": int((~ok_w).sum()),
+        "output_compared_tokens": int(cmp.sum()),
+        "output_rms": rms,
+        "max_abs_diff": float(diff.max()) if diff.size else 0.0,
+        "max_rel_rms": float(rel.max()) if rel.size else 0.0,
+        "p99_rel_rms": float(np.percentile(rel, 99)) if rel.size else 0.0,
+        "reference": "oracle float64 layer output, unrounded; GPU value = the delivered bf16 output",
+    }
+    return timing, parity
 
 
 if __name__ == "__main__":

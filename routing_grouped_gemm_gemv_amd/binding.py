@@ -18,7 +18,9 @@ from typing import Optional
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libmoe.so")
+# MOE_LIB names another build of the same library (the sanitized host-only
+# build the CPU tests load); by default the in-tree libmoe.so
+LIB_PATH = os.environ.get("MOE_LIB") or os.path.join(_PKG, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_BF16, MOE_F32 = 0, 1
