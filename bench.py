@@ -608,6 +608,16 @@ def cpu_baseline(cfg, inp, n, gpu):
     diff = np.abs(out32[cmp] - ref.out[cmp])
     rms = float(np.sqrt(np.mean(ref.out[cmp] ** 2))) if cmp.any() else 0.0
     rel = diff / rms if rms > 0 else diff
+    # elements over 2e-2 RMS, and whether the final rounding accounts for
+    # each: within one bf16 ulp of the float64 reference rounded once to bf16
+    r64 = ref.out[cmp]
+    r32 = r64.astype(np.float32)
+    ru = r32.view(np.uint32)
+    rne = (((ru + 0x7FFF + ((ru >> 16) & 1)) >> 16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    _, ex = np.frexp(rne)
+    ulp = np.ldexp(1.0, np.where(rne == 0, -133, ex - 8))
+    over = rel > 2e-2
+    dist_ulp = np.abs(out32[cmp] - rne) / ulp
     parity = {
         "token_count": int(n),
         "mismatch_count": int((~same & ~ref.exempt).sum()),
@@ -619,6 +629,9 @@ def cpu_baseline(cfg, inp, n, gpu):
         "max_abs_diff": float(diff.max()) if diff.size else 0.0,
         "max_rel_rms": float(rel.max()) if rel.size else 0.0,
         "p99_rel_rms": float(np.percentile(rel, 99)) if rel.size else 0.0,
+        "over_2e-2_rms_count": int(over.sum()),
+        "over_2e-2_rms_max_ulp_from_rne_bf16_of_ref": float(dist_ulp[over].max()) if over.any() else 0.0,
+        "share_within_1ulp_of_rne_bf16_of_ref": float(np.mean(dist_ulp <= 1.0)) if dist_ulp.size else 1.0,
         "reference": "oracle float64 layer output, unrounded; GPU value = the delivered bf16 output",
     }
     return timing, parity

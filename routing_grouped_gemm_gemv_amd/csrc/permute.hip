@@ -165,10 +165,18 @@ __global__ __launch_bounds__(256) void permute_scatter_kernel(
 
 // All three passes in one workgroup when every pair fits one block (the
 // block's base rows are zero), for decode-sized batches: one launch instead
-// of three, the same rows.
+// of three, the same rows.  Up to 256 pairs the ids go to LDS once and
+// permute_small places them.
 __global__ __launch_bounds__(256) void permute_single_kernel(
     const int32_t* __restrict__ ids, int64_t P, int K, int E, int ppb, int id_bits, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ perm_token, int32_t* __restrict__ inv_pos) {
+    if (P <= kSmallPairs) {  // uniform
+        __shared__ int pairs[kSmallPairs];
+        if (threadIdx.x < P) pairs[threadIdx.x] = ids[threadIdx.x];
+        __syncthreads();
+        permute_small(pairs, static_cast<int>(P), K, E, counts, offsets, perm_token, inv_pos);
+        return;
+    }
     permute_one_block(ids, P, K, E, ppb, id_bits, counts, offsets, perm_token, inv_pos);
 }
 

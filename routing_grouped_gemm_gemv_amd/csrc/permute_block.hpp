@@ -151,4 +151,76 @@ __device__ __forceinline__ void permute_one_block(const int32_t* __restrict__ id
     wave_scatter(ids, P, K, E, w_begin, w_end, id_bits, hist[wv], perm_token, inv_pos);
 }
 
+// The permutation of at most 256 pairs in one 256-thread workgroup, thread p
+// taking pair p, from ids already in LDS (pairs[0 .. P)): each thread walks
+// every pair once, counting those of its expert and those of its expert
+// before it; the first pair of each expert stores the count; a block scan of
+// the counts (four consecutive experts per thread) gives the offsets, and a
+// pair's row is its expert's offset plus the pairs of that expert before it
+// (token order within an expert, as in the multi-block path).  No atomics.
+// Every thread of the workgroup must call this.
+constexpr int kSmallPairs = 256;
+
+__device__ __forceinline__ void permute_small(const int* pairs, int P, int K, int E, int32_t* __restrict__ counts,
+                                              int32_t* __restrict__ offsets, int32_t* __restrict__ perm_token,
+                                              int32_t* __restrict__ inv_pos) {
+    __shared__ int cnt[kMaxExperts];
+    __shared__ int wsum[kPermWaves];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wv = tid >> 6;
+    for (int e = tid; e < E; e += 256) cnt[e] = 0;
+    const int ep = tid < P ? pairs[tid] : -1;
+    const bool valid = ep >= 0 && ep < E;
+    int before = 0, same = 0;
+    for (int q = 0; q < P; ++q) {
+        const int eq = pairs[q];
+        before += (eq == ep && q < tid) ? 1 : 0;
+        same += eq == ep ? 1 : 0;
+    }
+    __syncthreads();  // cnt zeroed
+    if (valid && before == 0) cnt[ep] = same;
+    __syncthreads();
+    int c[4];
+    int local = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int e = 4 * tid + j;
+        c[j] = e < E ? cnt[e] : 0;
+        local += c[j];
+    }
+    int incl = local;  // inclusive scan over the wave
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int v = __shfl_up(incl, d);
+        if (lane >= d) incl += v;
+    }
+    if (lane == 63) wsum[wv] = incl;
+    __syncthreads();
+    int run = incl - local;
+    for (int w = 0; w < wv; ++w) run += wsum[w];
+    __syncthreads();  // every count read before the offsets replace them
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int e = 4 * tid + j;
+        if (e < E) {
+            counts[e] = c[j];
+            offsets[e] = run;
+            cnt[e] = run;
+        }
+        run += c[j];
+    }
+    if (tid == 255) offsets[E] = run;
+    __syncthreads();
+    if (tid < P) {
+        if (valid) {
+            const int pos = cnt[ep] + before;
+            perm_token[pos] = tid / K;
+            inv_pos[tid] = pos;
+        } else {
+            inv_pos[tid] = -1;
+        }
+    }
+}
+
 }  // namespace moe

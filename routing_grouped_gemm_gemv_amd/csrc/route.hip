@@ -450,11 +450,12 @@ __device__ __forceinline__ int row_max_i32(int v) {
 
 // The picks of P rows (lane r of a row holds its r-th pick: my_e, my_s) in
 // ascending id order with their weights, to ids_out / w_out.
+// ids_lds, if given, receives the ids too (at the same index as ids_out).
 template <int P>
 __device__ __forceinline__ void write_picks16(const int (&my_e)[P], const double (&my_s)[P], const int64_t (&t)[P],
                                               const bool (&live)[P], const bool (&kept)[P], int K, int renorm,
                                               double route_scale, int32_t* __restrict__ ids_out,
-                                              float* __restrict__ w_out) {
+                                              float* __restrict__ w_out, int* ids_lds = nullptr) {
     const int lane = lane_id();
     const int j = lane & 15;
     const int rbase = lane & 48;
@@ -480,9 +481,11 @@ __device__ __forceinline__ void write_picks16(const int (&my_e)[P], const double
                 const double wv = renorm ? (my_s[p] / den) * route_scale : my_s[p] * route_scale;
                 ids_out[t[p] * K + rank] = my_e[p];
                 w_out[t[p] * K + rank] = static_cast<float>(wv);
+                if (ids_lds != nullptr) ids_lds[t[p] * K + rank] = my_e[p];
             } else {
                 ids_out[t[p] * K + j] = -1;
                 w_out[t[p] * K + j] = 0.f;
+                if (ids_lds != nullptr) ids_lds[t[p] * K + j] = -1;
             }
         }
     }
@@ -802,13 +805,13 @@ __global__ __launch_bounds__(256) void topk_kernel(
 // dispatch permutation in one workgroup, one launch instead of two.  Wave w
 // takes tokens w, w + 4, ... and picks exactly as topk_kernel does; the
 // barrier makes the ids visible to the workgroup, and the permutation
-// follows as permute_single_kernel computes it.
+// follows from LDS (permute_small, the rows of the multi-block path).
 template <int EPL>
 __global__ __launch_bounds__(256) void topk_permute_kernel(
     const double* __restrict__ logits, int64_t T, int E, int K, int score, int renorm, double route_scale,
     const float* __restrict__ bias, const uint8_t* __restrict__ mask, float* __restrict__ logits_out,
     int32_t* __restrict__ ids_out, float* __restrict__ w_out, const int32_t* __restrict__ given, int n_group,
-    int topk_group, int ppb, int id_bits, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int topk_group, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ perm_token, int32_t* __restrict__ inv_pos) {
     const int lane = lane_id();
     const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
@@ -825,7 +828,10 @@ __global__ __launch_bounds__(256) void topk_permute_kernel(
                         topk_group);
     }
     __syncthreads();  // every token's ids written and visible to the workgroup
-    permute_one_block(ids_out, T * K, K, E, ppb, id_bits, counts, offsets, perm_token, inv_pos);
+    __shared__ int pairs[kSmallPairs];  // T * K <= 8 * 16 pairs
+    if (threadIdx.x < T * K) pairs[threadIdx.x] = ids_out[threadIdx.x];
+    __syncthreads();
+    permute_small(pairs, static_cast<int>(T * K), K, E, counts, offsets, perm_token, inv_pos);
 }
 
 // scratch of rows16_select per wave: 4 rows x 32 slots x 16 bytes, for each
@@ -862,15 +868,17 @@ __global__ __launch_bounds__(256) void topk_rows16_kernel(
 }
 
 // topk_permute_kernel for layers whose top-k runs in rows of sixteen lanes:
-// 16 tokens per pass, then the permutation of every pair.
+// 16 tokens per pass, the picks kept in LDS as well, then the permutation of
+// every pair from there (T * K <= 8 * 16 pairs: permute_small).
 template <int EPL16>
 __global__ __launch_bounds__(256) void topk_permute_rows16_kernel(
     const double* __restrict__ logits, int64_t T, int E, int K, int score, int renorm, double route_scale,
     const float* __restrict__ bias, const uint8_t* __restrict__ mask, float* __restrict__ logits_out,
-    int32_t* __restrict__ ids_out, float* __restrict__ w_out, const int32_t* __restrict__ given, int ppb,
-    int id_bits, int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm_token,
+    int32_t* __restrict__ ids_out, float* __restrict__ w_out, const int32_t* __restrict__ given,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm_token,
     int32_t* __restrict__ inv_pos) {
     __shared__ __attribute__((aligned(16))) uint8_t scr_raw[4 * kRowScr];
+    __shared__ int pairs[kSmallPairs];
     const int j = lane_id() & 15;
     const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
     for (int64_t tb = 0; tb < T; tb += 16) {
@@ -889,10 +897,10 @@ __global__ __launch_bounds__(256) void topk_permute_rows16_kernel(
             rows16_given<EPL16, 1>(lg_of, t, live, E, K, score, given, kept, my_e, my_s);
         else
             rows16_select<EPL16, 1>(lg_of, live, E, K, score, bias, (lds_u8*)(scr_raw) + wv * kRowScr, my_e, my_s);
-        write_picks16<1>(my_e, my_s, t, live, kept, K, renorm, route_scale, ids_out, w_out);
+        write_picks16<1>(my_e, my_s, t, live, kept, K, renorm, route_scale, ids_out, w_out, pairs);
     }
-    __syncthreads();  // every token's ids written and visible to the workgroup
-    permute_one_block(ids_out, T * K, K, E, ppb, id_bits, counts, offsets, perm_token, inv_pos);
+    __syncthreads();  // every pick in LDS
+    permute_small(pairs, static_cast<int>(T * K), K, E, counts, offsets, perm_token, inv_pos);
 }
 
 // ---------------------------------------------------------------------------
@@ -1263,13 +1271,12 @@ hipError_t launch_route_permute(const void* x, const void* router, int64_t T, in
                                 int32_t* perm_token, int32_t* inv_pos, hipStream_t stream) {
     hipError_t err = launch_router_logits(x, router, T, D, E, dtype, logits64, stream);
     if (err != hipSuccess) return err;
-    const PermutePlan pl = permute_plan(T * K, E);  // one block: T * K <= 8 * 16 pairs
-    const double rs = static_cast<double>(route_scale);
+    const double rs = static_cast<double>(route_scale);  // one workgroup: T * K <= 8 * 16 pairs
     if (topk_rows16(E, n_group)) {
 #define MOE_TOPK16_PERMUTE(EPL16)                                                                              \
     topk_permute_rows16_kernel<EPL16><<<1, 256, 0, stream>>>(logits64, T, E, K, score, renorm, rs, bias, mask,  \
-                                                             logits_out, ids, w, given, pl.pairs_per_block,   \
-                                                             pl.id_bits, counts, offsets, perm_token, inv_pos)
+                                                             logits_out, ids, w, given, counts, offsets,       \
+                                                             perm_token, inv_pos)
         if (E <= 64) MOE_TOPK16_PERMUTE(4);
         else if (E <= 128) MOE_TOPK16_PERMUTE(8);
         else if (E <= 256) MOE_TOPK16_PERMUTE(16);
@@ -1279,9 +1286,8 @@ hipError_t launch_route_permute(const void* x, const void* router, int64_t T, in
     }
 #define MOE_TOPK_PERMUTE(EPL)                                                                               \
     topk_permute_kernel<EPL><<<1, 256, 0, stream>>>(logits64, T, E, K, score, renorm, rs, bias, mask,      \
-                                                    logits_out, ids, w, given, n_group, topk_group,         \
-                                                    pl.pairs_per_block, pl.id_bits, counts, offsets, perm_token, \
-                                                    inv_pos)
+                                                    logits_out, ids, w, given, n_group, topk_group, counts, \
+                                                    offsets, perm_token, inv_pos)
     if (E <= 64) MOE_TOPK_PERMUTE(1);
     else if (E <= 128) MOE_TOPK_PERMUTE(2);
     else if (E <= 256) MOE_TOPK_PERMUTE(4);
