@@ -147,9 +147,14 @@ __device__ __forceinline__ void skinny_loop(const uint16_t* const (&ap)[4], cons
 // Blocks below `split` work on problem p0, the others on p1 (the routed
 // experts and the shared expert of one layer in one launch: both are weight
 // streams too short to fill the chip on their own).
+// gate_up: two waves per work item, wave 0 streaming the gate rows and wave 1
+// the up rows (each the same MFMA chain as one wave doing both), the up
+// accumulators meeting the gate ones in LDS for the epilogue: twice the waves
+// in flight for the same weight stream.
 template <bool GATE_UP>
-__global__ __launch_bounds__(64) void skinny_kernel(SkinnyParams p0, SkinnyParams p1, int64_t split) {
-    const int lane = threadIdx.x;
+__global__ __launch_bounds__(GATE_UP ? 128 : 64) void skinny_kernel(SkinnyParams p0, SkinnyParams p1, int64_t split) {
+    const int lane = threadIdx.x & 63;
+    const int half = GATE_UP ? static_cast<int>(threadIdx.x >> 6) : 0;  // gate_up: 0 gate rows, 1 up rows
     const bool second = static_cast<int64_t>(blockIdx.x) >= split;
     const SkinnyParams p = second ? p1 : p0;
     const int64_t L = second ? static_cast<int64_t>(blockIdx.x) - split : static_cast<int64_t>(blockIdx.x);
@@ -172,15 +177,25 @@ __global__ __launch_bounds__(64) void skinny_kernel(SkinnyParams p0, SkinnyParam
     }
     const int n = 16 * slice + (lane & 15);
     const uint16_t* wg = p.w + static_cast<int64_t>(g) * p.w_group_stride;
-    const uint16_t* bp = wg + static_cast<int64_t>(n) * p.Kd + kq;
-    const uint16_t* cp = GATE_UP ? wg + static_cast<int64_t>(p.I + n) * p.Kd + kq : bp;
+    const uint16_t* bp = wg + static_cast<int64_t>(half * p.I + n) * p.Kd + kq;
 
     f32x4 acc[4], acc_u[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc[r] = acc_u[r] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int S = p.Kd / 32;
-    if (nb == 1) skinny_loop<GATE_UP, 1, 8>(ap, bp, cp, S, nb, acc, acc_u);
-    else skinny_loop<GATE_UP, 4, 4>(ap, bp, cp, S, nb, acc, acc_u);
+    if (nb == 1) skinny_loop<false, 1, 8>(ap, bp, bp, S, nb, acc, acc_u);
+    else skinny_loop<false, 4, 4>(ap, bp, bp, S, nb, acc, acc_u);
+    if (GATE_UP) {
+        __shared__ f32x4 up_acc[4][64];
+        if (half == 1) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) up_acc[r][lane] = acc[r];
+        }
+        __syncthreads();
+        if (half == 1) return;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc_u[r] = up_acc[r][lane];
+    }
 
     // lane holds row r0 + 16 r + lane % 16 and the 4 columns 16 slice + 4 (lane / 16) + i
     const int col = 16 * slice + 4 * (lane >> 4);
@@ -258,7 +273,7 @@ hipError_t launch_experts_skinny(const void* x, const int32_t* perm_token, const
     const SkinnyProblem a = skinny_problem(x, perm_token, offsets, G, rows_max, D, I, gate_up, down, y,
                                            skinny_act(ws, rows_max, G, D, I));
     const int64_t b1 = a.units * (I / 16), b2 = a.units * (D / 16);
-    skinny_kernel<true><<<static_cast<unsigned>(b1), 64, 0, stream>>>(a.gu, a.gu, b1);
+    skinny_kernel<true><<<static_cast<unsigned>(b1), 128, 0, stream>>>(a.gu, a.gu, b1);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     skinny_kernel<false><<<static_cast<unsigned>(b2), 64, 0, stream>>>(a.dn, a.dn, b2);
@@ -275,7 +290,7 @@ hipError_t launch_experts_skinny_pair(const void* x, const int32_t* perm_token, 
                                            static_cast<uint16_t*>(act_s));
     const int64_t a1 = a.units * (I / 16), a2 = a.units * (D / 16);
     const int64_t n1 = a1 + b.units * (Is / 16), n2 = a2 + b.units * (D / 16);
-    skinny_kernel<true><<<static_cast<unsigned>(n1), 64, 0, stream>>>(a.gu, b.gu, a1);
+    skinny_kernel<true><<<static_cast<unsigned>(n1), 128, 0, stream>>>(a.gu, b.gu, a1);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     skinny_kernel<false><<<static_cast<unsigned>(n2), 64, 0, stream>>>(a.dn, b.dn, a2);
