@@ -448,40 +448,73 @@ __device__ __forceinline__ int row_max_i32(int v) {
     return max(v, dpp_i32<0x140>(v));
 }
 
+// How many lanes of this lane's row hold a value v below x (the other 15
+// lanes through row rotations).
+template <int S>
+__device__ __forceinline__ void count_step(int v, int x, int& n) {
+    n += dpp_i32<0x120 + S>(v) < x ? 1 : 0;  // row_ror:S
+}
+__device__ __forceinline__ int row_count_below(int v, int x) {
+    int n = 0;
+    count_step<1>(v, x, n);
+    count_step<2>(v, x, n);
+    count_step<3>(v, x, n);
+    count_step<4>(v, x, n);
+    count_step<5>(v, x, n);
+    count_step<6>(v, x, n);
+    count_step<7>(v, x, n);
+    count_step<8>(v, x, n);
+    count_step<9>(v, x, n);
+    count_step<10>(v, x, n);
+    count_step<11>(v, x, n);
+    count_step<12>(v, x, n);
+    count_step<13>(v, x, n);
+    count_step<14>(v, x, n);
+    count_step<15>(v, x, n);
+    return n;
+}
+
 // The picks of P rows (lane r of a row holds its r-th pick: my_e, my_s) in
-// ascending id order with their weights, to ids_out / w_out.
+// ascending id order with their weights, to ids_out / w_out.  The
+// renormalising sum adds the picks' scores in ascending id order, through
+// the wave's scratch (the rows16_select slots, free again by now).
 // ids_lds, if given, receives the ids too (at the same index as ids_out).
 template <int P>
 __device__ __forceinline__ void write_picks16(const int (&my_e)[P], const double (&my_s)[P], const int64_t (&t)[P],
                                               const bool (&live)[P], const bool (&kept)[P], int K, int renorm,
                                               double route_scale, int32_t* __restrict__ ids_out,
-                                              float* __restrict__ w_out, int* ids_lds = nullptr) {
+                                              float* __restrict__ w_out, lds_u8* scr, int* ids_lds = nullptr) {
     const int lane = lane_id();
     const int j = lane & 15;
     const int rbase = lane & 48;
+    const int row = lane >> 4;
+    int rank[P];
 #pragma unroll
     for (int p = 0; p < P; ++p) {
-        // ascending id order: rank of each pick among the row's K picks
-        int rank = 0;
-        for (int i = 0; i < K; ++i) {
-            const int ei = lane_get(my_e[p], rbase + i);
-            rank += (j < K && ei < my_e[p]) ? 1 : 0;
-        }
+        // ascending id order: rank of each pick among the row's K picks (K <= 16)
+        // (every lane takes part in the rotations; lanes past K hold no pick)
+        const int below = row_count_below(j < K ? my_e[p] : 0x7FFFFFFF, my_e[p]);
+        rank[p] = j < K ? below : 0;
+        if (renorm && j < K)
+            *reinterpret_cast<__attribute__((address_space(3))) double*>(scr + ((p * 4 + row) * 32 + rank[p]) * 16) =
+                my_s[p];
+    }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
         double den = 1.0;
         if (renorm) {
             den = 0.0;
-            for (int r = 0; r < K; ++r) {
-                const uint64_t holders = __ballot(j < K && rank == r);
-                const int holder = __builtin_ctzll((holders >> rbase) & 0xFFFFull) + rbase;
-                den += lane_get_f64(my_s[p], holder);
-            }
+            for (int r = 0; r < K; ++r)
+                den += *reinterpret_cast<const __attribute__((address_space(3))) double*>(scr + ((p * 4 + row) * 32 + r) *
+                                                                                           16);
         }
         if (live[p] && j < K) {
             if (kept[p]) {
                 const double wv = renorm ? (my_s[p] / den) * route_scale : my_s[p] * route_scale;
-                ids_out[t[p] * K + rank] = my_e[p];
-                w_out[t[p] * K + rank] = static_cast<float>(wv);
-                if (ids_lds != nullptr) ids_lds[t[p] * K + rank] = my_e[p];
+                ids_out[t[p] * K + rank[p]] = my_e[p];
+                w_out[t[p] * K + rank[p]] = static_cast<float>(wv);
+                if (ids_lds != nullptr) ids_lds[t[p] * K + rank[p]] = my_e[p];
             } else {
                 ids_out[t[p] * K + j] = -1;
                 w_out[t[p] * K + j] = 0.f;
@@ -489,6 +522,7 @@ __device__ __forceinline__ void write_picks16(const int (&my_e)[P], const double
             }
         }
     }
+    __builtin_amdgcn_wave_barrier();  // the scratch is read before the next use
 }
 
 // ---- top-k of one token per row of sixteen lanes ------------------------------
@@ -528,6 +562,21 @@ __device__ __forceinline__ double row_score(double l, int score, double m, doubl
     return score == 0 ? exp(l - m) / z : elem_score(l, score);
 }
 
+// scratch of rows16_select per wave: 4 rows x 32 slots x 16 bytes for each of
+// the P tokens per row, then one slot per lane that takes the compaction's
+// stores of non-candidates (so that no store needs a branch)
+constexpr int kRowScr = 4 * 32 * 16;
+constexpr int kDumpScr = 64 * 16;
+
+// The selection bias of this lane's experts j, j + 16, ... (0 without a
+// bias or past E); the same for every token, so loaded once per kernel.
+template <int EPL16>
+__device__ __forceinline__ void load_bias16(const float* __restrict__ bias, int E, float (&bv)[EPL16]) {
+    const int j = lane_id() & 15;
+#pragma unroll
+    for (int i = 0; i < EPL16; ++i) bv[i] = (bias != nullptr && j + 16 * i < E) ? bias[j + 16 * i] : 0.0f;
+}
+
 // Rank of key a among the 2 x 16 keys (k0, k1) of this lane's row: how many
 // of them are larger.  The keys of a row are distinct or zero.
 template <int S>
@@ -556,6 +605,82 @@ __device__ __forceinline__ void row_ranks(uint64_t k0, uint64_t k1, int& r0, int
     rank_step<14>(k0, k1, r0, r1);
     rank_step<15>(k0, k1, r0, r1);
 }
+// the same with one key per lane (the row's candidates fit its 16 lanes)
+template <int S>
+__device__ __forceinline__ void rank_step1(uint64_t k0, int& r0) {
+    r0 += dpp_u64<0x120 + S>(k0) > k0 ? 1 : 0;  // row_ror:S
+}
+__device__ __forceinline__ int row_rank1(uint64_t k0) {
+    int r0 = 0;
+    rank_step1<1>(k0, r0);
+    rank_step1<2>(k0, r0);
+    rank_step1<3>(k0, r0);
+    rank_step1<4>(k0, r0);
+    rank_step1<5>(k0, r0);
+    rank_step1<6>(k0, r0);
+    rank_step1<7>(k0, r0);
+    rank_step1<8>(k0, r0);
+    rank_step1<9>(k0, r0);
+    rank_step1<10>(k0, r0);
+    rank_step1<11>(k0, r0);
+    rank_step1<12>(k0, r0);
+    rank_step1<13>(k0, r0);
+    rank_step1<14>(k0, r0);
+    rank_step1<15>(k0, r0);
+    return r0;
+}
+
+// The compacted candidates of each row (slot k: logit, id, bias) get their
+// float64 score and choice key, H slots per lane (lane j takes slots j and
+// j + 16); each candidate's rank among its row's candidates (how many keys
+// are larger) places the K best at slots 0 .. K-1 (score, id).  One slot per
+// lane when no row of the wave has more than 16 candidates; both give the
+// same placement.
+template <int H, int P>
+__device__ __forceinline__ void rows16_place(lds_u8* scr, const int (&n_row)[P], const double (&m)[P],
+                                             const double (&z)[P], int score, int K) {
+    const int lane = lane_id();
+    const int j = lane & 15;
+    const int row = lane >> 4;
+    uint64_t key[P][H];
+    double sc[P][H];
+    int ce[P][H];
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+#pragma unroll
+        for (int h = 0; h < H; ++h) {
+            key[p][h] = 0ull;
+            sc[p][h] = 0.0;
+            ce[p][h] = 0;
+            const int slot = j + 16 * h;
+            if (slot < n_row[p]) {
+                const u32x4 rec = *reinterpret_cast<lds_u32x4*>(scr + ((p * 4 + row) * 32 + slot) * 16);
+                const double l =
+                    __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(rec[1]) << 32) | rec[0]));
+                ce[p][h] = static_cast<int>(rec[2]);
+                sc[p][h] = row_score(l, score, m[p], z[p]);
+                const double c = sc[p][h] + static_cast<double>(__uint_as_float(rec[3]));
+                key[p][h] = choice_key(c, ce[p][h]);
+            }
+        }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        int rk[H];
+        if constexpr (H == 2) row_ranks(key[p][0], key[p][1], rk[0], rk[1]);
+        else rk[0] = row_rank1(key[p][0]);
+#pragma unroll
+        for (int h = 0; h < H; ++h) {
+            if (j + 16 * h < n_row[p] && rk[h] < K) {
+                const uint64_t sb = static_cast<uint64_t>(__double_as_longlong(sc[p][h]));
+                const u32x4 rec = {static_cast<uint32_t>(sb), static_cast<uint32_t>(sb >> 32),
+                                   static_cast<uint32_t>(ce[p][h]), 0u};
+                *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(scr + ((p * 4 + row) * 32 + rk[h]) * 16) =
+                    rec;
+            }
+        }
+    }
+}
 
 // The K largest choices (score + bias, ties to the lower id) of the P tokens
 // of this lane's row; lane r < K of the row receives one pick and its score
@@ -574,14 +699,11 @@ __device__ __forceinline__ void row_ranks(uint64_t k0, uint64_t k1, int& r0, int
 // call this.
 template <int EPL16, int P, typename LG>
 __device__ __forceinline__ void rows16_select(LG lg_of, const bool (&live)[P], int E, int K, int score,
-                                              const float* __restrict__ bias, lds_u8* scr, int (&my_e)[P],
-                                              double (&my_s)[P]) {
+                                              const float* __restrict__ bias, const float (&bv)[EPL16], lds_u8* scr,
+                                              int (&my_e)[P], double (&my_s)[P]) {
     const int lane = lane_id();
     const int j = lane & 15;
     const int row = lane >> 4;
-    float bv[EPL16];  // the selection bias of this lane's experts (all tokens alike)
-#pragma unroll
-    for (int i = 0; i < EPL16; ++i) bv[i] = (bias != nullptr && j + 16 * i < E) ? bias[j + 16 * i] : 0.0f;
     double lg[P][EPL16];
 #pragma unroll
     for (int p = 0; p < P; ++p)
@@ -617,13 +739,18 @@ __device__ __forceinline__ void rows16_select(LG lg_of, const bool (&live)[P], i
             const float rz = static_cast<float>(1.0 / z[p]);
 #pragma unroll
             for (int i = 0; i < EPL16; ++i) c32[i] = j + 16 * i < E ? c32[i] * rz + bv[i] : -INFINITY;
+        } else if (score == 2) {  // one loop per score: no branch per slot
+#pragma unroll
+            for (int i = 0; i < EPL16; ++i) {
+                const float l = static_cast<float>(lg[p][i]);
+                const float sc32 = sqrtf(fmaxf(l, 0.0f) + log1pf(__expf(-fabsf(l))));
+                c32[i] = j + 16 * i < E ? sc32 + bv[i] : -INFINITY;
+            }
         } else {
 #pragma unroll
             for (int i = 0; i < EPL16; ++i) {
                 const float l = static_cast<float>(lg[p][i]);
-                float sc32;
-                if (score == 2) sc32 = sqrtf(fmaxf(l, 0.0f) + log1pf(__expf(-fabsf(l))));
-                else sc32 = __builtin_amdgcn_rcpf(1.0f + __expf(-l));
+                const float sc32 = __builtin_amdgcn_rcpf(1.0f + __expf(-l));
                 c32[i] = j + 16 * i < E ? sc32 + bv[i] : -INFINITY;
             }
         }
@@ -648,62 +775,30 @@ __device__ __forceinline__ void rows16_select(LG lg_of, const bool (&live)[P], i
     }
 
     if (__ballot(over) == 0ull) {
-        // candidate k of row r of token p at slot (p, r, k): logit, id, bias
+        // candidate k of row r of token p at slot (p, r, k): logit, id, bias;
+        // every slot of the lane is stored, the non-candidates to the lane's
+        // dump slot
+        const int dump = (P * 4 * 32 + lane) * 16;
 #pragma unroll
         for (int p = 0; p < P; ++p) {
             int k = off[p];
 #pragma unroll
             for (int i = 0; i < EPL16; ++i) {
-                if ((cm[p] >> i) & 1u) {
-                    const uint64_t lb = static_cast<uint64_t>(__double_as_longlong(lg[p][i]));
-                    const u32x4 rec = {static_cast<uint32_t>(lb), static_cast<uint32_t>(lb >> 32),
-                                       static_cast<uint32_t>(j + 16 * i), __float_as_uint(bv[i])};
-                    *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(scr + ((p * 4 + row) * 32 + k) * 16) =
-                        rec;
-                    ++k;
-                }
+                const bool c = (cm[p] >> i) & 1u;
+                const uint64_t lb = static_cast<uint64_t>(__double_as_longlong(lg[p][i]));
+                const u32x4 rec = {static_cast<uint32_t>(lb), static_cast<uint32_t>(lb >> 32),
+                                   static_cast<uint32_t>(j + 16 * i), __float_as_uint(bv[i])};
+                *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(scr + (c ? ((p * 4 + row) * 32 + k) * 16
+                                                                                       : dump)) = rec;
+                k += c ? 1 : 0;
             }
         }
         __builtin_amdgcn_wave_barrier();
-        uint64_t key[P][2];
-        double sc[P][2];
-        int ce[P][2];
+        bool wide = false;
 #pragma unroll
-        for (int p = 0; p < P; ++p)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                key[p][h] = 0ull;
-                sc[p][h] = 0.0;
-                ce[p][h] = 0;
-                const int slot = j + 16 * h;
-                if (slot < n_row[p]) {
-                    const u32x4 rec = *reinterpret_cast<lds_u32x4*>(scr + ((p * 4 + row) * 32 + slot) * 16);
-                    const double l =
-                        __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(rec[1]) << 32) | rec[0]));
-                    ce[p][h] = static_cast<int>(rec[2]);
-                    sc[p][h] = row_score(l, score, m[p], z[p]);
-                    const double c = sc[p][h] + static_cast<double>(__uint_as_float(rec[3]));
-                    key[p][h] = choice_key(c, ce[p][h]);
-                }
-            }
-        __builtin_amdgcn_wave_barrier();
-        // the K best of each row to slots 0 .. K-1 of its scratch (by rank)
-#pragma unroll
-        for (int p = 0; p < P; ++p) {
-            int r0, r1;
-            row_ranks(key[p][0], key[p][1], r0, r1);
-            const int rk[2] = {r0, r1};
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                if (j + 16 * h < n_row[p] && rk[h] < K) {
-                    const uint64_t sb = static_cast<uint64_t>(__double_as_longlong(sc[p][h]));
-                    const u32x4 rec = {static_cast<uint32_t>(sb), static_cast<uint32_t>(sb >> 32),
-                                       static_cast<uint32_t>(ce[p][h]), 0u};
-                    *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(scr + ((p * 4 + row) * 32 + rk[h]) *
-                                                                                        16) = rec;
-                }
-            }
-        }
+        for (int p = 0; p < P; ++p) wide = wide || n_row[p] > 16;
+        if (__ballot(wide) == 0ull) rows16_place<1, P>(scr, n_row, m, z, score, K);
+        else rows16_place<2, P>(scr, n_row, m, z, score, K);
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
         for (int p = 0; p < P; ++p) {
@@ -834,9 +929,6 @@ __global__ __launch_bounds__(256) void topk_permute_kernel(
     permute_small(pairs, static_cast<int>(T * K), K, E, counts, offsets, perm_token, inv_pos);
 }
 
-// scratch of rows16_select per wave: 4 rows x 32 slots x 16 bytes, for each
-// of the P tokens per row
-constexpr int kRowScr = 4 * 32 * 16;
 
 // The top-k of 16 tokens per 256-thread workgroup, one per row of sixteen
 // lanes (layers without group-limited select, E <= 512).
@@ -845,7 +937,7 @@ __global__ __launch_bounds__(256) void topk_rows16_kernel(
     const double* __restrict__ logits, int64_t T, int E, int K, int score, int renorm, double route_scale,
     const float* __restrict__ bias, const uint8_t* __restrict__ mask, float* __restrict__ logits_out,
     int32_t* __restrict__ ids_out, float* __restrict__ w_out, const int32_t* __restrict__ given) {
-    __shared__ __attribute__((aligned(16))) uint8_t scr_raw[4 * kRowScr];
+    __shared__ __attribute__((aligned(16))) uint8_t scr_raw[4 * (kRowScr + kDumpScr)];
     const int j = lane_id() & 15;
     const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
     int64_t t[1];
@@ -860,11 +952,15 @@ __global__ __launch_bounds__(256) void topk_rows16_kernel(
     kept[0] = live[0] && ((mask == nullptr) || (mask[t[0]] != 0));
     int my_e[1];
     double my_s[1];
-    if (given != nullptr)
+    lds_u8* scr = (lds_u8*)(scr_raw) + wv * (kRowScr + kDumpScr);
+    if (given != nullptr) {
         rows16_given<EPL16, 1>(lg_of, t, live, E, K, score, given, kept, my_e, my_s);
-    else
-        rows16_select<EPL16, 1>(lg_of, live, E, K, score, bias, (lds_u8*)(scr_raw) + wv * kRowScr, my_e, my_s);
-    write_picks16<1>(my_e, my_s, t, live, kept, K, renorm, route_scale, ids_out, w_out);
+    } else {
+        float bv[EPL16];
+        load_bias16<EPL16>(bias, E, bv);
+        rows16_select<EPL16, 1>(lg_of, live, E, K, score, bias, bv, scr, my_e, my_s);
+    }
+    write_picks16<1>(my_e, my_s, t, live, kept, K, renorm, route_scale, ids_out, w_out, scr);
 }
 
 // topk_permute_kernel for layers whose top-k runs in rows of sixteen lanes:
@@ -877,10 +973,13 @@ __global__ __launch_bounds__(256) void topk_permute_rows16_kernel(
     int32_t* __restrict__ ids_out, float* __restrict__ w_out, const int32_t* __restrict__ given,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm_token,
     int32_t* __restrict__ inv_pos) {
-    __shared__ __attribute__((aligned(16))) uint8_t scr_raw[4 * kRowScr];
+    __shared__ __attribute__((aligned(16))) uint8_t scr_raw[4 * (kRowScr + kDumpScr)];
     __shared__ int pairs[kSmallPairs];
     const int j = lane_id() & 15;
     const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+    lds_u8* scr = (lds_u8*)(scr_raw) + wv * (kRowScr + kDumpScr);
+    float bv[EPL16];
+    load_bias16<EPL16>(given == nullptr ? bias : nullptr, E, bv);
     for (int64_t tb = 0; tb < T; tb += 16) {
         int64_t t[1];
         bool live[1], kept[1];
@@ -896,8 +995,8 @@ __global__ __launch_bounds__(256) void topk_permute_rows16_kernel(
         if (given != nullptr)
             rows16_given<EPL16, 1>(lg_of, t, live, E, K, score, given, kept, my_e, my_s);
         else
-            rows16_select<EPL16, 1>(lg_of, live, E, K, score, bias, (lds_u8*)(scr_raw) + wv * kRowScr, my_e, my_s);
-        write_picks16<1>(my_e, my_s, t, live, kept, K, renorm, route_scale, ids_out, w_out, pairs);
+            rows16_select<EPL16, 1>(lg_of, live, E, K, score, bias, bv, scr, my_e, my_s);
+        write_picks16<1>(my_e, my_s, t, live, kept, K, renorm, route_scale, ids_out, w_out, scr, pairs);
     }
     __syncthreads();  // every pick in LDS
     permute_small(pairs, static_cast<int>(T * K), K, E, counts, offsets, perm_token, inv_pos);
@@ -932,7 +1031,7 @@ struct RouteTile {
     static constexpr int TBP_MAX = EMAX > 256 ? 32 : 64;
     static constexpr int TBP = TB < TBP_MAX ? TB : TBP_MAX;  // tokens whose logits are in LDS at a time
     static constexpr int LOGB = TBP * EMAX * 8; // float64 logits of one pass
-    static constexpr int SCRB = 4 * 2 * 4 * 32 * 16;  // top-k candidate slots: 4 waves x 2 tokens x 4 rows x 32
+    static constexpr int SCRB = 4 * (2 * kRowScr + kDumpScr);  // top-k scratch: 4 waves, up to 2 tokens per row
     static constexpr int SMEM = RING > LOGB + SCRB ? RING : LOGB + SCRB;
     static constexpr int XPER = TB / 32;       // 8-row DMA instructions per wave per chunk
     static constexpr int WPER = EMAX / 32;
@@ -946,6 +1045,7 @@ template <typename RT>
 __device__ __forceinline__ void route_topk_pass(const __attribute__((address_space(3))) double* lgs, lds_u8* scr_base,
                                                 int64_t tp, int64_t T, int E, int K, int score, int renorm,
                                                 double route_scale, const float* __restrict__ bias,
+                                                const float (&bv)[RT::EMAX / 16],
                                                 const uint8_t* __restrict__ mask, float* __restrict__ logits_out,
                                                 int32_t* __restrict__ ids_out, float* __restrict__ w_out) {
     const int lane = lane_id();
@@ -973,8 +1073,15 @@ __device__ __forceinline__ void route_topk_pass(const __attribute__((address_spa
         auto lg_of = [&](int p, int e) { return lgs[tl[p] * RT::EMAX + e]; };
         int my_e[P];
         double my_s[P];
-        rows16_select<EPL16, P>(lg_of, live, E, K, score, bias, scr_base + wv * (P * kRowScr), my_e, my_s);
-        write_picks16<P>(my_e, my_s, t, live, kept, K, renorm, route_scale, ids_out, w_out);
+        lds_u8* scr = scr_base + wv * (P * kRowScr + kDumpScr);
+        if constexpr (EPL16 > 16) {  // 32 bias registers held across the pass would spill
+            float bvi[EPL16];
+            load_bias16<EPL16>(bias, E, bvi);
+            rows16_select<EPL16, P>(lg_of, live, E, K, score, bias, bvi, scr, my_e, my_s);
+        } else {
+            rows16_select<EPL16, P>(lg_of, live, E, K, score, bias, bv, scr, my_e, my_s);
+        }
+        write_picks16<P>(my_e, my_s, t, live, kept, K, renorm, route_scale, ids_out, w_out, scr);
     }
 }
 
@@ -1107,6 +1214,8 @@ __global__ __launch_bounds__(256) void route_fused_bf16_kernel(
     // Logits to LDS, TBP tokens per pass ([TBP][EMAX] float64), and the
     // top-k of those tokens from there.
     __attribute__((address_space(3))) double* lgs = (__attribute__((address_space(3))) double*)(smem);
+    float bv[RT::EMAX / 16];  // (loaded per token block instead past 256 experts)
+    load_bias16<RT::EMAX / 16>(RT::EMAX > 256 ? nullptr : bias, E, bv);
 #pragma unroll
     for (int h = 0; h < RT::TB / RT::TBP; ++h) {
         if (h > 0) __syncthreads();  // the previous pass is done with its logits
@@ -1124,8 +1233,8 @@ __global__ __launch_bounds__(256) void route_fused_bf16_kernel(
         }
         __syncthreads();
         const int64_t tp = t0 + h * RT::TBP;  // first token of the pass
-        route_topk_pass<RT>(lgs, smem + RT::LOGB, tp, T, E, K, score, renorm, route_scale, bias, mask, logits_out,
-                            ids_out, w_out);
+        route_topk_pass<RT>(lgs, smem + RT::LOGB, tp, T, E, K, score, renorm, route_scale, bias, bv, mask,
+                            logits_out, ids_out, w_out);
     }
 }
 
