@@ -12,9 +12,11 @@
 //                     ballot per id bit, finds for every lane the lanes holding
 //                     the same expert (a "match mask").  The lowest such lane
 //                     adds the popcount to the wave's LDS histogram row.
-//   pass 2 (scan):    one workgroup per expert scans that expert's block
-//                     counts: the expert's count and, per block, the pairs of
-//                     the expert in earlier blocks.
+//   pass 2 (scan):    over more than kScanInScatter blocks, one workgroup per
+//                     expert scans that expert's block counts: the expert's
+//                     count and, per block, the pairs of the expert in
+//                     earlier blocks.  Up to kScanInScatter blocks, each
+//                     block of pass 3 sums the few counts it needs itself.
 //   pass 3 (scatter): each block scans the expert counts (the offsets; block
 //                     0 stores them), recomputes its wave histograms, turns
 //                     them into per-wave bases, and walks its segments again;
@@ -47,6 +49,11 @@ size_t permute_ws_bytes(int64_t P, int E) {
     const PermutePlan pl = permute_plan(P, E);
     return 2 * sizeof(int32_t) * static_cast<size_t>(E) * pl.blocks;
 }
+
+// Up to this many blocks the scatter pass sums the block counts itself (one
+// launch fewer); above it, the per-expert loop of loads costs more than the
+// separate scan launch.
+constexpr int kScanInScatter = 64;
 
 
 
@@ -100,8 +107,8 @@ __global__ __launch_bounds__(256) void permute_scan_kernel(
     if (tid == 255) counts[blockIdx.x] = part[255];
 }
 
-// Exclusive scan of the E expert counts into offs[0..E] (256 threads).
-__device__ __forceinline__ void scan_counts(const int32_t* __restrict__ counts, int E, int* offs, int* part) {
+// Exclusive scan of the E expert counts (in LDS) into offs[0..E] (256 threads).
+__device__ __forceinline__ void scan_counts(const int* counts, int E, int* offs, int* part) {
     const int tid = threadIdx.x;
     int v[4];
     int sum = 0;
@@ -130,17 +137,44 @@ __device__ __forceinline__ void scan_counts(const int32_t* __restrict__ counts, 
     __syncthreads();
 }
 
+// block_base == nullptr: the block sums its counts from block_hist (and
+// block 0 stores the expert counts); else block_base and counts come from
+// permute_scan_kernel.
 __global__ __launch_bounds__(256) void permute_scatter_kernel(
     const int32_t* __restrict__ ids, int64_t P, int K, int E, int ppb, int nblocks, int id_bits,
-    const int32_t* __restrict__ block_base, const int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ perm_token, int32_t* __restrict__ inv_pos) {
+    const int32_t* __restrict__ block_hist, const int32_t* __restrict__ block_base, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm_token, int32_t* __restrict__ inv_pos) {
     __shared__ int hist[kPermWaves][kMaxExperts];
     __shared__ int offs[kMaxExperts + 1];
+    __shared__ int cnt[kMaxExperts];    // pairs of each expert
+    __shared__ int before[kMaxExperts]; // pairs of each expert in earlier blocks
     __shared__ int part[256];
     const int tid = threadIdx.x;
     const int wv = tid >> 6;
     for (int i = tid; i < kPermWaves * E; i += 256) hist[i / E][i % E] = 0;
-    scan_counts(counts, E, offs, part);
+    if (block_base == nullptr) {
+        // row e of block_hist: expert e's pairs per block, in block order
+        for (int e = tid; e < E; e += 256) {
+            const int32_t* row = block_hist + static_cast<int64_t>(e) * nblocks;
+            int pre = 0, tot = 0;
+#pragma unroll 8
+            for (int b = 0; b < nblocks; ++b) {
+                const int v = row[b];
+                pre += b < static_cast<int>(blockIdx.x) ? v : 0;
+                tot += v;
+            }
+            cnt[e] = tot;
+            before[e] = pre;
+            if (blockIdx.x == 0) counts[e] = tot;
+        }
+    } else {
+        for (int e = tid; e < E; e += 256) {
+            cnt[e] = counts[e];
+            before[e] = block_base[static_cast<int64_t>(e) * nblocks + blockIdx.x];
+        }
+    }
+    __syncthreads();
+    scan_counts(cnt, E, offs, part);
     if (blockIdx.x == 0)
         for (int e = tid; e <= E; e += 256) offsets[e] = offs[e];
     const int64_t base = static_cast<int64_t>(blockIdx.x) * ppb;
@@ -151,7 +185,7 @@ __global__ __launch_bounds__(256) void permute_scatter_kernel(
     __syncthreads();
     // per-wave base rows: block base of the expert plus earlier waves' pairs
     for (int e = tid; e < E; e += 256) {
-        int run = offs[e] + block_base[static_cast<int64_t>(e) * nblocks + blockIdx.x];
+        int run = offs[e] + before[e];
 #pragma unroll
         for (int w = 0; w < kPermWaves; ++w) {
             const int h = hist[w][e];
@@ -191,17 +225,20 @@ hipError_t launch_permute(const int32_t* ids, int64_t T, int K, int E, int32_t* 
         return hipGetLastError();
     }
     int32_t* block_hist = ws_i32;
-    int32_t* block_base = ws_i32 + static_cast<int64_t>(E) * pl.blocks;
+    int32_t* block_base = nullptr;
     permute_count_kernel<<<pl.blocks, 256, 0, stream>>>(ids, P, E, pl.pairs_per_block, pl.blocks, pl.id_bits,
                                                        block_hist);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    permute_scan_kernel<<<E, 256, 0, stream>>>(block_hist, pl.blocks, block_base, counts);
-    err = hipGetLastError();
-    if (err != hipSuccess) return err;
+    if (pl.blocks > kScanInScatter) {
+        block_base = ws_i32 + static_cast<int64_t>(E) * pl.blocks;
+        permute_scan_kernel<<<E, 256, 0, stream>>>(block_hist, pl.blocks, block_base, counts);
+        err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
     permute_scatter_kernel<<<pl.blocks, 256, 0, stream>>>(ids, P, K, E, pl.pairs_per_block, pl.blocks,
-                                                         pl.id_bits, block_base, counts, offsets, perm_token,
-                                                         inv_pos);
+                                                         pl.id_bits, block_hist, block_base, counts, offsets,
+                                                         perm_token, inv_pos);
     return hipGetLastError();
 }
 
