@@ -1036,6 +1036,8 @@ struct RouteTile {
     static constexpr int XPER = TB / 32;       // 8-row DMA instructions per wave per chunk
     static constexpr int WPER = EMAX / 32;
     static_assert(TB % 32 == 0 && EMAX % 32 == 0, "8-row DMA groups over 4 waves");
+    // the stage wait counts on hidden chunk st being older than router chunk st
+    static_assert(XS > WS, "hidden rows run further ahead than router rows");
     static_assert(SMEM <= 160 * 1024, "LDS");
 };
 
