@@ -125,21 +125,6 @@ def dense_reference(cfg, rows: int, reps: int = 5):
     print(json.dumps({"dense_reference": res, "total_ms": total_ms, "tflops": flops / total_ms / 1e9}), flush=True)
 
 
-def gpu_spin_cycles(stream, target_ms=1.0):
-    """Argument of torch.cuda._sleep that keeps the GPU busy for about
-    target_ms (calibrated once with events)."""
-    import torch
-    n = 1 << 20
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda._sleep(n)  # first call outside the timing
-    e0.record(stream)
-    torch.cuda._sleep(n)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = max(e0.elapsed_time(e1), 1e-3)
-    return int(n * target_ms / ms)
-
-
 def stage_bytes(cfg, T, nvalid_pairs):
     """Algorithmic HBM bytes of the route, permute and combine stages."""
     b = cfg.operand_bytes
@@ -247,14 +232,7 @@ def main():
     sh_shape = shape.replace(E=1, K=1, I=cfg.Is, Is=0, n_group=1, topk_group=1) if cfg.Is else None
     names = ["route", "permute", "experts_routed"] + (["experts_shared"] if cfg.Is else []) + ["combine"]
 
-    # The stage calls are enqueued while the GPU is still busy with a spin of
-    # about a millisecond, so that each interval between events is the stage's
-    # GPU time and not the host's latency of issuing the call (the first
-    # stages of a layer otherwise wait for the host).
-    spin = gpu_spin_cycles(stream)
-
     def run_stages(evs):
-        torch.cuda._sleep(spin)
         evs[0].record(stream)
         B.moe_route(shape, x, layer.weights["router"], layer.sel_bias, None, None, tr["topk_ids"], tr["topk_w"], ws)
         evs[1].record(stream)
@@ -276,14 +254,12 @@ def main():
 
     for _ in range(max(1, args.warmup)):
         run_stages([torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)])
-        torch.cuda.synchronize()
     torch.cuda.synchronize()
     all_evs = []
     for _ in range(args.steps):
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
         run_stages(evs)
         all_evs.append(evs)
-        torch.cuda.synchronize()  # the next spin starts from an idle GPU
     torch.cuda.synchronize()
     stage_ms = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in all_evs])) for i, n in enumerate(names)}
     staged_total = float(np.mean([e[0].elapsed_time(e[-1]) for e in all_evs]))

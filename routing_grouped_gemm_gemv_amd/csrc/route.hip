@@ -1087,12 +1087,15 @@ __device__ __forceinline__ void route_topk_pass(const __attribute__((address_spa
     }
 }
 
-template <int TBB, int NBW>
+// TOPK false: the same k loop, and the float64 logits go to logits64 [T][E]
+// instead of the top-k (the logits of the two-kernel paths: group-limited
+// select, replay, the backward's recompute).
+template <int TBB, int NBW, bool TOPK = true>
 __global__ __launch_bounds__(256) void route_fused_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int64_t T, int D, int E, int K,
     int score, int renorm, double route_scale, const float* __restrict__ bias,
     const uint8_t* __restrict__ mask, float* __restrict__ logits_out, int32_t* __restrict__ ids_out,
-    float* __restrict__ w_out) {
+    float* __restrict__ w_out, double* __restrict__ logits64 = nullptr) {
     using RT = RouteTile<TBB, NBW>;
     __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[RT::SMEM];
     lds_u8* smem = (lds_u8*)(smem_raw);  // the array lives in LDS: an address-space cast
@@ -1235,6 +1238,15 @@ __global__ __launch_bounds__(256) void route_fused_bf16_kernel(
         }
         __syncthreads();
         const int64_t tp = t0 + h * RT::TBP;  // first token of the pass
+        if constexpr (!TOPK) {
+            // the pass's logits to memory, consecutive threads on consecutive logits
+            const int rows = static_cast<int>(min(static_cast<int64_t>(RT::TBP), T - tp));
+            for (int c = static_cast<int>(threadIdx.x); c < rows * E; c += 256) {
+                const int r = c / E, e = c - r * E;
+                logits64[(tp + r) * E + e] = lgs[r * RT::EMAX + e];
+            }
+            continue;
+        }
         route_topk_pass<RT>(lgs, smem + RT::LOGB, tp, T, E, K, score, renorm, route_scale, bias, bv, mask,
                             logits_out, ids_out, w_out);
     }
@@ -1320,8 +1332,45 @@ static bool route_small(int64_t T, int E, int dtype) {
     return dtype == 0 && T <= 1024 && T * E <= kRouteSmallTE;
 }
 
+// The fused router's workgroup tile for T tokens and E <= 512 experts: TBB
+// 16-token blocks, NBW 16-expert blocks per wave.  Larger token tiles cut the
+// router-matrix traffic per token once there are enough of them to give every
+// CU one; smaller ones keep every CU busy on shorter batches.  The logits and
+// picks do not depend on the tile.
+static void route_tile(int64_t T, int E, int& tbb, int& nbw) {
+    const int64_t cus = compute_units();
+    const bool wide = T >= 64 * cus;
+    if (E <= 64) { tbb = wide ? 4 : 2; nbw = 1; }
+    else if (E <= 128) { tbb = wide ? 4 : 2; nbw = 2; }
+    else if (E <= 256) { tbb = T >= 128 * cus ? 8 : 4; nbw = 4; }
+    else { tbb = wide ? 4 : 2; nbw = 8; }
+}
+
 hipError_t launch_router_logits(const void* x, const void* router, int64_t T, int D, int E,
                                 int dtype, double* logits64, hipStream_t stream) {
+    if (dtype == 0 && E <= 512 && !route_small(T, E, dtype)) {
+        // the fused router's k loop, logits to memory
+        int tbb = 0, nbw = 0;
+        route_tile(T, E, tbb, nbw);
+        // (the 128-token tile of this variant spills inside its k loop, where
+        // a reload waits for every DMA in flight: 64-token tiles instead)
+        if (tbb == 8) tbb = 4;
+        const uint16_t* xb = static_cast<const uint16_t*>(x);
+        const uint16_t* wb = static_cast<const uint16_t*>(router);
+#define MOE_LOGITS(TBB, NBW)                                                                                  \
+    route_fused_bf16_kernel<TBB, NBW, false><<<static_cast<unsigned>((T + 16 * TBB - 1) / (16 * TBB)), 256, 0, \
+                                                stream>>>(xb, wb, T, D, E, 0, 0, 0, 0.0, nullptr, nullptr,      \
+                                                          nullptr, nullptr, nullptr, logits64)
+        if (tbb == 4 && nbw == 1) MOE_LOGITS(4, 1);
+        else if (tbb == 2 && nbw == 1) MOE_LOGITS(2, 1);
+        else if (tbb == 4 && nbw == 2) MOE_LOGITS(4, 2);
+        else if (tbb == 2 && nbw == 2) MOE_LOGITS(2, 2);
+        else if (tbb == 4 && nbw == 4) MOE_LOGITS(4, 4);
+        else if (tbb == 4 && nbw == 8) MOE_LOGITS(4, 8);
+        else MOE_LOGITS(2, 8);
+#undef MOE_LOGITS
+        return hipGetLastError();
+    }
     if (route_small(T, E, dtype)) {
         dim3 grid(static_cast<unsigned>((T + 15) / 16), static_cast<unsigned>((E + 15) / 16));
         router_logits_split_kernel<<<grid, 64 * kSplitW, 0, stream>>>(
@@ -1427,18 +1476,15 @@ hipError_t launch_route(const void* x, const void* router, int64_t T, int D, int
     route_fused_bf16_kernel<TBB, NBW><<<static_cast<unsigned>((T + 16 * TBB - 1) / (16 * TBB)), 256, 0, \
                                          stream>>>(xb, wb, T, D, E, K, score, renorm, rs, bias, mask,      \
                                                    logits_out, ids, w)
-    // Larger token tiles cut the router-matrix traffic per token once there
-    // are enough of them to give every CU one; smaller ones keep every CU
-    // busy on shorter batches.  The logits and picks do not depend on the
-    // tile.
-    const bool wide = T >= 64 * static_cast<int64_t>(compute_units());
-    if (E <= 64 && wide) MOE_ROUTE(4, 1);
-    else if (E <= 64) MOE_ROUTE(2, 1);
-    else if (E <= 128 && wide) MOE_ROUTE(4, 2);
-    else if (E <= 128) MOE_ROUTE(2, 2);
-    else if (E <= 256 && T >= 128 * static_cast<int64_t>(compute_units())) MOE_ROUTE(8, 4);
-    else if (E <= 256) MOE_ROUTE(4, 4);
-    else if (T >= 64 * static_cast<int64_t>(compute_units())) MOE_ROUTE(4, 8);
+    int tbb = 0, nbw = 0;
+    route_tile(T, E, tbb, nbw);
+    if (tbb == 4 && nbw == 1) MOE_ROUTE(4, 1);
+    else if (tbb == 2 && nbw == 1) MOE_ROUTE(2, 1);
+    else if (tbb == 4 && nbw == 2) MOE_ROUTE(4, 2);
+    else if (tbb == 2 && nbw == 2) MOE_ROUTE(2, 2);
+    else if (tbb == 8 && nbw == 4) MOE_ROUTE(8, 4);
+    else if (tbb == 4 && nbw == 4) MOE_ROUTE(4, 4);
+    else if (tbb == 4 && nbw == 8) MOE_ROUTE(4, 8);
     else MOE_ROUTE(2, 8);
 #undef MOE_ROUTE
     return hipGetLastError();
