@@ -843,6 +843,142 @@ __device__ __forceinline__ void rows16_select(LG lg_of, const bool (&live)[P], i
     }
 }
 
+// Group-limited select in a row of sixteen lanes, the selection of
+// topk_token's group stage: experts form n_group groups of 16 SP consecutive
+// ids (group g: slots g SP .. g SP + SP - 1 of every lane), a group's score
+// is the sum of its two largest float64 choices, the topk_group best groups
+// are kept (ties to the lower group id), and K rounds of row argmax over the
+// kept experts' keys pick the experts; lane r of the row receives the r-th
+// pick and its score.  Every choice is evaluated in float64 (the group sums
+// need the exact two largest of every group).  Every lane of the wave must
+// call this.
+__device__ __forceinline__ void row_top2_f64(double& a, double& b) {
+    top2_merge(a, b, dpp_f64<0xB1>(a), dpp_f64<0xB1>(b));    // quad_perm(1,0,3,2)
+    top2_merge(a, b, dpp_f64<0x4E>(a), dpp_f64<0x4E>(b));    // quad_perm(2,3,0,1)
+    top2_merge(a, b, dpp_f64<0x141>(a), dpp_f64<0x141>(b));  // row_half_mirror
+    top2_merge(a, b, dpp_f64<0x140>(a), dpp_f64<0x140>(b));  // row_mirror
+}
+
+// lane g of the row receives the score of group g (groups of SP slots)
+template <int EPL16, int SP>
+__device__ __forceinline__ void group_scores16(const double (&ch)[EPL16], int E, double& gsc) {
+    static_assert(EPL16 % SP == 0 && EPL16 / SP <= 16, "groups of whole slots, at most one per lane");
+    const int j = lane_id() & 15;
+#pragma unroll
+    for (int g = 0; g < EPL16 / SP; ++g) {
+        double a = -INFINITY, b = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < SP; ++k) {
+            const int i = g * SP + k;
+            if (j + 16 * i < E) {
+                const double v = ch[i];
+                if (v > a) {
+                    b = a;
+                    a = v;
+                } else if (v > b) {
+                    b = v;
+                }
+            }
+        }
+        row_top2_f64(a, b);
+        if (j == g) gsc = a + b;
+    }
+}
+
+// slots per lane of one group (16 SP experts) where the sixteen-lane group
+// select applies, else 0: groups of 16, 32, 64 or 128 experts, at most 16
+// groups
+__host__ __device__ inline int grouped16_sp(int E, int n_group) {
+    if (n_group <= 1 || E % n_group != 0 || n_group > 16) return 0;
+    const int gs = E / n_group;
+    return (gs == 16 || gs == 32 || gs == 64 || gs == 128) ? gs / 16 : 0;
+}
+
+template <int EPL16, typename LG>
+__device__ __forceinline__ void rows16_grouped(LG lg_of, int E, int K, int score, const float (&bv)[EPL16],
+                                               int n_group, int topk_group, int& my_e, double& my_s) {
+    const int lane = lane_id();
+    const int j = lane & 15;
+    const int rbase = lane & 48;
+    double lg[EPL16];
+#pragma unroll
+    for (int i = 0; i < EPL16; ++i) lg[i] = j + 16 * i < E ? lg_of(0, j + 16 * i) : 0.0;
+    double m = 0.0, z = 1.0;
+    if (score == 0) {  // the softmax of row_softmax, from registers
+        double mx = -1.7976931348623157e308;
+#pragma unroll
+        for (int i = 0; i < EPL16; ++i)
+            if (j + 16 * i < E) mx = fmax(mx, lg[i]);
+        m = row_max_f64(mx);
+        double part = 0.0;
+#pragma unroll
+        for (int i = 0; i < EPL16; ++i)
+            if (j + 16 * i < E) part += static_cast<double>(__expf(static_cast<float>(lg[i] - m)));
+        z = row_sum_f64(part);
+    }
+    double sc[EPL16], ch[EPL16];
+    uint64_t key[EPL16];
+#pragma unroll
+    for (int i = 0; i < EPL16; ++i) {
+        const int e = j + 16 * i;
+        sc[i] = e < E ? row_score(lg[i], score, m, z) : 0.0;
+    }
+#pragma unroll
+    for (int i = 0; i < EPL16; ++i) {
+        const int e = j + 16 * i;
+        ch[i] = sc[i] + static_cast<double>(bv[i]);
+        key[i] = e < E ? choice_key(ch[i], e) : 0ull;
+    }
+    const int sp = grouped16_sp(E, n_group);
+    double gsc = 0.0;
+    if (sp == 1) {
+        if constexpr (EPL16 <= 16) group_scores16<EPL16, 1>(ch, E, gsc);
+    } else if (sp == 2) {
+        group_scores16<EPL16, 2>(ch, E, gsc);
+    } else if (sp == 4) {
+        if constexpr (EPL16 >= 4) group_scores16<EPL16, 4>(ch, E, gsc);
+    } else {
+        if constexpr (EPL16 >= 8) group_scores16<EPL16, 8>(ch, E, gsc);
+    }
+    uint64_t gkey = j < n_group ? choice_key(gsc, j) : 0ull;
+    uint32_t keep = 0u;
+    for (int r = 0; r < topk_group; ++r) {
+        const uint64_t win = row_max_u64(gkey);
+        const int g = 1023 - static_cast<int>(win & 0x3FFull);
+        keep |= 1u << g;
+        if (j == g) gkey = 0ull;
+    }
+    const int sh = sp == 1 ? 0 : sp == 2 ? 1 : sp == 4 ? 2 : 3;  // slot i lies in group i >> sh
+#pragma unroll
+    for (int i = 0; i < EPL16; ++i)
+        if (((keep >> (i >> sh)) & 1u) == 0u) key[i] = 0ull;
+    // K rounds of row argmax; lane r keeps the r-th pick
+    my_e = -1;
+    my_s = 0.0;
+    for (int r = 0; r < K; ++r) {
+        uint64_t best = key[0];
+#pragma unroll
+        for (int i = 1; i < EPL16; ++i) best = umax64(best, key[i]);
+        const uint64_t win = row_max_u64(best);
+        const int ew = 1023 - static_cast<int>(win & 0x3FFull);
+        const int owner = ew & 15;
+        const int slot = ew >> 4;
+        double sw = 0.0;
+#pragma unroll
+        for (int i = 0; i < EPL16; ++i) {
+            if (j == owner && i == slot) {
+                sw = sc[i];
+                key[i] = 0ull;
+            }
+        }
+        sw = lane_get_f64(sw, rbase + owner);
+        if (j == r) {
+            my_e = ew;
+            my_s = sw;
+        }
+    }
+}
+
 // Replay: lane j < K of the row takes the given id given[t * K + j]; a token
 // whose K given ids are not distinct ids in [0, E) is dropped (kept false).
 // The scores are those of rows16_select.  Every lane of the wave must call
@@ -932,11 +1068,12 @@ __global__ __launch_bounds__(256) void topk_permute_kernel(
 
 // The top-k of 16 tokens per 256-thread workgroup, one per row of sixteen
 // lanes (layers without group-limited select, E <= 512).
-template <int EPL16>
+template <int EPL16, bool GRP = false>
 __global__ __launch_bounds__(256) void topk_rows16_kernel(
     const double* __restrict__ logits, int64_t T, int E, int K, int score, int renorm, double route_scale,
     const float* __restrict__ bias, const uint8_t* __restrict__ mask, float* __restrict__ logits_out,
-    int32_t* __restrict__ ids_out, float* __restrict__ w_out, const int32_t* __restrict__ given) {
+    int32_t* __restrict__ ids_out, float* __restrict__ w_out, const int32_t* __restrict__ given, int n_group,
+    int topk_group) {
     __shared__ __attribute__((aligned(16))) uint8_t scr_raw[4 * (kRowScr + kDumpScr)];
     const int j = lane_id() & 15;
     const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
@@ -958,7 +1095,8 @@ __global__ __launch_bounds__(256) void topk_rows16_kernel(
     } else {
         float bv[EPL16];
         load_bias16<EPL16>(bias, E, bv);
-        rows16_select<EPL16, 1>(lg_of, live, E, K, score, bias, bv, scr, my_e, my_s);
+        if constexpr (GRP) rows16_grouped<EPL16>(lg_of, E, K, score, bv, n_group, topk_group, my_e[0], my_s[0]);
+        else rows16_select<EPL16, 1>(lg_of, live, E, K, score, bias, bv, scr, my_e, my_s);
     }
     write_picks16<1>(my_e, my_s, t, live, kept, K, renorm, route_scale, ids_out, w_out, scr);
 }
@@ -966,12 +1104,12 @@ __global__ __launch_bounds__(256) void topk_rows16_kernel(
 // topk_permute_kernel for layers whose top-k runs in rows of sixteen lanes:
 // 16 tokens per pass, the picks kept in LDS as well, then the permutation of
 // every pair from there (T * K <= 8 * 16 pairs: permute_small).
-template <int EPL16>
+template <int EPL16, bool GRP = false>
 __global__ __launch_bounds__(256) void topk_permute_rows16_kernel(
     const double* __restrict__ logits, int64_t T, int E, int K, int score, int renorm, double route_scale,
     const float* __restrict__ bias, const uint8_t* __restrict__ mask, float* __restrict__ logits_out,
-    int32_t* __restrict__ ids_out, float* __restrict__ w_out, const int32_t* __restrict__ given,
-    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm_token,
+    int32_t* __restrict__ ids_out, float* __restrict__ w_out, const int32_t* __restrict__ given, int n_group,
+    int topk_group, int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm_token,
     int32_t* __restrict__ inv_pos) {
     __shared__ __attribute__((aligned(16))) uint8_t scr_raw[4 * (kRowScr + kDumpScr)];
     __shared__ int pairs[kSmallPairs];
@@ -992,10 +1130,12 @@ __global__ __launch_bounds__(256) void topk_permute_rows16_kernel(
         kept[0] = live[0] && ((mask == nullptr) || (mask[t[0]] != 0));
         int my_e[1];
         double my_s[1];
-        if (given != nullptr)
+        if (given != nullptr) {
             rows16_given<EPL16, 1>(lg_of, t, live, E, K, score, given, kept, my_e, my_s);
-        else
-            rows16_select<EPL16, 1>(lg_of, live, E, K, score, bias, bv, scr, my_e, my_s);
+        } else {
+            if constexpr (GRP) rows16_grouped<EPL16>(lg_of, E, K, score, bv, n_group, topk_group, my_e[0], my_s[0]);
+            else rows16_select<EPL16, 1>(lg_of, live, E, K, score, bias, bv, scr, my_e, my_s);
+        }
         write_picks16<1>(my_e, my_s, t, live, kept, K, renorm, route_scale, ids_out, w_out, scr, pairs);
     }
     __syncthreads();  // every pick in LDS
@@ -1043,11 +1183,11 @@ struct RouteTile {
 
 // Top-k of the TBP tokens starting at token tp whose float64 logits are in
 // lgs ([TBP][EMAX]); scr: the candidate slots of the screened selection.
-template <typename RT>
+template <typename RT, bool GRP>
 __device__ __forceinline__ void route_topk_pass(const __attribute__((address_space(3))) double* lgs, lds_u8* scr_base,
                                                 int64_t tp, int64_t T, int E, int K, int score, int renorm,
                                                 double route_scale, const float* __restrict__ bias,
-                                                const float (&bv)[RT::EMAX / 16],
+                                                const float (&bv)[RT::EMAX / 16], int n_group, int topk_group,
                                                 const uint8_t* __restrict__ mask, float* __restrict__ logits_out,
                                                 int32_t* __restrict__ ids_out, float* __restrict__ w_out) {
     const int lane = lane_id();
@@ -1058,6 +1198,31 @@ __device__ __forceinline__ void route_topk_pass(const __attribute__((address_spa
     constexpr int EPL16 = RT::EMAX / 16;
     constexpr int P = (RT::TB > RT::TBP || EPL16 > 16) ? 1 : 2;
     static_assert(RT::TBP % (16 * P) == 0, "tokens per wave pass");
+    if constexpr (GRP) {  // group-limited select: one token per row at a time
+        lds_u8* scr = scr_base + wv * (P * kRowScr + kDumpScr);
+        for (int tb = 4 * wv; tb < RT::TBP; tb += 16) {
+            const int tl = tb + (lane >> 4);
+            int64_t t[1];
+            bool live[1], kept[1];
+            t[0] = t0 + tl;
+            live[0] = t[0] < T;
+            if (logits_out && live[0])
+                for (int e = lane & 15; e < E; e += 16)
+                    logits_out[t[0] * E + e] = static_cast<float>(lgs[tl * RT::EMAX + e]);
+            kept[0] = live[0] && ((mask == nullptr) || (mask[t[0]] != 0));
+            auto lg_of = [&](int, int e) { return lgs[tl * RT::EMAX + e]; };
+            int my_e[1];
+            double my_s[1];
+            if constexpr (EPL16 > 16) {
+                float bvi[EPL16];
+                load_bias16<EPL16>(bias, E, bvi);
+                rows16_grouped<EPL16>(lg_of, E, K, score, bvi, n_group, topk_group, my_e[0], my_s[0]);
+            } else {
+                rows16_grouped<EPL16>(lg_of, E, K, score, bv, n_group, topk_group, my_e[0], my_s[0]);
+            }
+            write_picks16<1>(my_e, my_s, t, live, kept, K, renorm, route_scale, ids_out, w_out, scr);
+        }
+    } else {
     for (int tb = 4 * P * wv; tb < RT::TBP; tb += 16 * P) {
         int64_t t[P];
         int tl[P];
@@ -1085,17 +1250,18 @@ __device__ __forceinline__ void route_topk_pass(const __attribute__((address_spa
         }
         write_picks16<P>(my_e, my_s, t, live, kept, K, renorm, route_scale, ids_out, w_out, scr);
     }
+    }
 }
 
 // TOPK false: the same k loop, and the float64 logits go to logits64 [T][E]
 // instead of the top-k (the logits of the two-kernel paths: group-limited
 // select, replay, the backward's recompute).
-template <int TBB, int NBW, bool TOPK = true>
+template <int TBB, int NBW, bool TOPK = true, bool GRP = false>
 __global__ __launch_bounds__(256) void route_fused_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int64_t T, int D, int E, int K,
     int score, int renorm, double route_scale, const float* __restrict__ bias,
     const uint8_t* __restrict__ mask, float* __restrict__ logits_out, int32_t* __restrict__ ids_out,
-    float* __restrict__ w_out, double* __restrict__ logits64 = nullptr) {
+    float* __restrict__ w_out, int n_group, int topk_group, double* __restrict__ logits64) {
     using RT = RouteTile<TBB, NBW>;
     __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[RT::SMEM];
     lds_u8* smem = (lds_u8*)(smem_raw);  // the array lives in LDS: an address-space cast
@@ -1247,8 +1413,8 @@ __global__ __launch_bounds__(256) void route_fused_bf16_kernel(
             }
             continue;
         }
-        route_topk_pass<RT>(lgs, smem + RT::LOGB, tp, T, E, K, score, renorm, route_scale, bias, bv, mask,
-                            logits_out, ids_out, w_out);
+        route_topk_pass<RT, GRP>(lgs, smem + RT::LOGB, tp, T, E, K, score, renorm, route_scale, bias, bv, n_group,
+                                 topk_group, mask, logits_out, ids_out, w_out);
     }
 }
 
@@ -1360,7 +1526,7 @@ hipError_t launch_router_logits(const void* x, const void* router, int64_t T, in
 #define MOE_LOGITS(TBB, NBW)                                                                                  \
     route_fused_bf16_kernel<TBB, NBW, false><<<static_cast<unsigned>((T + 16 * TBB - 1) / (16 * TBB)), 256, 0, \
                                                 stream>>>(xb, wb, T, D, E, 0, 0, 0, 0.0, nullptr, nullptr,      \
-                                                          nullptr, nullptr, nullptr, logits64)
+                                                          nullptr, nullptr, nullptr, 1, 1, logits64)
         if (tbb == 4 && nbw == 1) MOE_LOGITS(4, 1);
         else if (tbb == 2 && nbw == 1) MOE_LOGITS(2, 1);
         else if (tbb == 4 && nbw == 2) MOE_LOGITS(4, 2);
@@ -1391,7 +1557,7 @@ hipError_t launch_router_logits(const void* x, const void* router, int64_t T, in
 
 // whether a layer's top-k runs in rows of sixteen lanes (rows16_select and
 // rows16_given) on every path, or one token per wave (topk_token) on every path
-static bool topk_rows16(int E, int n_group) { return E <= 512 && n_group <= 1; }
+static bool topk_rows16(int E, int n_group) { return E <= 512 && (n_group <= 1 || grouped16_sp(E, n_group) > 0); }
 
 hipError_t launch_topk(const double* logits64, int64_t T, int E, int K, int score, int renorm,
                        float route_scale, int n_group, int topk_group, const float* bias, const uint8_t* mask,
@@ -1399,14 +1565,20 @@ hipError_t launch_topk(const double* logits64, int64_t T, int E, int K, int scor
     const double rs = static_cast<double>(route_scale);
     if (topk_rows16(E, n_group)) {
         const unsigned grid = static_cast<unsigned>((T + 15) / 16);
-#define MOE_TOPK16(EPL16)                                                                                    \
-    topk_rows16_kernel<EPL16><<<grid, 256, 0, stream>>>(logits64, T, E, K, score, renorm, rs, bias, mask, \
-                                                         logits_out, ids, w, given)
+#define MOE_TOPK16_G(EPL16, GRP)                                                                              \
+    topk_rows16_kernel<EPL16, GRP><<<grid, 256, 0, stream>>>(logits64, T, E, K, score, renorm, rs, bias, mask, \
+                                                              logits_out, ids, w, given, n_group, topk_group)
+#define MOE_TOPK16(EPL16)                                                        \
+    do {                                                                         \
+        if (n_group > 1 && given == nullptr) MOE_TOPK16_G(EPL16, true);          \
+        else MOE_TOPK16_G(EPL16, false);                                         \
+    } while (0)
         if (E <= 64) MOE_TOPK16(4);
         else if (E <= 128) MOE_TOPK16(8);
         else if (E <= 256) MOE_TOPK16(16);
         else MOE_TOPK16(32);
 #undef MOE_TOPK16
+#undef MOE_TOPK16_G
         return hipGetLastError();
     }
     const unsigned grid = static_cast<unsigned>((T + 3) / 4);
@@ -1433,15 +1605,22 @@ hipError_t launch_route_permute(const void* x, const void* router, int64_t T, in
     if (err != hipSuccess) return err;
     const double rs = static_cast<double>(route_scale);  // one workgroup: T * K <= 8 * 16 pairs
     if (topk_rows16(E, n_group)) {
-#define MOE_TOPK16_PERMUTE(EPL16)                                                                              \
-    topk_permute_rows16_kernel<EPL16><<<1, 256, 0, stream>>>(logits64, T, E, K, score, renorm, rs, bias, mask,  \
-                                                             logits_out, ids, w, given, counts, offsets,       \
-                                                             perm_token, inv_pos)
+#define MOE_TOPK16_PERMUTE_G(EPL16, GRP)                                                                     \
+    topk_permute_rows16_kernel<EPL16, GRP><<<1, 256, 0, stream>>>(logits64, T, E, K, score, renorm, rs, bias,  \
+                                                                  mask, logits_out, ids, w, given, n_group,    \
+                                                                  topk_group, counts, offsets, perm_token,     \
+                                                                  inv_pos)
+#define MOE_TOPK16_PERMUTE(EPL16)                                                \
+    do {                                                                         \
+        if (n_group > 1 && given == nullptr) MOE_TOPK16_PERMUTE_G(EPL16, true);  \
+        else MOE_TOPK16_PERMUTE_G(EPL16, false);                                 \
+    } while (0)
         if (E <= 64) MOE_TOPK16_PERMUTE(4);
         else if (E <= 128) MOE_TOPK16_PERMUTE(8);
         else if (E <= 256) MOE_TOPK16_PERMUTE(16);
         else MOE_TOPK16_PERMUTE(32);
 #undef MOE_TOPK16_PERMUTE
+#undef MOE_TOPK16_PERMUTE_G
         return hipGetLastError();
     }
 #define MOE_TOPK_PERMUTE(EPL)                                                                               \
@@ -1457,7 +1636,12 @@ hipError_t launch_route_permute(const void* x, const void* router, int64_t T, in
     return hipGetLastError();
 }
 
-bool route_fused(int E, int dtype, int n_group) { return dtype == 0 && E <= 512 && n_group <= 1; }
+// (group-limited select in the fused kernel up to 256 experts: past that its
+// float64 choices of every slot, next to the other pass's logits, spill into
+// the k loop; the two-kernel path takes those layers)
+bool route_fused(int E, int dtype, int n_group) {
+    return dtype == 0 && E <= 512 && (n_group <= 1 || (E <= 256 && grouped16_sp(E, n_group) > 0));
+}
 
 hipError_t launch_route(const void* x, const void* router, int64_t T, int D, int E, int K, int dtype,
                         int score, int renorm, float route_scale, int n_group, int topk_group, const float* bias,
@@ -1472,10 +1656,15 @@ hipError_t launch_route(const void* x, const void* router, int64_t T, int D, int
     const double rs = static_cast<double>(route_scale);
     const uint16_t* xb = static_cast<const uint16_t*>(x);
     const uint16_t* wb = static_cast<const uint16_t*>(router);
-#define MOE_ROUTE(TBB, NBW)                                                                              \
-    route_fused_bf16_kernel<TBB, NBW><<<static_cast<unsigned>((T + 16 * TBB - 1) / (16 * TBB)), 256, 0, \
-                                         stream>>>(xb, wb, T, D, E, K, score, renorm, rs, bias, mask,      \
-                                                   logits_out, ids, w)
+#define MOE_ROUTE_G(TBB, NBW, GRP)                                                                          \
+    route_fused_bf16_kernel<TBB, NBW, true, GRP><<<static_cast<unsigned>((T + 16 * TBB - 1) / (16 * TBB)), 256, \
+                                                   0, stream>>>(xb, wb, T, D, E, K, score, renorm, rs, bias, mask, \
+                                                                logits_out, ids, w, n_group, topk_group, nullptr)
+#define MOE_ROUTE(TBB, NBW)                                 \
+    do {                                                    \
+        if (n_group > 1) MOE_ROUTE_G(TBB, NBW, true);       \
+        else MOE_ROUTE_G(TBB, NBW, false);                  \
+    } while (0)
     int tbb = 0, nbw = 0;
     route_tile(T, E, tbb, nbw);
     if (tbb == 4 && nbw == 1) MOE_ROUTE(4, 1);
@@ -1487,6 +1676,7 @@ hipError_t launch_route(const void* x, const void* router, int64_t T, int D, int
     else if (tbb == 4 && nbw == 8) MOE_ROUTE(4, 8);
     else MOE_ROUTE(2, 8);
 #undef MOE_ROUTE
+#undef MOE_ROUTE_G
     return hipGetLastError();
 }
 
