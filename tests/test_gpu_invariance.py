@@ -116,19 +116,19 @@ def test_prefixes_across_the_decode_paths(name):
         assert torch.equal(trs["topk_w"].view(torch.int32), trf["topk_w"][:T].view(torch.int32)), T
 
 
-@pytest.mark.parametrize("name", ["q30", "qnext", "dsv4"])
+@pytest.mark.parametrize("name", ["q30", "qnext", "dsv4", "dspark"])
 def test_router_tiles_give_the_same_bits(name):
     """The fused router picks its token tile from T and the CU count (larger
     tiles once every CU gets one).  A batch exactly at the switch runs the
     larger tile, the same batch without its last token the smaller one: the
     float32 logits, ids and weights of every common token are the same
-    bits."""
+    bits.  With at most 16 experts (the top-1 draft layer) the switch is
+    between the small-batch router (up to 8192 tokens) and the fused one."""
     import routing_grouped_gemm_gemv_amd.binding as B
     from tests.gpu_util import make_layer
 
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    per_cu = {"q30": 64, "qnext": 64, "dsv4": 128}[name]
-    T = per_cu * cus
+    T = {"q30": 64 * cus, "qnext": 64 * cus, "dsv4": 128 * cus, "dspark": 8193}[name]
     cfg = get_config(name)
     inp = make_inputs(cfg, T=T)
     layer = make_layer(inp)
