@@ -526,11 +526,11 @@ __device__ __forceinline__ void write_picks16(const int (&my_e)[P], const double
 }
 
 // ---- top-k of one token per row of sixteen lanes ------------------------------
-// Every routing path of a layer without group-limited select and with at most
-// 512 experts selects through the functions below (the fused router, the
-// top-k kernel, the decode top-k + permute kernel and replay), so a token's
-// ids and weights are the same bits whichever kernel runs and whatever the
-// batch.  Row r of a wave (lanes 16r .. 16r+15) takes one token; lane j of
+// Every routing path of a layer with at most 512 experts (with group-limited
+// select: groups of 16 to 128 experts, at most 16 groups) selects through the
+// functions below (the fused router, the top-k kernel, the decode top-k +
+// permute kernel and replay), so a token's ids and weights are the same bits
+// whichever kernel runs and whatever the batch.  Row r of a wave (lanes 16r .. 16r+15) takes one token; lane j of
 // the row covers experts j, j + 16, ... (EPL16 slots, those past E unused).
 // The float64 logits are read through lg_of(p, e): the logit of expert e of
 // the row's p-th token, from LDS or from memory.
@@ -1067,7 +1067,7 @@ __global__ __launch_bounds__(256) void topk_permute_kernel(
 
 
 // The top-k of 16 tokens per 256-thread workgroup, one per row of sixteen
-// lanes (layers without group-limited select, E <= 512).
+// lanes (E <= 512; GRP: group-limited select, rows16_grouped).
 template <int EPL16, bool GRP = false>
 __global__ __launch_bounds__(256) void topk_rows16_kernel(
     const double* __restrict__ logits, int64_t T, int E, int K, int score, int renorm, double route_scale,
@@ -1559,8 +1559,9 @@ hipError_t launch_router_logits(const void* x, const void* router, int64_t T, in
     return hipGetLastError();
 }
 
-// whether a layer's top-k runs in rows of sixteen lanes (rows16_select and
-// rows16_given) on every path, or one token per wave (topk_token) on every path
+// whether a layer's top-k runs in rows of sixteen lanes (rows16_select or
+// rows16_grouped, and rows16_given) on every path, or one token per wave
+// (topk_token) on every path
 static bool topk_rows16(int E, int n_group) { return E <= 512 && (n_group <= 1 || grouped16_sp(E, n_group) > 0); }
 
 hipError_t launch_topk(const double* logits64, int64_t T, int E, int K, int score, int renorm,
