@@ -30,7 +30,9 @@
 // 32-wide halves with the fragments of the next half read ahead.  For
 // gate_up the weight rows of a tile are gate rows and the matching up rows,
 // so the SwiGLU epilogue pairs registers of the same wave.  The epilogue
-// stages the bf16 tile in LDS and stores whole rows in 16-byte pieces.
+// stages the bf16 tile in LDS and stores whole rows in 16-byte pieces; the
+// first stage of the workgroup's next tile is fetched meanwhile, so a tile
+// starts with its operands already on the way.
 //
 // fp32 kernel (the fp32-operand mode): 128 x 128 tiles staged through
 // registers, 16x16x4 f32 MFMA.
@@ -278,8 +280,13 @@ __global__ __launch_bounds__(1024) void build_tile_table_kernel(const int32_t* _
     }
 }
 
+// Descriptor of tile L.  L is uniform over the workgroup and the table is
+// written by an earlier launch, so it comes through the scalar data cache
+// (no vector-memory wait, which would also wait for the output stores of
+// the tile before).
 __device__ __forceinline__ Tile2 load_tile(const GemmParams& p, int L) {
-    const u32x4 d = p.tiles[L];
+    typedef const __attribute__((address_space(4))) u32x4 const_u32x4;
+    const u32x4 d = ((const_u32x4*)p.tiles)[L];
     Tile2 t;
     t.g = static_cast<int>(d.x);
     t.m0 = static_cast<int64_t>(d.y);
@@ -316,65 +323,78 @@ __device__ __forceinline__ int take_tile(int32_t* ctl, const Queues& qs, int& q)
     return -1;
 }
 
-// One tile of BM rows x BN weight rows (gate_up: BN/2 gate rows and the
-// matching BN/2 up rows).  Stage st holds k = 64 st .. 64 st + 63 of all the
-// tile's rows; each DMA instruction moves 8 rows x 128 bytes.  A stage feeds
-// two 32-wide MFMA sub-steps, and one wait + barrier per stage serves both.
-// claim: a work-queue counter that lane 0 of wave 0 increments once the
-// first stage has landed (so the atomic never holds up the prologue); the
-// value it returns is the result (0 elsewhere).
-template <bool GATE_UP, int BM, int BN>
-__device__ __forceinline__ int tile_pipeline(const GemmParams& p, const Tile2& tc, lds_u8* smem, int32_t* claim) {
-    constexpr int kWN = BM == 256 ? 2 : 4;
-    constexpr int kRow = 128;
-    constexpr int kStage = (BM + BN) * kRow;
-    constexpr int kDmaA = BM / 32;   // 8-row DMA instructions per wave per stage
-    constexpr int kDmaB = BN / 32;
-    constexpr int kDma = kDmaA + kDmaB;
-    static_assert(2 * kStage <= kLds2, "LDS");
-    static_assert(kDma <= 32, "DMA issue slots");
+// Lane index computed where it is used: the asm keeps the compiler from
+// hoisting per-lane addresses out of the persistent loop and holding
+// (spilling) them across the k loop.
+__device__ __forceinline__ int fresh_lane() {
+    int l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
+}
 
-    // The thread index passes through an empty asm so that the per-lane
-    // addresses below are computed per tile, not hoisted out of the
-    // persistent loop and kept (spilled) across the pipeline.
-    int tid = threadIdx.x;
-    asm volatile("" : "+v"(tid));
-    const int lane = tid & 63;
-    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wv / kWN;
-    const int wn = wv % kWN;
-    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem));
+// Stages.  A tile is BM rows x BN weight rows (gate_up: BN/2 gate rows and
+// the matching BN/2 up rows); stage st holds k = 64 st .. 64 st + 63 of all of
+// them, 128 bytes a row.  Each DMA instruction moves 8 rows x 128 bytes: lane
+// l lands on row l / 8 of its 8-row group at physical chunk l % 8 and fetches
+// logical chunk (l % 8) ^ (row % 8).  Byte offsets fit 32 bits: x, the
+// activations and one group's weights are each below 4 GiB (checked by the
+// launcher).
+template <int BM, int BN>
+struct StageShape {
+    static constexpr int kBytes = (BM + BN) * kRowBytes;
+    static constexpr int kDmaA = BM / 32;  // 8-row DMA instructions per wave per stage
+    static constexpr int kDma = BM / 32 + BN / 32;
+};
 
-    const uint8_t* __restrict__ abase = static_cast<const uint8_t*>(p.a);
-    const uint8_t* __restrict__ wbase =
-        static_cast<const uint8_t*>(p.w) + static_cast<int64_t>(tc.g) * p.w_group_stride * 2;
-    // lane l lands on row l / 8 of its 8-row group at physical chunk l % 8 and
-    // fetches logical chunk (l % 8) ^ (row % 8).  Byte offsets fit 32 bits: x,
-    // the activations and one group's weights are each below 4 GiB (checked
-    // by the launcher).  Offsets are recomputed per DMA from a few registers;
-    // only the gathered rows of gate_up are held (their token ids are loads).
+// Gate_up: the byte offset of the x row (plus the lane's chunk) behind each
+// of the lane's BM / 32 A rows, through the permutation when there is one;
+// computed once per tile ahead of its first stage.  Rows past the group
+// repeat its last row and are never stored.
+template <int BM>
+__device__ __forceinline__ void a_offsets(const GemmParams& p, const Tile2& tc, int lane, int wv, uint32_t (&aoff)[8]) {
     const int chunk = (lane & 7) ^ (lane >> 3);
     const uint32_t row_bytes = static_cast<uint32_t>(p.Kd) * 2;
-    const int ra = wv * (BM / 4) + (lane >> 3);  // tile row of A instruction 0
-    const int rb = wv * (BN / 4) + (lane >> 3);  // weight row of B instruction 0
-    const bool gather = GATE_UP && p.perm != nullptr;
-    uint32_t aoff_g[GATE_UP ? kDmaA : 1];
-    if (GATE_UP) {
+    const int ra = wv * (BM / 4) + (lane >> 3);
+    uint32_t row[BM / 32];
+    if (p.perm != nullptr) {
 #pragma unroll
-        for (int i = 0; i < kDmaA; ++i) {
+        for (int i = 0; i < BM / 32; ++i) {
             const int r = ra + 8 * i;
-            const int rr = r < tc.rows ? r : tc.rows - 1;  // rows past the group repeat its last row; never stored
-            aoff_g[i] = gather ? static_cast<uint32_t>(p.perm[tc.m0 + rr]) * row_bytes + chunk * 16 : 0u;
+            row[i] = static_cast<uint32_t>(p.perm[tc.m0 + (r < tc.rows ? r : tc.rows - 1)]);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < BM / 32; ++i) {
+            const int r = ra + 8 * i;
+            row[i] = static_cast<uint32_t>(tc.m0 + (r < tc.rows ? r : tc.rows - 1));
         }
     }
-    auto a_off = [&](int i) -> uint32_t {
-        if (GATE_UP && gather) return aoff_g[i];
-        const int r = ra + 8 * i;
-        const int rr = r < tc.rows ? r : tc.rows - 1;
-        return static_cast<uint32_t>(tc.m0 + rr) * row_bytes + chunk * 16;
-    };
-    auto b_off = [&](int i) -> uint32_t {
-        const int r = rb + 8 * i;
+#pragma unroll
+    for (int i = 0; i < BM / 32; ++i) aoff[i] = row[i] * row_bytes + chunk * 16;
+}
+
+// DMA number dq of the calling wave for stage st of tile tc into the stage
+// buffer at LDS byte stage_off; stages past the end fetch the last one again.
+template <bool GATE_UP, int BM, int BN>
+__device__ __forceinline__ void stage_dma(const GemmParams& p, const Tile2& tc, const uint32_t (&aoff)[8], int lane,
+                                          int wv, uint32_t lds0, int st, uint32_t stage_off, int dq) {
+    constexpr int kDmaA = StageShape<BM, BN>::kDmaA;
+    const int chunk = (lane & 7) ^ (lane >> 3);
+    const uint32_t row_bytes = static_cast<uint32_t>(p.Kd) * 2;
+    const int ns = p.Kd / 64;
+    const uint32_t kb = static_cast<uint32_t>(st < ns ? st : ns - 1) * kRowBytes;
+    if (dq < kDmaA) {
+        uint32_t off;
+        if (GATE_UP) {
+            off = aoff[dq];
+        } else {
+            const int r = wv * (BM / 4) + (lane >> 3) + 8 * dq;
+            const int rr = r < tc.rows ? r : tc.rows - 1;
+            off = static_cast<uint32_t>(tc.m0 + rr) * row_bytes + chunk * 16;
+        }
+        dma16(static_cast<const uint8_t*>(p.a), off + kb, lds0 + stage_off + (wv * (BM / 4) + 8 * dq) * kRowBytes);
+    } else {
+        const int r = wv * (BN / 4) + (lane >> 3) + 8 * (dq - kDmaA);
         int wrow;
         if (GATE_UP) {
             int c = tc.n * 128 + (r % (BN / 2));  // gate row; the matching up row is I + c
@@ -384,10 +404,76 @@ __device__ __forceinline__ int tile_pipeline(const GemmParams& p, const Tile2& t
             wrow = tc.n * 256 + r;
             if (wrow >= p.ldo) wrow = p.ldo - 1;
         }
-        return static_cast<uint32_t>(wrow) * row_bytes + chunk * 16;
-    };
-    const int a_dst = wv * (BM / 4) * kRow;
-    const int b_dst = BM * kRow + wv * (BN / 4) * kRow;
+        const uint8_t* wbase = static_cast<const uint8_t*>(p.w) + static_cast<int64_t>(tc.g) * p.w_group_stride * 2;
+        dma16(wbase, static_cast<uint32_t>(wrow) * row_bytes + chunk * 16 + kb,
+              lds0 + stage_off + (BM + wv * (BN / 4) + 8 * (dq - kDmaA)) * kRowBytes);
+    }
+}
+
+// Every DMA of stage st (0 or 1) of tile tc, of either shape, into stage
+// buffer st; for gate_up, first the tile's A row offsets (st == 0).
+template <bool GATE_UP>
+__device__ __forceinline__ void first_stage(const GemmParams& p, const Tile2& tc, uint32_t (&aoff)[8], int lane, int wv,
+                                            uint32_t lds0, int st) {
+    if (tc.tail) {
+        using S = StageShape<128, 512>;
+        if (GATE_UP && st == 0) a_offsets<128>(p, tc, lane, wv, aoff);
+#pragma unroll
+        for (int dq = 0; dq < S::kDma; ++dq)
+            stage_dma<GATE_UP, 128, 512>(p, tc, aoff, lane, wv, lds0, st, st * S::kBytes, dq);
+    } else {
+        using S = StageShape<256, 256>;
+        if (GATE_UP && st == 0) a_offsets<256>(p, tc, lane, wv, aoff);
+#pragma unroll
+        for (int dq = 0; dq < S::kDma; ++dq)
+            stage_dma<GATE_UP, 256, 256>(p, tc, aoff, lane, wv, lds0, st, st * S::kBytes, dq);
+    }
+}
+
+// LDS byte that carries the next tile's index from wave 0 to the others:
+// past stage 0 of either tile shape and below every output staging area.
+constexpr int kNextWord = StageShape<128, 512>::kBytes;
+static_assert(StageShape<256, 256>::kBytes <= kNextWord, "LDS");
+
+// Output stores of one tile per thread: gate_up 64 KB, down 128 KB, in
+// 16-byte pieces over 256 threads.  Every one is issued (rows and columns
+// outside the output are dropped by the buffer range check), so the number in
+// flight behind a tile is this constant.
+template <bool GATE_UP>
+constexpr int kTileStores = GATE_UP ? 16 : 32;
+
+// One tile: k loop, epilogue, and the start of the next tile.
+//
+// On entry stages 0 and 1 of tc are in flight (issued by the tile before, or
+// before the first tile); after a tile (after_tile) that tile's output stores
+// were issued between them.  The k loop steps through each stage in two
+// 32-wide MFMA sub-steps with one wait + barrier per stage.
+//
+// Epilogue: the bf16 output is staged in LDS above kNextWord and stored in
+// 16-byte pieces of whole rows (down: in two halves, one after the other).
+// Meanwhile stage 0 of the next tile is fetched below kNextWord, and stage 1
+// once every wave is done with the staging area.  Returns the next tile's
+// index (uniform; -1 when none is left) with tn and naoff its descriptor and
+// (gate_up) A row offsets.
+template <bool GATE_UP, int BM, int BN>
+__device__ __forceinline__ int tile_pipeline(const GemmParams& p, const Tile2& tc, const uint32_t (&aoff)[8],
+                                             lds_u8* smem, int wv, bool after_tile, const Queues& qs, int& q,
+                                             Tile2& tn, uint32_t (&naoff)[8]) {
+    using S = StageShape<BM, BN>;
+    constexpr int kWN = BM == 256 ? 2 : 4;
+    constexpr int kRow = kRowBytes;
+    constexpr int kStage = S::kBytes;
+    constexpr int kDma = S::kDma;
+    constexpr int kStores = kTileStores<GATE_UP>;
+    static_assert(2 * kStage <= kLds2, "LDS");
+    static_assert(kDma <= 32, "DMA issue slots");
+    static_assert(kStores + kDma <= 63, "vmcnt");
+
+    const int lane = fresh_lane();
+    const int tid = wv * 64 + lane;
+    const int wm = wv / kWN;
+    const int wn = wv % kWN;
+    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem));
 
     // fragment of sub-step j (k 32j .. 32j+31 of the stage): logical chunk
     // 4j + lane/16 of row lane%16 (+ 16 per block), physical chunk ^ (lane % 8)
@@ -407,10 +493,8 @@ __device__ __forceinline__ int tile_pipeline(const GemmParams& p, const Tile2& t
         for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int ns = p.Kd / 64;  // stages of the k loop
-    auto dma = [&](int st, uint32_t stage_off, int q) {
-        const uint32_t kb = static_cast<uint32_t>(st < ns ? st : ns - 1) * kRow;
-        if (q < kDmaA) dma16(abase, a_off(q) + kb, lds0 + stage_off + a_dst + q * 8 * kRow);
-        else dma16(wbase, b_off(q - kDmaA) + kb, lds0 + stage_off + b_dst + (q - kDmaA) * 8 * kRow);
+    auto dma = [&](int st, uint32_t stage_off, int dq) {
+        stage_dma<GATE_UP, BM, BN>(p, tc, aoff, lane, wv, lds0, st, stage_off, dq);
     };
     auto frag = [&](uint32_t stage_off, int xo, int k) -> u32x4 {
         const lds_u8* st = smem + stage_off;
@@ -429,30 +513,26 @@ __device__ __forceinline__ int tile_pipeline(const GemmParams& p, const Tile2& t
             for (int h = 0; h < 2; ++h) {
 #pragma unroll
                 for (int nb = 4 * h; nb < 4 * h + 4; ++nb) acc[mb][nb] = mfma_bf16(f[1 + nb], a, acc[mb][nb]);
-                const int q = 2 * mb + h;
-                if (q < 8) {
-                    g[2 * q] = frag(rs, xo, 2 * q);
-                    g[2 * q + 1] = frag(rs, xo, 2 * q + 1);
+                const int qq = 2 * mb + h;
+                if (qq < 8) {
+                    g[2 * qq] = frag(rs, xo, 2 * qq);
+                    g[2 * qq + 1] = frag(rs, xo, 2 * qq + 1);
                 }
                 if (do_dma) {
                     constexpr int kPer = (kDma + 15) / 16;  // DMAs per 4 MFMAs
 #pragma unroll
                     for (int u = 0; u < kPer; ++u)
-                        if (q * kPer + u < kDma) dma(dst, ds, q * kPer + u);
+                        if (qq * kPer + u < kDma) dma(dst, ds, qq * kPer + u);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
     };
 
-    dma(0, 0, 0);
-#pragma unroll
-    for (int q = 1; q < kDma; ++q) dma(0, 0, q);
-#pragma unroll
-    for (int q = 0; q < kDma; ++q) dma(1, kStage, q);
-    wait_vmem<kDma>();
-    int claimed = 0;
-    if (wv == 0 && lane == 0) claimed = __hip_atomic_fetch_add(claim, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // stage 0 has landed once at most stage 1 (and, after a tile, its
+    // stores) is still in flight
+    if (after_tile) wait_vmem<kStores + kDma>();
+    else wait_vmem<kDma>();
     __syncthreads();
     u32x4 f0[16], f1[16];
 #pragma unroll
@@ -472,53 +552,104 @@ __device__ __forceinline__ int tile_pipeline(const GemmParams& p, const Tile2& t
     wait_vmem<0>();
     __syncthreads();
 
+
+    // Output pieces of PR rows x PC columns: gate_up one piece, down two
+    // (the row halves of a 256-row tile, the column halves of a tail tile).
     constexpr int NC = GATE_UP ? BN / 2 : BN;
-    constexpr int kOutRow = NC * 2 + 16;
-    static_assert(BM * kOutRow <= kLds2, "LDS");
-    const int row0 = wm * 128 + (lane & 15);
-    const int c4 = 4 * (lane >> 4);
-    if (GATE_UP) {
+    constexpr int kPieces = GATE_UP ? 1 : 2;
+    constexpr int PR = GATE_UP ? BM : 128;
+    constexpr int PC = GATE_UP ? NC : 256;
+    constexpr bool kSplitRows = !GATE_UP && BM == 256;
+    constexpr int kOutRow = PC * 2 + 16;
+    constexpr int kStg = kLds2 - PR * kOutRow;
+    static_assert(kStg >= kNextWord + 16, "LDS");
+    static_assert(kPieces * PR * PC * 2 == kStores * 256 * 16, "stores per thread");
+    const int my_piece = GATE_UP ? 0 : (kSplitRows ? wm : (wn >> 1));
+    const int lrow0 = (kSplitRows ? 0 : wm * 128) + (lane & 15);
+    const int lcol0 = (GATE_UP ? wn * 64 : (kSplitRows ? wn : (wn & 1)) * 128) + 4 * (lane >> 4);
+    auto stage_out = [&]() {
+        if (GATE_UP) {
 #pragma unroll
-        for (int mb = 0; mb < 8; ++mb)
+            for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb) {
-                const uint32_t w0 = pack_bf16(silu_mul_fast(acc[mb][nb][0], acc[mb][nb + 4][0]),
-                                              silu_mul_fast(acc[mb][nb][1], acc[mb][nb + 4][1]));
-                const uint32_t w1 = pack_bf16(silu_mul_fast(acc[mb][nb][2], acc[mb][nb + 4][2]),
-                                              silu_mul_fast(acc[mb][nb][3], acc[mb][nb + 4][3]));
-                const int off = (row0 + mb * 16) * kOutRow + (wn * 64 + nb * 16 + c4) * 2;
-                *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(smem + off) = u32x2{w0, w1};
-            }
-    } else {
+                for (int nb = 0; nb < 4; ++nb) {
+                    const uint32_t w0 = pack_bf16(silu_mul_fast(acc[mb][nb][0], acc[mb][nb + 4][0]),
+                                                  silu_mul_fast(acc[mb][nb][1], acc[mb][nb + 4][1]));
+                    const uint32_t w1 = pack_bf16(silu_mul_fast(acc[mb][nb][2], acc[mb][nb + 4][2]),
+                                                  silu_mul_fast(acc[mb][nb][3], acc[mb][nb + 4][3]));
+                    const int off = kStg + (lrow0 + mb * 16) * kOutRow + (lcol0 + nb * 16) * 2;
+                    *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(smem + off) = u32x2{w0, w1};
+                }
+        } else {
 #pragma unroll
-        for (int mb = 0; mb < 8; ++mb)
+            for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
-            for (int nb = 0; nb < 8; ++nb) {
-                const uint32_t w0 = pack_bf16(acc[mb][nb][0], acc[mb][nb][1]);
-                const uint32_t w1 = pack_bf16(acc[mb][nb][2], acc[mb][nb][3]);
-                const int off = (row0 + mb * 16) * kOutRow + (wn * 128 + nb * 16 + c4) * 2;
-                *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(smem + off) = u32x2{w0, w1};
-            }
-    }
-    __syncthreads();
-    constexpr int kChunks = NC / 8;
+                for (int nb = 0; nb < 8; ++nb) {
+                    const uint32_t w0 = pack_bf16(acc[mb][nb][0], acc[mb][nb][1]);
+                    const uint32_t w1 = pack_bf16(acc[mb][nb][2], acc[mb][nb][3]);
+                    const int off = kStg + (lrow0 + mb * 16) * kOutRow + (lcol0 + nb * 16) * 2;
+                    *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(smem + off) = u32x2{w0, w1};
+                }
+        }
+    };
+    // the tile's rows through a buffer resource: rows at or past tc.rows fall
+    // outside its range, columns past the output are sent outside it
+    constexpr int kChunks = PC / 8;
     constexpr int kRowsPerPass = 256 / kChunks;
-    const int col_base = GATE_UP ? tc.n * 128 : tc.n * 256;
     const int col_lim = GATE_UP ? p.I : p.ldo;
     const int ch = tid % kChunks;
-    const int col = col_base + ch * 8;
-    uint8_t* __restrict__ out = static_cast<uint8_t*>(p.out);
-#pragma unroll 4
-    for (int r = tid / kChunks; r < BM; r += kRowsPerPass) {
-        const u32x4 v = *reinterpret_cast<lds_u32x4*>(smem + r * kOutRow + ch * 16);
-        if (r < tc.rows && col < col_lim)
-            *reinterpret_cast<u32x4*>(out + ((tc.m0 + r) * p.ldo + col) * 2) = v;
+    const int r0 = tid / kChunks;
+    uint8_t* obase = static_cast<uint8_t*>(p.out) + tc.m0 * p.ldo * 2;
+    const __amdgpu_buffer_rsrc_t orsrc =
+        __builtin_amdgcn_make_buffer_rsrc(obase, static_cast<short>(0), tc.rows * p.ldo * 2, 0x00020000);
+    auto store_piece = [&](int h) {
+        const int col = (GATE_UP ? tc.n * 128 : tc.n * 256) + (GATE_UP || kSplitRows ? 0 : 256 * h) + ch * 8;
+        const int rb = kSplitRows ? 128 * h : 0;
+#pragma unroll
+        for (int i = 0; i < PR / kRowsPerPass; ++i) {
+            const int r = r0 + i * kRowsPerPass;
+            const u32x4 v = *reinterpret_cast<lds_u32x4*>(smem + kStg + r * kOutRow + ch * 16);
+            const uint32_t off = col < col_lim ? static_cast<uint32_t>((rb + r) * p.ldo + col) * 2u : 0x80000000u;
+            __builtin_amdgcn_raw_buffer_store_b128(v, orsrc, off, 0, 0);
+        }
+    };
+
+    // the next tile: wave 0 claims the next one of its queue range while
+    // its output is staged (or, with that range used up, takes one from the
+    // others) and leaves the index in LDS for the other waves
+    int ticket = 0;
+    if (wv == 0 && lane == 0)
+        ticket = __hip_atomic_fetch_add(p.ctl + ctl_queue(q), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (my_piece == 0) stage_out();
+    if (wv == 0) {
+        int nx = queue_tile(qs, q, __builtin_amdgcn_readfirstlane(ticket));
+        if (nx < 0) {
+            q = (q + 1) & 7;
+            nx = take_tile(p.ctl, qs, q);
+        }
+        if (lane == 0) *reinterpret_cast<__attribute__((address_space(3))) int*>(smem + kNextWord) = nx;
     }
-    return claimed;
+    __syncthreads();
+    const int next = __builtin_amdgcn_readfirstlane(*reinterpret_cast<__attribute__((address_space(3))) int*>(smem + kNextWord));
+    if (next >= 0) {
+        tn = load_tile(p, next);
+        first_stage<GATE_UP>(p, tn, naoff, lane, wv, lds0, 0);
+    }
+    store_piece(0);
+    if (kPieces == 2) {
+        __syncthreads();
+        if (my_piece == 1) stage_out();
+        __syncthreads();
+        store_piece(1);
+    }
+    // every wave is done with the staging area (and with the next index)
+    __syncthreads();
+    if (next >= 0) first_stage<GATE_UP>(p, tn, naoff, lane, wv, lds0, 1);
+    return next;
 }
 
-// Value of wave 0 to every wave of the workgroup (through LDS word 0, which
-// no stage or output row is using at this point).
+// Value of wave 0 to every wave of the workgroup (through LDS word 0, before
+// any stage is fetched).
 __device__ __forceinline__ int broadcast_from_wave0(lds_u8* smem, int v) {
     __syncthreads();
     if (threadIdx.x == 0) *reinterpret_cast<__attribute__((address_space(3))) int*>(smem) = v;
@@ -529,35 +660,41 @@ __device__ __forceinline__ int broadcast_from_wave0(lds_u8* smem, int v) {
 }
 
 // Persistent: one workgroup per CU takes tiles from the work queues until
-// none are left; the next tile of its range is claimed while the current one
-// runs.
+// none are left; each tile claims the next one while it runs and starts
+// fetching it while its own output is stored.
 template <bool GATE_UP>
 __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmParams p) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[kLds2];
     lds_u8* lds = (lds_u8*)(smem);  // the array lives in LDS: an address-space cast
-    const bool w0 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) == 0;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     Queues qs;
     qs.total = p.ctl[0];
     qs.per = (qs.total + 7) >> 3;
     int q = blockIdx.x & 7;
     int L = -1;
-    if (w0) L = take_tile(p.ctl, qs, q);
-    L = broadcast_from_wave0(lds, L);
-    while (L >= 0) {
-        const Tile2 tc = load_tile(p, L);
-        int32_t* ctr = p.ctl + ctl_queue(q);
-        int claim;
-        if (tc.tail) claim = tile_pipeline<GATE_UP, 128, 512>(p, tc, lds, ctr);
-        else claim = tile_pipeline<GATE_UP, 256, 256>(p, tc, lds, ctr);
-        int next = -1;
-        if (w0) {
-            next = queue_tile(qs, q, __builtin_amdgcn_readfirstlane(claim));
-            if (next < 0) {
-                q = (q + 1) & 7;
-                next = take_tile(p.ctl, qs, q);
-            }
-        }
-        L = broadcast_from_wave0(lds, next);
+    if (wv == 0) L = take_tile(p.ctl, qs, q);
+    L = __builtin_amdgcn_readfirstlane(broadcast_from_wave0(lds, L));
+    if (L < 0) return;
+    Tile2 tc = load_tile(p, L);
+    uint32_t aoff[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+    {
+        const int lane = fresh_lane();
+        const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
+        first_stage<GATE_UP>(p, tc, aoff, lane, wv, lds0, 0);
+        first_stage<GATE_UP>(p, tc, aoff, lane, wv, lds0, 1);
+    }
+    bool after_tile = false;
+    for (;;) {
+        Tile2 tn;
+        uint32_t naoff[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+        int next;
+        if (tc.tail) next = tile_pipeline<GATE_UP, 128, 512>(p, tc, aoff, lds, wv, after_tile, qs, q, tn, naoff);
+        else next = tile_pipeline<GATE_UP, 256, 256>(p, tc, aoff, lds, wv, after_tile, qs, q, tn, naoff);
+        if (next < 0) break;
+        tc = tn;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) aoff[i] = naoff[i];
+        after_tile = true;
     }
 }
 
