@@ -112,33 +112,73 @@ __device__ __forceinline__ bool skinny_locate(const SkinnyParams& p, int64_t L, 
     return true;
 }
 
-// The k loop of one wave over RB row blocks (nb of them valid, uniform) with
-// U 32-wide steps of loads issued before their MFMAs.
-template <bool GATE_UP, int RB, int U>
-__device__ __forceinline__ void skinny_loop(const uint16_t* const (&ap)[4], const uint16_t* bp, const uint16_t* cp,
-                                            int S, int nb, f32x4 (&acc)[4], f32x4 (&acc_u)[4]) {
-    for (int s0 = 0; s0 < S; s0 += U) {
-        u32x4 a[U][RB], b[U], c[U];
+// The k loop of one wave over RB row blocks (nb of them valid, uniform):
+// batches of U 32-wide steps, double-buffered, so the loads of the next
+// batch are in flight while the MFMAs of the current one run; the last
+// S % U steps follow on their own.  Operand pointers advance per batch and
+// each load is an immediate offset from them.  The MFMAs take the steps in
+// ascending order, as in a plain loop.
+template <int RB, int U>
+__device__ __forceinline__ void skinny_loop(const uint16_t* const (&ap)[4], const uint16_t* bp, int S, int nb,
+                                            f32x4 (&acc)[4]) {
+    const uint16_t* aq[RB];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) aq[r] = ap[r];
+    const uint16_t* bq = bp;
+    u32x4 a0[U][RB], b0[U], a1[U][RB], b1[U];
+    auto load = [&](u32x4 (&a)[U][RB], u32x4 (&b)[U]) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int s = s0 + u < S ? s0 + u : S - 1;
-            b[u] = *reinterpret_cast<const u32x4*>(bp + 32 * s);
-            if (GATE_UP) c[u] = *reinterpret_cast<const u32x4*>(cp + 32 * s);
+            b[u] = *reinterpret_cast<const u32x4*>(bq + 32 * u);
 #pragma unroll
-            for (int r = 0; r < RB; ++r)
-                if (r < nb) a[u][r] = *reinterpret_cast<const u32x4*>(ap[r] + 32 * s);
+            for (int r = 0; r < RB; ++r) a[u][r] = *reinterpret_cast<const u32x4*>(aq[r] + 32 * u);
         }
-        __builtin_amdgcn_sched_barrier(0);  // every load of the batch is in flight before the first MFMA
+        bq += 32 * U;
+#pragma unroll
+        for (int r = 0; r < RB; ++r) aq[r] += 32 * U;
+    };
+    auto mma = [&](const u32x4 (&a)[U][RB], const u32x4 (&b)[U], int n) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            if (s0 + u >= S) break;  // uniform
+            if (u >= n) break;  // uniform
 #pragma unroll
             for (int r = 0; r < RB; ++r) {
                 if (r >= nb) break;  // uniform
                 acc[r] = mfma_bf16(b[u], a[u][r], acc[r]);
-                if (GATE_UP) acc_u[r] = mfma_bf16(c[u], a[u][r], acc_u[r]);
             }
         }
+    };
+    const int full = S / U;
+    if (full > 0) {
+        load(a0, b0);  // batch 0
+        int i = 0;     // batch i is in a0
+        for (; i + 2 < full; i += 2) {
+            load(a1, b1);
+            __builtin_amdgcn_sched_barrier(0);
+            mma(a0, b0, U);
+            load(a0, b0);
+            __builtin_amdgcn_sched_barrier(0);
+            mma(a1, b1, U);
+        }
+        if (i + 1 < full) {
+            load(a1, b1);
+            __builtin_amdgcn_sched_barrier(0);
+            mma(a0, b0, U);
+            mma(a1, b1, U);
+        } else {
+            mma(a0, b0, U);
+        }
+    }
+    const int rem = S - full * U;
+    if (rem > 0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (u >= rem) break;  // uniform
+            b0[u] = *reinterpret_cast<const u32x4*>(bq + 32 * u);
+#pragma unroll
+            for (int r = 0; r < RB; ++r) a0[u][r] = *reinterpret_cast<const u32x4*>(aq[r] + 32 * u);
+        }
+        mma(a0, b0, rem);
     }
 }
 
@@ -183,8 +223,8 @@ __global__ __launch_bounds__(GATE_UP ? 128 : 64) void skinny_kernel(SkinnyParams
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc[r] = acc_u[r] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int S = p.Kd / 32;
-    if (nb == 1) skinny_loop<false, 1, 8>(ap, bp, bp, S, nb, acc, acc_u);
-    else skinny_loop<false, 4, 4>(ap, bp, bp, S, nb, acc, acc_u);
+    if (nb == 1) skinny_loop<1, 8>(ap, bp, S, nb, acc);
+    else skinny_loop<4, 4>(ap, bp, S, nb, acc);
     if (GATE_UP) {
         __shared__ f32x4 up_acc[4][64];
         if (half == 1) {
