@@ -45,9 +45,17 @@ PermutePlan permute_plan(int64_t P, int E) {
     return pl;
 }
 
+static_assert(kPermWaves == 4, "the count pass stores a block's wave counts as one int4 per expert");
+
+// Workspace of the multi-block path, in int32: block histogram [E][blocks],
+// block bases [E][blocks], then (from a 16-byte boundary) the wave
+// histograms [E][blocks][kPermWaves].
+static int64_t wave_hist_at(int64_t eb) { return (2 * eb + 3) & ~static_cast<int64_t>(3); }
+
 size_t permute_ws_bytes(int64_t P, int E) {
     const PermutePlan pl = permute_plan(P, E);
-    return 2 * sizeof(int32_t) * static_cast<size_t>(E) * pl.blocks;
+    const int64_t eb = static_cast<int64_t>(E) * pl.blocks;
+    return sizeof(int32_t) * static_cast<size_t>(wave_hist_at(eb) + kPermWaves * eb);
 }
 
 // Up to this many blocks the scatter pass sums the block counts itself (one
@@ -59,7 +67,7 @@ constexpr int kScanInScatter = 64;
 
 __global__ __launch_bounds__(256) void permute_count_kernel(
     const int32_t* __restrict__ ids, int64_t P, int E, int ppb, int nblocks, int id_bits,
-    int32_t* __restrict__ block_hist) {
+    int32_t* __restrict__ block_hist, int32_t* __restrict__ wave_hist) {
     __shared__ int hist[kPermWaves][kMaxExperts];
     const int tid = threadIdx.x;
     const int wv = tid >> 6;
@@ -69,8 +77,11 @@ __global__ __launch_bounds__(256) void permute_count_kernel(
     const int per_wave = ppb / kPermWaves;
     wave_histogram(ids, P, E, base + wv * per_wave, base + (wv + 1) * per_wave, id_bits, hist[wv]);
     __syncthreads();
-    for (int e = tid; e < E; e += 256)
-        block_hist[static_cast<int64_t>(e) * nblocks + blockIdx.x] = hist[0][e] + hist[1][e] + hist[2][e] + hist[3][e];
+    for (int e = tid; e < E; e += 256) {
+        const int64_t i = static_cast<int64_t>(e) * nblocks + blockIdx.x;
+        block_hist[i] = hist[0][e] + hist[1][e] + hist[2][e] + hist[3][e];
+        reinterpret_cast<int4*>(wave_hist)[i] = int4{hist[0][e], hist[1][e], hist[2][e], hist[3][e]};
+    }
 }
 
 // Exclusive scan of one expert's block counts (workgroup e scans row e of
@@ -139,11 +150,13 @@ __device__ __forceinline__ void scan_counts(const int* counts, int E, int* offs,
 
 // block_base == nullptr: the block sums its counts from block_hist (and
 // block 0 stores the expert counts); else block_base and counts come from
-// permute_scan_kernel.
+// permute_scan_kernel.  The per-wave counts of the block come from the count
+// pass (wave_hist), so the ids are walked once here.
 __global__ __launch_bounds__(256) void permute_scatter_kernel(
     const int32_t* __restrict__ ids, int64_t P, int K, int E, int ppb, int nblocks, int id_bits,
-    const int32_t* __restrict__ block_hist, const int32_t* __restrict__ block_base, int32_t* __restrict__ counts,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ perm_token, int32_t* __restrict__ inv_pos) {
+    const int32_t* __restrict__ block_hist, const int32_t* __restrict__ block_base,
+    const int32_t* __restrict__ wave_hist, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ perm_token, int32_t* __restrict__ inv_pos) {
     __shared__ int hist[kPermWaves][kMaxExperts];
     __shared__ int offs[kMaxExperts + 1];
     __shared__ int cnt[kMaxExperts];    // pairs of each expert
@@ -151,7 +164,13 @@ __global__ __launch_bounds__(256) void permute_scatter_kernel(
     __shared__ int part[256];
     const int tid = threadIdx.x;
     const int wv = tid >> 6;
-    for (int i = tid; i < kPermWaves * E; i += 256) hist[i / E][i % E] = 0;
+    for (int e = tid; e < E; e += 256) {
+        const int4 h = reinterpret_cast<const int4*>(wave_hist)[static_cast<int64_t>(e) * nblocks + blockIdx.x];
+        hist[0][e] = h.x;
+        hist[1][e] = h.y;
+        hist[2][e] = h.z;
+        hist[3][e] = h.w;
+    }
     if (block_base == nullptr) {
         // row e of block_hist: expert e's pairs per block, in block order
         for (int e = tid; e < E; e += 256) {
@@ -181,8 +200,6 @@ __global__ __launch_bounds__(256) void permute_scatter_kernel(
     const int per_wave = ppb / kPermWaves;
     const int64_t w_begin = base + wv * per_wave;
     const int64_t w_end = w_begin + per_wave;
-    wave_histogram(ids, P, E, w_begin, w_end, id_bits, hist[wv]);
-    __syncthreads();
     // per-wave base rows: block base of the expert plus earlier waves' pairs
     for (int e = tid; e < E; e += 256) {
         int run = offs[e] + before[e];
@@ -224,21 +241,23 @@ hipError_t launch_permute(const int32_t* ids, int64_t T, int K, int E, int32_t* 
                                                      perm_token, inv_pos);
         return hipGetLastError();
     }
+    const int64_t eb = static_cast<int64_t>(E) * pl.blocks;
     int32_t* block_hist = ws_i32;
     int32_t* block_base = nullptr;
+    int32_t* wave_hist = ws_i32 + wave_hist_at(eb);  // 16-byte aligned, as the workspace is
     permute_count_kernel<<<pl.blocks, 256, 0, stream>>>(ids, P, E, pl.pairs_per_block, pl.blocks, pl.id_bits,
-                                                       block_hist);
+                                                       block_hist, wave_hist);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     if (pl.blocks > kScanInScatter) {
-        block_base = ws_i32 + static_cast<int64_t>(E) * pl.blocks;
+        block_base = ws_i32 + eb;
         permute_scan_kernel<<<E, 256, 0, stream>>>(block_hist, pl.blocks, block_base, counts);
         err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
     permute_scatter_kernel<<<pl.blocks, 256, 0, stream>>>(ids, P, K, E, pl.pairs_per_block, pl.blocks,
-                                                         pl.id_bits, block_hist, block_base, counts, offsets,
-                                                         perm_token, inv_pos);
+                                                         pl.id_bits, block_hist, block_base, wave_hist, counts,
+                                                         offsets, perm_token, inv_pos);
     return hipGetLastError();
 }
 

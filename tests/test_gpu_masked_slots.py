@@ -22,7 +22,8 @@ from tests.gpu_util import to_dev, to_host
 pytestmark = pytest.mark.gpu
 
 E, K, D = 64, 6, 512
-T_BIG = 16448    # above the combine kernel switch (16385 tokens)
+T_BIG = 16449    # above the combine kernel switch (16385 tokens); odd, so the
+                 # two-token workgroups of the large-batch kernel end on a lone token
 T_SMALL = 100    # below it; the first T_SMALL tokens of the big batch
 
 
