@@ -47,9 +47,10 @@ PermutePlan permute_plan(int64_t P, int E) {
 
 static_assert(kPermWaves == 4, "the count pass stores a block's wave counts as one int4 per expert");
 
-// Workspace of the multi-block path, in int32: block histogram [E][blocks],
-// block bases [E][blocks], then (from a 16-byte boundary) the wave
-// histograms [E][blocks][kPermWaves].
+// Workspace of the multi-block path, in int32: block histogram [E][blocks]
+// (an expert's counts contiguous, for the scan), block bases [E][blocks], then
+// (from a 16-byte boundary) the wave histograms [blocks][E][kPermWaves] (a
+// block's counts contiguous, for its scatter pass).
 static int64_t wave_hist_at(int64_t eb) { return (2 * eb + 3) & ~static_cast<int64_t>(3); }
 
 size_t permute_ws_bytes(int64_t P, int E) {
@@ -78,9 +79,9 @@ __global__ __launch_bounds__(256) void permute_count_kernel(
     wave_histogram(ids, P, E, base + wv * per_wave, base + (wv + 1) * per_wave, id_bits, hist[wv]);
     __syncthreads();
     for (int e = tid; e < E; e += 256) {
-        const int64_t i = static_cast<int64_t>(e) * nblocks + blockIdx.x;
-        block_hist[i] = hist[0][e] + hist[1][e] + hist[2][e] + hist[3][e];
-        reinterpret_cast<int4*>(wave_hist)[i] = int4{hist[0][e], hist[1][e], hist[2][e], hist[3][e]};
+        block_hist[static_cast<int64_t>(e) * nblocks + blockIdx.x] = hist[0][e] + hist[1][e] + hist[2][e] + hist[3][e];
+        reinterpret_cast<int4*>(wave_hist)[static_cast<int64_t>(blockIdx.x) * E + e] =
+            int4{hist[0][e], hist[1][e], hist[2][e], hist[3][e]};
     }
 }
 
@@ -165,7 +166,7 @@ __global__ __launch_bounds__(256) void permute_scatter_kernel(
     const int tid = threadIdx.x;
     const int wv = tid >> 6;
     for (int e = tid; e < E; e += 256) {
-        const int4 h = reinterpret_cast<const int4*>(wave_hist)[static_cast<int64_t>(e) * nblocks + blockIdx.x];
+        const int4 h = reinterpret_cast<const int4*>(wave_hist)[static_cast<int64_t>(blockIdx.x) * E + e];
         hist[0][e] = h.x;
         hist[1][e] = h.y;
         hist[2][e] = h.z;

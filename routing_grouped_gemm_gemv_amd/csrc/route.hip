@@ -486,7 +486,6 @@ __device__ __forceinline__ void write_picks16(const int (&my_e)[P], const double
                                               float* __restrict__ w_out, lds_u8* scr, int* ids_lds = nullptr) {
     const int lane = lane_id();
     const int j = lane & 15;
-    const int rbase = lane & 48;
     const int row = lane >> 4;
     int rank[P];
 #pragma unroll
