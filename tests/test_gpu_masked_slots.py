@@ -108,3 +108,35 @@ def test_masked_slots_across_the_combine_switch(combine_mode, with_shared):
     assert np.array_equal(sbf, bbf[:T_SMALL])
     print(f"[masked-slots] combine={combine_mode} shared={with_shared}: T={T_SMALL} and T={T_BIG} "
           f"bit-exact against the oracle and equal on the common tokens", flush=True)
+
+
+@pytest.mark.parametrize("k_slots,dim", [(1, 4608), (2, 256), (3, 1536), (8, 1536)])
+def test_large_batch_combine_slot_counts(k_slots, dim):
+    """The large-batch bf16 combine at slot counts and widths the layer
+    workloads do not reach: K rounded up to 1, 2, 4 and 8 slots, and hidden
+    sizes that end inside a thread's four-chunk round (256, 1536) or start a
+    second round (4608); an odd batch, single empty slots and fully masked
+    tokens; bit for bit against the oracle's float32 fold."""
+    from routing_grouped_gemm_gemv_amd import Shape
+    from routing_grouped_gemm_gemv_amd import binding as B
+    T = 16391  # above the switch (16385 tokens), odd
+    rng = np.random.default_rng(1000 + 10 * k_slots + dim)
+    P = T * k_slots
+    inv = rng.permutation(P).astype(np.int32).reshape(T, k_slots)
+    inv[rng.random((T, k_slots)) < 0.05] = -1
+    inv[::997] = -1
+    vals = rng.standard_normal((P, dim), dtype=np.float32).view(np.uint32)
+    y = ((vals + 0x7FFF + ((vals >> 16) & 1)) >> 16).astype(np.uint16)
+    w = rng.uniform(-2.0, 2.0, (T, k_slots)).astype(np.float32)
+    sv = rng.standard_normal((T, dim), dtype=np.float32).view(np.uint32)
+    sh = ((sv + 0x7FFF + ((sv >> 16) & 1)) >> 16).astype(np.uint16)
+    shape = Shape(T=T, D=dim, E=64, K=k_slots, I=64, dtype="bf16")
+    d_y, d_inv, d_w, d_sh = to_dev(y), to_dev(inv), to_dev(w), to_dev(sh)
+    out32 = torch.empty(T, dim, dtype=torch.float32, device="cuda")
+    outbf = torch.empty(T, dim, dtype=torch.bfloat16, device="cuda")
+    B.moe_combine(shape, d_y, d_inv, d_w, d_sh, out32)
+    B.moe_combine(shape, d_y, d_inv, d_w, d_sh, outbf)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(out32).view(np.uint32), oracle.combine_fp32(y, inv, w, sh, out="f32").view(np.uint32))
+    assert np.array_equal(to_host(outbf), oracle.combine_fp32(y, inv, w, sh, out="bf16"))
+    print(f"[combine-slots] K={k_slots} D={dim} T={T}: bit-exact against the oracle", flush=True)
