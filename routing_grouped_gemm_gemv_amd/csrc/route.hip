@@ -21,6 +21,8 @@
 #include "kernels.hpp"
 #include "permute_block.hpp"
 
+#include <type_traits>
+
 namespace moe {
 
 // ---------------------------------------------------------------------------
@@ -1182,7 +1184,8 @@ struct RouteTile {
 
 // Top-k of the TBP tokens starting at token tp whose float64 logits are in
 // lgs ([TBP][EMAX]); scr: the candidate slots of the screened selection.
-template <typename RT, bool GRP>
+// LAST: no other pass's logits are held in registers any more.
+template <typename RT, bool GRP, bool LAST>
 __device__ __forceinline__ void route_topk_pass(const __attribute__((address_space(3))) double* lgs, lds_u8* scr_base,
                                                 int64_t tp, int64_t T, int E, int K, int score, int renorm,
                                                 double route_scale, const float* __restrict__ bias,
@@ -1193,9 +1196,10 @@ __device__ __forceinline__ void route_topk_pass(const __attribute__((address_spa
     const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
     const int64_t t0 = tp;
     // P tokens per row of sixteen lanes at a time: two where registers allow
-    // (the 128-token tile holds the other pass's logits in registers meanwhile)
+    // (during the first pass of a 128-token tile the other pass's logits are
+    // still held in registers; its last pass has them free)
     constexpr int EPL16 = RT::EMAX / 16;
-    constexpr int P = (RT::TB > RT::TBP || EPL16 > 16) ? 1 : 2;
+    constexpr int P = ((RT::TB > RT::TBP && !LAST) || EPL16 > 16) ? 1 : 2;
     static_assert(RT::TBP % (16 * P) == 0, "tokens per wave pass");
     if constexpr (GRP) {  // group-limited select: one token per row at a time
         lds_u8* scr = scr_base + wv * (P * kRowScr + kDumpScr);
@@ -1386,8 +1390,10 @@ __global__ __launch_bounds__(256) void route_fused_bf16_kernel(
     __attribute__((address_space(3))) double* lgs = (__attribute__((address_space(3))) double*)(smem);
     float bv[RT::EMAX / 16];  // (loaded per token block instead past 256 experts)
     load_bias16<RT::EMAX / 16>(RT::EMAX > 256 ? nullptr : bias, E, bv);
-#pragma unroll
-    for (int h = 0; h < RT::TB / RT::TBP; ++h) {
+    constexpr int NP = RT::TB / RT::TBP;  // passes
+    static_assert(NP == 1 || NP == 2, "one or two top-k passes per tile");
+    auto pass = [&](auto hc) {
+        constexpr int h = decltype(hc)::value;
         if (h > 0) __syncthreads();  // the previous pass is done with its logits
 #pragma unroll
         for (int a = 0; a < TBB; ++a) {
@@ -1410,11 +1416,13 @@ __global__ __launch_bounds__(256) void route_fused_bf16_kernel(
                 const int r = c / E, e = c - r * E;
                 logits64[(tp + r) * E + e] = lgs[r * RT::EMAX + e];
             }
-            continue;
+        } else {
+            route_topk_pass<RT, GRP, h == NP - 1>(lgs, smem + RT::LOGB, tp, T, E, K, score, renorm, route_scale, bias,
+                                                  bv, n_group, topk_group, mask, logits_out, ids_out, w_out);
         }
-        route_topk_pass<RT, GRP>(lgs, smem + RT::LOGB, tp, T, E, K, score, renorm, route_scale, bias, bv, n_group,
-                                 topk_group, mask, logits_out, ids_out, w_out);
-    }
+    };
+    pass(std::integral_constant<int, 0>{});
+    if constexpr (NP > 1) pass(std::integral_constant<int, 1>{});
 }
 
 // ---------------------------------------------------------------------------
