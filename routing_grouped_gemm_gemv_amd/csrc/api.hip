@@ -388,6 +388,19 @@ static moe_status forward_impl(const moe_shape* shape, const moe_weights* weight
                              "permute launch")) != MOE_OK)
             return st;
     }
+    if (T == 1 && shape->dtype == 0 && shape->combine == MOE_COMBINE_F32_FOLD &&
+        moe::decode_combine_fits(T, shape->K, shape->Is > 0) && moe::experts_use_skinny(shape->K, shape->E, 0) &&
+        (shape->Is == 0 || shared_with_routed(shape))) {
+        // one token: the experts' down projections and the combine in one launch
+        // (the same bits as the launches below)
+        if ((st = hip_status(moe::launch_experts_decode_combine(
+                                 x, perm, offsets, shape->E, shape->K, shape->D, shape->I, weights->gate_up,
+                                 weights->down, y, exw, shape->Is, weights->gate_up_shared, weights->down_shared, sh,
+                                 base + L.shared_act, ids, inv, tw, out_dtype == MOE_F32 ? 1 : 0, out, stream),
+                             "experts + combine launch")) != MOE_OK)
+            return st;
+        return ok();
+    }
     if (shared_with_routed(shape)) {
         if ((st = hip_status(moe::launch_experts_skinny_pair(
                                  x, perm, offsets, shape->E, T * shape->K, shape->D, shape->I, weights->gate_up,

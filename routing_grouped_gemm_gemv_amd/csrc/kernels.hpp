@@ -66,6 +66,14 @@ hipError_t launch_experts(const void* x, int64_t x_rows, const int32_t* perm_tok
 // 16-column weight slice, the same bits as launch_experts; bf16 only, the
 // same workspace
 bool experts_use_skinny(int64_t rows_max, int G, int dtype);
+// one token whose K picks (and shared expert) fit one workgroup of the fused
+// down + combine kernel
+bool decode_combine_fits(int64_t T, int K, bool shared);
+hipError_t launch_experts_decode_combine(const void* x, const int32_t* perm_token, const int32_t* offsets, int G,
+                                         int K, int D, int I, const void* gate_up, const void* down, void* y,
+                                         void* ws, int Is, const void* gate_up_s, const void* down_s, void* y_s,
+                                         void* act_s, const int32_t* ids, const int32_t* inv_pos, const float* w,
+                                         int out_f32, void* out, hipStream_t stream);
 hipError_t launch_experts_skinny(const void* x, const int32_t* perm_token, const int32_t* offsets, int G,
                                  int64_t rows_max, int D, int I, const void* gate_up, const void* down, void* y,
                                  void* ws, hipStream_t stream);

@@ -252,6 +252,82 @@ __global__ __launch_bounds__(GATE_UP ? 128 : 64) void skinny_kernel(SkinnyParams
     }
 }
 
+// One token: the down projections of its K routed experts (and of the
+// shared expert) and the combine, in one launch.  Workgroup n takes output
+// columns 16 n .. 16 n + 15; its wave j < K computes pick j's 16 columns
+// exactly as skinny_kernel<false> does (its group holds one row, so every
+// MFMA row is that row; the same chain over I in ascending 32-wide steps),
+// stores them to y as bf16 and hands them to LDS; wave K does the shared
+// expert's.  Wave 0 then folds them as the combine does: from +0, in pick
+// order (ascending expert id) fl32(w_j * f32(y_j)), then f32(shared), no
+// fused multiply-add, one rounding to bf16 (or the float32 sum); a token
+// with no pick gives +0.  The same bits as the down launch followed by the
+// combine, one launch and one pass over y fewer.
+constexpr int kDecodeWaves = 8;  // at most two waves per SIMD: 256 registers each
+
+__global__ __launch_bounds__(64 * kDecodeWaves) void skinny_down_combine_kernel(
+    SkinnyParams rp, SkinnyParams sp, int K, const int32_t* __restrict__ ids, const int32_t* __restrict__ inv_pos,
+    const float* __restrict__ w, int out_f32, void* __restrict__ out) {
+    __shared__ float red[kDecodeWaves][16];
+    const int lane = threadIdx.x & 63;
+    const int j = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+    const int slice = blockIdx.x;
+    const bool shared_wave = j == K;
+    const SkinnyParams& p = shared_wave ? sp : rp;
+    int row = 0;   // the pick's row of the activations and of y
+    int g = 0;     // its expert
+    bool live = true;
+    if (!shared_wave) {
+        row = inv_pos[j];
+        g = ids[j];
+        live = row >= 0 && g >= 0;
+    }
+    if (live) {
+        const int kq = 8 * (lane >> 4);
+        const uint16_t* ap[4];
+        ap[0] = p.a + static_cast<int64_t>(row) * p.Kd + kq;
+        ap[1] = ap[2] = ap[3] = ap[0];
+        const int n = 16 * slice + (lane & 15);
+        const uint16_t* bp = p.w + static_cast<int64_t>(g) * p.w_group_stride + static_cast<int64_t>(n) * p.Kd + kq;
+        f32x4 acc[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+        skinny_loop<1, 8>(ap, bp, p.Kd / 32, 1, acc);
+        // lanes 0, 16, 32, 48 hold the row's columns 16 slice + 4 (lane / 16) + i
+        if ((lane & 15) == 0) {
+            const int c = 4 * (lane >> 4);
+            uint16_t b[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                b[i] = f32_to_bf16(acc[0][i]);
+                red[j][c + i] = bf16_to_f32(b[i]);
+            }
+            const uint32_t w0 = static_cast<uint32_t>(b[0]) | (static_cast<uint32_t>(b[1]) << 16);
+            const uint32_t w1 = static_cast<uint32_t>(b[2]) | (static_cast<uint32_t>(b[3]) << 16);
+            *reinterpret_cast<u32x2*>(p.out + static_cast<int64_t>(row) * p.N + 16 * slice + c) = u32x2{w0, w1};
+        }
+    }
+    __syncthreads();
+    if (j == 0 && lane < 16) {
+#pragma clang fp contract(off)
+        const int col = 16 * slice + lane;
+        float acc = 0.0f;
+        bool kept = false;
+        for (int q = 0; q < K; ++q) {
+            if (inv_pos[q] < 0 || ids[q] < 0) continue;
+            kept = true;
+            const float prod = w[q] * red[q][lane];
+            acc = acc + prod;
+        }
+        if (kept && sp.w != nullptr) acc = acc + red[K][lane];
+        if (!kept) acc = 0.0f;
+        if (out_f32) static_cast<float*>(out)[col] = acc;
+        else static_cast<uint16_t*>(out)[col] = f32_to_bf16(acc);
+    }
+}
+
+bool decode_combine_fits(int64_t T, int K, bool shared) { return T == 1 && K + (shared ? 1 : 0) <= kDecodeWaves; }
+
 bool experts_use_skinny(int64_t rows_max, int G, int dtype) {
     // bf16 operands and decode-sized batches: at most 4 rows per expert on
     // average (measured crossover with the tiled kernels on the Qwen3-30B-
@@ -334,6 +410,37 @@ hipError_t launch_experts_skinny_pair(const void* x, const int32_t* perm_token, 
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     skinny_kernel<false><<<static_cast<unsigned>(n2), 64, 0, stream>>>(a.dn, b.dn, a2);
+    return hipGetLastError();
+}
+
+// One token (decode_combine_fits): the gate_up launch of launch_experts_skinny
+// or launch_experts_skinny_pair, then skinny_down_combine_kernel in place of
+// the down launch and the combine.  y, y_s and act_s as there; ids, inv_pos
+// and w the pick's ids, rows and weights; out [D] bf16 or float32.
+hipError_t launch_experts_decode_combine(const void* x, const int32_t* perm_token, const int32_t* offsets, int G,
+                                         int K, int D, int I, const void* gate_up, const void* down, void* y,
+                                         void* ws, int Is, const void* gate_up_s, const void* down_s, void* y_s,
+                                         void* act_s, const int32_t* ids, const int32_t* inv_pos, const float* w,
+                                         int out_f32, void* out, hipStream_t stream) {
+    const SkinnyProblem a = skinny_problem(x, perm_token, offsets, G, K, D, I, gate_up, down, y,
+                                           skinny_act(ws, K, G, D, I));
+    SkinnyParams sdn{};  // no shared expert: w stays null
+    if (Is > 0) {
+        const SkinnyProblem b = skinny_problem(x, nullptr, nullptr, 1, 1, D, Is, gate_up_s, down_s, y_s,
+                                               static_cast<uint16_t*>(act_s));
+        const int64_t a1 = a.units * (I / 16);
+        const int64_t n1 = a1 + b.units * (Is / 16);
+        skinny_kernel<true><<<static_cast<unsigned>(n1), 128, 0, stream>>>(a.gu, b.gu, a1);
+        sdn = b.dn;
+    } else {
+        const int64_t b1 = a.units * (I / 16);
+        skinny_kernel<true><<<static_cast<unsigned>(b1), 128, 0, stream>>>(a.gu, a.gu, b1);
+    }
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const int waves = K + (Is > 0 ? 1 : 0);
+    skinny_down_combine_kernel<<<static_cast<unsigned>(D / 16), 64 * waves, 0, stream>>>(a.dn, sdn, K, ids, inv_pos,
+                                                                                         w, out_f32, out);
     return hipGetLastError();
 }
 
