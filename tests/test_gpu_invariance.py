@@ -146,3 +146,33 @@ def test_router_tiles_give_the_same_bits(name):
         res.append((lg, ids, w))
     for a, b in zip(res[0], res[1]):
         assert torch.equal(a[: T - 1].view(torch.int32), b.view(torch.int32))
+
+
+@pytest.mark.parametrize("name", ["q30", "dsv4"])
+def test_single_token_down_and_combine_launch(name):
+    """One token runs its experts' down projections and the combine in one
+    launch; a batch of three runs them as separate launches.  The first token
+    must give the same float32 output, the same expert outputs in the trace
+    (y at its picks' rows, and the shared expert's row), and a masked single
+    token a zero row with no picks."""
+    cfg = get_config(name, T=3)
+    inp = make_inputs(cfg)
+    layer = make_layer(inp)
+    x = to_dev(inp.x)
+    o3, t3 = layer.forward(x, out_dtype=torch.float32, trace=True)
+    o1, t1 = layer.forward(x[:1].contiguous(), out_dtype=torch.float32, trace=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(o1).view(np.uint32), to_host(o3)[:1].view(np.uint32))
+    i1, i3 = to_host(t1["inv_pos"]), to_host(t3["inv_pos"])
+    y1, y3 = to_host(t1["y"]), to_host(t3["y"])
+    assert np.array_equal(to_host(t1["topk_ids"])[0], to_host(t3["topk_ids"])[0])
+    for j in range(cfg.K):
+        assert np.array_equal(y1[i1[0, j]], y3[i3[0, j]]), j
+    if cfg.Is:
+        assert np.array_equal(to_host(t1["shared_out"])[0], to_host(t3["shared_out"])[0])
+    m = torch.zeros(1, dtype=torch.uint8, device="cuda")
+    om, tm = layer.forward(x[:1].contiguous(), mask=m, trace=True)
+    torch.cuda.synchronize()
+    assert np.all(to_host(om) == 0) and np.all(to_host(tm["topk_ids"]) == -1)
+    print(f"[decode-combine] {name}: T = 1 float32 output and trace equal to the 3-token batch's; masked row zero",
+          flush=True)
