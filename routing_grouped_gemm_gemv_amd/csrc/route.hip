@@ -1439,12 +1439,14 @@ constexpr int kRdU = 8;
 // float32 MFMA chain from zero), the chunks meet in LDS, and each output adds
 // them in float64 in chunk order.  A decode-sized batch has few blocks, so a
 // wave per block walking the chunks one after another would wait for D/256
-// dependent memory round trips; here there are D/2048.
-constexpr int kSplitW = 8;
-
-__global__ __launch_bounds__(64 * kSplitW) void router_logits_split_kernel(const uint16_t* __restrict__ x,
-                                                                        const uint16_t* __restrict__ w, int64_t T,
-                                                                        int D, int E, double* __restrict__ out) {
+// dependent memory round trips; here there are D/(256 SW): SW = 16 waves when
+// D > 2048 (one round for the 4096-wide layers), else 8.  Which wave computes
+// a chunk changes no bit.
+template <int SW>
+__global__ __launch_bounds__(64 * SW) void router_logits_split_kernel(const uint16_t* __restrict__ x,
+                                                                   const uint16_t* __restrict__ w, int64_t T, int D,
+                                                                   int E, double* __restrict__ out) {
+    constexpr int kSplitW = SW;
     __shared__ __attribute__((aligned(16))) float part[kSplitW][64][4];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -1550,8 +1552,10 @@ hipError_t launch_router_logits(const void* x, const void* router, int64_t T, in
     }
     if (route_small(T, E, dtype)) {
         dim3 grid(static_cast<unsigned>((T + 15) / 16), static_cast<unsigned>((E + 15) / 16));
-        router_logits_split_kernel<<<grid, 64 * kSplitW, 0, stream>>>(
-            static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(router), T, D, E, logits64);
+        const uint16_t* xb = static_cast<const uint16_t*>(x);
+        const uint16_t* wb = static_cast<const uint16_t*>(router);
+        if (D > 2048) router_logits_split_kernel<16><<<grid, 64 * 16, 0, stream>>>(xb, wb, T, D, E, logits64);
+        else router_logits_split_kernel<8><<<grid, 64 * 8, 0, stream>>>(xb, wb, T, D, E, logits64);
         return hipGetLastError();
     }
     if (dtype == 0) {
