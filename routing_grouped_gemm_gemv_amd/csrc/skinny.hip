@@ -263,12 +263,16 @@ __global__ __launch_bounds__(GATE_UP ? 128 : 64) void skinny_kernel(SkinnyParams
 // fused multiply-add, one rounding to bf16 (or the float32 sum); a token
 // with no pick gives +0.  The same bits as the down launch followed by the
 // combine, one launch and one pass over y fewer.
-constexpr int kDecodeWaves = 8;  // at most two waves per SIMD: 256 registers each
+// NW waves: 8 (two per SIMD, 256 registers each, k batches of U = 8 steps) or
+// 16 (four per SIMD, 128 registers, batches of U = 4 steps: the same MFMA
+// chain, k ascending).
+constexpr int kDecodeWaves = 16;
 
-__global__ __launch_bounds__(64 * kDecodeWaves) void skinny_down_combine_kernel(
+template <int NW, int U>
+__global__ __launch_bounds__(64 * NW) void skinny_down_combine_kernel(
     SkinnyParams rp, SkinnyParams sp, int K, const int32_t* __restrict__ ids, const int32_t* __restrict__ inv_pos,
     const float* __restrict__ w, int out_f32, void* __restrict__ out) {
-    __shared__ float red[kDecodeWaves][16];
+    __shared__ float red[NW][16];
     const int lane = threadIdx.x & 63;
     const int j = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
     const int slice = blockIdx.x;
@@ -292,7 +296,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void skinny_down_combine_kernel(
         f32x4 acc[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
-        skinny_loop<1, 8>(ap, bp, p.Kd / 32, 1, acc);
+        skinny_loop<1, U>(ap, bp, p.Kd / 32, 1, acc);
         // lanes 0, 16, 32, 48 hold the row's columns 16 slice + 4 (lane / 16) + i
         if ((lane & 15) == 0) {
             const int c = 4 * (lane >> 4);
@@ -439,8 +443,11 @@ hipError_t launch_experts_decode_combine(const void* x, const int32_t* perm_toke
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int waves = K + (Is > 0 ? 1 : 0);
-    skinny_down_combine_kernel<<<static_cast<unsigned>(D / 16), 64 * waves, 0, stream>>>(a.dn, sdn, K, ids, inv_pos,
-                                                                                         w, out_f32, out);
+    const unsigned grid = static_cast<unsigned>(D / 16);
+    if (waves <= 8)
+        skinny_down_combine_kernel<8, 8><<<grid, 64 * waves, 0, stream>>>(a.dn, sdn, K, ids, inv_pos, w, out_f32, out);
+    else
+        skinny_down_combine_kernel<16, 4><<<grid, 64 * waves, 0, stream>>>(a.dn, sdn, K, ids, inv_pos, w, out_f32, out);
     return hipGetLastError();
 }
 

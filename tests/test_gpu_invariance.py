@@ -148,7 +148,7 @@ def test_router_tiles_give_the_same_bits(name):
         assert torch.equal(a[: T - 1].view(torch.int32), b.view(torch.int32))
 
 
-@pytest.mark.parametrize("name", ["q30", "dsv4"])
+@pytest.mark.parametrize("name", ["q30", "dsv4", "qnext"])
 def test_single_token_down_and_combine_launch(name):
     """One token runs its experts' down projections and the combine in one
     launch; a batch of three runs them as separate launches.  The first token
